@@ -1,0 +1,283 @@
+"""Python binding of libnanochat.so, the MI355X training-step library for
+nanochat's dense GPT.
+
+Argument marshalling only: every function here forwards to the C entry point
+of the same name in ``include/nanochat.h``; all computation runs in the HIP
+kernels behind it. Device buffers are torch tensors (torch supplies device
+memory and streams, nothing else). There is no fallback: if the library is
+not built, or no GPU is present, the compute calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnanochat.so")
+
+NC_F32, NC_BF16 = 0, 1
+NC_OK = 0
+NC_ERR = {-1: "NC_ERR_INVALID_CONFIG", -2: "NC_ERR_UNSUPPORTED", -3: "NC_ERR_NULL",
+          -4: "NC_ERR_ALIGN", -5: "NC_ERR_WORKSPACE", -6: "NC_ERR_HIP", -7: "NC_ERR_ARG"}
+NC_STATUS_TOKEN_RANGE, NC_STATUS_TARGET_RANGE, NC_STATUS_NONFINITE_LOSS = 1, 2, 4
+EPI_STORE_T, EPI_STORE_F32, EPI_ADD_F32, EPI_RELU2, EPI_RELU2_BWD = 0, 1, 2, 3, 4
+
+
+class NcConfig(ctypes.Structure):
+    _fields_ = [("depth", ctypes.c_int32), ("vocab_size", ctypes.c_int32),
+                ("seq_len", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("n_kv_head", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("softcap", ctypes.c_float), ("rope_base", ctypes.c_float),
+                ("rms_eps", ctypes.c_float), ("init_std", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
+
+    def __repr__(self):
+        return ("NcConfig(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")")
+
+
+class NcTensorInfo(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("offset", ctypes.c_uint64),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class NcError(RuntimeError):
+    def __init__(self, code, func, hip=0):
+        self.code = code
+        super().__init__(f"{func} -> {NC_ERR.get(code, code)}"
+                         + (f" (hip error {hip})" if code == -6 else ""))
+
+
+_lib = None
+_P, _I32, _U64, _F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_float
+_CFG = ctypes.POINTER(NcConfig)
+_SIGS = {
+    "nc_config_from_depth": [_I32, _I32, _I32, _I32, _I32, _CFG],
+    "nc_validate_config": [_CFG],
+    "nc_param_count": [_CFG, ctypes.POINTER(_U64)],
+    "nc_param_layout": [_CFG, ctypes.POINTER(NcTensorInfo), _I32, ctypes.POINTER(_I32)],
+    "nc_workspace_bytes": [_CFG, _I32, ctypes.POINTER(_U64)],
+    "nc_token_losses_offset": [_CFG, _I32, ctypes.POINTER(_U64)],
+    "nc_init_params": [_U64, _CFG, _P, _P],
+    "nc_forward_loss": [_CFG, _P, _P, _P, _P, _U64, _P, _P],
+    "nc_forward_backward": [_CFG, _P, _P, _P, _P, _P, _U64, _P, _P],
+    "nc_read_device_status": [_P, ctypes.POINTER(ctypes.c_uint32), _P],
+    "nc_status_string": [ctypes.c_int],
+    "nc_last_hip_error": [],
+    "nc_op_gemm": [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P],
+    "nc_op_wgrad": [_I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P],
+    "nc_op_rmsnorm_fwd": [_I32, _P, _I32, _I32, _F32, _P, _P, _P],
+    "nc_op_rmsnorm_bwd": [_I32, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P],
+    "nc_op_rope_qknorm_fwd": [_I32, _P, _I32, _I32, _I32, _F32, _F32, _P, _P, _P],
+    "nc_op_rope_qknorm_bwd": [_I32, _P, _P, _I32, _I32, _I32, _P, _P, _P],
+    "nc_op_attn_fwd": [_I32, _P, _I32, _I32, _I32, _P, _P, _P],
+    "nc_op_attn_bwd": [_I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P],
+    "nc_op_softcap_ce": [_I32, _P, _P, _I32, _I32, _F32, _F32, _P, _P, _P, _P],
+}
+
+
+def lib():
+    """Loads the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_char_p if name == "nc_status_string" else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc, name):
+    if rc != NC_OK:
+        raise NcError(rc, name, lib().nc_last_hip_error())
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dt(dtype):
+    if isinstance(dtype, int):
+        return dtype              # passed through; the library rejects unknown codes
+    return {"f32": NC_F32, "bf16": NC_BF16}[dtype]
+
+
+# ---------------------------------------------------------------- host calls
+
+def nc_config_from_depth(depth, vocab_size, seq_len, batch, dtype="bf16") -> NcConfig:
+    cfg = NcConfig()
+    _check(lib().nc_config_from_depth(depth, vocab_size, seq_len, batch, _dt(dtype),
+                                      ctypes.byref(cfg)), "nc_config_from_depth")
+    return cfg
+
+
+def nc_validate_config(cfg) -> int:
+    return lib().nc_validate_config(ctypes.byref(cfg))
+
+
+def nc_param_count(cfg) -> int:
+    n = _U64()
+    _check(lib().nc_param_count(ctypes.byref(cfg), ctypes.byref(n)), "nc_param_count")
+    return n.value
+
+
+def nc_param_layout(cfg):
+    n = _I32()
+    _check(lib().nc_param_layout(ctypes.byref(cfg), None, 0, ctypes.byref(n)), "nc_param_layout")
+    arr = (NcTensorInfo * n.value)()
+    _check(lib().nc_param_layout(ctypes.byref(cfg), arr, n.value, ctypes.byref(n)), "nc_param_layout")
+    return [(t.name.decode(), int(t.offset), int(t.rows), int(t.cols)) for t in arr]
+
+
+def nc_workspace_bytes(cfg, with_backward=True) -> int:
+    n = _U64()
+    _check(lib().nc_workspace_bytes(ctypes.byref(cfg), int(with_backward), ctypes.byref(n)),
+           "nc_workspace_bytes")
+    return n.value
+
+
+def nc_token_losses_offset(cfg, with_backward=True) -> int:
+    n = _U64()
+    _check(lib().nc_token_losses_offset(ctypes.byref(cfg), int(with_backward), ctypes.byref(n)),
+           "nc_token_losses_offset")
+    return n.value
+
+
+def nc_status_string(code) -> str:
+    return lib().nc_status_string(code).decode()
+
+
+# ---------------------------------------------------------------- device calls
+
+def nc_init_params(seed, cfg, params, stream=None):
+    _check(lib().nc_init_params(seed, ctypes.byref(cfg), _ptr(params), _stream(stream)),
+           "nc_init_params")
+
+
+def nc_forward_loss(cfg, params, tokens, targets, ws, loss, stream=None):
+    _check(lib().nc_forward_loss(ctypes.byref(cfg), _ptr(params), _ptr(tokens), _ptr(targets),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _ptr(loss),
+                                 _stream(stream)), "nc_forward_loss")
+
+
+def nc_forward_backward(cfg, params, tokens, targets, grads, ws, loss, stream=None):
+    _check(lib().nc_forward_backward(ctypes.byref(cfg), _ptr(params), _ptr(tokens), _ptr(targets),
+                                     _ptr(grads), _ptr(ws), ws.numel() * ws.element_size(),
+                                     _ptr(loss), _stream(stream)), "nc_forward_backward")
+
+
+def nc_read_device_status(ws, stream=None) -> int:
+    f = ctypes.c_uint32()
+    _check(lib().nc_read_device_status(_ptr(ws), ctypes.byref(f), _stream(stream)),
+           "nc_read_device_status")
+    return f.value
+
+
+def nc_op_gemm(dtype, a_kcontig, b_kcontig, epilogue, A, B, C, C2, M, N, K, lda, ldb, ldc,
+               stream=None):
+    _check(lib().nc_op_gemm(_dt(dtype), int(a_kcontig), int(b_kcontig), epilogue, _ptr(A), _ptr(B),
+                            _ptr(C), _ptr(C2), M, N, K, lda, ldb, ldc, _stream(stream)), "nc_op_gemm")
+
+
+def nc_op_wgrad(dtype, X1, X2, dW, partial, M, N1, N2, splits, stream=None):
+    _check(lib().nc_op_wgrad(_dt(dtype), _ptr(X1), _ptr(X2), _ptr(dW), _ptr(partial), M, N1, N2,
+                             splits, _stream(stream)), "nc_op_wgrad")
+
+
+def nc_op_rmsnorm_fwd(dtype, x, M, d, eps, y, rinv, stream=None):
+    _check(lib().nc_op_rmsnorm_fwd(_dt(dtype), _ptr(x), M, d, eps, _ptr(y), _ptr(rinv),
+                                   _stream(stream)), "nc_op_rmsnorm_fwd")
+
+
+def nc_op_rmsnorm_bwd(dtype, dy, y, rinv, M, d, dx, accumulate, g, stream=None):
+    _check(lib().nc_op_rmsnorm_bwd(_dt(dtype), _ptr(dy), _ptr(y), _ptr(rinv), M, d, _ptr(dx),
+                                   int(accumulate), _ptr(g), _stream(stream)), "nc_op_rmsnorm_bwd")
+
+
+def nc_op_rope_qknorm_fwd(dtype, qkv, B, T, H, base, eps, rinv_qk, cs, stream=None):
+    _check(lib().nc_op_rope_qknorm_fwd(_dt(dtype), _ptr(qkv), B, T, H, base, eps, _ptr(rinv_qk),
+                                       _ptr(cs), _stream(stream)), "nc_op_rope_qknorm_fwd")
+
+
+def nc_op_rope_qknorm_bwd(dtype, dqkv, qkv, B, T, H, rinv_qk, cs, stream=None):
+    _check(lib().nc_op_rope_qknorm_bwd(_dt(dtype), _ptr(dqkv), _ptr(qkv), B, T, H, _ptr(rinv_qk),
+                                       _ptr(cs), _stream(stream)), "nc_op_rope_qknorm_bwd")
+
+
+def nc_op_attn_fwd(dtype, qkv, B, T, H, o, lse, stream=None):
+    _check(lib().nc_op_attn_fwd(_dt(dtype), _ptr(qkv), B, T, H, _ptr(o), _ptr(lse),
+                                _stream(stream)), "nc_op_attn_fwd")
+
+
+def nc_op_attn_bwd(dtype, qkv, o, dout, lse, delta, B, T, H, dqkv, stream=None):
+    _check(lib().nc_op_attn_bwd(_dt(dtype), _ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
+                                B, T, H, _ptr(dqkv), _stream(stream)), "nc_op_attn_bwd")
+
+
+def nc_op_softcap_ce(dtype, logits, targets, R, V, cap, w, loss_rows, dlogits, status, stream=None):
+    _check(lib().nc_op_softcap_ce(_dt(dtype), _ptr(logits), _ptr(targets), R, V, cap, w,
+                                  _ptr(loss_rows), _ptr(dlogits), _ptr(status), _stream(stream)),
+           "nc_op_softcap_ce")
+
+
+# ---------------------------------------------------------------- buffers
+
+class Step:
+    """Owns the torch-allocated device buffers of one training-step shape and
+    calls the library on them. ``params`` holds nc_param_count elements of the
+    config's dtype (bf16 as torch.bfloat16), ``grads`` the fp32 gradient."""
+
+    def __init__(self, cfg: NcConfig, device="cuda", with_backward=True):
+        import torch
+        self.cfg = cfg
+        self.device = torch.device(device)
+        n = nc_param_count(cfg)
+        pdt = torch.bfloat16 if cfg.dtype == NC_BF16 else torch.float32
+        self.params = torch.zeros(n, dtype=pdt, device=self.device)
+        self.grads = torch.zeros(n, dtype=torch.float32, device=self.device) if with_backward else None
+        self.ws = torch.empty(nc_workspace_bytes(cfg, with_backward), dtype=torch.uint8,
+                              device=self.device)
+        self.loss = torch.zeros(1, dtype=torch.float32, device=self.device)
+        self.with_backward = with_backward
+        self.layout = nc_param_layout(cfg)
+
+    def init(self, seed):
+        nc_init_params(seed, self.cfg, self.params)
+
+    def forward_loss(self, tokens, targets):
+        nc_forward_loss(self.cfg, self.params, tokens, targets, self.ws, self.loss)
+        return self.loss
+
+    def forward_backward(self, tokens, targets):
+        nc_forward_backward(self.cfg, self.params, tokens, targets, self.grads, self.ws, self.loss)
+        return self.loss
+
+    def token_losses(self):
+        import torch
+        off = nc_token_losses_offset(self.cfg, self.with_backward)
+        M = self.cfg.batch * self.cfg.seq_len
+        return self.ws[off:off + 4 * M].view(torch.float32).view(self.cfg.batch, self.cfg.seq_len)
+
+    def status(self):
+        return nc_read_device_status(self.ws)
+
+    def tensor(self, buf, name):
+        for n, off, r, c in self.layout:
+            if n == name:
+                return buf[off:off + r * c].view(r, c)
+        raise KeyError(name)

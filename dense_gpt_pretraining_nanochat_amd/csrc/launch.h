@@ -1,0 +1,93 @@
+// Host-side launch interface of the HIP kernels. Every function enqueues work
+// on `stream` and returns hipSuccess or the launch error; none allocates.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nc {
+
+enum class DType { F32 = 0, BF16 = 1 };
+
+// ---- GEMM: C[M,N] (op)= sum_k A(m,k) * B(n,k) ---------------------------
+// A(m,k) = a_kcontig ? A[m*lda + k] : A[k*lda + m]   (likewise for B)
+enum class Epi {
+  StoreT,      // C (element type T) = acc
+  StoreF32,    // C (float) = acc
+  AddF32,      // C (float) += acc
+  Relu2,       // C (T) = u = acc; C2 (T) = relu(u)^2  (u rounded to T first)
+  Relu2Bwd,    // C (T) = acc * 2 * relu(C2[m,n])       (C2 holds u, type T)
+  PartialF32,  // C (float) + split*M*ldc = acc over this split's K range
+};
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  void* C;
+  void* C2;
+  int M, N, K;
+  int lda, ldb, ldc, ldc2;
+  int splits;        // K slices (PartialF32 only); K % (splits * 64) == 0
+};
+hipError_t gemm(DType t, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs& g,
+                hipStream_t stream);
+// dst[i] (=|+=) sum_s part[s*n + i], s = 0..splits-1, in a fixed order.
+hipError_t splitk_reduce(const float* part, int splits, size_t n, float* dst, bool accumulate,
+                         hipStream_t stream);
+
+// ---- norms and embedding --------------------------------------------------
+// x[m,:] = n(E[tok[m],:]) (fp32), rinv[m]; ids outside [0,V) are clamped and flagged.
+hipError_t embed_norm_fwd(DType t, const void* E, const int32_t* tok, int M, int d, int V,
+                          float eps, float* x, float* rinv, uint32_t* status, hipStream_t s);
+// y[m,:] = n(x[m,:]) as T, rinv[m]
+hipError_t rmsnorm_fwd(DType t, const float* x, int M, int d, float eps, void* y, float* rinv,
+                       hipStream_t s);
+// dx[m,:] (=|+=) rinv*(dy - y*mean(dy*y)); optionally g = T(dx)
+hipError_t rmsnorm_bwd(DType t, const float* dy, const void* y, const float* rinv, int M, int d,
+                       float* dx, bool accumulate, void* g, hipStream_t s);
+// embedding-norm backward + deterministic scatter into dE (fp32, every row written)
+struct EmbedBwdScratch {
+  int32_t* counts;   // [V + 1]
+  int32_t* offsets;  // [V + 1]
+  int32_t* cursor;   // [V]
+  int32_t* list;     // [M]
+  float* de;         // [M, d]
+};
+hipError_t embed_bwd(DType t, const void* E, const int32_t* tok, const float* rinv0,
+                     const float* dx, int M, int d, int V, EmbedBwdScratch ws, float* dE,
+                     hipStream_t s);
+
+// ---- rotary + QK-norm -------------------------------------------------------
+hipError_t rope_table(int T, int half, double base, float* cs, hipStream_t s);  // [T, half] cos, then sin
+// in place on qkv[M, ldq]: H query heads at cols [0, H*128), the key head at [H*128, H*128+128)
+hipError_t rope_qknorm_fwd(DType t, void* qkv, int ldq, int M, int T, int H, const float* cs,
+                           float eps, float* rinv_qk, hipStream_t s);
+hipError_t rope_qknorm_bwd(DType t, void* dqkv, int ldd, const void* qkv, int ldq, int M, int T,
+                           int H, const float* cs, const float* rinv_qk, hipStream_t s);
+
+// ---- attention -------------------------------------------------------------
+// qkv: [B*T, ldq] with q heads, then k, then v (each 128 wide); o: [B*T, H*128]; lse: [B, H, T]
+hipError_t attn_fwd(DType t, const void* qkv, int ldq, int B, int T, int H, void* o, float* lse,
+                    hipStream_t s);
+// delta[b,h,t] = <dO, O>
+hipError_t attn_bwd_delta(DType t, const void* o, const void* dout, int B, int T, int H,
+                          float* delta, hipStream_t s);
+// writes dq into dqkv[:, 0:H*128], dk and dv into the next two 128-col blocks
+hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const float* lse,
+                    const float* delta, int B, int T, int H, void* dqkv, int ldd, hipStream_t s);
+
+// ---- cross-entropy -----------------------------------------------------------
+// rows of fp32 logits [R, V]: per-row loss (fp32) and dlogits (T) = (softmax(z)-onehot)*(1-(z/c)^2)*w
+hipError_t softcap_ce(DType t, const float* logits, const int32_t* tgt, int R, int V, float cap,
+                      float w, float* loss_rows, void* dlogits, uint32_t* status, hipStream_t s);
+hipError_t loss_mean(const float* loss_rows, int M, float* out, uint32_t* status, hipStream_t s);
+
+// ---- init and utilities -----------------------------------------------------
+struct InitSeg {
+  size_t begin, end;   // element range [begin, end)
+  double std;
+};
+hipError_t init_params(DType t, uint64_t seed, const InitSeg* segs, int nseg, size_t total,
+                       void* params, hipStream_t s);
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace nc

@@ -1,0 +1,599 @@
+// Host side of the library: config validation, the flat parameter layout, the
+// workspace plan and the kernel sequence of one training step. Stateless:
+// every buffer belongs to the caller and every launch goes on the caller's
+// stream. See include/nanochat.h for the contract of each entry point.
+#include "../../include/nanochat.h"
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "launch.h"
+
+using nc::DType;
+using nc::Epi;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+constexpr uint64_t kAlign = 256;
+
+inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+struct Dims {
+  int L, d, H, F, Q, V, T, B;
+  int64_t M;
+  size_t esz;   // bytes per element of dtype
+  DType dt;
+};
+
+int validate(const nc_config* c) {
+  if (!c) return NC_ERR_NULL;
+  if (c->n_kv_head != 1 || c->head_dim != 128) return NC_ERR_UNSUPPORTED;
+  if (c->depth < 2 || c->depth > 32) return NC_ERR_INVALID_CONFIG;
+  if (c->vocab_size < 128 || c->vocab_size > 65536 || c->vocab_size % 128) return NC_ERR_INVALID_CONFIG;
+  if (c->seq_len < 64 || c->seq_len % 64) return NC_ERR_INVALID_CONFIG;
+  if (c->batch < 1) return NC_ERR_INVALID_CONFIG;
+  if ((int64_t)c->batch * c->seq_len > (int64_t)1 << 30) return NC_ERR_INVALID_CONFIG;
+  if (!(c->softcap > 0.f) || !(c->rope_base > 1.f) || !(c->rms_eps >= 0.f) || !(c->init_std > 0.f))
+    return NC_ERR_INVALID_CONFIG;
+  if (c->dtype != NC_F32 && c->dtype != NC_BF16) return NC_ERR_INVALID_CONFIG;
+  return NC_OK;
+}
+
+Dims dims_of(const nc_config* c) {
+  Dims D;
+  D.L = c->depth;
+  D.d = 64 * c->depth;
+  D.H = D.d / 128;
+  D.F = 4 * D.d;
+  D.Q = D.d + 256;
+  D.V = c->vocab_size;
+  D.T = c->seq_len;
+  D.B = c->batch;
+  D.M = (int64_t)c->batch * c->seq_len;
+  D.dt = c->dtype == NC_BF16 ? DType::BF16 : DType::F32;
+  D.esz = c->dtype == NC_BF16 ? 2 : 4;
+  return D;
+}
+
+struct Tensor {
+  const char* kind;
+  int layer;
+  int64_t rows, cols;
+  uint64_t offset;
+};
+
+std::vector<Tensor> layout_of(const Dims& D) {
+  std::vector<Tensor> t;
+  uint64_t off = 0;
+  auto add = [&](const char* k, int l, int64_t r, int64_t c) {
+    t.push_back({k, l, r, c, off});
+    off = align_up(off + (uint64_t)(r * c), 128);
+  };
+  add("E", -1, D.V, D.d);
+  for (int l = 0; l < D.L; ++l) {
+    add("Wqkv", l, D.Q, D.d);
+    add("Wo", l, D.d, D.d);
+    add("Wfc", l, D.F, D.d);
+    add("Wpr", l, D.d, D.F);
+  }
+  add("U", -1, D.V, D.d);
+  return t;
+}
+
+uint64_t param_elems(const Dims& D) {
+  const auto t = layout_of(D);
+  return align_up(t.back().offset + (uint64_t)(t.back().rows * t.back().cols), 128);
+}
+
+// lm_head rows processed per chunk: bounds the fp32 logits buffer at
+// Mc * V * 4 bytes (2 GiB at V = 65,536).
+int64_t chunk_rows(const Dims& D) { return std::min<int64_t>(D.M, 8192); }
+
+// split-K factor for a weight gradient with `tiles` 128x128 output tiles and
+// contraction length K: aim for >= 1024 workgroups.
+int wgrad_splits(int64_t tiles, int64_t K) {
+  int s = 1;
+  while (s < 16 && tiles * s < 1024 && K % (64 * (2 * s)) == 0) s *= 2;
+  return s;
+}
+
+int64_t tiles_of(int64_t n1, int64_t n2) { return ((n1 + 127) / 128) * ((n2 + 127) / 128); }
+
+struct LayerActs {
+  uint64_t h, rinv1, qkv, rqk, o, lse, h2, rinv2, u, a;
+};
+
+struct Plan {
+  uint64_t status, cs, x, rinv0, xf, rinvf, loss_rows, logits, dlog;
+  std::vector<LayerActs> acts;
+  // backward only
+  uint64_t dx, g, dh, dbig, dout, delta, partial, counts, offsets, cursor, list;
+  uint64_t total;
+};
+
+Plan plan_of(const Dims& D, bool bwd) {
+  Plan p{};
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t o = off;
+    off = align_up(off + std::max<uint64_t>(bytes, 1), kAlign);
+    return o;
+  };
+  const uint64_t M = D.M, e = D.esz;
+  const uint64_t Mc = chunk_rows(D);
+  p.status = take(256);
+  p.cs = take((uint64_t)D.T * 64 * 2 * 4);
+  p.x = take(M * D.d * 4);
+  p.rinv0 = take(M * 4);
+  p.xf = take(M * D.d * e);
+  p.rinvf = take(M * 4);
+  p.loss_rows = take(M * 4);
+  p.logits = take(Mc * D.V * 4);
+  p.dlog = take(Mc * D.V * e);
+  const int nsets = bwd ? D.L : 1;
+  for (int l = 0; l < nsets; ++l) {
+    LayerActs a;
+    a.h = take(M * D.d * e);
+    a.rinv1 = take(M * 4);
+    a.qkv = take(M * D.Q * e);
+    a.rqk = take(M * (D.H + 1) * 4);
+    a.o = take(M * D.d * e);
+    a.lse = take(M * D.H * 4);
+    a.h2 = take(M * D.d * e);
+    a.rinv2 = take(M * 4);
+    a.u = take(M * D.F * e);
+    a.a = take(M * D.F * e);
+    p.acts.push_back(a);
+  }
+  if (bwd) {
+    p.dx = take(M * D.d * 4);
+    p.g = take(M * D.d * e);
+    p.dh = take(M * D.d * 4);
+    p.dbig = take(M * std::max(D.F, D.Q) * e);
+    p.dout = take(M * D.d * e);
+    p.delta = take(M * D.H * 4);
+    uint64_t part = 0;
+    const int64_t shapes[4][2] = {{D.Q, D.d}, {D.d, D.d}, {D.F, D.d}, {D.d, D.F}};
+    for (auto& s : shapes) {
+      const int sp = wgrad_splits(tiles_of(s[0], s[1]), D.M);
+      if (sp > 1) part = std::max<uint64_t>(part, (uint64_t)sp * s[0] * s[1] * 4);
+    }
+    p.partial = take(part);
+    p.counts = take((uint64_t)(D.V + 1) * 4);
+    p.offsets = take((uint64_t)(D.V + 1) * 4);
+    p.cursor = take((uint64_t)D.V * 4);
+    p.list = take(M * 4);
+  }
+  p.total = off;
+  return p;
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p) % kAlign != 0; }
+
+#define HIPCHECK(expr)                          \
+  do {                                          \
+    hipError_t _e = (expr);                     \
+    if (_e != hipSuccess) {                     \
+      g_last_hip = (int)_e;                     \
+      return NC_ERR_HIP;                        \
+    }                                           \
+  } while (0)
+
+template <typename P>
+P* at(void* base, uint64_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(base) + off);
+}
+
+// dW[N1,N2] = X1^T X2 over M rows
+hipError_t wgrad(DType dt, const void* X1, const void* X2, float* dW, float* partial, int64_t M,
+                 int N1, int N2, int splits, hipStream_t s) {
+  nc::GemmArgs g{};
+  g.A = X1;
+  g.B = X2;
+  g.M = N1;
+  g.N = N2;
+  g.K = (int)M;
+  g.lda = N1;
+  g.ldb = N2;
+  g.ldc = N2;
+  g.splits = splits;
+  if (splits == 1) {
+    g.C = dW;
+    return nc::gemm(dt, false, false, Epi::StoreF32, g, s);
+  }
+  g.C = partial;
+  hipError_t e = nc::gemm(dt, false, false, Epi::PartialF32, g, s);
+  if (e != hipSuccess) return e;
+  return nc::splitk_reduce(partial, splits, (size_t)N1 * N2, dW, false, s);
+}
+
+hipError_t gemm_simple(DType dt, bool ak, bool bk, Epi epi, const void* A, const void* B, void* C,
+                       void* C2, int64_t M, int N, int K, int lda, int ldb, int ldc, int ldc2,
+                       hipStream_t s) {
+  nc::GemmArgs g{};
+  g.A = A;
+  g.B = B;
+  g.C = C;
+  g.C2 = C2;
+  g.M = (int)M;
+  g.N = N;
+  g.K = K;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.ldc = ldc;
+  g.ldc2 = ldc2;
+  g.splits = 1;
+  return nc::gemm(dt, ak, bk, epi, g, s);
+}
+
+int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
+             const int32_t* targets, float* grads, void* ws, uint64_t ws_bytes, float* loss_dev,
+             void* stream, bool bwd) {
+  int rc = validate(cfg);
+  if (rc) return rc;
+  if (!params || !tokens || !targets || !ws || !loss_dev || (bwd && !grads)) return NC_ERR_NULL;
+  if (misaligned(params) || misaligned(tokens) || misaligned(targets) || misaligned(ws) ||
+      misaligned(loss_dev) || (bwd && misaligned(grads)))
+    return NC_ERR_ALIGN;
+  const Dims D = dims_of(cfg);
+  const Plan P = plan_of(D, bwd);
+  if (ws_bytes < P.total) return NC_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const DType dt = D.dt;
+  const size_t e = D.esz;
+  const auto lay = layout_of(D);
+  auto W = [&](int idx) { return static_cast<const char*>(params) + lay[idx].offset * e; };
+  auto G = [&](int idx) { return grads + lay[idx].offset; };
+  const int iE = 0, iU = 1 + 4 * D.L;
+  const int64_t M = D.M;
+  const float eps = cfg->rms_eps;
+
+  uint32_t* status = at<uint32_t>(ws, P.status);
+  float* cs = at<float>(ws, P.cs);
+  float* x = at<float>(ws, P.x);
+  float* rinv0 = at<float>(ws, P.rinv0);
+  void* xf = at<char>(ws, P.xf);
+  float* rinvf = at<float>(ws, P.rinvf);
+  float* loss_rows = at<float>(ws, P.loss_rows);
+  float* logits = at<float>(ws, P.logits);
+  void* dlog = at<char>(ws, P.dlog);
+
+  HIPCHECK(nc::fill_zero(status, 256, s));
+  HIPCHECK(nc::rope_table(D.T, 64, (double)cfg->rope_base, cs, s));
+  HIPCHECK(nc::embed_norm_fwd(dt, W(iE), tokens, (int)M, D.d, D.V, eps, x, rinv0, status, s));
+
+  // ---------------- forward through the blocks ----------------
+  for (int l = 0; l < D.L; ++l) {
+    const LayerActs& A = P.acts[bwd ? l : 0];
+    void* h = at<char>(ws, A.h);
+    void* qkv = at<char>(ws, A.qkv);
+    void* o = at<char>(ws, A.o);
+    void* h2 = at<char>(ws, A.h2);
+    void* u = at<char>(ws, A.u);
+    void* a = at<char>(ws, A.a);
+    const int base = 1 + 4 * l;
+    HIPCHECK(nc::rmsnorm_fwd(dt, x, (int)M, D.d, eps, h, at<float>(ws, A.rinv1), s));
+    HIPCHECK(gemm_simple(dt, true, true, Epi::StoreT, h, W(base + 0), qkv, nullptr, M, D.Q, D.d,
+                         D.d, D.d, D.Q, 0, s));
+    HIPCHECK(nc::rope_qknorm_fwd(dt, qkv, D.Q, (int)M, D.T, D.H, cs, eps, at<float>(ws, A.rqk), s));
+    HIPCHECK(nc::attn_fwd(dt, qkv, D.Q, D.B, D.T, D.H, o, at<float>(ws, A.lse), s));
+    HIPCHECK(gemm_simple(dt, true, true, Epi::AddF32, o, W(base + 1), x, nullptr, M, D.d, D.d,
+                         D.d, D.d, D.d, 0, s));
+    HIPCHECK(nc::rmsnorm_fwd(dt, x, (int)M, D.d, eps, h2, at<float>(ws, A.rinv2), s));
+    HIPCHECK(gemm_simple(dt, true, true, Epi::Relu2, h2, W(base + 2), u, a, M, D.F, D.d, D.d,
+                         D.d, D.F, D.F, s));
+    HIPCHECK(gemm_simple(dt, true, true, Epi::AddF32, a, W(base + 3), x, nullptr, M, D.d, D.F,
+                         D.F, D.F, D.d, 0, s));
+  }
+  HIPCHECK(nc::rmsnorm_fwd(dt, x, (int)M, D.d, eps, xf, rinvf, s));
+
+  // ---------------- lm_head + softcap cross-entropy, by row chunks ----------------
+  const int64_t Mc = chunk_rows(D);
+  float* dxf = bwd ? at<float>(ws, P.dh) : nullptr;
+  const float w = 1.0f / (float)M;
+  for (int64_t r0 = 0; r0 < M; r0 += Mc) {
+    const int64_t mc = std::min<int64_t>(Mc, M - r0);
+    const char* xfc = static_cast<const char*>(xf) + r0 * D.d * e;
+    HIPCHECK(gemm_simple(dt, true, true, Epi::StoreF32, xfc, W(iU), logits, nullptr, mc, D.V,
+                         D.d, D.d, D.d, D.V, 0, s));
+    HIPCHECK(nc::softcap_ce(dt, logits, targets + r0, (int)mc, D.V, cfg->softcap, w,
+                            loss_rows + r0, bwd ? dlog : nullptr, status, s));
+    if (bwd) {
+      // dxf = dlog . U ; dU (+)= dlog^T . xf
+      HIPCHECK(gemm_simple(dt, true, false, Epi::StoreF32, dlog, W(iU), dxf + r0 * D.d, nullptr,
+                           mc, D.d, D.V, D.V, D.d, D.d, 0, s));
+      HIPCHECK(gemm_simple(dt, false, false, r0 == 0 ? Epi::StoreF32 : Epi::AddF32, dlog, xfc,
+                           G(iU), nullptr, D.V, D.d, (int)mc, D.V, D.d, D.d, 0, s));
+    }
+  }
+  HIPCHECK(nc::loss_mean(loss_rows, (int)M, loss_dev, status, s));
+  if (!bwd) return NC_OK;
+
+  // ---------------- backward ----------------
+  float* dx = at<float>(ws, P.dx);
+  void* g = at<char>(ws, P.g);
+  float* dh = at<float>(ws, P.dh);
+  void* dbig = at<char>(ws, P.dbig);
+  void* dout = at<char>(ws, P.dout);
+  float* delta = at<float>(ws, P.delta);
+  float* partial = at<float>(ws, P.partial);
+  HIPCHECK(nc::rmsnorm_bwd(dt, dxf, xf, rinvf, (int)M, D.d, dx, false, g, s));
+  const int sQ = wgrad_splits(tiles_of(D.Q, D.d), M), sO = wgrad_splits(tiles_of(D.d, D.d), M);
+  const int sFC = wgrad_splits(tiles_of(D.F, D.d), M), sPR = wgrad_splits(tiles_of(D.d, D.F), M);
+  for (int l = D.L - 1; l >= 0; --l) {
+    const LayerActs& A = P.acts[l];
+    const int base = 1 + 4 * l;
+    void* h = at<char>(ws, A.h);
+    void* qkv = at<char>(ws, A.qkv);
+    void* o = at<char>(ws, A.o);
+    void* h2 = at<char>(ws, A.h2);
+    void* u = at<char>(ws, A.u);
+    void* a = at<char>(ws, A.a);
+    // MLP: x_out = x_mid + relu(h2 Wfc^T)^2 Wpr^T
+    HIPCHECK(wgrad(dt, g, a, G(base + 3), partial, M, D.d, D.F, sPR, s));
+    HIPCHECK(gemm_simple(dt, true, false, Epi::Relu2Bwd, g, W(base + 3), dbig, u, M, D.F, D.d,
+                         D.d, D.F, D.F, D.F, s));
+    HIPCHECK(wgrad(dt, dbig, h2, G(base + 2), partial, M, D.F, D.d, sFC, s));
+    HIPCHECK(gemm_simple(dt, true, false, Epi::StoreF32, dbig, W(base + 2), dh, nullptr, M, D.d,
+                         D.F, D.F, D.d, D.d, 0, s));
+    HIPCHECK(nc::rmsnorm_bwd(dt, dh, h2, at<float>(ws, A.rinv2), (int)M, D.d, dx, true, g, s));
+    // attention: x_mid = x_in + o Wo^T
+    HIPCHECK(wgrad(dt, g, o, G(base + 1), partial, M, D.d, D.d, sO, s));
+    HIPCHECK(gemm_simple(dt, true, false, Epi::StoreT, g, W(base + 1), dout, nullptr, M, D.d, D.d,
+                         D.d, D.d, D.d, 0, s));
+    HIPCHECK(nc::attn_bwd_delta(dt, o, dout, D.B, D.T, D.H, delta, s));
+    HIPCHECK(nc::attn_bwd(dt, qkv, D.Q, dout, at<float>(ws, A.lse), delta, D.B, D.T, D.H, dbig,
+                          D.Q, s));
+    HIPCHECK(nc::rope_qknorm_bwd(dt, dbig, D.Q, qkv, D.Q, (int)M, D.T, D.H, cs,
+                                 at<float>(ws, A.rqk), s));
+    HIPCHECK(wgrad(dt, dbig, h, G(base + 0), partial, M, D.Q, D.d, sQ, s));
+    HIPCHECK(gemm_simple(dt, true, false, Epi::StoreF32, dbig, W(base + 0), dh, nullptr, M, D.d,
+                         D.Q, D.Q, D.d, D.d, 0, s));
+    HIPCHECK(nc::rmsnorm_bwd(dt, dh, h, at<float>(ws, A.rinv1), (int)M, D.d, dx, true, g, s));
+  }
+  nc::EmbedBwdScratch es;
+  es.counts = at<int32_t>(ws, P.counts);
+  es.offsets = at<int32_t>(ws, P.offsets);
+  es.cursor = at<int32_t>(ws, P.cursor);
+  es.list = at<int32_t>(ws, P.list);
+  es.de = dh;
+  HIPCHECK(nc::embed_bwd(dt, W(iE), tokens, rinv0, dx, (int)M, D.d, D.V, es, G(iE), s));
+  return NC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nc_config_from_depth(int32_t depth, int32_t vocab_size, int32_t seq_len, int32_t batch,
+                         int32_t dtype, nc_config* out) {
+  if (!out) return NC_ERR_NULL;
+  nc_config c;
+  c.depth = depth;
+  c.vocab_size = vocab_size;
+  c.seq_len = seq_len;
+  c.batch = batch;
+  c.n_kv_head = 1;
+  c.head_dim = 128;
+  c.softcap = 15.0f;
+  c.rope_base = 10000.0f;
+  c.rms_eps = 1e-6f;
+  c.init_std = 0.02f;
+  c.dtype = dtype;
+  const int rc = validate(&c);
+  if (rc) return rc;
+  *out = c;
+  return NC_OK;
+}
+
+int nc_validate_config(const nc_config* cfg) { return validate(cfg); }
+
+int nc_param_count(const nc_config* cfg, uint64_t* n) {
+  const int rc = validate(cfg);
+  if (rc) return rc;
+  if (!n) return NC_ERR_NULL;
+  *n = param_elems(dims_of(cfg));
+  return NC_OK;
+}
+
+int nc_param_layout(const nc_config* cfg, nc_tensor_info* out, int32_t cap, int32_t* n) {
+  const int rc = validate(cfg);
+  if (rc) return rc;
+  if (!n || (cap > 0 && !out)) return NC_ERR_NULL;
+  const auto t = layout_of(dims_of(cfg));
+  *n = (int32_t)t.size();
+  for (int i = 0; i < (int)t.size() && i < cap; ++i) {
+    memset(out[i].name, 0, sizeof(out[i].name));
+    if (t[i].layer < 0) snprintf(out[i].name, sizeof(out[i].name), "%s", t[i].kind);
+    else snprintf(out[i].name, sizeof(out[i].name), "h%d.%s", t[i].layer, t[i].kind);
+    out[i].offset = t[i].offset;
+    out[i].rows = t[i].rows;
+    out[i].cols = t[i].cols;
+  }
+  return NC_OK;
+}
+
+int nc_workspace_bytes(const nc_config* cfg, int32_t with_backward, uint64_t* bytes) {
+  const int rc = validate(cfg);
+  if (rc) return rc;
+  if (!bytes) return NC_ERR_NULL;
+  *bytes = plan_of(dims_of(cfg), with_backward != 0).total;
+  return NC_OK;
+}
+
+int nc_token_losses_offset(const nc_config* cfg, int32_t with_backward, uint64_t* byte_offset) {
+  const int rc = validate(cfg);
+  if (rc) return rc;
+  if (!byte_offset) return NC_ERR_NULL;
+  *byte_offset = plan_of(dims_of(cfg), with_backward != 0).loss_rows;
+  return NC_OK;
+}
+
+int nc_init_params(uint64_t seed, const nc_config* cfg, void* params, void* stream) {
+  const int rc = validate(cfg);
+  if (rc) return rc;
+  if (!params) return NC_ERR_NULL;
+  if (misaligned(params)) return NC_ERR_ALIGN;
+  const Dims D = dims_of(cfg);
+  const auto lay = layout_of(D);
+  std::vector<nc::InitSeg> segs;
+  const double base = (double)cfg->init_std;
+  const double proj = 1.0 / sqrt(2.0 * (double)D.L);
+  for (const auto& t : lay) {
+    const bool is_proj = !strcmp(t.kind, "Wo") || !strcmp(t.kind, "Wpr");
+    segs.push_back({t.offset, t.offset + (uint64_t)(t.rows * t.cols), base * (is_proj ? proj : 1.0)});
+  }
+  HIPCHECK(nc::init_params(D.dt, seed, segs.data(), (int)segs.size(), param_elems(D), params,
+                           static_cast<hipStream_t>(stream)));
+  return NC_OK;
+}
+
+int nc_forward_loss(const nc_config* cfg, const void* params, const int32_t* tokens,
+                    const int32_t* targets, void* ws, uint64_t ws_bytes, float* loss_dev,
+                    void* stream) {
+  return run_step(cfg, params, tokens, targets, nullptr, ws, ws_bytes, loss_dev, stream, false);
+}
+
+int nc_forward_backward(const nc_config* cfg, const void* params, const int32_t* tokens,
+                        const int32_t* targets, float* grads, void* ws, uint64_t ws_bytes,
+                        float* loss_dev, void* stream) {
+  return run_step(cfg, params, tokens, targets, grads, ws, ws_bytes, loss_dev, stream, true);
+}
+
+int nc_read_device_status(const void* ws, uint32_t* flags, void* stream) {
+  if (!ws || !flags) return NC_ERR_NULL;
+  if (misaligned(ws)) return NC_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HIPCHECK(hipMemcpyAsync(flags, ws, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+  HIPCHECK(hipStreamSynchronize(s));
+  return NC_OK;
+}
+
+const char* nc_status_string(int code) {
+  switch (code) {
+    case NC_OK: return "ok";
+    case NC_ERR_INVALID_CONFIG: return "invalid config";
+    case NC_ERR_UNSUPPORTED: return "unsupported config (n_kv_head must be 1, head_dim 128)";
+    case NC_ERR_NULL: return "null pointer";
+    case NC_ERR_ALIGN: return "device pointer not 256-byte aligned";
+    case NC_ERR_WORKSPACE: return "workspace too small";
+    case NC_ERR_HIP: return "HIP launch or runtime error";
+    case NC_ERR_ARG: return "argument out of range";
+    default: return "unknown status";
+  }
+}
+
+int nc_last_hip_error(void) { return g_last_hip; }
+
+// ---------------- single-step entry points ----------------
+
+static bool bad_dtype(int32_t t) { return t != NC_F32 && t != NC_BF16; }
+static DType dt_of(int32_t t) { return t == NC_BF16 ? DType::BF16 : DType::F32; }
+
+int nc_op_gemm(int32_t dtype, int32_t a_kcontig, int32_t b_kcontig, int32_t epilogue,
+               const void* A, const void* B, void* C, void* C2, int32_t M, int32_t N, int32_t K,
+               int32_t lda, int32_t ldb, int32_t ldc, void* stream) {
+  if (bad_dtype(dtype) || epilogue < 0 || epilogue > 4) return NC_ERR_ARG;
+  if (!A || !B || !C || ((epilogue == 3 || epilogue == 4) && !C2)) return NC_ERR_NULL;
+  if (M <= 0 || N <= 0 || K <= 0 || M % 16 || N % 16 || K % 64) return NC_ERR_ARG;
+  const int vec = dtype == NC_BF16 ? 8 : 4;
+  if (lda % vec || ldb % vec || ldc % 4) return NC_ERR_ARG;
+  if (lda < (a_kcontig ? K : M) || ldb < (b_kcontig ? K : N) || ldc < N) return NC_ERR_ARG;
+  static const Epi map[5] = {Epi::StoreT, Epi::StoreF32, Epi::AddF32, Epi::Relu2, Epi::Relu2Bwd};
+  HIPCHECK(gemm_simple(dt_of(dtype), a_kcontig != 0, b_kcontig != 0, map[epilogue], A, B, C, C2, M,
+                       N, K, lda, ldb, ldc, ldc, static_cast<hipStream_t>(stream)));
+  return NC_OK;
+}
+
+int nc_op_wgrad(int32_t dtype, const void* X1, const void* X2, float* dW, float* partial,
+                int32_t M, int32_t N1, int32_t N2, int32_t splits, void* stream) {
+  if (bad_dtype(dtype)) return NC_ERR_ARG;
+  if (!X1 || !X2 || !dW || (splits > 1 && !partial)) return NC_ERR_NULL;
+  if (M <= 0 || N1 <= 0 || N2 <= 0 || N1 % 16 || N2 % 16 || splits < 1 || M % (64 * splits))
+    return NC_ERR_ARG;
+  HIPCHECK(wgrad(dt_of(dtype), X1, X2, dW, partial, M, N1, N2, splits,
+                 static_cast<hipStream_t>(stream)));
+  return NC_OK;
+}
+
+int nc_op_rmsnorm_fwd(int32_t dtype, const float* x, int32_t M, int32_t d, float eps, void* y,
+                      float* rinv, void* stream) {
+  if (bad_dtype(dtype)) return NC_ERR_ARG;
+  if (!x || !y || !rinv) return NC_ERR_NULL;
+  if (M <= 0 || d <= 0 || d % 64 || d > 2048) return NC_ERR_ARG;
+  HIPCHECK(nc::rmsnorm_fwd(dt_of(dtype), x, M, d, eps, y, rinv, static_cast<hipStream_t>(stream)));
+  return NC_OK;
+}
+
+int nc_op_rmsnorm_bwd(int32_t dtype, const float* dy, const void* y, const float* rinv, int32_t M,
+                      int32_t d, float* dx, int32_t accumulate, void* g, void* stream) {
+  if (bad_dtype(dtype)) return NC_ERR_ARG;
+  if (!dy || !y || !rinv || !dx) return NC_ERR_NULL;
+  if (M <= 0 || d <= 0 || d % 64 || d > 2048) return NC_ERR_ARG;
+  HIPCHECK(nc::rmsnorm_bwd(dt_of(dtype), dy, y, rinv, M, d, dx, accumulate != 0, g,
+                           static_cast<hipStream_t>(stream)));
+  return NC_OK;
+}
+
+int nc_op_rope_qknorm_fwd(int32_t dtype, void* qkv, int32_t B, int32_t T, int32_t H, float base,
+                          float eps, float* rinv_qk, float* cs, void* stream) {
+  if (bad_dtype(dtype)) return NC_ERR_ARG;
+  if (!qkv || !rinv_qk || !cs) return NC_ERR_NULL;
+  if (B <= 0 || T <= 0 || H < 1 || H > 16) return NC_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  HIPCHECK(nc::rope_table(T, 64, (double)base, cs, s));
+  HIPCHECK(nc::rope_qknorm_fwd(dt_of(dtype), qkv, H * 128 + 256, B * T, T, H, cs, eps, rinv_qk, s));
+  return NC_OK;
+}
+
+int nc_op_rope_qknorm_bwd(int32_t dtype, void* dqkv, const void* qkv, int32_t B, int32_t T,
+                          int32_t H, const float* rinv_qk, const float* cs, void* stream) {
+  if (bad_dtype(dtype)) return NC_ERR_ARG;
+  if (!dqkv || !qkv || !rinv_qk || !cs) return NC_ERR_NULL;
+  if (B <= 0 || T <= 0 || H < 1 || H > 16) return NC_ERR_ARG;
+  const int ld = H * 128 + 256;
+  HIPCHECK(nc::rope_qknorm_bwd(dt_of(dtype), dqkv, ld, qkv, ld, B * T, T, H, cs, rinv_qk,
+                               static_cast<hipStream_t>(stream)));
+  return NC_OK;
+}
+
+int nc_op_attn_fwd(int32_t dtype, const void* qkv, int32_t B, int32_t T, int32_t H, void* o,
+                   float* lse, void* stream) {
+  if (bad_dtype(dtype)) return NC_ERR_ARG;
+  if (!qkv || !o || !lse) return NC_ERR_NULL;
+  if (B <= 0 || T < 64 || T % 64 || H < 1 || H > 16) return NC_ERR_ARG;
+  HIPCHECK(nc::attn_fwd(dt_of(dtype), qkv, H * 128 + 256, B, T, H, o, lse,
+                        static_cast<hipStream_t>(stream)));
+  return NC_OK;
+}
+
+int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* dout,
+                   const float* lse, float* delta, int32_t B, int32_t T, int32_t H, void* dqkv,
+                   void* stream) {
+  if (bad_dtype(dtype)) return NC_ERR_ARG;
+  if (!qkv || !o || !dout || !lse || !delta || !dqkv) return NC_ERR_NULL;
+  if (B <= 0 || T < 64 || T % 64 || H < 1 || H > 16) return NC_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int ld = H * 128 + 256;
+  HIPCHECK(nc::attn_bwd_delta(dt_of(dtype), o, dout, B, T, H, delta, s));
+  HIPCHECK(nc::attn_bwd(dt_of(dtype), qkv, ld, dout, lse, delta, B, T, H, dqkv, ld, s));
+  return NC_OK;
+}
+
+int nc_op_softcap_ce(int32_t dtype, const float* logits, const int32_t* targets, int32_t R,
+                     int32_t V, float cap, float w, float* loss_rows, void* dlogits,
+                     uint32_t* status, void* stream) {
+  if (bad_dtype(dtype)) return NC_ERR_ARG;
+  if (!logits || !targets || !loss_rows || !status) return NC_ERR_NULL;
+  if (R <= 0 || V <= 0 || V % 4 || V > 65536 || !(cap > 0.f)) return NC_ERR_ARG;
+  HIPCHECK(nc::softcap_ce(dt_of(dtype), logits, targets, R, V, cap, w, loss_rows, dlogits, status,
+                          static_cast<hipStream_t>(stream)));
+  return NC_OK;
+}
+
+}  // extern "C"

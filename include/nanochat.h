@@ -1,0 +1,206 @@
+/*
+ * nanochat.h — C ABI of the MI355X (gfx950) training-step library for
+ * nanochat's depth-parameterised dense GPT.
+ *
+ * What the step computes (pages cited by title and section):
+ *   - untied token embedding E[V,d] and lm_head U[V,d]; RMSNorm (no learnable
+ *     parameters) after the embedding, before each attention and MLP block,
+ *     and before lm_head; bias-free linear layers; rotary position embedding
+ *     with QK-norm; causal multi-query attention (all query heads share one
+ *     K/V head); relu^2 MLP; tanh logit softcap
+ *       (followin.io release article, section "純手寫 8000 行代碼，
+ *        “Agent 幫不上忙”", architecture list);
+ *   - width = 64 * depth, 128-dim heads, 4x MLP, context 2048 at depth 20
+ *       (wmrh.cn tutorial, section 2.2; vnrom.net "nanochat: khung thử
+ *        nghiệm…", section "Thiết kế depth-only scaling");
+ *   - vocabulary of 65,536 ids (wmrh.cn tutorial, section 2.1);
+ *   - next-token cross-entropy, averaged over all B*T positions
+ *       (wmrh.cn tutorial, section 2.3);
+ *   - bf16 or fp32 parameters and activations, chosen explicitly
+ *       (vnrom.net, section "Cấu trúc thư mục và module chính": precision is
+ *        set by hand, no autocast). Accumulation is always fp32; the residual
+ *        stream and its gradient are fp32 in both modes.
+ *
+ * Conventions the pages leave open are fixed as: RMSNorm eps = 1e-6; rotary
+ * on half-split pairs (j, j+64) with angle t * base^(-2j/128), base 10000,
+ * applied before the QK RMSNorm; attention scale 1/sqrt(128); softcap
+ * z = c*tanh(l/c), c = 15; natural-log loss.
+ *
+ * Memory and ownership: the caller owns every device buffer (params, grads,
+ * tokens, targets, workspace, loss). The library never allocates or frees
+ * device memory and keeps no state between calls; two calls may run
+ * concurrently only with distinct workspaces. All device pointers must be
+ * 256-byte aligned. `stream` is a hipStream_t (NULL = the default stream);
+ * every device-side effect is enqueued on it and the call returns before the
+ * work completes.
+ *
+ * Errors: every function returns NC_OK (0) or a negative NC_ERR_* code. The
+ * checks on arguments happen on the host before anything is enqueued; a
+ * failed check enqueues nothing. NC_ERR_HIP means a launch failed; the HIP
+ * error code is kept per thread (nc_last_hip_error). Problems only visible on
+ * the device (a token or target id outside [0, V), which the kernels clamp to
+ * stay in bounds, or a non-finite loss) set bits in a status word inside the
+ * workspace, read with nc_read_device_status. Nothing throws across the ABI.
+ */
+#ifndef NANOCHAT_H_
+#define NANOCHAT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ------------------------------------------------------- */
+#define NC_OK 0
+#define NC_ERR_INVALID_CONFIG (-1) /* a config field out of range            */
+#define NC_ERR_UNSUPPORTED (-2)    /* n_kv_head != 1 or head_dim != 128       */
+#define NC_ERR_NULL (-3)           /* a required pointer is NULL              */
+#define NC_ERR_ALIGN (-4)          /* a device pointer is not 256-B aligned   */
+#define NC_ERR_WORKSPACE (-5)      /* ws_bytes below nc_workspace_bytes       */
+#define NC_ERR_HIP (-6)            /* a HIP launch or runtime call failed     */
+#define NC_ERR_ARG (-7)            /* another argument is out of range        */
+
+/* ---- device status bits (nc_read_device_status) ------------------------- */
+#define NC_STATUS_TOKEN_RANGE 1u    /* a token id was outside [0, V)          */
+#define NC_STATUS_TARGET_RANGE 2u   /* a target id was outside [0, V)         */
+#define NC_STATUS_NONFINITE_LOSS 4u /* the mean loss is NaN or infinite       */
+
+typedef enum { NC_F32 = 0, NC_BF16 = 1 } nc_dtype;
+
+/* Model and batch shape. Derived sizes: d = 64*depth, H = d/128 query heads,
+ * F = 4*d, one K/V head, M = batch*seq_len tokens per call. */
+typedef struct {
+  int32_t depth;      /* L, 2..32 (so H <= 16)                                 */
+  int32_t vocab_size; /* V, multiple of 128, 128..65536                        */
+  int32_t seq_len;    /* T, multiple of 64, >= 64                              */
+  int32_t batch;      /* B >= 1                                                */
+  int32_t n_kv_head;  /* must be 1 (multi-query attention)                     */
+  int32_t head_dim;   /* must be 128                                           */
+  float softcap;      /* c > 0; 15 in every workload                           */
+  float rope_base;    /* > 1; 10000                                            */
+  float rms_eps;      /* >= 0; 1e-6                                            */
+  float init_std;     /* > 0; 0.02 (used by nc_init_params)                    */
+  int32_t dtype;      /* nc_dtype of params and activations                    */
+} nc_config;
+
+/* One parameter tensor: [rows, cols] row-major ([out, in]: y = x W^T),
+ * starting `offset` elements into the flat parameter buffer. */
+typedef struct {
+  char name[32];
+  uint64_t offset;
+  int64_t rows, cols;
+} nc_tensor_info;
+
+/* Fills *out with the shape implied by depth (width 64*depth, 128-dim heads,
+ * one K/V head, softcap 15, rope base 10000, eps 1e-6, init std 0.02) and
+ * validates it. Host only. */
+int nc_config_from_depth(int32_t depth, int32_t vocab_size, int32_t seq_len, int32_t batch,
+                         int32_t dtype, nc_config* out);
+
+/* NC_OK if the config is supported, else the error code. Host only. */
+int nc_validate_config(const nc_config* cfg);
+
+/* Element count of the flat parameter buffer (and of the gradient buffer),
+ * padding included. Order: E, then per layer Wqkv[d+256, d] (query heads 0..H-1,
+ * then the key rows, then the value rows), Wo[d, d], Wfc[4d, d], Wpr[d, 4d],
+ * then U. Every tensor starts on a multiple of 128 elements. Host only. */
+int nc_param_count(const nc_config* cfg, uint64_t* n_elems);
+
+/* Writes up to `cap` tensor records in buffer order and sets *n to the total
+ * number of tensors (4*depth + 2). Host only. */
+int nc_param_layout(const nc_config* cfg, nc_tensor_info* out, int32_t cap, int32_t* n);
+
+/* Bytes of workspace a call needs; with_backward selects nc_forward_backward
+ * (saves every layer's activations) over nc_forward_loss. Host only. */
+int nc_workspace_bytes(const nc_config* cfg, int32_t with_backward, uint64_t* bytes);
+
+/* Byte offset inside the workspace of the per-token losses (fp32 [B*T],
+ * row-major like tokens), valid after a forward call until the next call on
+ * the same workspace. Host only. */
+int nc_token_losses_offset(const nc_config* cfg, int32_t with_backward, uint64_t* byte_offset);
+
+/* Initialises the flat parameter buffer (nc_param_count elements of dtype):
+ * element i of every tensor = std * N(0,1) from a counter-based generator
+ * (SplitMix64 outputs 2i, 2i+1 for `seed` through Box-Muller, in float64,
+ * rounded to float32 and then to dtype); std = init_std, divided by
+ * sqrt(2*depth) for Wo and Wpr; padding = 0. Deterministic in (seed, cfg). */
+int nc_init_params(uint64_t seed, const nc_config* cfg, void* params, void* stream);
+
+/* Mean next-token loss (fp32, written to *loss_dev) of tokens -> targets,
+ * both int32 [batch, seq_len] on the device. */
+int nc_forward_loss(const nc_config* cfg, const void* params, const int32_t* tokens,
+                    const int32_t* targets, void* ws, uint64_t ws_bytes, float* loss_dev,
+                    void* stream);
+
+/* Forward, loss and backward. grads (fp32, nc_param_count elements, same
+ * layout as params) is OVERWRITTEN with d(mean loss)/d(params); padding
+ * elements are left untouched. */
+int nc_forward_backward(const nc_config* cfg, const void* params, const int32_t* tokens,
+                        const int32_t* targets, float* grads, void* ws, uint64_t ws_bytes,
+                        float* loss_dev, void* stream);
+
+/* Copies the workspace status word to *flags (synchronises on the stream)
+ * and clears nothing; each forward call resets it. */
+int nc_read_device_status(const void* ws, uint32_t* flags, void* stream);
+
+/* Human-readable text for a return code. */
+const char* nc_status_string(int code);
+
+/* HIP error code of this thread's last NC_ERR_HIP (0 if none). */
+int nc_last_hip_error(void);
+
+/* ---- single-step entry points -------------------------------------------
+ * Each runs one stage of the step on caller buffers, for per-stage parity
+ * tests and per-kernel timing. dtype is nc_dtype; "T" below means its
+ * element type (float or bf16). Shapes are row-major. */
+
+/* C[M,N] (op)= sum_k A(m,k) B(n,k), with A(m,k) = A[m*lda+k] when a_kcontig,
+ * else A[k*lda+m] (same for B). epilogue: 0 store T, 1 store fp32,
+ * 2 add into fp32, 3 relu^2 (C = u as T, C2 = relu(u)^2 as T),
+ * 4 relu^2 backward (C = acc * 2*relu(C2) as T, C2 = u as T).
+ * M, N multiples of 16; K a multiple of 64. */
+int nc_op_gemm(int32_t dtype, int32_t a_kcontig, int32_t b_kcontig, int32_t epilogue,
+               const void* A, const void* B, void* C, void* C2, int32_t M, int32_t N, int32_t K,
+               int32_t lda, int32_t ldb, int32_t ldc, void* stream);
+
+/* Weight-gradient contraction dW[N1,N2] = X1^T X2 over M rows (X1 [M,N1],
+ * X2 [M,N2], type T), split over `splits` K slices with a fixed-order fp32
+ * reduction through `partial` (splits*N1*N2 floats; unused when splits = 1). */
+int nc_op_wgrad(int32_t dtype, const void* X1, const void* X2, float* dW, float* partial,
+                int32_t M, int32_t N1, int32_t N2, int32_t splits, void* stream);
+
+/* y = n(x) (T), rinv per row; x fp32 [M,d]. */
+int nc_op_rmsnorm_fwd(int32_t dtype, const float* x, int32_t M, int32_t d, float eps, void* y,
+                      float* rinv, void* stream);
+/* dx (=|+=) rinv*(dy - y*mean(dy*y)); g (optional) = T(dx). */
+int nc_op_rmsnorm_bwd(int32_t dtype, const float* dy, const void* y, const float* rinv, int32_t M,
+                      int32_t d, float* dx, int32_t accumulate, void* g, void* stream);
+/* In place on qkv [B*T, d+256]: rotary then RMSNorm on the H query heads and
+ * the key head; rinv_qk [B*T, H+1]; cs scratch >= T*128 floats. */
+int nc_op_rope_qknorm_fwd(int32_t dtype, void* qkv, int32_t B, int32_t T, int32_t H, float base,
+                          float eps, float* rinv_qk, float* cs, void* stream);
+/* In place on dqkv (same layout): gradient through the QK-norm then the
+ * inverse rotation; v columns untouched. cs must hold the table written by
+ * the forward call. */
+int nc_op_rope_qknorm_bwd(int32_t dtype, void* dqkv, const void* qkv, int32_t B, int32_t T,
+                          int32_t H, const float* rinv_qk, const float* cs, void* stream);
+/* o [B*T, H*128] (T), lse [B, H, T] fp32 from qkv [B*T, d+256]. */
+int nc_op_attn_fwd(int32_t dtype, const void* qkv, int32_t B, int32_t T, int32_t H, void* o,
+                   float* lse, void* stream);
+/* dqkv [B*T, d+256] (T) from qkv, o, dout [B*T, H*128], lse; delta scratch
+ * [B, H, T] fp32. */
+int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* dout,
+                   const float* lse, float* delta, int32_t B, int32_t T, int32_t H, void* dqkv,
+                   void* stream);
+/* Per-row loss and (if dlogits != NULL) w-scaled logit gradient (T) from fp32
+ * logits [R, V]; status: device word for range flags (may not be NULL). */
+int nc_op_softcap_ce(int32_t dtype, const float* logits, const int32_t* targets, int32_t R,
+                     int32_t V, float cap, float w, float* loss_rows, void* dlogits,
+                     uint32_t* status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NANOCHAT_H_ */

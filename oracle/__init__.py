@@ -19,11 +19,12 @@ Pages cited in this package (titles as printed on them):
 """
 from .model import (OracleConfig, layout, param_count, unpack, forward_loss,
                     forward_backward, rmsnorm, rmsnorm_bwd, rope_tables,
-                    rope, rope_bwd, causal_mqa, row_forward)
+                    rope, rope_bwd, causal_mqa, causal_mqa_bwd, softcap_ce_rows,
+                    row_forward)
 from .rng import splitmix64_stream, init_params
 
 __all__ = [
     "OracleConfig", "layout", "param_count", "unpack", "forward_loss",
     "forward_backward", "rmsnorm", "rmsnorm_bwd", "rope_tables", "rope",
-    "rope_bwd", "causal_mqa", "row_forward", "splitmix64_stream", "init_params",
+    "rope_bwd", "causal_mqa", "causal_mqa_bwd", "softcap_ce_rows", "row_forward", "splitmix64_stream", "init_params",
 ]

@@ -29,7 +29,7 @@ What is computed, and where the pages fix it:
     depth 30 -> 1920 wide, 15 heads)
       [tutorial] section 2.2 table; [harness] "Thiết kế depth-only scaling"
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   RMSNorm n(v) = v / sqrt(mean(v^2) + eps), eps = 1e-6; pre-norm residual
   blocks x += f(n(x)); a final norm before lm_head; rotary on half-split pairs
   (j, j + D/2) with angle t * base^(-2j/D), base 10000, positions 0..T-1 in
@@ -145,8 +145,9 @@ def rmsnorm(v: np.ndarray, eps: float):
 
 
 def rmsnorm_bwd(dy: np.ndarray, y: np.ndarray, rinv: np.ndarray) -> np.ndarray:
-    """Gradient through y = v * rinv(v):
-    dv = rinv * (dy - y * mean(dy * y)) (derived in DESIGN.md)."""
+    """Gradient through y = v * rinv(v), n = len(v):
+    d rinv / d v_j = -rinv^3 v_j / n, hence
+    dv = rinv * (dy - y * mean(dy * y))."""
     return rinv * (dy - y * np.mean(dy * y, axis=-1, keepdims=True))
 
 
@@ -235,6 +236,40 @@ def row_forward(cfg: OracleConfig, P: dict, tok: np.ndarray, keep: bool):
     return z, cache
 
 
+def causal_mqa_bwd(qh, kh, v, o, do):
+    """Gradients of causal_mqa: with P the attention weights,
+    dv_u = sum_h sum_{t>=u} P dO, dP = dO v^T, delta = rowsum(dO * O),
+    dS = P (dP - delta), dq = dS k / sqrt(D), dk = sum_h dS^T q / sqrt(D).
+    Returns (dqh [T,H,D], dkh [T,D], dv [T,D])."""
+    D = qh.shape[-1]
+    _, p = causal_mqa(qh, kh, v)                           # recompute P [H,T,T]
+    dv = np.einsum("htu,thd->ud", p, do)                   # summed over heads
+    dp = np.einsum("thd,ud->htu", do, v)
+    delta = np.einsum("thd,thd->ht", do, o)                # rowsum(P * dP)
+    ds = p * (dp - delta[:, :, None])
+    dqh = np.einsum("htu,ud->thd", ds, kh) / math.sqrt(D)
+    dkh = np.einsum("htu,thd->ud", ds, qh) / math.sqrt(D)
+    return dqh, dkh, dv
+
+
+def softcap_ce_grad(z, lse, tgt, c, w):
+    """Gradient of w * sum_t (lse_t - z[t, tgt_t]) with respect to the raw
+    logits l, where z = c tanh(l / c): w (softmax(z) - onehot) (1 - (z/c)^2)."""
+    T = z.shape[0]
+    dz = np.exp(z - lse[:, None])
+    dz[np.arange(T), tgt] -= 1.0
+    dz *= w
+    return dz * (1.0 - (z / c) ** 2)
+
+
+def softcap_ce_rows(logits, tgt, c, w):
+    """Per-row loss and logit gradient of the capped cross-entropy for raw
+    logits [R, V] (the lm_head output). Returns (loss [R], dlogits [R, V])."""
+    z = c * np.tanh(np.asarray(logits, dtype=np.float64) / c)
+    lt, lse = _token_losses(z, tgt)
+    return lt, softcap_ce_grad(z, lse, tgt, c, w)
+
+
 def _token_losses(z: np.ndarray, tgt: np.ndarray):
     zmax = z.max(axis=-1, keepdims=True)
     lse = (zmax + np.log(np.exp(z - zmax).sum(axis=-1, keepdims=True)))[:, 0]
@@ -302,12 +337,7 @@ def _row_backward(cfg, P, G, tok, tgt, z, lse, cache, w):
     d, H, D, L, c = cfg.d, cfg.n_head, cfg.head_dim, cfg.depth, cfg.softcap
     cos, sin = cache["cos"], cache["sin"]
 
-    # cross-entropy on the capped logits: dL/dz = w * (softmax(z) - onehot)
-    dz = np.exp(z - lse[:, None])
-    dz[np.arange(T), tgt] -= 1.0
-    dz *= w
-    # softcap z = c * tanh(l / c): dz/dl = 1 - tanh^2 = 1 - (z / c)^2
-    dl = dz * (1.0 - (z / c) ** 2)
+    dl = softcap_ce_grad(z, lse, tgt, c, w)
     # lm_head: l = xf U^T
     G["U"] += dl.T @ cache["xf"]
     dxf = dl @ P["U"]
@@ -328,14 +358,7 @@ def _row_backward(cfg, P, G, tok, tgt, z, lse, cache, w):
         G[f"h{l}.Wo"] += dx.T @ a_["o"]
         do = (dx @ Wo).reshape(T, H, D)
         qh, kh, v = a_["qh"], a_["kh"], a_["v"]
-        o = a_["o"].reshape(T, H, D)
-        _, p = causal_mqa(qh, kh, v)                       # recompute P [H,T,T]
-        dv = np.einsum("htu,thd->ud", p, do)               # summed over heads
-        dp = np.einsum("thd,ud->htu", do, v)
-        delta = np.einsum("thd,thd->ht", do, o)            # rowsum(P * dP)
-        ds = p * (dp - delta[:, :, None])
-        dqh = np.einsum("htu,ud->thd", ds, kh) / math.sqrt(D)
-        dkh = np.einsum("htu,thd->ud", ds, qh) / math.sqrt(D)
+        dqh, dkh, dv = causal_mqa_bwd(qh, kh, v, a_["o"].reshape(T, H, D), do)
         # QK-norm, then the transposed rotation
         dq = rope_bwd(rmsnorm_bwd(dqh, qh, a_["rq"]), cos, sin)
         dk = rope_bwd(rmsnorm_bwd(dkh, kh, a_["rk"]), cos, sin)

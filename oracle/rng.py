@@ -7,7 +7,8 @@ written independently, by the library's init kernel) is:
 
   * every element i of the flat parameter buffer gets
         std(tensor) * N_i,   N_i ~ N(0, 1)
-    with std = 0.02, divided by sqrt(2 * depth) for the attention output
+    with std = init_std (0.02 as the float32 the config carries, widened to
+    float64), divided by sqrt(2 * depth) for the attention output
     projection Wo and the MLP output projection Wpr; padding elements are 0;
   * N_i comes from a counter-based stream: SplitMix64 (Steele, Lea and Flood,
     "Fast Splittable Pseudorandom Number Generators", OOPSLA 2014) seeded with
@@ -56,12 +57,12 @@ def f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
-def init_params(cfg: OracleConfig, seed: int, dtype: str) -> np.ndarray:
+def init_params(cfg: OracleConfig, seed: int, dtype: str, init_std: float = 0.02) -> np.ndarray:
     """The whole flat buffer under the rule above. Returns float32 values
     (dtype 'f32') or uint16 bf16 bit patterns (dtype 'bf16')."""
     n = param_count(cfg, padded=True)
     out = np.zeros(n, dtype=np.float32)
-    base = 0.02
+    base = float(np.float32(init_std))
     proj_scale = 1.0 / np.sqrt(2.0 * cfg.depth)
     for name, off, r, c in layout(cfg):
         std = base * (proj_scale if name.endswith(".Wo") or name.endswith(".Wpr") else 1.0)

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, validates configs and arguments before touching the GPU, and
+lays out parameters exactly as the oracle's independent layout does.
+No compute call runs here (no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import dense_gpt_pretraining_nanochat_amd as nc
+from dense_gpt_pretraining_nanochat_amd.config import PRESETS, param_count
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "nanochat.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nc_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = nc.lib()
+    names = _declared()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in nc._SIGS, f"binding lacks {n}"
+
+
+def _cfg(name):
+    c = PRESETS[name]
+    return nc.nc_config_from_depth(c.depth, c.vocab_size, c.seq_len, c.batch, c.dtype)
+
+
+@pytest.mark.parametrize("name", list(PRESETS))
+def test_layout_matches_oracle(name):
+    c = PRESETS[name]
+    cfg = _cfg(name)
+    ocfg = oracle.OracleConfig(depth=c.depth, vocab=c.vocab_size, seq_len=c.seq_len, batch=c.batch)
+    assert nc.nc_param_layout(cfg) == oracle.layout(ocfg)
+    assert nc.nc_param_count(cfg) == oracle.param_count(ocfg, padded=True)
+    assert oracle.param_count(ocfg) == param_count(c)
+    assert (cfg.n_kv_head, cfg.head_dim, cfg.softcap, cfg.rope_base) == (1, 128, 15.0, 10000.0)
+
+
+def test_param_counts_of_the_workloads():
+    counts = {k: param_count(c) for k, c in PRESETS.items()}
+    assert counts == {"C1": 524_288, "C2": 7_077_888, "C3": 173_801_472,
+                      "C4": 502_005_760, "C5": 949_092_352}
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 512, 64, 2, 0), -1),          # depth below 2
+    ((33, 512, 64, 2, 0), -1),         # H would exceed 16
+    ((2, 500, 64, 2, 0), -1),          # vocab not a multiple of 128
+    ((2, 65536 + 128, 64, 2, 0), -1),  # ids would not fit 16 bits
+    ((2, 512, 96, 2, 0), -1),          # seq_len not a multiple of 64
+    ((2, 512, 64, 0, 0), -1),          # empty batch
+    ((2, 512, 64, 2, 7), -1),          # unknown dtype
+])
+def test_config_validation(args, code):
+    with pytest.raises(nc.NcError) as e:
+        nc.nc_config_from_depth(*args)
+    assert e.value.code == code
+
+
+def test_unsupported_heads():
+    cfg = _cfg("C1")
+    cfg.n_kv_head = 2
+    assert nc.nc_validate_config(cfg) == -2
+    cfg.n_kv_head, cfg.head_dim = 1, 64
+    assert nc.nc_validate_config(cfg) == -2
+
+
+def test_argument_checks_before_any_launch():
+    """Null, misaligned and short-workspace calls return their codes without
+    enqueueing anything (safe with fake device addresses on a CPU host)."""
+    L = nc.lib()
+    cfg = _cfg("C1")
+    need = nc.nc_workspace_bytes(cfg, True)
+    a = 1 << 20                                          # 256-aligned fake address
+    p = ctypes.c_void_p
+    rc = L.nc_forward_backward(ctypes.byref(cfg), None, p(a), p(a), p(a), p(a), need, p(a), None)
+    assert rc == -3
+    rc = L.nc_forward_backward(ctypes.byref(cfg), p(a + 4), p(a), p(a), p(a), p(a), need, p(a), None)
+    assert rc == -4
+    rc = L.nc_forward_backward(ctypes.byref(cfg), p(a), p(a), p(a), p(a), p(a), need - 1, p(a), None)
+    assert rc == -5
+    need_f = nc.nc_workspace_bytes(cfg, False)
+    assert need_f < need
+    rc = L.nc_forward_loss(ctypes.byref(cfg), p(a), p(a), p(a), p(a), need_f - 256, p(a), None)
+    assert rc == -5
+    assert L.nc_init_params(1, ctypes.byref(cfg), None, None) == -3
+    assert L.nc_init_params(1, ctypes.byref(cfg), p(a + 128), None) == -4
+    assert L.nc_op_gemm(1, 1, 1, 9, p(a), p(a), p(a), None, 16, 16, 64, 64, 64, 16, None) == -7
+    assert L.nc_op_gemm(1, 1, 1, 0, p(a), p(a), p(a), None, 16, 16, 48, 64, 64, 16, None) == -7
+    assert L.nc_op_gemm(1, 1, 1, 3, p(a), p(a), p(a), None, 16, 16, 64, 64, 64, 16, None) == -3
+    assert L.nc_op_attn_fwd(1, p(a), 1, 96, 1, p(a), p(a), None) == -7
+
+
+def test_status_strings():
+    assert nc.nc_status_string(0) == "ok"
+    for code in range(-7, 0):
+        assert nc.nc_status_string(code) not in ("", "unknown status")
+
+
+def test_workspace_grows_with_batch_and_depth():
+    w1 = nc.nc_workspace_bytes(nc.nc_config_from_depth(4, 8192, 512, 1, 1))
+    w2 = nc.nc_workspace_bytes(nc.nc_config_from_depth(4, 8192, 512, 2, 1))
+    w3 = nc.nc_workspace_bytes(nc.nc_config_from_depth(5, 8192, 512, 2, 1))
+    assert w1 < w2 < w3
+    c4 = _cfg("C4")
+    assert nc.nc_workspace_bytes(c4, True) < 64 * 2 ** 30     # fits easily in 288 GB
+    off = nc.nc_token_losses_offset(c4, True)
+    assert off % 256 == 0 and off + 4 * 65536 <= nc.nc_workspace_bytes(c4, True)

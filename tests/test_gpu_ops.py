@@ -1,0 +1,260 @@
+"""Per-kernel parity on the GPU: each single-step entry point of the C ABI
+against the oracle's corresponding step (or plain float64 linear algebra for
+the contractions), on seeded inputs with ragged tiles."""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import bf16_dev, check_bf16, cosine, dev, host64, max_rel, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import dense_gpt_pretraining_nanochat_amd as nc  # noqa: E402
+
+
+def _as(a64, dtype):
+    """Device copy of float64 data in the mode's element type, and the exact
+    float64 value of what was stored (the oracle's input)."""
+    if dtype == "bf16":
+        t = bf16_dev(a64)
+    else:
+        t = dev(a64.astype(np.float32))
+    return t, host64(t)
+
+
+def _empty(shape, dtype):
+    return torch.zeros(shape, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32, device="cuda")
+
+
+# ---------------------------------------------------------------- GEMM
+
+GEMM_CASES = [
+    # (a_kcontig, b_kcontig, epilogue)
+    (1, 1, nc.EPI_STORE_T), (1, 1, nc.EPI_STORE_F32), (1, 1, nc.EPI_ADD_F32), (1, 1, nc.EPI_RELU2),
+    (1, 0, nc.EPI_STORE_T), (1, 0, nc.EPI_STORE_F32), (1, 0, nc.EPI_RELU2_BWD),
+    (0, 0, nc.EPI_STORE_F32),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ak,bk,epi", GEMM_CASES)
+@pytest.mark.parametrize("M,N,K", [(192, 208, 128), (64, 48, 640), (256, 384, 1280)])
+def test_gemm(dtype, ak, bk, epi, M, N, K):
+    rng = np.random.default_rng(M * 7 + N * 3 + K + 11 * epi + 5 * ak + bk)
+    A64 = rng.standard_normal((M, K) if ak else (K, M))
+    B64 = rng.standard_normal((N, K) if bk else (K, N))
+    A, A64 = _as(A64, dtype)
+    B, B64 = _as(B64, dtype)
+    Am = A64 if ak else A64.T
+    Bm = B64 if bk else B64.T
+    ref = Am @ Bm.T                                                   # [M, N]
+    lda, ldb = (K if ak else M), (K if bk else N)
+    out_f32 = epi in (nc.EPI_STORE_F32, nc.EPI_ADD_F32)
+    C = torch.zeros((M, N), dtype=torch.float32, device="cuda") if out_f32 else _empty((M, N), dtype)
+    C2 = None
+    if epi == nc.EPI_ADD_F32:
+        base = rng.standard_normal((M, N)).astype(np.float32)
+        C.copy_(torch.from_numpy(base))
+        ref = ref + base
+    if epi == nc.EPI_RELU2:
+        C2 = _empty((M, N), dtype)
+    if epi == nc.EPI_RELU2_BWD:
+        C2, u64 = _as(rng.standard_normal((M, N)), dtype)
+        ref = ref * 2.0 * np.maximum(u64, 0.0)
+    nc.nc_op_gemm(dtype, ak, bk, epi, A, B, C, C2, M, N, K, lda, ldb, N)
+    torch.cuda.synchronize()
+    got = host64(C)
+    # products are exact and accumulate in fp32; a bf16 output rounds once more
+    scale = np.abs(ref).max()
+    if dtype == "bf16" and not out_f32:
+        assert np.all(np.abs(got - ref) <= 2 ** -8 * np.abs(ref) + 1e-5 * scale)
+    else:
+        assert max_rel(got, ref) <= 1e-5, max_rel(got, ref)
+    if epi == nc.EPI_RELU2:
+        a_ref = np.maximum(got, 0.0) ** 2                            # from the stored u
+        a = host64(C2)
+        assert np.abs(a - a_ref).max() <= (2 ** -8 if dtype == "bf16" else 1e-6) * np.abs(a_ref).max()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("splits", [1, 2, 4])
+def test_wgrad_splitk(dtype, splits):
+    rng = np.random.default_rng(splits)
+    M, N1, N2 = 1024, 272, 192
+    X1, X1_64 = _as(rng.standard_normal((M, N1)), dtype)
+    X2, X2_64 = _as(rng.standard_normal((M, N2)), dtype)
+    dW = torch.zeros((N1, N2), dtype=torch.float32, device="cuda")
+    part = torch.zeros((splits, N1, N2), dtype=torch.float32, device="cuda")
+    nc.nc_op_wgrad(dtype, X1, X2, dW, part, M, N1, N2, splits)
+    torch.cuda.synchronize()
+    ref = X1_64.T @ X2_64
+    assert max_rel(host64(dW), ref) < 1e-5
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("M,d", [(37, 128), (256, 1280), (64, 1664), (8, 2048)])
+def test_rmsnorm_fwd_bwd(dtype, M, d):
+    rng = np.random.default_rng(d + M)
+    x64 = rng.standard_normal((M, d)) * 3.0
+    x = dev(x64.astype(np.float32))
+    x64 = host64(x)
+    y = _empty((M, d), dtype)
+    rinv = torch.zeros(M, dtype=torch.float32, device="cuda")
+    nc.nc_op_rmsnorm_fwd(dtype, x, M, d, 1e-6, y, rinv)
+    torch.cuda.synchronize()
+    yo, ro = oracle.rmsnorm(x64, 1e-6)
+    tol = 2 ** -8 if dtype == "bf16" else 2e-6
+    assert max_rel(host64(y), yo) <= tol
+    assert max_rel(host64(rinv), ro[:, 0]) <= 2e-6
+    # backward, accumulating into an existing dx, with the bf16 copy
+    dy64 = rng.standard_normal((M, d))
+    dy = dev(dy64.astype(np.float32))
+    dy64 = host64(dy)
+    dx0 = rng.standard_normal((M, d)).astype(np.float32)
+    dx = dev(dx0)
+    g = _empty((M, d), dtype)
+    nc.nc_op_rmsnorm_bwd(dtype, dy, y, rinv, M, d, dx, 1, g)
+    torch.cuda.synchronize()
+    ref = dx0 + oracle.rmsnorm_bwd(dy64, host64(y), host64(rinv)[:, None])
+    assert max_rel(host64(dx), ref) <= 1e-5
+    assert max_rel(host64(g), host64(dx)) <= (2 ** -8 if dtype == "bf16" else 0.0)
+
+
+# ---------------------------------------------------------------- rotary + QK-norm
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,H", [(2, 64, 1), (1, 256, 10), (2, 128, 13)])
+def test_rope_qknorm(dtype, B, T, H):
+    rng = np.random.default_rng(B * T + H)
+    d = 128 * H
+    Q = d + 256
+    M = B * T
+    qkv, qkv64 = _as(rng.standard_normal((M, Q)), dtype)
+    rq = torch.zeros((M, H + 1), dtype=torch.float32, device="cuda")
+    cs = torch.zeros(T * 128, dtype=torch.float32, device="cuda")
+    nc.nc_op_rope_qknorm_fwd(dtype, qkv, B, T, H, 10000.0, 1e-6, rq, cs)
+    torch.cuda.synchronize()
+    cfg = oracle.OracleConfig(depth=2, vocab=128, seq_len=T, batch=B)
+    cos, sin = oracle.rope_tables(cfg)
+    z = qkv64.reshape(B, T, Q)
+    q = z[:, :, :d].reshape(B, T, H, 128)
+    k = z[:, :, d:d + 128]
+    qh, rqo = oracle.rmsnorm(np.stack([oracle.rope(q[b], cos, sin) for b in range(B)]), 1e-6)
+    kh, rko = oracle.rmsnorm(np.stack([oracle.rope(k[b], cos, sin) for b in range(B)]), 1e-6)
+    got = host64(qkv).reshape(B, T, Q)
+    tol = 2 ** -8 if dtype == "bf16" else 2e-6
+    assert max_rel(got[:, :, :d].reshape(B, T, H, 128), qh) <= tol
+    assert max_rel(got[:, :, d:d + 128], kh) <= tol
+    assert np.array_equal(got[:, :, d + 128:], z[:, :, d + 128:])          # v untouched
+    r = host64(rq).reshape(B, T, H + 1)
+    assert max_rel(r[:, :, :H], rqo[..., 0]) <= 2e-5 and max_rel(r[:, :, H], rko[..., 0]) <= 2e-5
+    # backward through QK-norm and the inverse rotation (in place on dqkv)
+    g, g64 = _as(rng.standard_normal((M, Q)), dtype)
+    nc.nc_op_rope_qknorm_bwd(dtype, g, qkv, B, T, H, rq, cs)
+    torch.cuda.synchronize()
+    gz = g64.reshape(B, T, Q)
+    yq = got[:, :, :d].reshape(B, T, H, 128)
+    yk = got[:, :, d:d + 128]
+    dq = np.stack([oracle.rope_bwd(oracle.rmsnorm_bwd(gz[b, :, :d].reshape(T, H, 128), yq[b],
+                                                      r[b, :, :H, None]), cos, sin) for b in range(B)])
+    dk = np.stack([oracle.rope_bwd(oracle.rmsnorm_bwd(gz[b, :, d:d + 128], yk[b], r[b, :, H:H + 1]),
+                                   cos, sin) for b in range(B)])
+    gg = host64(g).reshape(B, T, Q)
+    assert max_rel(gg[:, :, :d].reshape(B, T, H, 128), dq) <= (2 ** -7 if dtype == "bf16" else 1e-5)
+    assert max_rel(gg[:, :, d:d + 128], dk) <= (2 ** -7 if dtype == "bf16" else 1e-5)
+    assert np.array_equal(gg[:, :, d + 128:], gz[:, :, d + 128:])
+
+
+# ---------------------------------------------------------------- attention
+
+def _attn_inputs(rng, B, T, H, dtype):
+    d = 128 * H
+    Q = d + 256
+    M = B * T
+    raw = rng.standard_normal((M, Q))
+    # unit-RMS q and k rows, as QK-norm leaves them
+    z = raw.reshape(M, H + 2, 128)
+    z[:, :H + 1] /= np.sqrt(np.mean(z[:, :H + 1] ** 2, axis=-1, keepdims=True))
+    return _as(z.reshape(M, Q), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,H", [(2, 64, 1), (1, 256, 3), (2, 192, 10), (1, 128, 13)])
+def test_attention_fwd_bwd(dtype, B, T, H):
+    rng = np.random.default_rng(B + T + H)
+    d = 128 * H
+    Q = d + 256
+    M = B * T
+    qkv, q64 = _attn_inputs(rng, B, T, H, dtype)
+    o = _empty((M, d), dtype)
+    lse = torch.zeros((B, H, T), dtype=torch.float32, device="cuda")
+    nc.nc_op_attn_fwd(dtype, qkv, B, T, H, o, lse)
+    torch.cuda.synchronize()
+    z = q64.reshape(B, T, Q)
+    oref = np.stack([oracle.causal_mqa(z[b, :, :d].reshape(T, H, 128), z[b, :, d:d + 128],
+                                       z[b, :, d + 128:])[0] for b in range(B)])
+    og = host64(o).reshape(B, T, H, 128)
+    if dtype == "f32":
+        assert max_rel(og, oref) <= 1e-5
+    else:
+        check_bf16(og, oref, "o", cos_min=0.99995, l2_max=5e-3)
+    # lse against the textbook value
+    s = np.einsum("bthd,bud->bhtu", z[:, :, :d].reshape(B, T, H, 128), z[:, :, d:d + 128]) / np.sqrt(128)
+    s = np.where(np.triu(np.ones((T, T), bool), 1)[None, None], -np.inf, s)
+    mx = s.max(-1, keepdims=True)
+    lref = (mx + np.log(np.exp(s - mx).sum(-1, keepdims=True)))[..., 0]
+    assert np.abs(host64(lse) - lref).max() <= (1e-4 if dtype == "f32" else 2e-3)
+
+    # backward: same O (as stored) for both sides
+    do, do64 = _as(rng.standard_normal((M, d)), dtype)
+    dqkv = _empty((M, Q), dtype)
+    delta = torch.zeros((B, H, T), dtype=torch.float32, device="cuda")
+    nc.nc_op_attn_bwd(dtype, qkv, o, do, lse, delta, B, T, H, dqkv)
+    torch.cuda.synchronize()
+    g = host64(dqkv).reshape(B, T, Q)
+    for b in range(B):
+        dq, dk, dv = oracle.causal_mqa_bwd(z[b, :, :d].reshape(T, H, 128), z[b, :, d:d + 128],
+                                           z[b, :, d + 128:], og[b], do64.reshape(B, T, H, 128)[b])
+        parts = [(g[b, :, :d].reshape(T, H, 128), dq, "dq"), (g[b, :, d:d + 128], dk, "dk"),
+                 (g[b, :, d + 128:], dv, "dv")]
+        for got, ref, name in parts:
+            if dtype == "f32":
+                assert max_rel(got, ref) <= 1e-4, (name, max_rel(got, ref))
+            else:
+                check_bf16(got, ref, name, cos_min=0.9999, l2_max=1.5e-2)
+
+
+# ---------------------------------------------------------------- cross-entropy
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("R,V", [(64, 512), (16, 65536), (33, 8192), (8, 384)])
+def test_softcap_ce(dtype, R, V):
+    rng = np.random.default_rng(R + V)
+    logits64 = rng.standard_normal((R, V)) * 8.0
+    logits = dev(logits64.astype(np.float32))
+    logits64 = host64(logits)
+    tgt = rng.integers(0, V, R).astype(np.int32)
+    tgt[0] = V - 1
+    w = 1.0 / (4 * R)
+    loss = torch.zeros(R, dtype=torch.float32, device="cuda")
+    dl = _empty((R, V), dtype)
+    status = torch.zeros(64, dtype=torch.int32, device="cuda")
+    nc.nc_op_softcap_ce(dtype, logits, dev(tgt), R, V, 15.0, w, loss, dl, status)
+    torch.cuda.synchronize()
+    lref, dref = oracle.softcap_ce_rows(logits64, tgt, 15.0, w)
+    assert max_rel(host64(loss), lref) <= 2e-6 * np.log(V)
+    got = host64(dl)
+    if dtype == "f32":
+        assert max_rel(got, dref) <= 1e-5
+    else:
+        check_bf16(got, dref, "dlogits", cos_min=0.99999, l2_max=5e-3)
+    assert int(status[0]) == 0
+    # out-of-range targets are clamped and flagged
+    bad = tgt.copy()
+    bad[1] = V + 5
+    nc.nc_op_softcap_ce(dtype, logits, dev(bad), R, V, 15.0, w, loss, None, status)
+    torch.cuda.synchronize()
+    assert int(status[0]) & nc.NC_STATUS_TARGET_RANGE

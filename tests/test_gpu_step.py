@@ -1,0 +1,172 @@
+"""Whole-step parity on the GPU through nc_forward_loss / nc_forward_backward
+against the fp64 oracle, on the same seeded parameters and tokens.
+
+Bars: fp32 mode - loss relative error <= 1e-4, per-tensor gradient max
+relative error <= 1e-3; bf16 mode - loss relative error <= 5e-3, per-tensor
+gradient cosine >= 0.999 and relative L2 error <= 3e-2."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_gpt_pretraining_nanochat_amd import inputs
+from dense_gpt_pretraining_nanochat_amd.config import PRESETS, SEEDS, TOKEN_LAW
+from tests.gpu_util import check_bf16, dev, host64, max_rel
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import dense_gpt_pretraining_nanochat_amd as nc  # noqa: E402
+
+
+def _setup(depth, V, T, B, dtype, pseed, dseed, law):
+    cfg = nc.nc_config_from_depth(depth, V, T, B, dtype)
+    ocfg = oracle.OracleConfig(depth=depth, vocab=V, seq_len=T, batch=B)
+    lay = oracle.layout(ocfg)
+    flat = inputs.make_params(lay, oracle.param_count(ocfg, padded=True), pseed, dtype, depth)
+    tok, tgt = inputs.make_tokens(V, T, B, dseed, law)
+    step = nc.Step(cfg)
+    if dtype == "bf16":
+        step.params.copy_(torch.from_numpy(flat.view(np.int16)).view(torch.bfloat16).cuda())
+    else:
+        step.params.copy_(torch.from_numpy(flat).cuda())
+    p64 = inputs.as_float64(flat, dtype)
+    return cfg, ocfg, step, p64, tok, tgt
+
+
+def _compare(ocfg, step, p64, tok, tgt, dtype):
+    step.grads.fill_(0)
+    step.forward_backward(dev(tok), dev(tgt))
+    torch.cuda.synchronize()
+    loss = float(step.loss.item())
+    grads = host64(step.grads)
+    oloss, og, otok = oracle.forward_backward(ocfg, p64, tok, tgt)
+    rel = abs(loss - oloss) / abs(oloss)
+    report = {"loss": loss, "oracle_loss": oloss, "loss_rel": rel}
+    for name, off, r, c in oracle.layout(ocfg):
+        g, o = grads[off:off + r * c], og[off:off + r * c]
+        if dtype == "f32":
+            report[name] = max_rel(g, o)
+            assert report[name] <= 1e-3, (name, report[name])
+        else:
+            report[name] = check_bf16(g, o, name)
+    assert rel <= (1e-4 if dtype == "f32" else 5e-3), report
+    tl = host64(step.token_losses())
+    assert np.abs(tl - otok).max() <= (1e-4 if dtype == "f32" else 5e-2) * max(1.0, np.abs(otok).max())
+    assert step.status() == 0
+    return report
+
+
+def test_c1_tiny_fp32():
+    pseed, dseed = SEEDS["C1"]
+    c = PRESETS["C1"]
+    _, ocfg, step, p64, tok, tgt = _setup(c.depth, c.vocab_size, c.seq_len, c.batch, "f32",
+                                          pseed, dseed, TOKEN_LAW["C1"])
+    _compare(ocfg, step, p64, tok, tgt, "f32")
+
+
+def test_c2_small_bf16():
+    pseed, dseed = SEEDS["C2"]
+    c = PRESETS["C2"]
+    _, ocfg, step, p64, tok, tgt = _setup(c.depth, c.vocab_size, c.seq_len, c.batch, "bf16",
+                                          pseed, dseed, TOKEN_LAW["C2"])
+    _compare(ocfg, step, p64, tok, tgt, "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_shapes(dtype):
+    """depth 3 (d = 192, H = 1: every 128-wide tile is ragged), one sequence of
+    64 tokens (fewer rows than a tile), V = 384, ids at V - 1 included."""
+    _, ocfg, step, p64, tok, tgt = _setup(3, 384, 64, 1, dtype, 11, 12, "uniform")
+    tok[0, 5] = 383
+    tgt[0, 9] = 383
+    _compare(ocfg, step, p64, tok, tgt, dtype)
+
+
+def test_max_vocab_ids():
+    """V = 65,536: ids at the top of the 16-bit range, tiny width."""
+    _, ocfg, step, p64, tok, tgt = _setup(2, 65536, 64, 2, "bf16", 21, 22, "zipf")
+    tok[0, :4] = [65535, 65534, 0, 65535]
+    tgt[1, :3] = [65535, 1, 65535]
+    _compare(ocfg, step, p64, tok, tgt, "bf16")
+
+
+def test_forward_loss_matches_forward_backward():
+    pseed, dseed = SEEDS["C2"]
+    c = PRESETS["C2"]
+    cfg, ocfg, step, p64, tok, tgt = _setup(c.depth, c.vocab_size, c.seq_len, 2, "bf16",
+                                            pseed, dseed, TOKEN_LAW["C2"])
+    fwd = nc.Step(cfg, with_backward=False)
+    fwd.params.copy_(step.params)
+    l1 = float(fwd.forward_loss(dev(tok), dev(tgt)).item())
+    l2 = float(step.forward_backward(dev(tok), dev(tgt)).item())
+    assert l1 == l2                                       # same kernels, same order
+    oloss = oracle.forward_loss(ocfg, p64, tok, tgt)
+    assert abs(l1 - oloss) / oloss <= 5e-3
+
+
+def test_deterministic_bitwise():
+    """Two calls give bit-identical loss and gradients (no float atomics; this
+    also catches races between workgroups)."""
+    pseed, dseed = SEEDS["C2"]
+    c = PRESETS["C2"]
+    _, _, step, _, tok, tgt = _setup(c.depth, c.vocab_size, c.seq_len, c.batch, "bf16",
+                                     pseed, dseed, TOKEN_LAW["C2"])
+    t, g = dev(tok), dev(tgt)
+    step.forward_backward(t, g)
+    l1, g1 = step.loss.clone(), step.grads.clone()
+    step.grads.fill_(7.0)
+    step.forward_backward(t, g)
+    torch.cuda.synchronize()
+    assert torch.equal(l1, step.loss)
+    assert torch.equal(g1, step.grads)
+
+
+def test_causality_on_gpu():
+    """Changing tokens after position t leaves the per-token losses at
+    positions <= t unchanged (bitwise)."""
+    _, _, step, _, tok, tgt = _setup(2, 512, 128, 1, "bf16", 31, 32, "uniform")
+    step.forward_backward(dev(tok), dev(tgt))
+    a = step.token_losses().clone()
+    tok2 = tok.copy()
+    tok2[0, 70:] = (tok2[0, 70:] + 3) % 512
+    step.forward_backward(dev(tok2), dev(tgt))
+    b = step.token_losses()
+    torch.cuda.synchronize()
+    assert torch.equal(a[0, :70], b[0, :70])
+    assert not torch.equal(a[0, 70:], b[0, 70:])
+
+
+def test_out_of_range_ids_are_flagged():
+    _, _, step, _, tok, tgt = _setup(2, 512, 64, 1, "bf16", 41, 42, "uniform")
+    tok[0, 3] = 600
+    tgt[0, 4] = -1
+    step.forward_backward(dev(tok), dev(tgt))
+    st = step.status()
+    assert st & nc.NC_STATUS_TOKEN_RANGE and st & nc.NC_STATUS_TARGET_RANGE
+    assert math.isfinite(float(step.loss.item()))
+
+
+@pytest.mark.parametrize("dtype,depth,V", [("f32", 2, 512), ("bf16", 4, 8192)])
+def test_init_matches_oracle_generator(dtype, depth, V):
+    """nc_init_params against the oracle's own SplitMix64 + Box-Muller rule."""
+    cfg = nc.nc_config_from_depth(depth, V, 64, 1, dtype)
+    ocfg = oracle.OracleConfig(depth=depth, vocab=V, seq_len=64, batch=1)
+    step = nc.Step(cfg, with_backward=False)
+    step.params.fill_(3.0)
+    step.init(1234)
+    torch.cuda.synchronize()
+    ref = oracle.init_params(ocfg, 1234, dtype)
+    if dtype == "bf16":
+        got = step.params.view(torch.int16).cpu().numpy().view(np.uint16)
+        gv = inputs.bf16_bits_to_f32(got).astype(np.float64)
+        rv = inputs.bf16_bits_to_f32(ref).astype(np.float64)
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(rv), 1e-30))) - 7)
+    else:
+        got = step.params.cpu().numpy()
+        gv, rv = got.astype(np.float64), ref.astype(np.float64)
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(rv), 1e-30))) - 23)
+    same = np.mean(gv == rv)
+    assert same >= 0.9999, same
+    assert np.all(np.abs(gv - rv) <= ulp)
