@@ -1,0 +1,182 @@
+"""Throughput of one training step (forward + loss + backward) of the
+depth-20 dense GPT on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload C4] [--no-cpu-baseline]
+
+Prints one JSON line: tokens/s for the whole step (inputs resident in HBM),
+milliseconds per step, MFU against the dense bf16 matrix-core peak, the
+roofline of the dominant kernel (timed live with HIP events on the stream it
+runs on) and the fp64 CPU oracle timed on a bounded sample of the same
+workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "train tokens/sec and MFU, depth-20 fwd+bwd step on 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0           # MI355X dense bf16 matrix cores
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+WORKLOAD_NAMES = {
+    "C1": "tiny GPT fwd+bwd fp32: depth 2, d 128, V 512, T 64, B 2",
+    "C2": "small GPT fwd+bwd bf16: depth 4, d 256, V 8192, T 512, B 8",
+    "C3": "mid GPT fwd+bwd bf16: depth 12, d 768, V 65536, T 2048, B 8",
+    "C4": "speedrun-shape GPT fwd+bwd bf16: depth 20, d 1280, 10 heads, 1 KV head, "
+          "V 65536, T 2048, B 32 (65,536 tokens/step)",
+    "C5": "GPT-2-grade GPT fwd+bwd bf16: depth 26, d 1664, V 65536, T 2048, B 16",
+}
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="C4", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    return ap.parse_args()
+
+
+def dominant_kernel_roofline(cfg, nc, torch, reps=20):
+    """Times the MLP up-projection GEMM (tokens x 4d x d, relu^2 epilogue;
+    the largest single contraction of the step) on its own, with HIP events
+    on the stream it is launched on."""
+    M = cfg.batch * cfg.seq_len
+    d = 64 * cfg.depth
+    F = 4 * d
+    bf = cfg.dtype == nc.NC_BF16
+    et = torch.bfloat16 if bf else torch.float32
+    A = torch.randn(M, d, device="cuda").to(et)
+    B = (torch.randn(F, d, device="cuda") * 0.02).to(et)
+    U = torch.empty(M, F, device="cuda", dtype=et)
+    Aout = torch.empty(M, F, device="cuda", dtype=et)
+    s = torch.cuda.current_stream()
+    for _ in range(3):
+        nc.nc_op_gemm(cfg.dtype, 1, 1, nc.EPI_RELU2, A, B, U, Aout, M, F, d, d, d, F, stream=s)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(s)
+    for _ in range(reps):
+        nc.nc_op_gemm(cfg.dtype, 1, 1, nc.EPI_RELU2, A, B, U, Aout, M, F, d, d, d, F, stream=s)
+    ev1.record(s)
+    ev1.synchronize()
+    sec = ev0.elapsed_time(ev1) / 1e3 / reps
+    flops = 2.0 * M * F * d
+    peak = PEAK_BF16_TFLOPS if bf else PEAK_F32_TFLOPS
+    ach = flops / sec / 1e12
+    del A, B, U, Aout
+    return {"kernel": "gemm_kernel<bf16,NT,Relu2> (MLP up-projection, fwd)",
+            "shape": [M, F, d], "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(ach / peak, 4), "avg_us": round(sec * 1e6, 2),
+            "flops_per_launch": flops, "traffic": None}
+
+
+def cpu_baseline(workload, ntok):
+    """The fp64 oracle (as it stands) on the first `ntok` tokens of one
+    sequence of the workload, forward + backward; tokens/s on this host."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from dense_gpt_pretraining_nanochat_amd import inputs
+    from dense_gpt_pretraining_nanochat_amd.config import PRESETS, SEEDS, TOKEN_LAW
+    c = PRESETS[workload]
+    pseed, dseed = SEEDS[workload]
+    ocfg = oracle.OracleConfig(depth=c.depth, vocab=c.vocab_size, seq_len=ntok, batch=1)
+    flat = inputs.make_params(oracle.layout(ocfg), oracle.param_count(ocfg, padded=True), pseed,
+                              c.dtype, c.depth)
+    p64 = inputs.as_float64(flat, c.dtype)
+    del flat
+    tok, tgt = inputs.make_tokens(c.vocab_size, c.seq_len, 1, dseed, TOKEN_LAW[workload])
+    tok, tgt = tok[:, :ntok], tgt[:, :ntok]
+    t0 = time.perf_counter()
+    oracle.forward_backward(ocfg, p64, tok, tgt)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(ntok / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{workload} model shapes, one sequence of {ntok} tokens (a causal prefix), "
+                      f"fp64 forward + loss + backward"}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import dense_gpt_pretraining_nanochat_amd as nc
+    from dense_gpt_pretraining_nanochat_amd import inputs
+    from dense_gpt_pretraining_nanochat_amd.config import (PRESETS, SEEDS, TOKEN_LAW, flops_per_step,
+                                                           flops_variants)
+
+    c = PRESETS[a.workload]
+    pseed, dseed = SEEDS[a.workload]
+    cfg = nc.nc_config_from_depth(c.depth, c.vocab_size, c.seq_len, c.batch, c.dtype)
+    step = nc.Step(cfg)
+    step.init(pseed)
+    tok, tgt = inputs.make_tokens(c.vocab_size, c.seq_len, c.batch, dseed, TOKEN_LAW[a.workload])
+    tok_d, tgt_d = torch.from_numpy(tok).cuda(), torch.from_numpy(tgt).cuda()
+    torch.cuda.synchronize()
+
+    for _ in range(a.warmup):
+        step.forward_backward(tok_d, tgt_d)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(s)
+    for _ in range(a.steps):
+        step.forward_backward(tok_d, tgt_d)
+    ev1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sec = ev0.elapsed_time(ev1) / 1e3 / a.steps
+    loss = float(step.loss.item())
+    status = step.status()
+    tokens = c.batch * c.seq_len
+    fl = flops_per_step(c)
+    out = {
+        "metric": METRIC,
+        "value": round(tokens / sec, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(sec * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic (seeded Zipf(1.1) token ids, random-init weights from nc_init_params)"
+                if TOKEN_LAW[a.workload] == "zipf" else "synthetic (seeded uniform ids)",
+        "config": {"workload": WORKLOAD_NAMES[a.workload], "batch": c.batch, "seq_len": c.seq_len,
+                   "tokens_per_step": tokens, "parallelism": "none (one GPU)"},
+        "mfu": round(fl / sec / (PEAK_BF16_TFLOPS * 1e12), 4),
+        "flops_per_step": fl,
+        "flops_variants": {k: float(v) for k, v in flops_variants(c).items()},
+        "loss": loss,
+        "device_status": status,
+        "wall_s_timed": round(wall, 3),
+    }
+    del step
+    torch.cuda.empty_cache()
+    out["roofline"] = dominant_kernel_roofline(cfg, nc, torch)
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,7 +33,8 @@ struct Dims {
 int validate(const nc_config* c) {
   if (!c) return NC_ERR_NULL;
   if (c->n_kv_head != 1 || c->head_dim != 128) return NC_ERR_UNSUPPORTED;
-  if (c->depth < 2 || c->depth > 32) return NC_ERR_INVALID_CONFIG;
+  // width 64*depth must hold whole 128-dim heads: depth even, H = depth/2 <= 16
+  if (c->depth < 2 || c->depth > 32 || c->depth % 2) return NC_ERR_INVALID_CONFIG;
   if (c->vocab_size < 128 || c->vocab_size > 65536 || c->vocab_size % 128) return NC_ERR_INVALID_CONFIG;
   if (c->seq_len < 64 || c->seq_len % 64) return NC_ERR_INVALID_CONFIG;
   if (c->batch < 1) return NC_ERR_INVALID_CONFIG;

@@ -72,7 +72,7 @@ typedef enum { NC_F32 = 0, NC_BF16 = 1 } nc_dtype;
 /* Model and batch shape. Derived sizes: d = 64*depth, H = d/128 query heads,
  * F = 4*d, one K/V head, M = batch*seq_len tokens per call. */
 typedef struct {
-  int32_t depth;      /* L, 2..32 (so H <= 16)                                 */
+  int32_t depth;      /* L, even, 2..32 (whole 128-dim heads, H = L/2 <= 16)   */
   int32_t vocab_size; /* V, multiple of 128, 128..65536                        */
   int32_t seq_len;    /* T, multiple of 64, >= 64                              */
   int32_t batch;      /* B >= 1                                                */

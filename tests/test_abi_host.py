@@ -54,7 +54,8 @@ def test_param_counts_of_the_workloads():
 
 @pytest.mark.parametrize("args,code", [
     ((1, 512, 64, 2, 0), -1),          # depth below 2
-    ((33, 512, 64, 2, 0), -1),         # H would exceed 16
+    ((34, 512, 64, 2, 0), -1),         # H would exceed 16
+    ((3, 512, 64, 2, 0), -1),          # width 192 is not a whole number of heads
     ((2, 500, 64, 2, 0), -1),          # vocab not a multiple of 128
     ((2, 65536 + 128, 64, 2, 0), -1),  # ids would not fit 16 bits
     ((2, 512, 96, 2, 0), -1),          # seq_len not a multiple of 64
@@ -110,7 +111,7 @@ def test_status_strings():
 def test_workspace_grows_with_batch_and_depth():
     w1 = nc.nc_workspace_bytes(nc.nc_config_from_depth(4, 8192, 512, 1, 1))
     w2 = nc.nc_workspace_bytes(nc.nc_config_from_depth(4, 8192, 512, 2, 1))
-    w3 = nc.nc_workspace_bytes(nc.nc_config_from_depth(5, 8192, 512, 2, 1))
+    w3 = nc.nc_workspace_bytes(nc.nc_config_from_depth(6, 8192, 512, 2, 1))
     assert w1 < w2 < w3
     c4 = _cfg("C4")
     assert nc.nc_workspace_bytes(c4, True) < 64 * 2 ** 30     # fits easily in 288 GB

@@ -76,11 +76,12 @@ def test_c2_small_bf16():
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_ragged_shapes(dtype):
-    """depth 3 (d = 192, H = 1: every 128-wide tile is ragged), one sequence of
-    64 tokens (fewer rows than a tile), V = 384, ids at V - 1 included."""
-    _, ocfg, step, p64, tok, tgt = _setup(3, 384, 64, 1, dtype, 11, 12, "uniform")
+    """depth 6 (H = 3 heads in one group), 3 sequences of 64 tokens (M = 192:
+    one and a half 128-row tiles; wgrad contractions of 192), V = 384 (three
+    lm_head tiles), ids at V - 1 included."""
+    _, ocfg, step, p64, tok, tgt = _setup(6, 384, 64, 3, dtype, 11, 12, "uniform")
     tok[0, 5] = 383
-    tgt[0, 9] = 383
+    tgt[2, 9] = 383
     _compare(ocfg, step, p64, tok, tgt, dtype)
 
 
