@@ -65,6 +65,7 @@ _SIGS = {
     "nc_last_hip_error": [],
     "nc_op_gemm": [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P],
     "nc_op_wgrad": [_I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P],
+    "nc_op_transpose": [_I32, _P, _I32, _I32, _I32, _P, _I32, _P],
     "nc_op_rmsnorm_fwd": [_I32, _P, _I32, _I32, _F32, _P, _P, _P],
     "nc_op_rmsnorm_bwd": [_I32, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P],
     "nc_op_rope_qknorm_fwd": [_I32, _P, _I32, _I32, _I32, _F32, _F32, _P, _P, _P],
@@ -197,6 +198,11 @@ def nc_op_gemm(dtype, a_kcontig, b_kcontig, epilogue, A, B, C, C2, M, N, K, lda,
 def nc_op_wgrad(dtype, X1, X2, dW, partial, M, N1, N2, splits, stream=None):
     _check(lib().nc_op_wgrad(_dt(dtype), _ptr(X1), _ptr(X2), _ptr(dW), _ptr(partial), M, N1, N2,
                              splits, _stream(stream)), "nc_op_wgrad")
+
+
+def nc_op_transpose(dtype, inp, R, C, ld_in, out, ld_out, stream=None):
+    _check(lib().nc_op_transpose(_dt(dtype), _ptr(inp), R, C, ld_in, _ptr(out), ld_out,
+                                 _stream(stream)), "nc_op_transpose")
 
 
 def nc_op_rmsnorm_fwd(dtype, x, M, d, eps, y, rinv, stream=None):

@@ -9,17 +9,25 @@
 // Layout: the fused projection buffer holds, per token, H query heads, then
 // the key head, then the value head, 128 values each (after rotary + QK-norm).
 //
+// Every tile is staged in LDS row-major ([row][128], 16-byte coalesced global
+// loads and LDS writes). Operands that a product needs with the row index as
+// its contraction index are read with the gfx950 LDS transpose read
+// (ds_read_b64_tr_b16): in each 16-lane group, source lane 4j+q names row
+// k0+j, columns n0+4q..n0+4q+3, and output lane i receives rows k0..k0+3 of
+// column n0+i - one matrix-core fragment.
+//
 // Forward (flash style, online softmax in the log2 domain): a workgroup owns
-// 32 query tokens and a group of up to 8 heads, one wavefront per head. Each
-// K/V tile of 64 keys is staged in LDS once and read by every head's
-// wavefront: K row-major, V transposed. The wavefront computes S^T = K Q^T so
-// that each lane column is one query row; its softmax statistics then live in
-// the lane, and P^T feeds O^T += V^T P^T straight from registers.
+// 32 query tokens and up to 8 heads, one wavefront per head. Each K/V tile of
+// 64 keys is staged once and read by every head's wavefront; the next tile is
+// prefetched into registers while the current one is in use (two LDS
+// buffers, one barrier per tile). A wavefront computes S^T = K Q^T so each lane
+// column is one query row: the softmax statistics stay in the lane and P^T
+// feeds O^T += V^T P^T straight from registers.
 //
 // Backward: dK/dV are summed over all heads and all later queries by the
-// workgroup that owns a 64-key block (16 keys per wavefront, accumulators in
-// registers); dQ is produced by a second kernel shaped like the forward.
-// Neither uses atomics, so results are bitwise reproducible.
+// workgroup that owns a 128-key block (32 keys per wavefront, accumulators in
+// registers); dQ comes from a second kernel shaped like the forward. Neither
+// uses atomics, so results are bitwise reproducible.
 #include <math.h>
 
 #include "common.h"
@@ -29,12 +37,16 @@ namespace nc {
 namespace {
 
 constexpr int D = 128;
-constexpr int BQ = 32;      // query tokens per workgroup (fwd, dQ)
-constexpr int BKV = 64;     // keys per tile (fwd, dQ) and per workgroup (dK/dV)
+constexpr int BQ = 32;        // query tokens per workgroup (fwd, dQ) / per step (dK/dV)
+constexpr int BKV = 64;       // keys per tile (fwd, dQ)
+constexpr int BKW = 128;      // keys per dK/dV workgroup (4 wavefronts x 32)
 constexpr int kMaxHeadsPerWG = 8;     // forward
-constexpr int kMaxHeadsPerWGdQ = 4;   // dQ holds Q, dO and dQ tiles: fewer, fatter waves
+constexpr int kMaxHeadsPerWGdQ = 4;   // dQ keeps Q, dO and dQ tiles in registers
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <typename T> struct Mma;
 template <> struct Mma<bf16> {
@@ -51,9 +63,13 @@ template <> struct Mma<float> {
   }
 };
 
-// A fragment whose contraction index runs over 16*NPT accumulator rows, built
-// from NPT accumulator tiles held by this lane (lane group g owns rows
-// 4g..4g+3 of each 16-row tile). bf16 takes two tiles (32 rows), fp32 one.
+// Fragments whose contraction index runs over accumulator rows. A lane of
+// group g holds rows 4g..4g+3 of each 16-row accumulator tile; bf16 fragments
+// span two tiles (contraction 32: rows 4g..4g+3, then 16+4g..16+4g+3), fp32
+// fragments one tile (contraction 16).
+//   pack(): the operand built from this lane's own accumulators;
+//   read(): the matching operand from a row-major LDS array X[k][mn] (stride in
+//           elements), lane (g, i) getting column mn0 + i.
 template <typename T> struct CFrag;
 template <> struct CFrag<bf16> {
   static constexpr int NPT = 2;
@@ -66,19 +82,25 @@ template <> struct CFrag<bf16> {
     }
     return r;
   }
-  // matching operand from a [row][k] LDS array (k contiguous): k = 4g..4g+3 of
-  // tile 0, then of tile 1
-  __device__ __forceinline__ static bf16x8 read(const bf16* row, int k0, int lg) {
-    const bf16x4 a = *reinterpret_cast<const bf16x4*>(row + k0 + 4 * lg);
-    const bf16x4 b = *reinterpret_cast<const bf16x4*>(row + k0 + 16 + 4 * lg);
-    return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  __device__ __forceinline__ static bf16x8 read(const bf16* X, int stride, int k0, int mn0,
+                                                int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    const bf16* p0 = X + (k0 + 4 * g + (s >> 2)) * stride + mn0 + 4 * (s & 3);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * stride));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, ab);
   }
 };
 template <> struct CFrag<float> {
   static constexpr int NPT = 1;
   __device__ __forceinline__ static f32x4 pack(const f32x4* t) { return t[0]; }
-  __device__ __forceinline__ static f32x4 read(const float* row, int k0, int lg) {
-    return *reinterpret_cast<const f32x4*>(row + k0 + 4 * lg);
+  __device__ __forceinline__ static f32x4 read(const float* X, int stride, int k0, int mn0,
+                                               int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const float* p = X + (k0 + 4 * g) * stride + mn0 + i;
+    return f32x4{p[0], p[stride], p[2 * stride], p[3 * stride]};
   }
 };
 
@@ -87,41 +109,50 @@ struct AttnTypes {
   static constexpr int VEC = Vec16<T>::N;
   static constexpr int KB = 4 * VEC;           // contraction per fragment
   static constexpr int NS = D / KB;            // fragments along the head dim
-  static constexpr int KSTR = D + VEC;         // [key][d] rows, 16-byte pad
-  static constexpr int TSTR64 = BKV + VEC;     // [d][64 keys] rows
-  static constexpr int TSTR32 = BQ + VEC;      // [d][32 rows] rows
+  static constexpr int KSTR = D + VEC;         // LDS row stride: 16-byte pad
+  static constexpr int DC = D / VEC;           // 16-byte chunks per 128-wide row
   typedef typename Vec16<T>::type V;
   typedef T T4 __attribute__((ext_vector_type(4)));
 };
 
-// Stage `nrows` rows (a multiple of 4) of 128 values from global (row stride ld)
-// into LDS row-major [row][KSTR] and/or transposed [d][tstr].
-template <typename T, bool ROWMAJOR, bool TRANS>
-__device__ __forceinline__ void stage_rows(const T* __restrict__ src, size_t ld, int nrows,
-                                           T* rm, T* tr, int tstr, int tid, int nthr) {
+// A tile of R rows of 128 values, two sources (e.g. K and V, or Q and dO),
+// staged row-major into two LDS arrays. bf16 prefetches into registers (up to
+// PF chunks per thread); fp32 stages synchronously.
+template <typename T, int R, int PF>
+struct PairStager {
   typedef AttnTypes<T> A;
-  constexpr int DC = D / A::VEC;
-  const int units = DC * (nrows / 4);
-  for (int u = tid; u < units; u += nthr) {
-    const int dc = u % DC, rg = u / DC;
-    typename A::V r4[4];
+  static constexpr int CHUNKS = 2 * R * A::DC;
+  typename A::V reg[PF];
+
+  __device__ __forceinline__ static const T* src_of(const T* s0, const T* s1, size_t ld, int c) {
+    const int which = c / (R * A::DC), r = (c / A::DC) % R, dc = c % A::DC;
+    return (which ? s1 : s0) + (size_t)r * ld + dc * A::VEC;
+  }
+  __device__ __forceinline__ static T* dst_of(T* d0, T* d1, int c) {
+    const int which = c / (R * A::DC), r = (c / A::DC) % R, dc = c % A::DC;
+    return (which ? d1 : d0) + r * A::KSTR + dc * A::VEC;
+  }
+  __device__ __forceinline__ void load(const T* s0, const T* s1, size_t ld, int tid, int nthr) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      r4[j] = *reinterpret_cast<const typename A::V*>(src + (size_t)(rg * 4 + j) * ld + dc * A::VEC);
-    if (ROWMAJOR) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<typename A::V*>(rm + (rg * 4 + j) * A::KSTR + dc * A::VEC) = r4[j];
-    }
-    if (TRANS) {
-#pragma unroll
-      for (int e = 0; e < A::VEC; ++e) {
-        typename A::T4 w = {r4[0][e], r4[1][e], r4[2][e], r4[3][e]};
-        *reinterpret_cast<typename A::T4*>(tr + (dc * A::VEC + e) * tstr + rg * 4) = w;
-      }
+    for (int i = 0; i < PF; ++i) {
+      const int c = tid + i * nthr;
+      if (c < CHUNKS) reg[i] = *reinterpret_cast<const typename A::V*>(src_of(s0, s1, ld, c));
     }
   }
-}
+  __device__ __forceinline__ void store(T* d0, T* d1, int tid, int nthr) const {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int c = tid + i * nthr;
+      if (c < CHUNKS) *reinterpret_cast<typename A::V*>(dst_of(d0, d1, c)) = reg[i];
+    }
+  }
+  __device__ __forceinline__ static void copy(const T* s0, const T* s1, size_t ld, T* d0, T* d1,
+                                              int tid, int nthr) {
+    for (int c = tid; c < CHUNKS; c += nthr)
+      *reinterpret_cast<typename A::V*>(dst_of(d0, d1, c)) =
+          *reinterpret_cast<const typename A::V*>(src_of(s0, s1, ld, c));
+  }
+};
 
 // workgroup -> (batch, query block, head group); heavy (late) query blocks first
 struct QBlock {
@@ -137,6 +168,8 @@ __device__ __forceinline__ QBlock qblock_of(int bid, int nqb, int ngroups) {
   return q;
 }
 
+constexpr bool kPrefetch(int esz) { return esz == 2; }
+
 // --------------------------------------------------------------------------
 // forward
 // --------------------------------------------------------------------------
@@ -146,8 +179,9 @@ __global__ __launch_bounds__(kMaxHeadsPerWG * 64) void attn_fwd_kernel(
     float* __restrict__ lse) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
-  __shared__ __align__(16) T Ks[BKV * A::KSTR];
-  __shared__ __align__(16) T Vt[D * A::TSTR64];
+  constexpr int TILE = BKV * A::KSTR;
+  __shared__ __align__(16) T Ks[2 * TILE];
+  __shared__ __align__(16) T Vs[2 * TILE];
 
   const int ngroups = (H + hpg - 1) / hpg;
   const QBlock qbk = qblock_of(blockIdx.x, Tn / BQ, ngroups);
@@ -155,7 +189,7 @@ __global__ __launch_bounds__(kMaxHeadsPerWG * 64) void attn_fwd_kernel(
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int h = qbk.hg * hpg + wave;
-  const bool active = h < H;
+  const bool active = wave < hpg && h < H;
   const size_t row0 = (size_t)qbk.b * Tn;
   const T* kbase = qkv + H * D;
   const T* vbase = qkv + (H + 1) * D;
@@ -175,81 +209,105 @@ __global__ __launch_bounds__(kMaxHeadsPerWG * 64) void attn_fwd_kernel(
   float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
   const float sc = kLog2e / sqrtf((float)D);
 
-  const int kv_end = tq0 + BQ;
-  for (int kv0 = 0; kv0 < kv_end; kv0 += BKV) {
-    __syncthreads();
-    stage_rows<T, true, false>(kbase + (row0 + kv0) * ldq, ldq, BKV, Ks, nullptr, 0, tid, nthr);
-    stage_rows<T, false, true>(vbase + (row0 + kv0) * ldq, ldq, BKV, nullptr, Vt, A::TSTR64, tid, nthr);
-    __syncthreads();
-    if (!active) continue;
+  constexpr bool PFT = kPrefetch(sizeof(T));
+  PairStager<T, BKV, PFT ? 8 : 1> stg;
+  const int ntiles = (tq0 + BQ + BKV - 1) / BKV;
+  if (PFT) {
+    stg.load(kbase + row0 * ldq, vbase + row0 * ldq, ldq, tid, nthr);
+    stg.store(Ks, Vs, tid, nthr);
+  } else {
+    PairStager<T, BKV, 1>::copy(kbase + row0 * ldq, vbase + row0 * ldq, ldq, Ks, Vs, tid, nthr);
+  }
+  __syncthreads();
 
-    f32x4 st[4][2];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) st[kt][0] = st[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < A::NS; ++s)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const V kf = *reinterpret_cast<const V*>(Ks + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
-        Mma<T>::run(st[kt][0], kf, qf[0][s]);
-        Mma<T>::run(st[kt][1], kf, qf[1][s]);
-      }
+  for (int it = 0; it < ntiles; ++it) {
+    const int kv0 = it * BKV;
+    const T* K = Ks + (it & 1) * TILE;
+    const T* Vv = Vs + (it & 1) * TILE;
+    T* Kn = Ks + ((it + 1) & 1) * TILE;
+    T* Vn = Vs + ((it + 1) & 1) * TILE;
+    const bool more = it + 1 < ntiles;
+    if (PFT && more)
+      stg.load(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq, ldq, tid, nthr);
 
-    const bool diag = kv0 + BKV > tq0;
-    float tmax[2] = {-INFINITY, -INFINITY};
+    if (active) {
+      f32x4 st[4][2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 4; ++kt) st[kt][0] = st[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int s = 0; s < A::NS; ++s)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = st[kt][c][r] * sc;
-          if (diag && kv0 + kt * 16 + lg * 4 + r > tq0 + c * 16 + l16) v = -INFINITY;
-          st[kt][c][r] = v;
-          tmax[c] = fmaxf(tmax[c], v);
+        for (int kt = 0; kt < 4; ++kt) {
+          const V kf = *reinterpret_cast<const V*>(K + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
+          Mma<T>::run(st[kt][0], kf, qf[0][s]);
+          Mma<T>::run(st[kt][1], kf, qf[1][s]);
         }
-    float alpha[2];
+      const bool diag = kv0 + BKV > tq0;
+      float tmax[2] = {-INFINITY, -INFINITY};
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const float mnew = fmaxf(mrow[c], group4_max(tmax[c]));
-      alpha[c] = exp2f(mrow[c] - mnew);
-      mrow[c] = mnew;
-    }
-    float psum[2] = {0.f, 0.f};
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+          for (int r = 0; r < 4; ++r) {
+            float v = st[kt][c][r] * sc;
+            if (diag && kv0 + kt * 16 + lg * 4 + r > tq0 + c * 16 + l16) v = -INFINITY;
+            st[kt][c][r] = v;
+            tmax[c] = fmaxf(tmax[c], v);
+          }
+      float alpha[2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(st[kt][c][r] - mrow[c]);
-          st[kt][c][r] = p;
-          psum[c] += p;
+      for (int c = 0; c < 2; ++c) {
+        const float mnew = fmaxf(mrow[c], group4_max(tmax[c]));
+        alpha[c] = exp2f(mrow[c] - mnew);
+        mrow[c] = mnew;
+      }
+      float psum[2] = {0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = exp2f(st[kt][c][r] - mrow[c]);
+            st[kt][c][r] = p;
+            psum[c] += p;
+          }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) lrow[c] = lrow[c] * alpha[c] + group4_sum(psum[c]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        oacc[i][0] *= alpha[0];
+        oacc[i][1] *= alpha[1];
+      }
+      constexpr int NPT = CFrag<T>::NPT;
+#pragma unroll
+      for (int kk = 0; kk < 4 / NPT; ++kk) {
+        f32x4 t0[NPT], t1[NPT];
+#pragma unroll
+        for (int q = 0; q < NPT; ++q) {
+          t0[q] = st[kk * NPT + q][0];
+          t1[q] = st[kk * NPT + q][1];
         }
+        const V pb0 = CFrag<T>::pack(t0), pb1 = CFrag<T>::pack(t1);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) lrow[c] = lrow[c] * alpha[c] + group4_sum(psum[c]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      oacc[i][0] *= alpha[0];
-      oacc[i][1] *= alpha[1];
-    }
-    constexpr int NPT = CFrag<T>::NPT;
-#pragma unroll
-    for (int kk = 0; kk < 4 / NPT; ++kk) {
-      f32x4 t0[NPT], t1[NPT];
-#pragma unroll
-      for (int q = 0; q < NPT; ++q) {
-        t0[q] = st[kk * NPT + q][0];
-        t1[q] = st[kk * NPT + q][1];
-      }
-      const V pb0 = CFrag<T>::pack(t0), pb1 = CFrag<T>::pack(t1);
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const V va = CFrag<T>::read(Vt + (dt * 16 + l16) * A::TSTR64, kk * 16 * NPT, lg);
-        Mma<T>::run(oacc[dt][0], va, pb0);
-        Mma<T>::run(oacc[dt][1], va, pb1);
+        for (int dt = 0; dt < 8; ++dt) {
+          const V va = CFrag<T>::read(Vv, A::KSTR, kk * 16 * NPT, dt * 16, lane);
+          Mma<T>::run(oacc[dt][0], va, pb0);
+          Mma<T>::run(oacc[dt][1], va, pb1);
+        }
       }
     }
+    if (more) {
+      if (PFT) {
+        stg.store(Kn, Vn, tid, nthr);
+      } else {
+        __syncthreads();   // single-buffered fp32 path: wait for readers first
+        PairStager<T, BKV, 1>::copy(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq,
+                                    ldq, Kn, Vn, tid, nthr);
+      }
+    }
+    __syncthreads();
   }
   if (!active) return;
   const int ldo = H * D;
@@ -301,9 +359,9 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64) void attn_bwd_dq_kernel(
     const float* __restrict__ delta, int Tn, int H, int hpg, T* __restrict__ dqkv, int ldd) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
-  __shared__ __align__(16) T Ks[BKV * A::KSTR];
-  __shared__ __align__(16) T Vs[BKV * A::KSTR];
-  __shared__ __align__(16) T Kt[D * A::TSTR64];
+  constexpr int TILE = BKV * A::KSTR;
+  __shared__ __align__(16) T Ks[2 * TILE];
+  __shared__ __align__(16) T Vs[2 * TILE];
 
   const int ngroups = (H + hpg - 1) / hpg;
   const QBlock qbk = qblock_of(blockIdx.x, Tn / BQ, ngroups);
@@ -311,7 +369,7 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64) void attn_bwd_dq_kernel(
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int h = qbk.hg * hpg + wave;
-  const bool active = h < H;
+  const bool active = wave < hpg && h < H;
   const size_t row0 = (size_t)qbk.b * Tn;
   const int ldo = H * D;
 
@@ -335,57 +393,82 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64) void attn_bwd_dq_kernel(
   const T* kbase = qkv + H * D;
   const T* vbase = qkv + (H + 1) * D;
 
-  const int kv_end = tq0 + BQ;
-  for (int kv0 = 0; kv0 < kv_end; kv0 += BKV) {
-    __syncthreads();
-    stage_rows<T, true, true>(kbase + (row0 + kv0) * ldq, ldq, BKV, Ks, Kt, A::TSTR64, tid, nthr);
-    stage_rows<T, true, false>(vbase + (row0 + kv0) * ldq, ldq, BKV, Vs, nullptr, 0, tid, nthr);
-    __syncthreads();
-    if (!active) continue;
+  constexpr bool PFT = kPrefetch(sizeof(T));
+  PairStager<T, BKV, PFT ? 8 : 1> stg;
+  const int ntiles = (tq0 + BQ + BKV - 1) / BKV;
+  if (PFT) {
+    stg.load(kbase + row0 * ldq, vbase + row0 * ldq, ldq, tid, nthr);
+    stg.store(Ks, Vs, tid, nthr);
+  } else {
+    PairStager<T, BKV, 1>::copy(kbase + row0 * ldq, vbase + row0 * ldq, ldq, Ks, Vs, tid, nthr);
+  }
+  __syncthreads();
 
-    f32x4 st[4][2], dpt[4][2];
+  for (int it = 0; it < ntiles; ++it) {
+    const int kv0 = it * BKV;
+    const T* K = Ks + (it & 1) * TILE;
+    const T* Vv = Vs + (it & 1) * TILE;
+    T* Kn = Ks + ((it + 1) & 1) * TILE;
+    T* Vn = Vs + ((it + 1) & 1) * TILE;
+    const bool more = it + 1 < ntiles;
+    if (PFT && more)
+      stg.load(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq, ldq, tid, nthr);
+
+    if (active) {
+      f32x4 st[4][2], dpt[4][2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-      st[kt][0] = st[kt][1] = dpt[kt][0] = dpt[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kt = 0; kt < 4; ++kt)
+        st[kt][0] = st[kt][1] = dpt[kt][0] = dpt[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < A::NS; ++s)
+      for (int s = 0; s < A::NS; ++s)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const V kf = *reinterpret_cast<const V*>(Ks + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
-        const V vf = *reinterpret_cast<const V*>(Vs + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
-        Mma<T>::run(st[kt][0], kf, qf[0][s]);
-        Mma<T>::run(st[kt][1], kf, qf[1][s]);
-        Mma<T>::run(dpt[kt][0], vf, df[0][s]);
-        Mma<T>::run(dpt[kt][1], vf, df[1][s]);
-      }
-    const bool diag = kv0 + BKV > tq0;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float p = exp2f(st[kt][c][r] * sc - lse2[c]);
-          if (diag && kv0 + kt * 16 + lg * 4 + r > tq0 + c * 16 + l16) p = 0.f;
-          st[kt][c][r] = p * (dpt[kt][c][r] - dl[c]);       // dS
+        for (int kt = 0; kt < 4; ++kt) {
+          const V kf = *reinterpret_cast<const V*>(K + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
+          const V vf = *reinterpret_cast<const V*>(Vv + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
+          Mma<T>::run(st[kt][0], kf, qf[0][s]);
+          Mma<T>::run(st[kt][1], kf, qf[1][s]);
+          Mma<T>::run(dpt[kt][0], vf, df[0][s]);
+          Mma<T>::run(dpt[kt][1], vf, df[1][s]);
         }
-    constexpr int NPT = CFrag<T>::NPT;
+      const bool diag = kv0 + BKV > tq0;
 #pragma unroll
-    for (int kk = 0; kk < 4 / NPT; ++kk) {
-      f32x4 t0[NPT], t1[NPT];
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int q = 0; q < NPT; ++q) {
-        t0[q] = st[kk * NPT + q][0];
-        t1[q] = st[kk * NPT + q][1];
-      }
-      const V b0 = CFrag<T>::pack(t0), b1 = CFrag<T>::pack(t1);
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const V ka = CFrag<T>::read(Kt + (dt * 16 + l16) * A::TSTR64, kk * 16 * NPT, lg);
-        Mma<T>::run(dq[dt][0], ka, b0);
-        Mma<T>::run(dq[dt][1], ka, b1);
+          for (int r = 0; r < 4; ++r) {
+            float p = exp2f(st[kt][c][r] * sc - lse2[c]);
+            if (diag && kv0 + kt * 16 + lg * 4 + r > tq0 + c * 16 + l16) p = 0.f;
+            st[kt][c][r] = p * (dpt[kt][c][r] - dl[c]);       // dS
+          }
+      constexpr int NPT = CFrag<T>::NPT;
+#pragma unroll
+      for (int kk = 0; kk < 4 / NPT; ++kk) {
+        f32x4 t0[NPT], t1[NPT];
+#pragma unroll
+        for (int q = 0; q < NPT; ++q) {
+          t0[q] = st[kk * NPT + q][0];
+          t1[q] = st[kk * NPT + q][1];
+        }
+        const V b0 = CFrag<T>::pack(t0), b1 = CFrag<T>::pack(t1);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const V ka = CFrag<T>::read(K, A::KSTR, kk * 16 * NPT, dt * 16, lane);   // K^T
+          Mma<T>::run(dq[dt][0], ka, b0);
+          Mma<T>::run(dq[dt][1], ka, b1);
+        }
       }
     }
+    if (more) {
+      if (PFT) {
+        stg.store(Kn, Vn, tid, nthr);
+      } else {
+        __syncthreads();
+        PairStager<T, BKV, 1>::copy(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq,
+                                    ldq, Kn, Vn, tid, nthr);
+      }
+    }
+    __syncthreads();
   }
   if (!active) return;
   const float scale = 1.0f / sqrtf((float)D);
@@ -404,8 +487,8 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64) void attn_bwd_dq_kernel(
 }
 
 // --------------------------------------------------------------------------
-// backward, dK and dV: one workgroup per 64-key block, 4 wavefronts x 16 keys,
-// looping over every later 32-token query block and every head.
+// backward, dK and dV: one workgroup per 128-key block, 4 wavefronts x 32
+// keys, looping over every later 32-token query block and every head.
 // --------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
@@ -413,101 +496,177 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     const float* __restrict__ delta, int Tn, int H, T* __restrict__ dqkv, int ldd) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
-  __shared__ __align__(16) T Qs[BQ * A::KSTR];
-  __shared__ __align__(16) T Qt[D * A::TSTR32];
-  __shared__ __align__(16) T Os[BQ * A::KSTR];
-  __shared__ __align__(16) T Ot[D * A::TSTR32];
-  __shared__ float lse_s[BQ], dl_s[BQ];
+  constexpr int TILE = BQ * A::KSTR;
+  __shared__ __align__(16) T Qs[2 * TILE];
+  __shared__ __align__(16) T Os[2 * TILE];
+  __shared__ float stat_s[2][2 * BQ];          // lse (log2 domain), then delta
 
-  const int nkb = Tn / BKV;
+  const int nkb = (Tn + BKW - 1) / BKW;
   const int b = blockIdx.x / nkb;
-  const int kblk = blockIdx.x % nkb;               // low key blocks carry the most work: first
-  const int kv0 = kblk * BKV;
+  const int kblk = blockIdx.x % nkb;           // low key blocks carry the most work: first
+  const int kv0 = kblk * BKW;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const size_t row0 = (size_t)b * Tn;
   const int ldo = H * D;
-  const int key = kv0 + wave * 16 + l16;           // this lane's key column
+  const int key0 = kv0 + wave * 32;            // this wave's 32 keys: key0 + 16*kt + l16
+  // T is a multiple of 64, so a wave's 32 keys are either all inside or all past T
+  const bool kact = key0 < Tn;
 
-  V kf[A::NS], vf[A::NS];
+  V kf[2][A::NS], vf[2][A::NS];
 #pragma unroll
-  for (int s = 0; s < A::NS; ++s) {
-    kf[s] = *reinterpret_cast<const V*>(qkv + (row0 + key) * ldq + H * D + s * A::KB + lg * A::VEC);
-    vf[s] = *reinterpret_cast<const V*>(qkv + (row0 + key) * ldq + (H + 1) * D + s * A::KB + lg * A::VEC);
-  }
-  f32x4 dk[8], dv[8];
+  for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dk[i] = dv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < A::NS; ++s) {
+      const size_t r = row0 + key0 + kt * 16 + l16;
+      kf[kt][s] = kact ? *reinterpret_cast<const V*>(qkv + r * ldq + H * D + s * A::KB + lg * A::VEC) : V{};
+      vf[kt][s] = kact ? *reinterpret_cast<const V*>(qkv + r * ldq + (H + 1) * D + s * A::KB + lg * A::VEC) : V{};
+    }
+  f32x4 dk[8][2], dv[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dk[i][0] = dk[i][1] = dv[i][0] = dv[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sc = kLog2e / sqrtf((float)D);
   constexpr int NPT = CFrag<T>::NPT;
 
-  for (int tq0 = kv0; tq0 < Tn; tq0 += BQ) {
-    for (int h = 0; h < H; ++h) {
-      __syncthreads();
-      stage_rows<T, true, true>(qkv + (row0 + tq0) * ldq + h * D, ldq, BQ, Qs, Qt, A::TSTR32, tid, 256);
-      stage_rows<T, true, true>(dout + (row0 + tq0) * ldo + h * D, ldo, BQ, Os, Ot, A::TSTR32, tid, 256);
-      if (tid < BQ) lse_s[tid] = lse[((size_t)b * H + h) * Tn + tq0 + tid] * kLog2e;
-      else if (tid < 2 * BQ) dl_s[tid - BQ] = delta[((size_t)b * H + h) * Tn + tq0 + tid - BQ];
-      __syncthreads();
+  // iteration space: query blocks tq0 = kv0, kv0+32, ... and heads h
+  const int nqb = (Tn - kv0) / BQ;
+  const int niter = nqb * H;
+  constexpr bool PFT = kPrefetch(sizeof(T));
+  auto qsrc = [&](int i) { return qkv + (row0 + kv0 + (i / H) * BQ) * ldq + (i % H) * D; };
+  auto osrc = [&](int i) { return dout + (row0 + kv0 + (i / H) * BQ) * ldo + (i % H) * D; };
+  auto stats = [&](int i, int buf) {
+    if (tid < 2 * BQ) {
+      const int h = i % H, t = kv0 + (i / H) * BQ + (tid % BQ);
+      const size_t idx = ((size_t)b * H + h) * Tn + t;
+      stat_s[buf][tid] = tid < BQ ? lse[idx] * kLog2e : delta[idx];
+    }
+  };
+  // Q and dO rows have different strides: staged chunk by chunk from either source
+  for (int c = tid; c < 2 * BQ * A::DC; c += 256) {
+    const int which = c / (BQ * A::DC), r = (c / A::DC) % BQ, dc = c % A::DC;
+    const T* src = which ? osrc(0) + (size_t)r * ldo : qsrc(0) + (size_t)r * ldq;
+    *reinterpret_cast<V*>((which ? Os : Qs) + r * A::KSTR + dc * A::VEC) =
+        *reinterpret_cast<const V*>(src + dc * A::VEC);
+  }
+  stats(0, 0);
+  __syncthreads();
 
-      // S[row][key] and dP[row][key] for 32 rows (2 tiles) x this wave's 16 keys
-      f32x4 sa[2], dpa[2];
-      sa[0] = sa[1] = dpa[0] = dpa[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < niter; ++it) {
+    const int tq0 = kv0 + (it / H) * BQ;
+    const T* Q = Qs + (it & 1) * TILE;
+    const T* O = Os + (it & 1) * TILE;
+    const float* lse_s = stat_s[it & 1];
+    const float* dl_s = stat_s[it & 1] + BQ;
+    const bool more = it + 1 < niter;
+    typename A::V pre[PFT ? 4 : 1];
+    if (PFT && more) {
 #pragma unroll
-      for (int s = 0; s < A::NS; ++s)
+      for (int i = 0; i < 4; ++i) {
+        const int c = tid + i * 256;         // 4 * 256 = 2 * BQ * DC chunks
+        const int which = c / (BQ * A::DC), r = (c / A::DC) % BQ, dc = c % A::DC;
+        const T* src = which ? osrc(it + 1) + (size_t)r * ldo : qsrc(it + 1) + (size_t)r * ldq;
+        pre[i] = *reinterpret_cast<const V*>(src + dc * A::VEC);
+      }
+    }
+
+    if (kact) {
+    // S[row][key] and dP[row][key]: 2 row tiles x 2 key tiles
+    f32x4 sa[2][2], dpa[2][2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const V qa = *reinterpret_cast<const V*>(Qs + (c * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
-          const V da = *reinterpret_cast<const V*>(Os + (c * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
-          Mma<T>::run(sa[c], qa, kf[s]);
-          Mma<T>::run(dpa[c], da, vf[s]);
+    for (int c = 0; c < 2; ++c) sa[c][0] = sa[c][1] = dpa[c][0] = dpa[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < A::NS; ++s)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const V qa = *reinterpret_cast<const V*>(Q + (c * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
+        const V da = *reinterpret_cast<const V*>(O + (c * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          Mma<T>::run(sa[c][kt], qa, kf[kt][s]);
+          Mma<T>::run(dpa[c][kt], da, vf[kt][s]);
         }
-      const bool diag = tq0 < kv0 + BKV;
-      f32x4 pa[2], dsa[2];
+      }
+    const bool diag = tq0 < key0 + 32;
+    f32x4 pa[2][2], dsa[2][2];   // [kt][c]
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int rl = c * 16 + lg * 4 + r;     // local query row
-          float p = exp2f(sa[c][r] * sc - lse_s[rl]);
-          if (diag && key > tq0 + rl) p = 0.f;
-          pa[c][r] = p;
-          dsa[c][r] = p * (dpa[c][r] - dl_s[rl]);
+          float p = exp2f(sa[c][kt][r] * sc - lse_s[rl]);
+          if (diag && key0 + kt * 16 + l16 > tq0 + rl) p = 0.f;
+          pa[kt][c][r] = p;
+          dsa[kt][c][r] = p * (dpa[c][kt][r] - dl_s[rl]);
         }
-      // dV^T[d][key] += dO^T[d][rows] P[rows][key];  dK^T += Q^T dS
+    // dV^T[d][key] += dO^T[d][rows] P[rows][key];  dK^T += Q^T dS
 #pragma unroll
-      for (int kk = 0; kk < 2 / NPT; ++kk) {
-        const V pb = CFrag<T>::pack(pa + kk * NPT);
-        const V sb = CFrag<T>::pack(dsa + kk * NPT);
+    for (int kk = 0; kk < 2 / NPT; ++kk)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const V pb = CFrag<T>::pack(pa[kt] + kk * NPT);
+        const V sb = CFrag<T>::pack(dsa[kt] + kk * NPT);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const V oa = CFrag<T>::read(Ot + (dt * 16 + l16) * A::TSTR32, kk * 16 * NPT, lg);
-          const V qa = CFrag<T>::read(Qt + (dt * 16 + l16) * A::TSTR32, kk * 16 * NPT, lg);
-          Mma<T>::run(dv[dt], oa, pb);
-          Mma<T>::run(dk[dt], qa, sb);
+          const V oa = CFrag<T>::read(O, A::KSTR, kk * 16 * NPT, dt * 16, lane);
+          const V qa = CFrag<T>::read(Q, A::KSTR, kk * 16 * NPT, dt * 16, lane);
+          Mma<T>::run(dv[dt][kt], oa, pb);
+          Mma<T>::run(dk[dt][kt], qa, sb);
         }
       }
     }
-  }
-  const float scale = 1.0f / sqrtf((float)D);
-  T* dkdst = dqkv + (row0 + key) * ldd + H * D;
-  T* dvdst = dqkv + (row0 + key) * ldd + (H + 1) * D;
+
+    if (more) {
+      T* Qn = Qs + ((it + 1) & 1) * TILE;
+      T* On = Os + ((it + 1) & 1) * TILE;
+      if (PFT) {
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    typename A::T4 wk, wv;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      wk[r] = from_f32<T>(dk[dt][r] * scale);
-      wv[r] = from_f32<T>(dv[dt][r]);
+        for (int i = 0; i < 4; ++i) {
+          const int c = tid + i * 256;
+          const int which = c / (BQ * A::DC), r = (c / A::DC) % BQ, dc = c % A::DC;
+          *reinterpret_cast<V*>((which ? On : Qn) + r * A::KSTR + dc * A::VEC) = pre[i];
+        }
+      } else {
+        __syncthreads();
+        for (int c = tid; c < 2 * BQ * A::DC; c += 256) {
+          const int which = c / (BQ * A::DC), r = (c / A::DC) % BQ, dc = c % A::DC;
+          const T* src = which ? osrc(it + 1) + (size_t)r * ldo : qsrc(it + 1) + (size_t)r * ldq;
+          *reinterpret_cast<V*>((which ? On : Qn) + r * A::KSTR + dc * A::VEC) =
+              *reinterpret_cast<const V*>(src + dc * A::VEC);
+        }
+      }
+      stats(it + 1, (it + 1) & 1);
     }
-    *reinterpret_cast<typename A::T4*>(dkdst + dt * 16 + lg * 4) = wk;
-    *reinterpret_cast<typename A::T4*>(dvdst + dt * 16 + lg * 4) = wv;
+    __syncthreads();
+  }
+  if (!kact) return;
+  const float scale = 1.0f / sqrtf((float)D);
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const size_t r = row0 + key0 + kt * 16 + l16;
+    T* dkdst = dqkv + r * ldd + H * D;
+    T* dvdst = dqkv + r * ldd + (H + 1) * D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      typename A::T4 wk, wv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        wk[q] = from_f32<T>(dk[dt][kt][q] * scale);
+        wv[q] = from_f32<T>(dv[dt][kt][q]);
+      }
+      *reinterpret_cast<typename A::T4*>(dkdst + dt * 16 + lg * 4) = wk;
+      *reinterpret_cast<typename A::T4*>(dvdst + dt * 16 + lg * 4) = wv;
+    }
   }
 }
 
-inline int heads_per_group(int H, int maxw) {
-  const int ng = (H + maxw - 1) / maxw;
-  return (H + ng - 1) / ng;
+// heads per workgroup <= maxw; at least 4 wavefronts so K/V staging has enough threads
+inline void head_groups(int H, int maxw, int* hpg, int* ng, int* waves) {
+  *ng = (H + maxw - 1) / maxw;
+  *hpg = (H + *ng - 1) / *ng;
+  *ng = (H + *hpg - 1) / *hpg;
+  *waves = *hpg < 4 ? 4 : *hpg;
 }
 
 }  // namespace
@@ -515,8 +674,9 @@ inline int heads_per_group(int H, int maxw) {
 hipError_t attn_fwd(DType t, const void* qkv, int ldq, int B, int T, int H, void* o, float* lse,
                     hipStream_t s) {
   if (T % BKV || H < 1 || H > 16) return hipErrorInvalidValue;
-  const int hpg = heads_per_group(H, kMaxHeadsPerWG), ng = (H + hpg - 1) / hpg;
-  dim3 grid(B * (T / BQ) * ng), block(64 * hpg);
+  int hpg, ng, waves;
+  head_groups(H, kMaxHeadsPerWG, &hpg, &ng, &waves);
+  dim3 grid(B * (T / BQ) * ng), block(64 * waves);
   if (t == DType::BF16)
     hipLaunchKernelGGL(attn_fwd_kernel<bf16>, grid, block, 0, s, static_cast<const bf16*>(qkv), ldq, T,
                        H, hpg, static_cast<bf16*>(o), lse);
@@ -542,9 +702,10 @@ hipError_t attn_bwd_delta(DType t, const void* o, const void* dout, int B, int T
 hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const float* lse,
                     const float* delta, int B, int T, int H, void* dqkv, int ldd, hipStream_t s) {
   if (T % BKV || H < 1 || H > 16) return hipErrorInvalidValue;
-  const int hpg = heads_per_group(H, kMaxHeadsPerWGdQ), ng = (H + hpg - 1) / hpg;
-  dim3 gq(B * (T / BQ) * ng), bq(64 * hpg);
-  dim3 gk(B * (T / BKV)), bk(256);
+  int hpg, ng, waves;
+  head_groups(H, kMaxHeadsPerWGdQ, &hpg, &ng, &waves);
+  dim3 gq(B * (T / BQ) * ng), bq(64 * waves);
+  dim3 gk(B * ((T + BKW - 1) / BKW)), bk(256);
   if (t == DType::BF16) {
     const bf16* q = static_cast<const bf16*>(qkv);
     const bf16* d = static_cast<const bf16*>(dout);

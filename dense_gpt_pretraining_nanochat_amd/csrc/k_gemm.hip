@@ -9,8 +9,10 @@
 // the residual add, the relu^2 activation of the MLP (same list) and its
 // derivative, so no separate elementwise pass touches HBM.
 //
-// Tiling: 128x128 output tile per 256-thread workgroup (4 wavefronts in a 2x2
-// grid, 64x64 per wavefront = 4x4 MFMA tiles of 16x16). Each K step stages a
+// Tiling: large bf16 products use a 256x256 output tile per 512-thread
+// workgroup (8 wavefronts in a 2x4 grid, 128x64 per wavefront = 8x4 MFMA
+// tiles of 16x16; 144 KB of LDS, one workgroup per CU); small or fp32 ones a
+// 128x128 tile per 256 threads (2x2 wavefronts of 64x64). Each K step stages a
 // 128-byte-wide slab of A and B in LDS (double-buffered, one barrier per step,
 // next slab prefetched into registers while the matrix cores work). bf16 uses
 // v_mfma_f32_16x16x32_bf16, fp32 uses four v_mfma_f32_16x16x4_f32 per 16-byte
@@ -19,13 +21,13 @@
 // the matrix-core reads are always 16-byte, K-contiguous LDS reads.
 // Workgroup ids are remapped so each XCD (8 per chip, own L2) walks a
 // contiguous, row-grouped range of output tiles.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace nc {
 namespace {
-
-constexpr int kThreads = 256;
 
 template <typename T> struct Mma;
 template <> struct Mma<bf16> {
@@ -43,17 +45,17 @@ template <> struct Mma<float> {
   }
 };
 
-// Global -> registers -> LDS for one operand slab of R rows x BK k-values.
-// LDS layout is [row][k] with a 16-byte pad per row.
-template <typename T, bool KC, int R>
+// Global -> registers -> LDS for one operand slab of R rows x BK k-values,
+// loaded by NTHR threads. LDS layout is [row][k] with a 16-byte pad per row.
+template <typename T, bool KC, int R, int NTHR>
 struct SlabLoader {
   static constexpr int VEC = Vec16<T>::N;
   static constexpr int BK = 128 / sizeof(T);
   static constexpr int LDSK = BK + VEC;
-  static constexpr int NL = R / 32;            // 16-byte loads per thread
+  static constexpr int NL = R * 8 / NTHR;      // 16-byte loads per thread
   typedef typename Vec16<T>::type V;
   typedef T V4 __attribute__((ext_vector_type(4)));
-  static_assert(KC || R % 128 == 0, "strided slabs need R % 128 == 0");
+  static_assert(NL >= 1 && (KC || NL % 4 == 0), "slab does not split evenly over the threads");
   V reg[NL];
 
   __device__ __forceinline__ void load(const T* __restrict__ p, int ld, int rows, int r0, int k0,
@@ -61,7 +63,7 @@ struct SlabLoader {
     if constexpr (KC) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const int c = tid + kThreads * i;
+        const int c = tid + NTHR * i;
         const int row = c >> 3, col = (c & 7) * VEC;
         const int gr = r0 + row;
         if (gr < rows) reg[i] = *reinterpret_cast<const V*>(p + (size_t)gr * ld + k0 + col);
@@ -71,7 +73,7 @@ struct SlabLoader {
       constexpr int RC = R / VEC;              // 16-byte chunks along the row dim
 #pragma unroll
       for (int u = 0; u < NL / 4; ++u) {
-        const int unit = tid + kThreads * u;
+        const int unit = tid + NTHR * u;
         const int rc = unit % RC, kg = unit / RC;
         const int gr = r0 + rc * VEC;
 #pragma unroll
@@ -88,7 +90,7 @@ struct SlabLoader {
     if constexpr (KC) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const int c = tid + kThreads * i;
+        const int c = tid + NTHR * i;
         const int row = c >> 3, col = (c & 7) * VEC;
         *reinterpret_cast<V*>(lds + row * LDSK + col) = reg[i];
       }
@@ -96,7 +98,7 @@ struct SlabLoader {
       constexpr int RC = R / VEC;
 #pragma unroll
       for (int u = 0; u < NL / 4; ++u) {
-        const int unit = tid + kThreads * u;
+        const int unit = tid + NTHR * u;
         const int rc = unit % RC, kg = unit / RC;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
@@ -108,8 +110,43 @@ struct SlabLoader {
   }
 };
 
+// C[m][n..n+3] = v under epilogue EPI
+template <typename T, Epi EPI>
+__device__ __forceinline__ void epilogue4(const GemmArgs& g, int split, int m, int n, f32x4 v) {
+  const size_t off = (size_t)m * g.ldc + n;
+  typedef T T4 __attribute__((ext_vector_type(4)));
+  if constexpr (EPI == Epi::StoreT) {
+    T4 w = {from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
+    *reinterpret_cast<T4*>(static_cast<T*>(g.C) + off) = w;
+  } else if constexpr (EPI == Epi::StoreF32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off) = v;
+  } else if constexpr (EPI == Epi::AddF32) {
+    f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off);
+    *p = *p + v;
+  } else if constexpr (EPI == Epi::PartialF32) {
+    float* base = static_cast<float*>(g.C) + (size_t)split * g.M * g.ldc;
+    *reinterpret_cast<f32x4*>(base + off) = v;
+  } else if constexpr (EPI == Epi::Relu2) {
+    T4 a;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float uf = fmaxf(v[r], 0.f);
+      a[r] = from_f32<T>(uf * uf);
+    }
+    *reinterpret_cast<T4*>(static_cast<T*>(g.C) + off) = a;
+  } else if constexpr (EPI == Epi::Relu2Bwd) {
+    // d relu(u)^2 / du = 2 relu(u) = 2 sqrt(a), a = relu(u)^2 as stored by Relu2
+    const T4 a = *reinterpret_cast<const T4*>(static_cast<const T*>(g.C2) + (size_t)m * g.ldc2 + n);
+    T4 w;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r] = from_f32<T>(v[r] * 2.f * sqrtf(to_f32(a[r])));
+    *reinterpret_cast<T4*>(static_cast<T*>(g.C) + off) = w;
+  }
+}
+
 template <typename T, bool AK, bool BKC, Epi EPI, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
+  constexpr int NTHR = WM * WN * 64;
   constexpr int VEC = Vec16<T>::N;
   constexpr int KB = 4 * VEC;                 // k per matrix-core fragment
   constexpr int BK = 128 / sizeof(T);         // k per LDS slab
@@ -117,7 +154,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 16, FN = TN / 16;
   typedef typename Vec16<T>::type V;
-  static_assert(WM * WN * kWave == kThreads, "4 wavefronts");
 
   __shared__ __align__(16) T smem[2 * (BM + BN) * LDSK];
 
@@ -151,8 +187,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   const T* __restrict__ A = static_cast<const T*>(g.A);
   const T* __restrict__ B = static_cast<const T*>(g.B);
 
-  SlabLoader<T, AK, BM> la;
-  SlabLoader<T, BKC, BN> lb;
+  SlabLoader<T, AK, BM, NTHR> la;
+  SlabLoader<T, BKC, BN, NTHR> lb;
   T* As0 = smem;
   T* Bs0 = smem + BM * LDSK;
   T* As1 = smem + (BM + BN) * LDSK;
@@ -209,36 +245,202 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     for (int j = 0; j < FN; ++j) {
       const int n = n0 + wn * TN + j * 16 + lg * 4;
       if (n >= g.N) continue;
-      const f32x4 v = acc[i][j];
-      const size_t off = (size_t)m * g.ldc + n;
-      typedef T T4 __attribute__((ext_vector_type(4)));
-      if constexpr (EPI == Epi::StoreT) {
-        T4 w = {from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
-        *reinterpret_cast<T4*>(static_cast<T*>(g.C) + off) = w;
-      } else if constexpr (EPI == Epi::StoreF32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off) = v;
-      } else if constexpr (EPI == Epi::AddF32) {
-        f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off);
-        *p = *p + v;
-      } else if constexpr (EPI == Epi::PartialF32) {
-        float* base = static_cast<float*>(g.C) + (size_t)split * g.M * g.ldc;
-        *reinterpret_cast<f32x4*>(base + off) = v;
-      } else if constexpr (EPI == Epi::Relu2) {
-        T4 u, a;
+      epilogue4<T, EPI>(g, split, m, n, acc[i][j]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 main-line contraction kernel, any operand order.
+// 256x256 tile, 8 wavefronts (2 x 4), 128x64 per wavefront computed with
+// v_mfma_f32_32x32x16_bf16 (4 x 2 tiles of 32x32, 128 fp32 accumulators).
+// Operand slabs are staged in LDS exactly as they sit in memory:
+//   K-contiguous operand: [256 rows][64 k] (+16-byte pad), fragments read with
+//     ds_read_b128 (lane l: row l%32, k = 8*(l/32)..+7);
+//   K-strided operand:    [64 k][256 rows] (+64-byte pad), fragments read with
+//     two LDS transpose reads (ds_read_b64_tr_b16): in each 16-lane group,
+//     source lane 4j+q names k row kb+j, columns c0+4q..+3, and output lane i
+//     receives k rows kb..kb+3 of column c0+i - so the same fragment layout
+//     comes out without any transpose pass in memory.
+// Fragments are double-buffered one 16-wide k step ahead (scheduling fences
+// keep the next step's reads ahead of this step's MFMAs). Global loads are
+// branch-free: indices past the matrix edge are clamped, which only feeds
+// output rows/columns that the epilogue never stores.
+// MFMA 32x32 output layout: lane l, value r holds row 8*(r/4) + 4*(l/32) + r%4,
+// column l%32 of the (B-rows x A-rows) product, i.e. C[m = l%32][n = ...].
+// ---------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <bool KC>
+struct BigSlab {
+  // K-contiguous: 256 x (64 + 8); K-strided: 64 x (256 + 32)
+  static constexpr int STRIDE = KC ? 72 : 288;
+  static constexpr int SIZE = KC ? 256 * 72 : 64 * 288;
+};
+
+// Global->register->LDS staging of one 256 x 64 operand slab by 512 threads.
+template <bool KC>
+struct BigLoader {
+  static constexpr int NL = 4;                 // 2048 16-byte chunks / 512 threads
+  const bf16* src[NL];
+  int dst[NL];
+  size_t kstep;                                // element offset of one 64-wide k step
+  bf16x8 reg[NL];
+  // rows: extent of the row (output) dimension; r0: first row of this tile
+  __device__ __forceinline__ void init(const bf16* base, int ld, int rows, int r0, int kbeg,
+                                       int tid) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          u[r] = from_f32<T>(v[r]);
-          const float uf = fmaxf(to_f32(u[r]), 0.f);
-          a[r] = from_f32<T>(uf * uf);
-        }
-        *reinterpret_cast<T4*>(static_cast<T*>(g.C) + off) = u;
-        *reinterpret_cast<T4*>(static_cast<T*>(g.C2) + (size_t)m * g.ldc2 + n) = a;
-      } else if constexpr (EPI == Epi::Relu2Bwd) {
-        const T4 u = *reinterpret_cast<const T4*>(static_cast<const T*>(g.C2) + (size_t)m * g.ldc2 + n);
-        T4 w;
+    for (int i = 0; i < NL; ++i) {
+      const int c = tid + 512 * i;
+      if constexpr (KC) {
+        const int row = c >> 3, col = (c & 7) * 8;
+        src[i] = base + (size_t)min(r0 + row, rows - 1) * ld + kbeg + col;
+        dst[i] = row * BigSlab<KC>::STRIDE + col;
+      } else {
+        const int kr = c >> 5, col = (c & 31) * 8;
+        src[i] = base + (size_t)(kbeg + kr) * ld + min(r0 + col, rows - 8);
+        dst[i] = kr * BigSlab<KC>::STRIDE + col;
+      }
+    }
+    kstep = KC ? 64 : (size_t)64 * ld;
+  }
+  __device__ __forceinline__ void load(int it) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[r] = from_f32<T>(v[r] * 2.f * fmaxf(to_f32(u[r]), 0.f));
-        *reinterpret_cast<T4*>(static_cast<T*>(g.C) + off) = w;
+    for (int i = 0; i < NL; ++i) reg[i] = *reinterpret_cast<const bf16x8*>(src[i] + it * kstep);
+  }
+  __device__ __forceinline__ void store(bf16* lds) const {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) *reinterpret_cast<bf16x8*>(lds + dst[i]) = reg[i];
+  }
+  // fragment of 32 rows starting at row `r` for k step `ks` (16 wide)
+  __device__ __forceinline__ static bf16x8 frag(const bf16* lds, int r, int ks, int lane) {
+    if constexpr (KC) {
+      return *reinterpret_cast<const bf16x8*>(lds + (r + (lane & 31)) * BigSlab<KC>::STRIDE +
+                                               ks * 16 + (lane >> 5) * 8);
+    } else {
+      const int q = lane >> 4, sl = lane & 15;
+      const bf16* p = lds + (ks * 16 + (q >> 1) * 8 + (sl >> 2)) * BigSlab<KC>::STRIDE + r +
+                      (q & 1) * 16 + 4 * (sl & 3);
+      const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+      const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * BigSlab<KC>::STRIDE));
+      const s16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      return __builtin_bit_cast(bf16x8, ab);
+    }
+  }
+};
+
+template <Epi EPI, bool AK, bool BKC>
+__global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int BM = 256, BN = 256, BK = 64;
+  constexpr int WM = 2, WN = 4, TM = BM / WM, TN = BN / WN;   // 128 x 64 per wave
+  constexpr int FM = TM / 32, FN = TN / 32;                   // 4 x 2 MFMA tiles
+  constexpr int SA = BigSlab<AK>::SIZE, SB = BigSlab<BKC>::SIZE;
+  __shared__ __align__(16) bf16 smem[2 * (SA + SB)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int wm = wave % WM, wn = wave / WM;
+
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  const int total = ntiles * g.splits;
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  if (bid >= total) return;
+  const int split = bid / ntiles;
+  const int t = bid - split * ntiles;
+  constexpr int GROUP = 8;
+  const int per_group = GROUP * tiles_n;
+  const int first_m = (t / per_group) * GROUP;
+  const int gsize = min(tiles_m - first_m, GROUP);
+  const int tm = first_m + (t % per_group) % gsize;
+  const int tn = (t % per_group) / gsize;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kps = g.K / g.splits;
+  const int kbeg = split * kps;
+  const int nk = kps / BK;
+
+  BigLoader<AK> la;
+  BigLoader<BKC> lb;
+  la.init(static_cast<const bf16*>(g.A), g.lda, g.M, m0, kbeg, tid);
+  lb.init(static_cast<const bf16*>(g.B), g.ldb, g.N, n0, kbeg, tid);
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  bf16* As0 = smem;
+  bf16* Bs0 = smem + SA;
+  bf16* As1 = smem + SA + SB;
+  bf16* Bs1 = As1 + SA;
+  la.load(0);
+  lb.load(0);
+  la.store(As0);
+  lb.store(Bs0);
+  __syncthreads();
+
+  const int ar = wm * TM, br = wn * TN;
+  for (int it = 0; it < nk; ++it) {
+    const bool odd = it & 1;
+    const bf16* As = odd ? As1 : As0;
+    const bf16* Bs = odd ? Bs1 : Bs0;
+    const bool more = it + 1 < nk;
+    if (more) {
+      la.load(it + 1);
+      lb.load(it + 1);
+    }
+    bf16x8 fa[2][FM], fb[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[0][i] = BigLoader<AK>::frag(As, ar + i * 32, 0, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[0][j] = BigLoader<BKC>::frag(Bs, br + j * 32, 0, lane);
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int cur = s & 1, nxt = cur ^ 1;
+      if (s + 1 < BK / 16) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) fa[nxt][i] = BigLoader<AK>::frag(As, ar + i * 32, s + 1, lane);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) fb[nxt][j] = BigLoader<BKC>::frag(Bs, br + j * 32, s + 1, lane);
+      }
+      // keep the next step's LDS reads ahead of this step's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) {
+      la.store(odd ? As0 : As1);
+      lb.store(odd ? Bs0 : Bs1);
+    }
+    __syncthreads();
+  }
+
+  // epilogue: lane holds C[m][n..n+3] for n = n_tile + 8q + 4*lh, q = 0..3
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * TM + i * 32 + l32;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * TN + j * 32 + q * 8 + lh * 4;
+        if (n >= g.N) continue;
+        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        epilogue4<bf16, EPI>(g, split, m, n, v);
       }
     }
   }
@@ -254,41 +456,56 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
   }
 }
 
-template <typename T, bool AK, bool BKC, Epi EPI>
-hipError_t launch(const GemmArgs& g, hipStream_t s) {
-  constexpr int BM = 128, BN = 128;
+template <typename T, bool AK, bool BKC, Epi EPI, int BM, int BN, int WM, int WN>
+hipError_t launch_tiles(const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.splits;
   const int grid = (tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_kernel<T, AK, BKC, EPI, BM, BN, 2, 2>), dim3(grid), dim3(kThreads), 0, s, g);
+  hipLaunchKernelGGL((gemm_kernel<T, AK, BKC, EPI, BM, BN, WM, WN>), dim3(grid), dim3(WM * WN * 64), 0,
+                     s, g);
   return hipGetLastError();
+}
+
+// Large bf16 products take the 256x256 tile when it still gives at least one
+// tile per CU; everything else (and fp32) the 128x128 tile.
+int choose_tile(bool bf16, const GemmArgs& g) {
+  if (!bf16 || g.tile == 128) return 128;
+  if (g.tile == 256) return 256;
+  const long big_tiles = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.splits;
+  return (g.M >= 256 && g.N >= 256 && big_tiles >= 256) ? 256 : 128;
+}
+
+template <typename T, bool AK, bool BKC, Epi EPI>
+hipError_t launch(const GemmArgs& g, hipStream_t s) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (choose_tile(true, g) == 256) {
+      const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.splits;
+      const int grid = (tiles + 7) / 8 * 8;
+      hipLaunchKernelGGL((gemm_bf16_kernel<EPI, AK, BKC>), dim3(grid), dim3(512), 0, s, g);
+      return hipGetLastError();
+    }
+  }
+  return launch_tiles<T, AK, BKC, EPI, 128, 128, 2, 2>(g, s);
+}
+
+template <typename T, bool AK, bool BKC>
+hipError_t dispatch_epi(Epi epi, const GemmArgs& g, hipStream_t s) {
+  switch (epi) {
+    case Epi::StoreT: return launch<T, AK, BKC, Epi::StoreT>(g, s);
+    case Epi::StoreF32: return launch<T, AK, BKC, Epi::StoreF32>(g, s);
+    case Epi::AddF32: return launch<T, AK, BKC, Epi::AddF32>(g, s);
+    case Epi::Relu2: return launch<T, AK, BKC, Epi::Relu2>(g, s);
+    case Epi::Relu2Bwd: return launch<T, AK, BKC, Epi::Relu2Bwd>(g, s);
+    case Epi::PartialF32: return launch<T, AK, BKC, Epi::PartialF32>(g, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T>
 hipError_t dispatch(bool ak, bool bk, Epi epi, const GemmArgs& g, hipStream_t s) {
-  if (ak && bk) {
-    switch (epi) {
-      case Epi::StoreT: return launch<T, true, true, Epi::StoreT>(g, s);
-      case Epi::StoreF32: return launch<T, true, true, Epi::StoreF32>(g, s);
-      case Epi::AddF32: return launch<T, true, true, Epi::AddF32>(g, s);
-      case Epi::Relu2: return launch<T, true, true, Epi::Relu2>(g, s);
-      default: break;
-    }
-  } else if (ak && !bk) {
-    switch (epi) {
-      case Epi::StoreT: return launch<T, true, false, Epi::StoreT>(g, s);
-      case Epi::StoreF32: return launch<T, true, false, Epi::StoreF32>(g, s);
-      case Epi::Relu2Bwd: return launch<T, true, false, Epi::Relu2Bwd>(g, s);
-      default: break;
-    }
-  } else if (!ak && !bk) {
-    switch (epi) {
-      case Epi::StoreF32: return launch<T, false, false, Epi::StoreF32>(g, s);
-      case Epi::AddF32: return launch<T, false, false, Epi::AddF32>(g, s);
-      case Epi::PartialF32: return launch<T, false, false, Epi::PartialF32>(g, s);
-      default: break;
-    }
-  }
-  return hipErrorInvalidValue;
+  if (ak && bk) return dispatch_epi<T, true, true>(epi, g, s);
+  if (ak && !bk) return dispatch_epi<T, true, false>(epi, g, s);
+  if (!ak && !bk) return dispatch_epi<T, false, false>(epi, g, s);
+  return dispatch_epi<T, false, true>(epi, g, s);
 }
 
 }  // namespace
@@ -301,6 +518,12 @@ hipError_t gemm(DType t, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs
   if (epi != Epi::PartialF32 && g.splits != 1) return hipErrorInvalidValue;
   return t == DType::BF16 ? dispatch<bf16>(a_kcontig, b_kcontig, epi, g, stream)
                           : dispatch<float>(a_kcontig, b_kcontig, epi, g, stream);
+}
+
+int gemm_tile(DType t, bool a_kcontig, bool b_kcontig, const GemmArgs& g) {
+  (void)a_kcontig;
+  (void)b_kcontig;
+  return choose_tile(t == DType::BF16, g);
 }
 
 hipError_t splitk_reduce(const float* part, int splits, size_t n, float* dst, bool accumulate,

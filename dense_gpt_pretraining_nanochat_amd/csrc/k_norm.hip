@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float* __restric
 }
 
 template <typename T, bool ACC, bool WRITE_G>
-__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restrict__ dy,
+__global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ dy,
                                                           const T* __restrict__ y,
                                                           const float* __restrict__ rinv, int M,
                                                           int d, float* __restrict__ dx,
@@ -114,14 +114,14 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float* __restric
   const int m = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (m >= M) return;
   const size_t base = (size_t)m * d;
-  f32x4 gy[kMaxVec];
+  float gy[kMaxVec][4];
   float yy[kMaxVec][4];
   float dot = 0.f;
 #pragma unroll
   for (int i = 0; i < kMaxVec; ++i) {
     const int c = (i * 64 + lane) * 4;
     if (c < d) {
-      gy[i] = *reinterpret_cast<const f32x4*>(dy + base + c);
+      load4(dy + base + c, gy[i]);
       load4(y + base + c, yy[i]);
       dot += gy[i][0] * yy[i][0] + gy[i][1] * yy[i][1] + gy[i][2] * yy[i][2] + gy[i][3] * yy[i][3];
     }
@@ -362,8 +362,9 @@ hipError_t rmsnorm_fwd(DType t, const float* x, int M, int d, float eps, void* y
 }
 
 template <typename T>
-static void launch_norm_bwd(const float* dy, const void* y, const float* rinv, int M, int d,
+static void launch_norm_bwd(const void* dyv, const void* y, const float* rinv, int M, int d,
                             float* dx, bool acc, void* g, hipStream_t s) {
+  const T* dy = static_cast<const T*>(dyv);
   const T* yt = static_cast<const T*>(y);
   T* gt = static_cast<T*>(g);
   dim3 grid(row_grid(M)), block(256);
@@ -373,7 +374,7 @@ static void launch_norm_bwd(const float* dy, const void* y, const float* rinv, i
   else hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, false, false>), grid, block, 0, s, dy, yt, rinv, M, d, dx, gt);
 }
 
-hipError_t rmsnorm_bwd(DType t, const float* dy, const void* y, const float* rinv, int M, int d,
+hipError_t rmsnorm_bwd(DType t, const void* dy, const void* y, const float* rinv, int M, int d,
                        float* dx, bool accumulate, void* g, hipStream_t s) {
   if (d % 4 || d > 2048) return hipErrorInvalidValue;
   if (t == DType::BF16) launch_norm_bwd<bf16>(dy, y, rinv, M, d, dx, accumulate, g, s);

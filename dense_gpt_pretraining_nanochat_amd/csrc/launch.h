@@ -15,8 +15,8 @@ enum class Epi {
   StoreT,      // C (element type T) = acc
   StoreF32,    // C (float) = acc
   AddF32,      // C (float) += acc
-  Relu2,       // C (T) = u = acc; C2 (T) = relu(u)^2  (u rounded to T first)
-  Relu2Bwd,    // C (T) = acc * 2 * relu(C2[m,n])       (C2 holds u, type T)
+  Relu2,       // C (T) = a = relu(acc)^2
+  Relu2Bwd,    // C (T) = acc * 2 * sqrt(C2[m,n])       (C2 holds a = relu(u)^2, type T)
   PartialF32,  // C (float) + split*M*ldc = acc over this split's K range
 };
 struct GemmArgs {
@@ -27,9 +27,15 @@ struct GemmArgs {
   int M, N, K;
   int lda, ldb, ldc, ldc2;
   int splits;        // K slices (PartialF32 only); K % (splits * 64) == 0
+  int tile;          // output tile edge: 0 = choose, 128 or 256 (256: bf16 only)
 };
 hipError_t gemm(DType t, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs& g,
                 hipStream_t stream);
+// Tile edge the kernel will use for these arguments (128 or 256).
+int gemm_tile(DType t, bool a_kcontig, bool b_kcontig, const GemmArgs& g);
+// out[c][r] = in[r][c] for an R x C matrix of T (row strides ld_in, ld_out)
+hipError_t transpose(DType t, const void* in, int R, int C, int ld_in, void* out, int ld_out,
+                     hipStream_t s);
 // dst[i] (=|+=) sum_s part[s*n + i], s = 0..splits-1, in a fixed order.
 hipError_t splitk_reduce(const float* part, int splits, size_t n, float* dst, bool accumulate,
                          hipStream_t stream);
@@ -41,8 +47,8 @@ hipError_t embed_norm_fwd(DType t, const void* E, const int32_t* tok, int M, int
 // y[m,:] = n(x[m,:]) as T, rinv[m]
 hipError_t rmsnorm_fwd(DType t, const float* x, int M, int d, float eps, void* y, float* rinv,
                        hipStream_t s);
-// dx[m,:] (=|+=) rinv*(dy - y*mean(dy*y)); optionally g = T(dx)
-hipError_t rmsnorm_bwd(DType t, const float* dy, const void* y, const float* rinv, int M, int d,
+// dx[m,:] (=|+=) rinv*(dy - y*mean(dy*y)); dy and y of type T; optionally g = T(dx)
+hipError_t rmsnorm_bwd(DType t, const void* dy, const void* y, const float* rinv, int M, int d,
                        float* dx, bool accumulate, void* g, hipStream_t s);
 // embedding-norm backward + deterministic scatter into dE (fp32, every row written)
 struct EmbedBwdScratch {

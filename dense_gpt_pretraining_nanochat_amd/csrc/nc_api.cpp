@@ -92,21 +92,31 @@ uint64_t param_elems(const Dims& D) {
 }
 
 // lm_head rows processed per chunk: bounds the fp32 logits buffer at
-// Mc * V * 4 bytes (2 GiB at V = 65,536).
-int64_t chunk_rows(const Dims& D) { return std::min<int64_t>(D.M, 8192); }
+// Mc * V * 4 bytes (4 GiB at V = 65,536).
+int64_t chunk_rows(const Dims& D) { return std::min<int64_t>(D.M, 16384); }
 
-// split-K factor for a weight gradient with `tiles` 128x128 output tiles and
-// contraction length K: aim for >= 1024 workgroups.
-int wgrad_splits(int64_t tiles, int64_t K) {
+// Split-K plan for a weight gradient dW[N1, N2] = X1^T X2 contracted over K
+// token rows (both operands read K-strided): the tile the kernel will pick,
+// and the smallest power-of-two split giving >= 2 workgroups per CU. K must
+// stay a multiple of 64 * splits.
+struct WgradPlan {
+  int tile;
+  int splits;
+  uint64_t partial_floats;
+};
+WgradPlan wgrad_plan(DType dt, int64_t N1, int64_t N2, int64_t K) {
+  WgradPlan p;
+  p.tile = (dt == DType::BF16 && N1 >= 256 && N2 >= 256) ? 256 : 128;
+  const int64_t tiles = ((N1 + p.tile - 1) / p.tile) * ((N2 + p.tile - 1) / p.tile);
   int s = 1;
-  while (s < 16 && tiles * s < 1024 && K % (64 * (2 * s)) == 0) s *= 2;
-  return s;
+  while (tiles * s < 512 && s < 32 && K % (64 * (2 * s)) == 0) s *= 2;
+  p.splits = s;
+  p.partial_floats = s > 1 ? (uint64_t)s * N1 * N2 : 0;
+  return p;
 }
 
-int64_t tiles_of(int64_t n1, int64_t n2) { return ((n1 + 127) / 128) * ((n2 + 127) / 128); }
-
 struct LayerActs {
-  uint64_t h, rinv1, qkv, rqk, o, lse, h2, rinv2, u, a;
+  uint64_t h, rinv1, qkv, rqk, o, lse, h2, rinv2, a;
 };
 
 struct Plan {
@@ -147,24 +157,20 @@ Plan plan_of(const Dims& D, bool bwd) {
     a.lse = take(M * D.H * 4);
     a.h2 = take(M * D.d * e);
     a.rinv2 = take(M * 4);
-    a.u = take(M * D.F * e);
     a.a = take(M * D.F * e);
     p.acts.push_back(a);
   }
   if (bwd) {
     p.dx = take(M * D.d * 4);
     p.g = take(M * D.d * e);
-    p.dh = take(M * D.d * 4);
+    p.dh = take(M * D.d * 4);        // T-typed input gradients; fp32 scratch for dE rows
     p.dbig = take(M * std::max(D.F, D.Q) * e);
     p.dout = take(M * D.d * e);
     p.delta = take(M * D.H * 4);
     uint64_t part = 0;
     const int64_t shapes[4][2] = {{D.Q, D.d}, {D.d, D.d}, {D.F, D.d}, {D.d, D.F}};
-    for (auto& s : shapes) {
-      const int sp = wgrad_splits(tiles_of(s[0], s[1]), D.M);
-      if (sp > 1) part = std::max<uint64_t>(part, (uint64_t)sp * s[0] * s[1] * 4);
-    }
-    p.partial = take(part);
+    for (auto& sh : shapes) part = std::max(part, wgrad_plan(D.dt, sh[0], sh[1], D.M).partial_floats);
+    p.partial = take(part * 4);
     p.counts = take((uint64_t)(D.V + 1) * 4);
     p.offsets = take((uint64_t)(D.V + 1) * 4);
     p.cursor = take((uint64_t)D.V * 4);
@@ -190,9 +196,10 @@ P* at(void* base, uint64_t off) {
   return reinterpret_cast<P*>(static_cast<char*>(base) + off);
 }
 
-// dW[N1,N2] = X1^T X2 over M rows
+// dW[N1,N2] = X1^T X2 over M rows (X1 [M, N1], X2 [M, N2]), both operands read
+// K-strided, split over K with a fixed-order fp32 reduction.
 hipError_t wgrad(DType dt, const void* X1, const void* X2, float* dW, float* partial, int64_t M,
-                 int N1, int N2, int splits, hipStream_t s) {
+                 int N1, int N2, const WgradPlan& p, hipStream_t s) {
   nc::GemmArgs g{};
   g.A = X1;
   g.B = X2;
@@ -202,15 +209,16 @@ hipError_t wgrad(DType dt, const void* X1, const void* X2, float* dW, float* par
   g.lda = N1;
   g.ldb = N2;
   g.ldc = N2;
-  g.splits = splits;
-  if (splits == 1) {
+  g.splits = p.splits;
+  g.tile = p.tile;
+  if (p.splits == 1) {
     g.C = dW;
     return nc::gemm(dt, false, false, Epi::StoreF32, g, s);
   }
   g.C = partial;
   hipError_t e = nc::gemm(dt, false, false, Epi::PartialF32, g, s);
   if (e != hipSuccess) return e;
-  return nc::splitk_reduce(partial, splits, (size_t)N1 * N2, dW, false, s);
+  return nc::splitk_reduce(partial, p.splits, (size_t)N1 * N2, dW, false, s);
 }
 
 hipError_t gemm_simple(DType dt, bool ak, bool bk, Epi epi, const void* A, const void* B, void* C,
@@ -275,7 +283,6 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
     void* qkv = at<char>(ws, A.qkv);
     void* o = at<char>(ws, A.o);
     void* h2 = at<char>(ws, A.h2);
-    void* u = at<char>(ws, A.u);
     void* a = at<char>(ws, A.a);
     const int base = 1 + 4 * l;
     HIPCHECK(nc::rmsnorm_fwd(dt, x, (int)M, D.d, eps, h, at<float>(ws, A.rinv1), s));
@@ -286,8 +293,8 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
     HIPCHECK(gemm_simple(dt, true, true, Epi::AddF32, o, W(base + 1), x, nullptr, M, D.d, D.d,
                          D.d, D.d, D.d, 0, s));
     HIPCHECK(nc::rmsnorm_fwd(dt, x, (int)M, D.d, eps, h2, at<float>(ws, A.rinv2), s));
-    HIPCHECK(gemm_simple(dt, true, true, Epi::Relu2, h2, W(base + 2), u, a, M, D.F, D.d, D.d,
-                         D.d, D.F, D.F, s));
+    HIPCHECK(gemm_simple(dt, true, true, Epi::Relu2, h2, W(base + 2), a, nullptr, M, D.F, D.d,
+                         D.d, D.d, D.F, 0, s));
     HIPCHECK(gemm_simple(dt, true, true, Epi::AddF32, a, W(base + 3), x, nullptr, M, D.d, D.F,
                          D.F, D.F, D.d, 0, s));
   }
@@ -295,7 +302,7 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
 
   // ---------------- lm_head + softcap cross-entropy, by row chunks ----------------
   const int64_t Mc = chunk_rows(D);
-  float* dxf = bwd ? at<float>(ws, P.dh) : nullptr;
+  void* dxf = bwd ? at<char>(ws, P.dh) : nullptr;
   const float w = 1.0f / (float)M;
   for (int64_t r0 = 0; r0 < M; r0 += Mc) {
     const int64_t mc = std::min<int64_t>(Mc, M - r0);
@@ -305,9 +312,11 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
     HIPCHECK(nc::softcap_ce(dt, logits, targets + r0, (int)mc, D.V, cfg->softcap, w,
                             loss_rows + r0, bwd ? dlog : nullptr, status, s));
     if (bwd) {
-      // dxf = dlog . U ; dU (+)= dlog^T . xf
-      HIPCHECK(gemm_simple(dt, true, false, Epi::StoreF32, dlog, W(iU), dxf + r0 * D.d, nullptr,
-                           mc, D.d, D.V, D.V, D.d, D.d, 0, s));
+      // dxf = dlog . U (U read K-strided: contraction over its rows)
+      HIPCHECK(gemm_simple(dt, true, false, Epi::StoreT, dlog, W(iU),
+                           static_cast<char*>(dxf) + r0 * D.d * e, nullptr, mc, D.d, D.V, D.V,
+                           D.d, D.d, 0, s));
+      // dU (+)= dlog^T . xf_chunk: both operands contracted over their rows
       HIPCHECK(gemm_simple(dt, false, false, r0 == 0 ? Epi::StoreF32 : Epi::AddF32, dlog, xfc,
                            G(iU), nullptr, D.V, D.d, (int)mc, D.V, D.d, D.d, 0, s));
     }
@@ -318,14 +327,15 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
   // ---------------- backward ----------------
   float* dx = at<float>(ws, P.dx);
   void* g = at<char>(ws, P.g);
-  float* dh = at<float>(ws, P.dh);
   void* dbig = at<char>(ws, P.dbig);
   void* dout = at<char>(ws, P.dout);
   float* delta = at<float>(ws, P.delta);
   float* partial = at<float>(ws, P.partial);
   HIPCHECK(nc::rmsnorm_bwd(dt, dxf, xf, rinvf, (int)M, D.d, dx, false, g, s));
-  const int sQ = wgrad_splits(tiles_of(D.Q, D.d), M), sO = wgrad_splits(tiles_of(D.d, D.d), M);
-  const int sFC = wgrad_splits(tiles_of(D.F, D.d), M), sPR = wgrad_splits(tiles_of(D.d, D.F), M);
+  const WgradPlan pQ = wgrad_plan(dt, D.Q, D.d, M), pO = wgrad_plan(dt, D.d, D.d, M);
+  const WgradPlan pFC = wgrad_plan(dt, D.F, D.d, M), pPR = wgrad_plan(dt, D.d, D.F, M);
+  void* dh = at<char>(ws, P.dh);
+  const int Mi = (int)M;
   for (int l = D.L - 1; l >= 0; --l) {
     const LayerActs& A = P.acts[l];
     const int base = 1 + 4 * l;
@@ -333,36 +343,35 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
     void* qkv = at<char>(ws, A.qkv);
     void* o = at<char>(ws, A.o);
     void* h2 = at<char>(ws, A.h2);
-    void* u = at<char>(ws, A.u);
     void* a = at<char>(ws, A.a);
     // MLP: x_out = x_mid + relu(h2 Wfc^T)^2 Wpr^T
-    HIPCHECK(wgrad(dt, g, a, G(base + 3), partial, M, D.d, D.F, sPR, s));
-    HIPCHECK(gemm_simple(dt, true, false, Epi::Relu2Bwd, g, W(base + 3), dbig, u, M, D.F, D.d,
+    HIPCHECK(wgrad(dt, g, a, G(base + 3), partial, M, D.d, D.F, pPR, s));
+    HIPCHECK(gemm_simple(dt, true, false, Epi::Relu2Bwd, g, W(base + 3), dbig, a, M, D.F, D.d,
                          D.d, D.F, D.F, D.F, s));
-    HIPCHECK(wgrad(dt, dbig, h2, G(base + 2), partial, M, D.F, D.d, sFC, s));
-    HIPCHECK(gemm_simple(dt, true, false, Epi::StoreF32, dbig, W(base + 2), dh, nullptr, M, D.d,
+    HIPCHECK(wgrad(dt, dbig, h2, G(base + 2), partial, M, D.F, D.d, pFC, s));
+    HIPCHECK(gemm_simple(dt, true, false, Epi::StoreT, dbig, W(base + 2), dh, nullptr, M, D.d,
                          D.F, D.F, D.d, D.d, 0, s));
-    HIPCHECK(nc::rmsnorm_bwd(dt, dh, h2, at<float>(ws, A.rinv2), (int)M, D.d, dx, true, g, s));
+    HIPCHECK(nc::rmsnorm_bwd(dt, dh, h2, at<float>(ws, A.rinv2), Mi, D.d, dx, true, g, s));
     // attention: x_mid = x_in + o Wo^T
-    HIPCHECK(wgrad(dt, g, o, G(base + 1), partial, M, D.d, D.d, sO, s));
+    HIPCHECK(wgrad(dt, g, o, G(base + 1), partial, M, D.d, D.d, pO, s));
     HIPCHECK(gemm_simple(dt, true, false, Epi::StoreT, g, W(base + 1), dout, nullptr, M, D.d, D.d,
                          D.d, D.d, D.d, 0, s));
     HIPCHECK(nc::attn_bwd_delta(dt, o, dout, D.B, D.T, D.H, delta, s));
     HIPCHECK(nc::attn_bwd(dt, qkv, D.Q, dout, at<float>(ws, A.lse), delta, D.B, D.T, D.H, dbig,
                           D.Q, s));
-    HIPCHECK(nc::rope_qknorm_bwd(dt, dbig, D.Q, qkv, D.Q, (int)M, D.T, D.H, cs,
+    HIPCHECK(nc::rope_qknorm_bwd(dt, dbig, D.Q, qkv, D.Q, Mi, D.T, D.H, cs,
                                  at<float>(ws, A.rqk), s));
-    HIPCHECK(wgrad(dt, dbig, h, G(base + 0), partial, M, D.Q, D.d, sQ, s));
-    HIPCHECK(gemm_simple(dt, true, false, Epi::StoreF32, dbig, W(base + 0), dh, nullptr, M, D.d,
+    HIPCHECK(wgrad(dt, dbig, h, G(base + 0), partial, M, D.Q, D.d, pQ, s));
+    HIPCHECK(gemm_simple(dt, true, false, Epi::StoreT, dbig, W(base + 0), dh, nullptr, M, D.d,
                          D.Q, D.Q, D.d, D.d, 0, s));
-    HIPCHECK(nc::rmsnorm_bwd(dt, dh, h, at<float>(ws, A.rinv1), (int)M, D.d, dx, true, g, s));
+    HIPCHECK(nc::rmsnorm_bwd(dt, dh, h, at<float>(ws, A.rinv1), Mi, D.d, dx, true, g, s));
   }
   nc::EmbedBwdScratch es;
   es.counts = at<int32_t>(ws, P.counts);
   es.offsets = at<int32_t>(ws, P.offsets);
   es.cursor = at<int32_t>(ws, P.cursor);
   es.list = at<int32_t>(ws, P.list);
-  es.de = dh;
+  es.de = static_cast<float*>(dh);
   HIPCHECK(nc::embed_bwd(dt, W(iE), tokens, rinv0, dx, (int)M, D.d, D.V, es, G(iE), s));
   return NC_OK;
 }
@@ -500,7 +509,7 @@ int nc_op_gemm(int32_t dtype, int32_t a_kcontig, int32_t b_kcontig, int32_t epil
                const void* A, const void* B, void* C, void* C2, int32_t M, int32_t N, int32_t K,
                int32_t lda, int32_t ldb, int32_t ldc, void* stream) {
   if (bad_dtype(dtype) || epilogue < 0 || epilogue > 4) return NC_ERR_ARG;
-  if (!A || !B || !C || ((epilogue == 3 || epilogue == 4) && !C2)) return NC_ERR_NULL;
+  if (!A || !B || !C || (epilogue == 4 && !C2)) return NC_ERR_NULL;
   if (M <= 0 || N <= 0 || K <= 0 || M % 16 || N % 16 || K % 64) return NC_ERR_ARG;
   const int vec = dtype == NC_BF16 ? 8 : 4;
   if (lda % vec || ldb % vec || ldc % 4) return NC_ERR_ARG;
@@ -517,8 +526,23 @@ int nc_op_wgrad(int32_t dtype, const void* X1, const void* X2, float* dW, float*
   if (!X1 || !X2 || !dW || (splits > 1 && !partial)) return NC_ERR_NULL;
   if (M <= 0 || N1 <= 0 || N2 <= 0 || N1 % 16 || N2 % 16 || splits < 1 || M % (64 * splits))
     return NC_ERR_ARG;
-  HIPCHECK(wgrad(dt_of(dtype), X1, X2, dW, partial, M, N1, N2, splits,
-                 static_cast<hipStream_t>(stream)));
+  WgradPlan p;
+  p.tile = 0;
+  p.splits = splits;
+  HIPCHECK(wgrad(dt_of(dtype), X1, X2, dW, partial, M, N1, N2, p, static_cast<hipStream_t>(stream)));
+  return NC_OK;
+}
+
+int nc_op_transpose(int32_t dtype, const void* in, int32_t R, int32_t C, int32_t ld_in, void* out,
+                    int32_t ld_out, void* stream) {
+  if (bad_dtype(dtype)) return NC_ERR_ARG;
+  if (!in || !out) return NC_ERR_NULL;
+  const int vec = dtype == NC_BF16 ? 8 : 4;
+  if (R <= 0 || C <= 0 || R % vec || C % vec || ld_in % vec || ld_out % vec || ld_in < C ||
+      ld_out < R)
+    return NC_ERR_ARG;
+  HIPCHECK(nc::transpose(dt_of(dtype), in, R, C, ld_in, out, ld_out,
+                         static_cast<hipStream_t>(stream)));
   return NC_OK;
 }
 
@@ -531,7 +555,7 @@ int nc_op_rmsnorm_fwd(int32_t dtype, const float* x, int32_t M, int32_t d, float
   return NC_OK;
 }
 
-int nc_op_rmsnorm_bwd(int32_t dtype, const float* dy, const void* y, const float* rinv, int32_t M,
+int nc_op_rmsnorm_bwd(int32_t dtype, const void* dy, const void* y, const float* rinv, int32_t M,
                       int32_t d, float* dx, int32_t accumulate, void* g, void* stream) {
   if (bad_dtype(dtype)) return NC_ERR_ARG;
   if (!dy || !y || !rinv || !dx) return NC_ERR_NULL;

@@ -158,8 +158,9 @@ int nc_last_hip_error(void);
 
 /* C[M,N] (op)= sum_k A(m,k) B(n,k), with A(m,k) = A[m*lda+k] when a_kcontig,
  * else A[k*lda+m] (same for B). epilogue: 0 store T, 1 store fp32,
- * 2 add into fp32, 3 relu^2 (C = u as T, C2 = relu(u)^2 as T),
- * 4 relu^2 backward (C = acc * 2*relu(C2) as T, C2 = u as T).
+ * 2 add into fp32, 3 relu^2 (C = relu(acc)^2 as T), 4 relu^2 backward
+ * (C = acc * 2*sqrt(C2) as T, where C2 holds a = relu(u)^2 as stored by
+ * epilogue 3, so 2*sqrt(a) = 2*relu(u)). C2 has row stride ldc.
  * M, N multiples of 16; K a multiple of 64. */
 int nc_op_gemm(int32_t dtype, int32_t a_kcontig, int32_t b_kcontig, int32_t epilogue,
                const void* A, const void* B, void* C, void* C2, int32_t M, int32_t N, int32_t K,
@@ -171,11 +172,17 @@ int nc_op_gemm(int32_t dtype, int32_t a_kcontig, int32_t b_kcontig, int32_t epil
 int nc_op_wgrad(int32_t dtype, const void* X1, const void* X2, float* dW, float* partial,
                 int32_t M, int32_t N1, int32_t N2, int32_t splits, void* stream);
 
+/* out[c][r] = in[r][c] for an R x C matrix of T (row strides ld_in, ld_out;
+ * R, C and both strides multiples of 16 bytes' worth of elements). */
+int nc_op_transpose(int32_t dtype, const void* in, int32_t R, int32_t C, int32_t ld_in, void* out,
+                    int32_t ld_out, void* stream);
+
 /* y = n(x) (T), rinv per row; x fp32 [M,d]. */
 int nc_op_rmsnorm_fwd(int32_t dtype, const float* x, int32_t M, int32_t d, float eps, void* y,
                       float* rinv, void* stream);
-/* dx (=|+=) rinv*(dy - y*mean(dy*y)); g (optional) = T(dx). */
-int nc_op_rmsnorm_bwd(int32_t dtype, const float* dy, const void* y, const float* rinv, int32_t M,
+/* dx (=|+=) rinv*(dy - y*mean(dy*y)) with dy and y of type T, dx fp32;
+ * g (optional) = T(dx). */
+int nc_op_rmsnorm_bwd(int32_t dtype, const void* dy, const void* y, const float* rinv, int32_t M,
                       int32_t d, float* dx, int32_t accumulate, void* g, void* stream);
 /* In place on qkv [B*T, d+256]: rotary then RMSNorm on the H query heads and
  * the key head; rinv_qk [B*T, H+1]; cs scratch >= T*128 floats. */
