@@ -98,7 +98,7 @@ def test_argument_checks_before_any_launch():
     assert L.nc_init_params(1, ctypes.byref(cfg), p(a + 128), None) == -4
     assert L.nc_op_gemm(1, 1, 1, 9, p(a), p(a), p(a), None, 16, 16, 64, 64, 64, 16, None) == -7
     assert L.nc_op_gemm(1, 1, 1, 0, p(a), p(a), p(a), None, 16, 16, 48, 64, 64, 16, None) == -7
-    assert L.nc_op_gemm(1, 1, 1, 3, p(a), p(a), p(a), None, 16, 16, 64, 64, 64, 16, None) == -3
+    assert L.nc_op_gemm(1, 1, 1, 4, p(a), p(a), p(a), None, 16, 16, 64, 64, 64, 16, None) == -3
     assert L.nc_op_attn_fwd(1, p(a), 1, 96, 1, p(a), p(a), None) == -7
 
 
