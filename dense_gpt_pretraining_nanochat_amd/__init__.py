@@ -71,7 +71,8 @@ _SIGS = {
     "nc_op_rope_qknorm_fwd": [_I32, _P, _I32, _I32, _I32, _F32, _F32, _P, _P, _P],
     "nc_op_rope_qknorm_bwd": [_I32, _P, _P, _I32, _I32, _I32, _P, _P, _P],
     "nc_op_attn_fwd": [_I32, _P, _I32, _I32, _I32, _P, _P, _P],
-    "nc_op_attn_bwd": [_I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P],
+    "nc_op_attn_bwd_scratch_bytes": [_I32, _I32],
+    "nc_op_attn_bwd": [_I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P],
     "nc_op_softcap_ce": [_I32, _P, _P, _I32, _I32, _F32, _F32, _P, _P, _P, _P],
 }
 
@@ -87,7 +88,8 @@ def lib():
         for name, args in _SIGS.items():
             f = getattr(L, name)
             f.argtypes = args
-            f.restype = ctypes.c_char_p if name == "nc_status_string" else ctypes.c_int
+            f.restype = {"nc_status_string": ctypes.c_char_p,
+                         "nc_op_attn_bwd_scratch_bytes": ctypes.c_uint64}.get(name, ctypes.c_int)
         _lib = L
     return _lib
 
@@ -230,9 +232,18 @@ def nc_op_attn_fwd(dtype, qkv, B, T, H, o, lse, stream=None):
                                 _stream(stream)), "nc_op_attn_fwd")
 
 
-def nc_op_attn_bwd(dtype, qkv, o, dout, lse, delta, B, T, H, dqkv, stream=None):
+def nc_op_attn_bwd_scratch_bytes(B, T) -> int:
+    return int(lib().nc_op_attn_bwd_scratch_bytes(B, T))
+
+
+def nc_op_attn_bwd(dtype, qkv, o, dout, lse, delta, B, T, H, dqkv, scratch=None, stream=None):
+    """scratch: a device buffer of nc_op_attn_bwd_scratch_bytes(B, T) bytes
+    (allocated here through torch when not given)."""
+    if scratch is None:
+        import torch
+        scratch = torch.empty(nc_op_attn_bwd_scratch_bytes(B, T), dtype=torch.uint8, device="cuda")
     _check(lib().nc_op_attn_bwd(_dt(dtype), _ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
-                                B, T, H, _ptr(dqkv), _stream(stream)), "nc_op_attn_bwd")
+                                B, T, H, _ptr(dqkv), _ptr(scratch), _stream(stream)), "nc_op_attn_bwd")
 
 
 def nc_op_softcap_ce(dtype, logits, targets, R, V, cap, w, loss_rows, dlogits, status, stream=None):

@@ -24,10 +24,12 @@
 // column is one query row: the softmax statistics stay in the lane and P^T
 // feeds O^T += V^T P^T straight from registers.
 //
-// Backward: dK/dV are summed over all heads and all later queries by the
-// workgroup that owns a 128-key block (32 keys per wavefront, accumulators in
-// registers); dQ comes from a second kernel shaped like the forward. Neither
-// uses atomics, so results are bitwise reproducible.
+// Backward: dK/dV of a 128-key block are summed over all heads and one chunk
+// of up to 512 later query tokens by one workgroup (32 keys per wavefront,
+// accumulators in registers), which keeps the work items even under the
+// causal mask; a second pass adds the chunk partials in a fixed order. dQ
+// comes from a kernel shaped like the forward. No atomics anywhere, so the
+// results are bitwise reproducible.
 #include <math.h>
 
 #include "common.h"
@@ -40,6 +42,7 @@ constexpr int D = 128;
 constexpr int BQ = 32;        // query tokens per workgroup (fwd, dQ) / per step (dK/dV)
 constexpr int BKV = 64;       // keys per tile (fwd, dQ)
 constexpr int BKW = 128;      // keys per dK/dV workgroup (4 wavefronts x 32)
+constexpr int QCH = 512;      // query tokens per dK/dV work item (partial sums per chunk)
 constexpr int kMaxHeadsPerWG = 8;     // forward
 constexpr int kMaxHeadsPerWGdQ = 4;   // dQ keeps Q, dO and dQ tiles in registers
 constexpr float kLog2e = 1.4426950408889634f;
@@ -335,16 +338,25 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o
                                                          const T* __restrict__ dout, int Tn,
                                                          int H, size_t total,
                                                          float* __restrict__ delta) {
-  const size_t w = blockIdx.x * 4ull + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  // 16 lanes per (token, head) row of 128, 16-byte loads
+  typedef AttnTypes<T> A;
+  constexpr int PER = D / 16;                  // elements per lane
+  const size_t w = blockIdx.x * 16ull + (threadIdx.x >> 4);
+  const int sl = threadIdx.x & 15;
   if (w >= total) return;
   const size_t m = w / H;
   const int h = (int)(w % H);
-  const size_t off = m * (size_t)(H * D) + h * D;
-  float s = to_f32(o[off + lane]) * to_f32(dout[off + lane]) +
-            to_f32(o[off + lane + 64]) * to_f32(dout[off + lane + 64]);
-  s = wave_sum(s);
-  if (lane == 0) {
+  const size_t off = m * (size_t)(H * D) + h * D + sl * PER;
+  float s = 0.f;
+#pragma unroll
+  for (int v = 0; v < PER / A::VEC; ++v) {
+    const typename A::V a = *reinterpret_cast<const typename A::V*>(o + off + v * A::VEC);
+    const typename A::V b = *reinterpret_cast<const typename A::V*>(dout + off + v * A::VEC);
+#pragma unroll
+    for (int e = 0; e < A::VEC; ++e) s += to_f32(a[e]) * to_f32(b[e]);
+  }
+  s = lane16_sum(s);
+  if (sl == 0) {
     const size_t b = m / Tn, t = m % Tn;
     delta[(b * H + h) * Tn + t] = s;
   }
@@ -490,10 +502,27 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64) void attn_bwd_dq_kernel(
 // backward, dK and dV: one workgroup per 128-key block, 4 wavefronts x 32
 // keys, looping over every later 32-token query block and every head.
 // --------------------------------------------------------------------------
+__host__ __device__ inline int dkv_chunks(int Tn, int kblk) {
+  return (Tn - kblk * BKW + QCH - 1) / QCH;
+}
+
+// Work item i (per batch) -> (key block, query chunk), key blocks in order.
+__device__ inline void dkv_item(int Tn, int i, int* kblk, int* chunk) {
+  const int nkb = (Tn + BKW - 1) / BKW;
+  int kb = 0;
+  for (; kb < nkb; ++kb) {
+    const int n = dkv_chunks(Tn, kb);
+    if (i < n) break;
+    i -= n;
+  }
+  *kblk = kb;
+  *chunk = i;
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     const T* __restrict__ qkv, int ldq, const T* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, int Tn, int H, T* __restrict__ dqkv, int ldd) {
+    const float* __restrict__ delta, int B, int Tn, int H, float* __restrict__ part) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
   constexpr int TILE = BQ * A::KSTR;
@@ -501,10 +530,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   __shared__ __align__(16) T Os[2 * TILE];
   __shared__ float stat_s[2][2 * BQ];          // lse (log2 domain), then delta
 
-  const int nkb = (Tn + BKW - 1) / BKW;
-  const int b = blockIdx.x / nkb;
-  const int kblk = blockIdx.x % nkb;           // low key blocks carry the most work: first
+  // items are numbered item-major, batch-minor: early (long) key blocks start first
+  const int b = blockIdx.x % B;
+  int kblk, chunk;
+  dkv_item(Tn, blockIdx.x / B, &kblk, &chunk);
   const int kv0 = kblk * BKW;
+  const int q0 = kv0 + chunk * QCH;                      // first query token of this chunk
+  const int q1 = min(Tn, q0 + QCH);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const size_t row0 = (size_t)b * Tn;
@@ -528,15 +560,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   const float sc = kLog2e / sqrtf((float)D);
   constexpr int NPT = CFrag<T>::NPT;
 
-  // iteration space: query blocks tq0 = kv0, kv0+32, ... and heads h
-  const int nqb = (Tn - kv0) / BQ;
+  // iteration space: query blocks tq0 = q0, q0+32, ... < q1 and heads h
+  const int nqb = (q1 - q0) / BQ;
   const int niter = nqb * H;
   constexpr bool PFT = kPrefetch(sizeof(T));
-  auto qsrc = [&](int i) { return qkv + (row0 + kv0 + (i / H) * BQ) * ldq + (i % H) * D; };
-  auto osrc = [&](int i) { return dout + (row0 + kv0 + (i / H) * BQ) * ldo + (i % H) * D; };
+  auto qsrc = [&](int i) { return qkv + (row0 + q0 + (i / H) * BQ) * ldq + (i % H) * D; };
+  auto osrc = [&](int i) { return dout + (row0 + q0 + (i / H) * BQ) * ldo + (i % H) * D; };
   auto stats = [&](int i, int buf) {
     if (tid < 2 * BQ) {
-      const int h = i % H, t = kv0 + (i / H) * BQ + (tid % BQ);
+      const int h = i % H, t = q0 + (i / H) * BQ + (tid % BQ);
       const size_t idx = ((size_t)b * H + h) * Tn + t;
       stat_s[buf][tid] = tid < BQ ? lse[idx] * kLog2e : delta[idx];
     }
@@ -552,7 +584,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   __syncthreads();
 
   for (int it = 0; it < niter; ++it) {
-    const int tq0 = kv0 + (it / H) * BQ;
+    const int tq0 = q0 + (it / H) * BQ;
     const T* Q = Qs + (it & 1) * TILE;
     const T* O = Os + (it & 1) * TILE;
     const float* lse_s = stat_s[it & 1];
@@ -641,24 +673,39 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     __syncthreads();
   }
   if (!kact) return;
-  const float scale = 1.0f / sqrtf((float)D);
+  // fp32 partial sums of this query chunk: part[chunk][token][0..127 dK, 128..255 dV]
+  const size_t M = (size_t)B * Tn;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    const size_t r = row0 + key0 + kt * 16 + l16;
-    T* dkdst = dqkv + r * ldd + H * D;
-    T* dvdst = dqkv + r * ldd + (H + 1) * D;
+    float* dst = part + ((size_t)chunk * M + row0 + key0 + kt * 16 + l16) * (2 * D);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      typename A::T4 wk, wv;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        wk[q] = from_f32<T>(dk[dt][kt][q] * scale);
-        wv[q] = from_f32<T>(dv[dt][kt][q]);
-      }
-      *reinterpret_cast<typename A::T4*>(dkdst + dt * 16 + lg * 4) = wk;
-      *reinterpret_cast<typename A::T4*>(dvdst + dt * 16 + lg * 4) = wv;
+      *reinterpret_cast<f32x4*>(dst + dt * 16 + lg * 4) = dk[dt][kt];
+      *reinterpret_cast<f32x4*>(dst + D + dt * 16 + lg * 4) = dv[dt][kt];
     }
   }
+}
+
+// dK (scaled by 1/sqrt(D)) and dV of each key: the sum of its chunk partials
+// in chunk order, written into the key and value columns of dqkv.
+template <typename T>
+__global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(const float* __restrict__ part,
+                                                              int B, int Tn, int H,
+                                                              T* __restrict__ dqkv, int ldd) {
+  const size_t M = (size_t)B * Tn;
+  const size_t row = blockIdx.x * 4ull + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int lane = threadIdx.x & 63;
+  const int t = (int)(row % Tn);
+  const int nch = dkv_chunks(Tn, t / BKW);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < nch; ++c)
+    acc += *reinterpret_cast<const f32x4*>(part + ((size_t)c * M + row) * (2 * D) + lane * 4);
+  const float scale = lane < 32 ? 1.0f / sqrtf((float)D) : 1.0f;
+  typedef T T4 __attribute__((ext_vector_type(4)));
+  T4 w = {from_f32<T>(acc[0] * scale), from_f32<T>(acc[1] * scale), from_f32<T>(acc[2] * scale),
+          from_f32<T>(acc[3] * scale)};
+  *reinterpret_cast<T4*>(dqkv + row * ldd + H * D + lane * 4) = w;
 }
 
 // heads per workgroup <= maxw; at least 4 wavefronts so K/V staging has enough threads
@@ -689,7 +736,7 @@ hipError_t attn_fwd(DType t, const void* qkv, int ldq, int B, int T, int H, void
 hipError_t attn_bwd_delta(DType t, const void* o, const void* dout, int B, int T, int H,
                           float* delta, hipStream_t s) {
   const size_t total = (size_t)B * T * H;
-  dim3 grid((unsigned)((total + 3) / 4)), block(256);
+  dim3 grid((unsigned)((total + 15) / 16)), block(256);
   if (t == DType::BF16)
     hipLaunchKernelGGL(attn_delta_kernel<bf16>, grid, block, 0, s, static_cast<const bf16*>(o),
                        static_cast<const bf16*>(dout), T, H, total, delta);
@@ -699,24 +746,35 @@ hipError_t attn_bwd_delta(DType t, const void* o, const void* dout, int B, int T
   return hipGetLastError();
 }
 
+size_t attn_bwd_scratch_floats(int B, int T) {
+  return (size_t)dkv_chunks(T, 0) * B * T * 2 * D;
+}
+
 hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const float* lse,
-                    const float* delta, int B, int T, int H, void* dqkv, int ldd, hipStream_t s) {
+                    const float* delta, int B, int T, int H, void* dqkv, int ldd, float* scratch,
+                    hipStream_t s) {
   if (T % BKV || H < 1 || H > 16) return hipErrorInvalidValue;
   int hpg, ng, waves;
   head_groups(H, kMaxHeadsPerWGdQ, &hpg, &ng, &waves);
   dim3 gq(B * (T / BQ) * ng), bq(64 * waves);
-  dim3 gk(B * ((T + BKW - 1) / BKW)), bk(256);
+  int items = 0;
+  for (int kb = 0; kb < (T + BKW - 1) / BKW; ++kb) items += dkv_chunks(T, kb);
+  dim3 gk(B * items), bk(256);
+  const size_t M = (size_t)B * T;
+  dim3 gr((unsigned)((M + 3) / 4)), br(256);
   if (t == DType::BF16) {
     const bf16* q = static_cast<const bf16*>(qkv);
     const bf16* d = static_cast<const bf16*>(dout);
     bf16* g = static_cast<bf16*>(dqkv);
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<bf16>, gk, bk, 0, s, q, ldq, d, lse, delta, T, H, g, ldd);
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<bf16>, gk, bk, 0, s, q, ldq, d, lse, delta, B, T, H, scratch);
+    hipLaunchKernelGGL(attn_dkv_reduce_kernel<bf16>, gr, br, 0, s, scratch, B, T, H, g, ldd);
     hipLaunchKernelGGL(attn_bwd_dq_kernel<bf16>, gq, bq, 0, s, q, ldq, d, lse, delta, T, H, hpg, g, ldd);
   } else {
     const float* q = static_cast<const float*>(qkv);
     const float* d = static_cast<const float*>(dout);
     float* g = static_cast<float*>(dqkv);
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<float>, gk, bk, 0, s, q, ldq, d, lse, delta, T, H, g, ldd);
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<float>, gk, bk, 0, s, q, ldq, d, lse, delta, B, T, H, scratch);
+    hipLaunchKernelGGL(attn_dkv_reduce_kernel<float>, gr, br, 0, s, scratch, B, T, H, g, ldd);
     hipLaunchKernelGGL(attn_bwd_dq_kernel<float>, gq, bq, 0, s, q, ldq, d, lse, delta, T, H, hpg, g, ldd);
   }
   return hipGetLastError();

@@ -13,7 +13,9 @@
 // One workgroup per row holds the whole fp32 row in registers (up to 64
 // values per thread at V = 65,536), so each logit is read once from HBM and
 // each gradient written once (6 bytes per logit in bf16 mode). Because
-// |z| <= c, exp(z - c) never overflows and needs no running maximum.
+// |z| <= c, exp(z - c) never overflows and needs no running maximum. tanh is
+// evaluated from one exponential (see tanh_fast) to keep the pass bound by
+// memory rather than by transcendental throughput.
 #include <math.h>
 
 #include "common.h"
@@ -23,6 +25,13 @@ namespace nc {
 namespace {
 
 constexpr int kMaxChunks = 16;   // float4 chunks per thread: 16 * 4 * 1024 = 65,536
+
+// tanh(x) = sign(x) (1 - e) / (1 + e) with e = exp(-2|x|): one exponential and
+// one reciprocal; e in (0, 1] so nothing overflows.
+__device__ __forceinline__ float tanh_fast(float x) {
+  const float e = __expf(-2.0f * fabsf(x));
+  return copysignf((1.0f - e) * __frcp_rn(1.0f + e), x);
+}
 
 template <typename T>
 __global__ __launch_bounds__(1024) void softcap_ce_kernel(const float* __restrict__ logits,
@@ -37,7 +46,8 @@ __global__ __launch_bounds__(1024) void softcap_ce_kernel(const float* __restric
   const float* src = logits + (size_t)row * V;
   const float inv_cap = 1.0f / cap;
 
-  f32x4 z[kMaxChunks];
+  // t = tanh(l / c) = z / c is kept per logit; exp(z - c) = exp(c (t - 1))
+  f32x4 tz[kMaxChunks];
   float se = 0.f;
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
@@ -46,8 +56,8 @@ __global__ __launch_bounds__(1024) void softcap_ce_kernel(const float* __restric
       const f32x4 l = *reinterpret_cast<const f32x4*>(src + c);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        z[i][e] = cap * tanhf(l[e] * inv_cap);
-        se += expf(z[i][e] - cap);
+        tz[i][e] = tanh_fast(l[e] * inv_cap);
+        se += __expf(cap * (tz[i][e] - 1.0f));
       }
     }
   }
@@ -59,7 +69,7 @@ __global__ __launch_bounds__(1024) void softcap_ce_kernel(const float* __restric
     t = t < 0 ? 0 : V - 1;
   }
   if (tid == 0) {
-    const float zt = cap * tanhf(src[t] * inv_cap);
+    const float zt = cap * tanh_fast(src[t] * inv_cap);
     loss_rows[row] = cap + logf(sum) - zt;
   }
   if (dl == nullptr) return;                       // loss only
@@ -71,9 +81,9 @@ __global__ __launch_bounds__(1024) void softcap_ce_kernel(const float* __restric
       float g[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float zc = z[i][e] * inv_cap;
-        const float p = expf(z[i][e] - cap) * inv_sum - (c + e == t ? 1.0f : 0.0f);
-        g[e] = w * p * (1.0f - zc * zc);
+        const float tc = tz[i][e];
+        const float p = __expf(cap * (tc - 1.0f)) * inv_sum - (c + e == t ? 1.0f : 0.0f);
+        g[e] = w * p * (1.0f - tc * tc);
       }
       typedef T T4 __attribute__((ext_vector_type(4)));
       T4 v = {from_f32<T>(g[0]), from_f32<T>(g[1]), from_f32<T>(g[2]), from_f32<T>(g[3])};

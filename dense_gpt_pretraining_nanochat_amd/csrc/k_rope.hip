@@ -7,8 +7,8 @@
 // t the position inside the sequence; then the head vector is normalised by
 // its RMS (the two steps commute exactly, rotation being orthogonal).
 //
-// One wavefront per head vector: lane j holds elements j and j + 64, so the
-// rotation is lane-local and the norm is one shuffle-tree reduction.
+// Sixteen lanes per head vector, each holding four elements of either half, so
+// the rotation is lane-local and the norm is a 16-lane shuffle reduction.
 // The kernels work in place on the fused [tokens, q heads | k | v] buffer.
 #include "common.h"
 #include "launch.h"
@@ -28,27 +28,58 @@ __global__ void rope_table_kernel(int T, int half, double base, float* __restric
   cs[(size_t)T * half + i] = (float)sin(th);
 }
 
+// 16 lanes per head vector: lane s holds elements 4s..4s+3 and 64+4s..64+4s+3,
+// so every rotation pair (j, j+64) stays in one lane; a wavefront covers four
+// head vectors with 8-byte accesses.
+template <typename T>
+struct Quad {
+  typedef T T4 __attribute__((ext_vector_type(4)));
+  __device__ __forceinline__ static void load(const T* p, float* o) {
+    const T4 v = *reinterpret_cast<const T4*>(p);
+    o[0] = to_f32(v[0]); o[1] = to_f32(v[1]); o[2] = to_f32(v[2]); o[3] = to_f32(v[3]);
+  }
+  __device__ __forceinline__ static void store(T* p, const float* o) {
+    const T4 v = {from_f32<T>(o[0]), from_f32<T>(o[1]), from_f32<T>(o[2]), from_f32<T>(o[3])};
+    *reinterpret_cast<T4*>(p) = v;
+  }
+};
+
 template <typename T>
 __global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(T* __restrict__ qkv, int ldq, int M,
                                                               int Tlen, int H,
                                                               const float* __restrict__ cs,
                                                               float eps,
                                                               float* __restrict__ rinv_qk) {
-  const int lane = threadIdx.x & 63;
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);     // (token, head) pair
+  const int sl = threadIdx.x & 15;
+  const size_t w = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);   // (token, head) pair
   const int nh = H + 1;
-  if (w >= M * nh) return;
-  const int m = w / nh, h = w % nh;
-  const int t = m % Tlen;
-  T* p = qkv + (size_t)m * ldq + h * 128;
-  const float a = to_f32(p[lane]), b = to_f32(p[lane + kHalf]);
-  const float c = cs[t * kHalf + lane], s = cs[(size_t)Tlen * kHalf + t * kHalf + lane];
-  const float ra = a * c - b * s, rb = a * s + b * c;
-  const float ss = wave_sum(ra * ra + rb * rb);
+  if (w >= (size_t)M * nh) return;                                  // whole 16-lane groups
+  const size_t m = w / nh;
+  const int h = (int)(w % nh);
+  const int t = (int)(m % Tlen);
+  T* p = qkv + m * ldq + h * 128 + 4 * sl;
+  float a[4], b[4];
+  Quad<T>::load(p, a);
+  Quad<T>::load(p + kHalf, b);
+  const f32x4 c = *reinterpret_cast<const f32x4*>(cs + t * kHalf + 4 * sl);
+  const f32x4 sn = *reinterpret_cast<const f32x4*>(cs + (size_t)Tlen * kHalf + t * kHalf + 4 * sl);
+  float ra[4], rb[4], ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ra[e] = a[e] * c[e] - b[e] * sn[e];
+    rb[e] = a[e] * sn[e] + b[e] * c[e];
+    ss += ra[e] * ra[e] + rb[e] * rb[e];
+  }
+  ss = lane16_sum(ss);
   const float r = 1.0f / sqrtf(ss * (1.0f / 128.0f) + eps);
-  p[lane] = from_f32<T>(ra * r);
-  p[lane + kHalf] = from_f32<T>(rb * r);
-  if (lane == 0) rinv_qk[(size_t)m * nh + h] = r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ra[e] *= r;
+    rb[e] *= r;
+  }
+  Quad<T>::store(p, ra);
+  Quad<T>::store(p + kHalf, rb);
+  if (sl == 0) rinv_qk[m * nh + h] = r;
 }
 
 // dz' = r (dy - y mean(dy y)) with y the saved normalised vector, then rotate by -theta
@@ -58,22 +89,36 @@ __global__ __launch_bounds__(256) void rope_qknorm_bwd_kernel(T* __restrict__ dq
                                                               int M, int Tlen, int H,
                                                               const float* __restrict__ cs,
                                                               const float* __restrict__ rinv_qk) {
-  const int lane = threadIdx.x & 63;
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int sl = threadIdx.x & 15;
+  const size_t w = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int nh = H + 1;
-  if (w >= M * nh) return;
-  const int m = w / nh, h = w % nh;
-  const int t = m % Tlen;
-  T* g = dqkv + (size_t)m * ldd + h * 128;
-  const T* y = qkv + (size_t)m * ldq + h * 128;
-  const float ga = to_f32(g[lane]), gb = to_f32(g[lane + kHalf]);
-  const float ya = to_f32(y[lane]), yb = to_f32(y[lane + kHalf]);
-  const float dot = wave_sum(ga * ya + gb * yb) * (1.0f / 128.0f);
-  const float r = rinv_qk[(size_t)m * nh + h];
-  const float da = r * (ga - ya * dot), db = r * (gb - yb * dot);
-  const float c = cs[t * kHalf + lane], s = cs[(size_t)Tlen * kHalf + t * kHalf + lane];
-  g[lane] = from_f32<T>(da * c + db * s);
-  g[lane + kHalf] = from_f32<T>(-da * s + db * c);
+  if (w >= (size_t)M * nh) return;
+  const size_t m = w / nh;
+  const int h = (int)(w % nh);
+  const int t = (int)(m % Tlen);
+  T* g = dqkv + m * ldd + h * 128 + 4 * sl;
+  const T* y = qkv + m * ldq + h * 128 + 4 * sl;
+  float ga[4], gb[4], ya[4], yb[4];
+  Quad<T>::load(g, ga);
+  Quad<T>::load(g + kHalf, gb);
+  Quad<T>::load(y, ya);
+  Quad<T>::load(y + kHalf, yb);
+  float dot = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) dot += ga[e] * ya[e] + gb[e] * yb[e];
+  dot = lane16_sum(dot) * (1.0f / 128.0f);
+  const float r = rinv_qk[m * nh + h];
+  const f32x4 c = *reinterpret_cast<const f32x4*>(cs + t * kHalf + 4 * sl);
+  const f32x4 sn = *reinterpret_cast<const f32x4*>(cs + (size_t)Tlen * kHalf + t * kHalf + 4 * sl);
+  float oa[4], ob[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float da = r * (ga[e] - ya[e] * dot), db = r * (gb[e] - yb[e] * dot);
+    oa[e] = da * c[e] + db * sn[e];
+    ob[e] = -da * sn[e] + db * c[e];
+  }
+  Quad<T>::store(g, oa);
+  Quad<T>::store(g + kHalf, ob);
 }
 
 }  // namespace
@@ -86,8 +131,8 @@ hipError_t rope_table(int T, int half, double base, float* cs, hipStream_t s) {
 
 hipError_t rope_qknorm_fwd(DType t, void* qkv, int ldq, int M, int T, int H, const float* cs,
                            float eps, float* rinv_qk, hipStream_t s) {
-  const int waves = M * (H + 1);
-  dim3 grid((waves + 3) / 4), block(256);
+  const size_t vecs = (size_t)M * (H + 1);
+  dim3 grid((unsigned)((vecs + 15) / 16)), block(256);
   if (t == DType::BF16)
     hipLaunchKernelGGL(rope_qknorm_fwd_kernel<bf16>, grid, block, 0, s, static_cast<bf16*>(qkv), ldq,
                        M, T, H, cs, eps, rinv_qk);
@@ -99,8 +144,8 @@ hipError_t rope_qknorm_fwd(DType t, void* qkv, int ldq, int M, int T, int H, con
 
 hipError_t rope_qknorm_bwd(DType t, void* dqkv, int ldd, const void* qkv, int ldq, int M, int T,
                            int H, const float* cs, const float* rinv_qk, hipStream_t s) {
-  const int waves = M * (H + 1);
-  dim3 grid((waves + 3) / 4), block(256);
+  const size_t vecs = (size_t)M * (H + 1);
+  dim3 grid((unsigned)((vecs + 15) / 16)), block(256);
   if (t == DType::BF16)
     hipLaunchKernelGGL(rope_qknorm_bwd_kernel<bf16>, grid, block, 0, s, static_cast<bf16*>(dqkv), ldd,
                        static_cast<const bf16*>(qkv), ldq, M, T, H, cs, rinv_qk);

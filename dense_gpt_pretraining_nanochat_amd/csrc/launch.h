@@ -77,9 +77,12 @@ hipError_t attn_fwd(DType t, const void* qkv, int ldq, int B, int T, int H, void
 // delta[b,h,t] = <dO, O>
 hipError_t attn_bwd_delta(DType t, const void* o, const void* dout, int B, int T, int H,
                           float* delta, hipStream_t s);
-// writes dq into dqkv[:, 0:H*128], dk and dv into the next two 128-col blocks
+// writes dq into dqkv[:, 0:H*128], dk and dv into the next two 128-col blocks;
+// scratch holds attn_bwd_scratch_floats(B, T) floats of partial dK/dV sums
+size_t attn_bwd_scratch_floats(int B, int T);
 hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const float* lse,
-                    const float* delta, int B, int T, int H, void* dqkv, int ldd, hipStream_t s);
+                    const float* delta, int B, int T, int H, void* dqkv, int ldd, float* scratch,
+                    hipStream_t s);
 
 // ---- cross-entropy -----------------------------------------------------------
 // rows of fp32 logits [R, V]: per-row loss (fp32) and dlogits (T) = (softmax(z)-onehot)*(1-(z/c)^2)*w

@@ -123,7 +123,7 @@ struct Plan {
   uint64_t status, cs, x, rinv0, xf, rinvf, loss_rows, logits, dlog;
   std::vector<LayerActs> acts;
   // backward only
-  uint64_t dx, g, dh, dbig, dout, delta, partial, counts, offsets, cursor, list;
+  uint64_t dx, g, dh, dbig, dout, delta, partial, attn_part, counts, offsets, cursor, list;
   uint64_t total;
 };
 
@@ -171,6 +171,7 @@ Plan plan_of(const Dims& D, bool bwd) {
     const int64_t shapes[4][2] = {{D.Q, D.d}, {D.d, D.d}, {D.F, D.d}, {D.d, D.F}};
     for (auto& sh : shapes) part = std::max(part, wgrad_plan(D.dt, sh[0], sh[1], D.M).partial_floats);
     p.partial = take(part * 4);
+    p.attn_part = take(nc::attn_bwd_scratch_floats(D.B, D.T) * 4);
     p.counts = take((uint64_t)(D.V + 1) * 4);
     p.offsets = take((uint64_t)(D.V + 1) * 4);
     p.cursor = take((uint64_t)D.V * 4);
@@ -358,7 +359,7 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
                          D.d, D.d, D.d, 0, s));
     HIPCHECK(nc::attn_bwd_delta(dt, o, dout, D.B, D.T, D.H, delta, s));
     HIPCHECK(nc::attn_bwd(dt, qkv, D.Q, dout, at<float>(ws, A.lse), delta, D.B, D.T, D.H, dbig,
-                          D.Q, s));
+                          D.Q, at<float>(ws, P.attn_part), s));
     HIPCHECK(nc::rope_qknorm_bwd(dt, dbig, D.Q, qkv, D.Q, Mi, D.T, D.H, cs,
                                  at<float>(ws, A.rqk), s));
     HIPCHECK(wgrad(dt, dbig, h, G(base + 0), partial, M, D.Q, D.d, pQ, s));
@@ -597,16 +598,21 @@ int nc_op_attn_fwd(int32_t dtype, const void* qkv, int32_t B, int32_t T, int32_t
   return NC_OK;
 }
 
+uint64_t nc_op_attn_bwd_scratch_bytes(int32_t B, int32_t T) {
+  if (B <= 0 || T <= 0) return 0;
+  return nc::attn_bwd_scratch_floats(B, T) * 4;
+}
+
 int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* dout,
                    const float* lse, float* delta, int32_t B, int32_t T, int32_t H, void* dqkv,
-                   void* stream) {
+                   float* scratch, void* stream) {
   if (bad_dtype(dtype)) return NC_ERR_ARG;
-  if (!qkv || !o || !dout || !lse || !delta || !dqkv) return NC_ERR_NULL;
+  if (!qkv || !o || !dout || !lse || !delta || !dqkv || !scratch) return NC_ERR_NULL;
   if (B <= 0 || T < 64 || T % 64 || H < 1 || H > 16) return NC_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int ld = H * 128 + 256;
   HIPCHECK(nc::attn_bwd_delta(dt_of(dtype), o, dout, B, T, H, delta, s));
-  HIPCHECK(nc::attn_bwd(dt_of(dtype), qkv, ld, dout, lse, delta, B, T, H, dqkv, ld, s));
+  HIPCHECK(nc::attn_bwd(dt_of(dtype), qkv, ld, dout, lse, delta, B, T, H, dqkv, ld, scratch, s));
   return NC_OK;
 }
 

@@ -196,11 +196,14 @@ int nc_op_rope_qknorm_bwd(int32_t dtype, void* dqkv, const void* qkv, int32_t B,
 /* o [B*T, H*128] (T), lse [B, H, T] fp32 from qkv [B*T, d+256]. */
 int nc_op_attn_fwd(int32_t dtype, const void* qkv, int32_t B, int32_t T, int32_t H, void* o,
                    float* lse, void* stream);
+/* Bytes of scratch nc_op_attn_bwd needs (fp32 partial dK/dV sums per
+ * 512-token query chunk); 0 for invalid sizes. Host only. */
+uint64_t nc_op_attn_bwd_scratch_bytes(int32_t B, int32_t T);
 /* dqkv [B*T, d+256] (T) from qkv, o, dout [B*T, H*128], lse; delta scratch
- * [B, H, T] fp32. */
+ * [B, H, T] fp32; scratch of nc_op_attn_bwd_scratch_bytes(B, T) bytes. */
 int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* dout,
                    const float* lse, float* delta, int32_t B, int32_t T, int32_t H, void* dqkv,
-                   void* stream);
+                   float* scratch, void* stream);
 /* Per-row loss and (if dlogits != NULL) w-scaled logit gradient (T) from fp32
  * logits [R, V]; status: device word for range flags (may not be NULL). */
 int nc_op_softcap_ce(int32_t dtype, const float* logits, const int32_t* targets, int32_t R,
