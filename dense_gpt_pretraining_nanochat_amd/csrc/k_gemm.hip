@@ -428,20 +428,28 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // epilogue: lane holds C[m][n..n+3] for n = n_tile + 8q + 4*lh, q = 0..3
+  // Epilogue, staged through LDS so that global accesses cover whole rows:
+  // the lane holds C[m][n..n+3] for m = 32i + l32, n = 32j + 8q + 4*lh; each
+  // wavefront writes one 32 x 64 fp32 block at a time into its own LDS region,
+  // then reads it back as 16-lane row segments (256 contiguous bytes per row).
+  constexpr int RS = TN + 4;                                   // padded row, floats
+  __syncthreads();                                             // slabs no longer needed
+  float* wl = reinterpret_cast<float*>(smem) + wave * 32 * RS;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * TM + i * 32 + l32;
-    if (m >= g.M) continue;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * TN + j * 32 + q * 8 + lh * 4;
-        if (n >= g.N) continue;
         const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        epilogue4<bf16, EPI>(g, split, m, n, v);
+        *reinterpret_cast<f32x4*>(wl + l32 * RS + j * 32 + q * 8 + lh * 4) = v;
       }
+#pragma unroll
+    for (int c = lane; c < 32 * (TN / 4); c += 64) {
+      const int r = c / (TN / 4), cc = (c % (TN / 4)) * 4;
+      const int m = m0 + wm * TM + i * 32 + r, n = n0 + wn * TN + cc;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(wl + r * RS + cc);
+      if (m < g.M && n < g.N) epilogue4<bf16, EPI>(g, split, m, n, v);
     }
   }
 }

@@ -9,6 +9,8 @@
 // One 64-lane wavefront owns one row (d <= 2048 floats): each lane keeps up to
 // 8 float4 of the row in registers, so a row is read from HBM once and written
 // once, with 16-byte coalesced accesses and a shuffle-tree reduction.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -147,170 +149,223 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ 
 }
 
 // ---- embedding backward -----------------------------------------------------
-// de[m] = n'(dx[m]) with y = x0 = E[tok[m]] * rinv0[m] recomputed; counts[tok]++
-template <typename T>
-__global__ __launch_bounds__(256) void embed_de_kernel(const T* __restrict__ E,
-                                                       const int32_t* __restrict__ tok,
-                                                       const float* __restrict__ rinv0,
-                                                       const float* __restrict__ dx, int M, int d,
-                                                       int V, float* __restrict__ de,
-                                                       int32_t* __restrict__ counts) {
-  const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (m >= M) return;
-  int id = tok[m];
-  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
-  const T* src = E + (size_t)id * d;
-  const float r = rinv0[m];
-  const size_t base = (size_t)m * d;
-  f32x4 gy[kMaxVec];
-  float yy[kMaxVec][4];
-  float dot = 0.f;
-#pragma unroll
-  for (int i = 0; i < kMaxVec; ++i) {
-    const int c = (i * 64 + lane) * 4;
-    if (c < d) {
-      gy[i] = *reinterpret_cast<const f32x4*>(dx + base + c);
-      load4(src + c, yy[i]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) yy[i][e] *= r;
-      dot += gy[i][0] * yy[i][0] + gy[i][1] * yy[i][1] + gy[i][2] * yy[i][2] + gy[i][3] * yy[i][3];
-    }
-  }
-  dot = wave_sum(dot) / d;
-#pragma unroll
-  for (int i = 0; i < kMaxVec; ++i) {
-    const int c = (i * 64 + lane) * 4;
-    if (c < d) {
-      f32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = r * (gy[i][e] - yy[i][e] * dot);
-      *reinterpret_cast<f32x4*>(de + base + c) = o;
-    }
-  }
-  if (lane == 0) atomicAdd(&counts[id], 1);
+// ---- embedding backward --------------------------------------------------
+// Every occurrence of token v normalises the same row E[v] (same rinv, same
+// y = E[v] * rinv), and the norm gradient is linear in the upstream gradient,
+// so dE[v] = rinv * (S - y * mean(S * y)) with S = sum of dx[m] over tok[m] == v.
+// S is summed in increasing m in fixed-size pieces whose partial sums are then
+// added in piece order, so the result is bitwise reproducible. Steps: count
+// tokens per id, scan the counts, bucket positions by id, sort each bucket,
+// sum pieces of kSeg rows (one workgroup each), add the pieces of long buckets
+// and apply the norm gradient.
+constexpr int kSeg = 64;         // rows of one bucket summed by one workgroup
+constexpr int kSortCap = 4096;   // buckets up to this size are sorted in LDS
+
+__device__ __forceinline__ int clamp_id(int t, int V) { return t < 0 ? 0 : (t >= V ? V - 1 : t); }
+
+__global__ void embed_count_kernel(const int32_t* __restrict__ tok, int M, int V,
+                                   int32_t* __restrict__ counts) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m < M) atomicAdd(&counts[clamp_id(tok[m], V)], 1);
 }
 
-// exclusive scan of counts[0..V) into offsets[0..V] and cursor[0..V), one block
-__global__ __launch_bounds__(1024) void scan_counts_kernel(const int32_t* __restrict__ counts,
-                                                           int V, int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ cursor) {
-  __shared__ int32_t part[1024];
+// One block: exclusive scans over ids of (rows, pieces, pieces of multi-piece
+// buckets); also writes the owning id of every piece.
+__global__ __launch_bounds__(1024) void embed_scan_kernel(const int32_t* __restrict__ counts, int V,
+                                                          EmbedBwdScratch ws) {
+  __shared__ int32_t sc[3][1024];
   const int tid = threadIdx.x;
   const int per = (V + 1023) / 1024;
   const int b = tid * per, e = min(b + per, V);
-  int s = 0;
-  for (int i = b; i < e; ++i) s += counts[i];
-  part[tid] = s;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {     // Hillis-Steele inclusive scan
-    const int v = tid >= o ? part[tid - o] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int run = tid ? part[tid - 1] : 0;
+  int a0 = 0, a1 = 0, a2 = 0;
   for (int i = b; i < e; ++i) {
-    offsets[i] = run;
-    cursor[i] = run;
-    run += counts[i];
+    const int n = counts[i], it = (n + kSeg - 1) / kSeg;
+    a0 += n;
+    a1 += it;
+    a2 += it > 1 ? it : 0;
   }
-  if (tid == 1023) offsets[V] = part[1023];
+  sc[0][tid] = a0;
+  sc[1][tid] = a1;
+  sc[2][tid] = a2;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {     // Hillis-Steele inclusive scans
+    int v0 = 0, v1 = 0, v2 = 0;
+    if (tid >= o) { v0 = sc[0][tid - o]; v1 = sc[1][tid - o]; v2 = sc[2][tid - o]; }
+    __syncthreads();
+    sc[0][tid] += v0;
+    sc[1][tid] += v1;
+    sc[2][tid] += v2;
+    __syncthreads();
+  }
+  int r0 = tid ? sc[0][tid - 1] : 0, r1 = tid ? sc[1][tid - 1] : 0, r2 = tid ? sc[2][tid - 1] : 0;
+  for (int i = b; i < e; ++i) {
+    const int n = counts[i], it = (n + kSeg - 1) / kSeg;
+    ws.offsets[i] = r0;
+    ws.cursor[i] = r0;
+    ws.item_off[i] = r1;
+    ws.part_off[i] = r2;
+    for (int j = 0; j < it; ++j) ws.item_bucket[r1 + j] = i;
+    r0 += n;
+    r1 += it;
+    r2 += it > 1 ? it : 0;
+  }
+  if (tid == 1023) {
+    ws.offsets[V] = sc[0][1023];
+    ws.item_off[V] = sc[1][1023];
+    ws.part_off[V] = sc[2][1023];
+  }
 }
 
 __global__ void fill_list_kernel(const int32_t* __restrict__ tok, int M, int V,
                                  int32_t* __restrict__ cursor, int32_t* __restrict__ list) {
   const int m = blockIdx.x * blockDim.x + threadIdx.x;
   if (m >= M) return;
-  int id = tok[m];
-  id = id < 0 ? 0 : (id >= V ? V - 1 : id);
-  list[atomicAdd(&cursor[id], 1)] = m;
+  list[atomicAdd(&cursor[clamp_id(tok[m], V)], 1)] = m;
 }
 
-constexpr int kSortCap = 4096;   // buckets up to this size are sorted in LDS
-
-// One block per vocabulary row: dE[v] = sum of de[m] over tok[m] == v, in
-// increasing m (a fixed order, so the result is bitwise reproducible).
-__global__ __launch_bounds__(256) void segment_sum_kernel(const int32_t* __restrict__ tok,
-                                                          const int32_t* __restrict__ offsets,
-                                                          const int32_t* __restrict__ list,
-                                                          const float* __restrict__ de, int M,
-                                                          int d, int V, float* __restrict__ dE) {
+// One block per id: put the bucket's positions in increasing order (the atomic
+// fill leaves them in arbitrary order). Small buckets: bitonic sort in LDS;
+// large ones: an ordered compaction of the token array, chunk by chunk.
+__global__ __launch_bounds__(256) void embed_sort_kernel(const int32_t* __restrict__ tok, int M,
+                                                         int V, const int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ list) {
   __shared__ int32_t idx[kSortCap];
   __shared__ int32_t runc[256];
   const int v = blockIdx.x;
   const int tid = threadIdx.x;
   const int beg = offsets[v], n = offsets[v + 1] - beg;
-  float* dst = dE + (size_t)v * d;
-  const int ncol4 = d / 4;                       // d <= 2048 -> <= 2 float4 per thread
-  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  if (n == 0) {
-  } else if (n <= kSortCap) {
+  if (n <= 1) return;
+  if (n <= kSortCap) {
     int np2 = 1;
     while (np2 < n) np2 <<= 1;
     for (int i = tid; i < np2; i += 256) idx[i] = i < n ? list[beg + i] : INT32_MAX;
     __syncthreads();
-    for (int k = 2; k <= np2; k <<= 1) {          // bitonic sort, ascending
+    for (int k = 2; k <= np2; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
         for (int i = tid; i < np2; i += 256) {
           const int p = i ^ j;
           if (p > i) {
-            const int a = idx[i], b = idx[p];
+            const int x = idx[i], y = idx[p];
             const bool up = (i & k) == 0;
-            if ((a > b) == up) { idx[i] = b; idx[p] = a; }
+            if ((x > y) == up) { idx[i] = y; idx[p] = x; }
           }
         }
         __syncthreads();
       }
     }
-    for (int s = 0; s < n; ++s) {
-      const float* row = de + (size_t)idx[s] * d;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int c4 = tid + q * 256;
-        if (c4 < ncol4) acc[q] += reinterpret_cast<const f32x4*>(row)[c4];
-      }
-    }
-  } else {
-    // large bucket: walk the token array in order, compacting matches per chunk
-    auto id_at = [&](int i) {
-      const int t = tok[i];
-      return t < 0 ? 0 : (t >= V ? V - 1 : t);
-    };
-    for (int c0 = 0; c0 < M; c0 += kSortCap) {
-      // ordered compaction: each thread scans a contiguous run of 16 positions
-      const int rb = c0 + tid * 16;
-      int local = 0;
-      for (int i = rb; i < min(rb + 16, M); ++i) local += (id_at(i) == v) ? 1 : 0;
-      runc[tid] = local;
+    for (int i = tid; i < n; i += 256) list[beg + i] = idx[i];
+    return;
+  }
+  constexpr int kRun = 32;                       // positions per thread per chunk
+  int w0 = beg;
+  for (int c0 = 0; c0 < M; c0 += 256 * kRun) {
+    const int rb = c0 + tid * kRun, re = min(rb + kRun, M);
+    int local = 0;
+    for (int i = rb; i < re; ++i) local += clamp_id(tok[i], V) == v ? 1 : 0;
+    runc[tid] = local;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      const int t2 = tid >= o ? runc[tid - o] : 0;
       __syncthreads();
-      for (int o = 1; o < 256; o <<= 1) {
-        const int t2 = tid >= o ? runc[tid - o] : 0;
-        __syncthreads();
-        runc[tid] += t2;
-        __syncthreads();
-      }
-      int w = runc[tid] - local;
-      for (int i = rb; i < min(rb + 16, M); ++i)
-        if (id_at(i) == v) idx[w++] = i;
-      const int total = runc[255];
-      __syncthreads();
-      for (int s = 0; s < total; ++s) {
-        const float* row = de + (size_t)idx[s] * d;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int c4 = tid + q * 256;
-          if (c4 < ncol4) acc[q] += reinterpret_cast<const f32x4*>(row)[c4];
-        }
-      }
+      runc[tid] += t2;
       __syncthreads();
     }
+    int w = w0 + runc[tid] - local;
+    for (int i = rb; i < re; ++i)
+      if (clamp_id(tok[i], V) == v) list[w++] = i;
+    w0 += runc[255];
+    __syncthreads();
   }
+}
+
+// dE[v] = rinv * (S - y * mean(S * y)), y = E[v] * rinv; all threads call it
+template <typename T>
+__device__ __forceinline__ void embed_finish_row(const T* __restrict__ E, int v, int d, float r,
+                                                 f32x4 S, bool active, float* __restrict__ dE) {
+  __shared__ float red[16];
+  const int c = threadIdx.x * 4;
+  float y[4] = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
+    load4(E + (size_t)v * d + c, y);
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int c4 = tid + q * 256;
-    if (c4 < ncol4) reinterpret_cast<f32x4*>(dst)[c4] = acc[q];
+    for (int k = 0; k < 4; ++k) y[k] *= r;
   }
+  float dot = S[0] * y[0] + S[1] * y[1] + S[2] * y[2] + S[3] * y[3];
+  dot = block_sum(dot, red) / d;
+  if (active) {
+    f32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = r * (S[k] - y[k] * dot);
+    *reinterpret_cast<f32x4*>(dE + (size_t)v * d + c) = o;
+  }
+}
+
+// One block per piece of <= kSeg rows of one bucket; thread t owns columns
+// 4t..4t+3. Single-piece buckets are finished here, the others leave a partial.
+template <typename T>
+__global__ __launch_bounds__(512) void embed_sum_kernel(const T* __restrict__ E,
+                                                        const float* __restrict__ rinv0,
+                                                        const float* __restrict__ dx, int d, int V,
+                                                        EmbedBwdScratch ws, float* __restrict__ dE) {
+  __shared__ int32_t rows[kSeg];
+  const int i = blockIdx.x;
+  if (i >= ws.item_off[V]) return;
+  const int tid = threadIdx.x;
+  const int v = ws.item_bucket[i];
+  const int j = i - ws.item_off[v];
+  const int beg = ws.offsets[v], n = ws.offsets[v + 1] - beg;
+  const int cnt = min(kSeg, n - j * kSeg);
+  if (tid < cnt) rows[tid] = ws.list[beg + j * kSeg + tid];
+  __syncthreads();
+  const bool active = tid * 4 < d;
+  const size_t c = active ? (size_t)tid * 4 : 0;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 8 <= cnt; s += 8) {                 // eight rows in flight, added in order
+    f32x4 t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = *reinterpret_cast<const f32x4*>(dx + (size_t)rows[s + u] * d + c);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += t[u];
+  }
+  for (; s < cnt; ++s) acc += *reinterpret_cast<const f32x4*>(dx + (size_t)rows[s] * d + c);
+  if (n <= kSeg) {
+    embed_finish_row(E, v, d, rinv0[rows[0]], acc, active, dE);
+  } else if (active) {
+    *reinterpret_cast<f32x4*>(ws.part + (size_t)(ws.part_off[v] + j) * d + c) = acc;
+  }
+}
+
+// One block per id: zero rows for unused ids; multi-piece buckets add their
+// partials in piece order and apply the norm gradient.
+template <typename T>
+__global__ __launch_bounds__(512) void embed_finish_kernel(const T* __restrict__ E,
+                                                           const float* __restrict__ rinv0, int d,
+                                                           EmbedBwdScratch ws,
+                                                           float* __restrict__ dE) {
+  const int v = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int beg = ws.offsets[v], n = ws.offsets[v + 1] - beg;
+  const bool active = tid * 4 < d;
+  const size_t c = active ? (size_t)tid * 4 : 0;
+  if (n == 0) {
+    if (active) *reinterpret_cast<f32x4*>(dE + (size_t)v * d + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  if (n <= kSeg) return;
+  const int items = (n + kSeg - 1) / kSeg;
+  const float* p = ws.part + (size_t)ws.part_off[v] * d + c;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 4 <= items; k += 4) {
+    f32x4 t[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t[u] = *reinterpret_cast<const f32x4*>(p + (size_t)(k + u) * d);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc += t[u];
+  }
+  for (; k < items; ++k) acc += *reinterpret_cast<const f32x4*>(p + (size_t)k * d);
+  embed_finish_row(E, v, d, rinv0[ws.list[beg]], acc, active, dE);
 }
 
 __global__ __launch_bounds__(1024) void loss_mean_kernel(const float* __restrict__ loss_rows,
@@ -382,24 +437,36 @@ hipError_t rmsnorm_bwd(DType t, const void* dy, const void* y, const float* rinv
   return hipGetLastError();
 }
 
+uint64_t embed_bwd_max_pieces(int64_t M, int V) {
+  return (uint64_t)std::min<int64_t>(M, V) + (uint64_t)(M / kSeg) + 1;
+}
+uint64_t embed_bwd_max_parts(int64_t M) { return 2 * (uint64_t)(M / kSeg) + 1; }
+
 hipError_t embed_bwd(DType t, const void* E, const int32_t* tok, const float* rinv0,
                      const float* dx, int M, int d, int V, EmbedBwdScratch ws, float* dE,
                      hipStream_t s) {
-  if (d % 4 || d > 2048) return hipErrorInvalidValue;
+  if (d % 4 || d > 2048 || M <= 0 || V <= 0) return hipErrorInvalidValue;
   hipError_t e = fill_zero(ws.counts, sizeof(int32_t) * (V + 1), s);
   if (e != hipSuccess) return e;
-  if (t == DType::BF16)
-    hipLaunchKernelGGL(embed_de_kernel<bf16>, dim3(row_grid(M)), dim3(256), 0, s,
-                       static_cast<const bf16*>(E), tok, rinv0, dx, M, d, V, ws.de, ws.counts);
-  else
-    hipLaunchKernelGGL(embed_de_kernel<float>, dim3(row_grid(M)), dim3(256), 0, s,
-                       static_cast<const float*>(E), tok, rinv0, dx, M, d, V, ws.de, ws.counts);
-  hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(1024), 0, s, ws.counts, V, ws.offsets,
-                     ws.cursor);
+  const int nthr = ((d / 4 + 63) / 64) * 64;
+  const unsigned pieces = (unsigned)embed_bwd_max_pieces(M, V);
+  hipLaunchKernelGGL(embed_count_kernel, dim3((M + 255) / 256), dim3(256), 0, s, tok, M, V,
+                     ws.counts);
+  hipLaunchKernelGGL(embed_scan_kernel, dim3(1), dim3(1024), 0, s, ws.counts, V, ws);
   hipLaunchKernelGGL(fill_list_kernel, dim3((M + 255) / 256), dim3(256), 0, s, tok, M, V,
                      ws.cursor, ws.list);
-  hipLaunchKernelGGL(segment_sum_kernel, dim3(V), dim3(256), 0, s, tok, ws.offsets, ws.list, ws.de,
-                     M, d, V, dE);
+  hipLaunchKernelGGL(embed_sort_kernel, dim3(V), dim3(256), 0, s, tok, M, V, ws.offsets, ws.list);
+  if (t == DType::BF16) {
+    const bf16* Eb = static_cast<const bf16*>(E);
+    hipLaunchKernelGGL(embed_sum_kernel<bf16>, dim3(pieces), dim3(nthr), 0, s, Eb, rinv0, dx, d, V,
+                       ws, dE);
+    hipLaunchKernelGGL(embed_finish_kernel<bf16>, dim3(V), dim3(nthr), 0, s, Eb, rinv0, d, ws, dE);
+  } else {
+    const float* Ef = static_cast<const float*>(E);
+    hipLaunchKernelGGL(embed_sum_kernel<float>, dim3(pieces), dim3(nthr), 0, s, Ef, rinv0, dx, d,
+                       V, ws, dE);
+    hipLaunchKernelGGL(embed_finish_kernel<float>, dim3(V), dim3(nthr), 0, s, Ef, rinv0, d, ws, dE);
+  }
   return hipGetLastError();
 }
 

@@ -52,12 +52,17 @@ hipError_t rmsnorm_bwd(DType t, const void* dy, const void* y, const float* rinv
                        float* dx, bool accumulate, void* g, hipStream_t s);
 // embedding-norm backward + deterministic scatter into dE (fp32, every row written)
 struct EmbedBwdScratch {
-  int32_t* counts;   // [V + 1]
-  int32_t* offsets;  // [V + 1]
-  int32_t* cursor;   // [V]
-  int32_t* list;     // [M]
-  float* de;         // [M, d]
+  int32_t* counts;       // [V + 1]
+  int32_t* offsets;      // [V + 1]
+  int32_t* cursor;       // [V]
+  int32_t* list;         // [M]
+  int32_t* item_off;     // [V + 1]
+  int32_t* part_off;     // [V + 1]
+  int32_t* item_bucket;  // [embed_bwd_max_pieces(M, V)]
+  float* part;           // [embed_bwd_max_parts(M), d]
 };
+uint64_t embed_bwd_max_pieces(int64_t M, int V);
+uint64_t embed_bwd_max_parts(int64_t M);
 hipError_t embed_bwd(DType t, const void* E, const int32_t* tok, const float* rinv0,
                      const float* dx, int M, int d, int V, EmbedBwdScratch ws, float* dE,
                      hipStream_t s);

@@ -124,6 +124,7 @@ struct Plan {
   std::vector<LayerActs> acts;
   // backward only
   uint64_t dx, g, dh, dbig, dout, delta, partial, attn_part, counts, offsets, cursor, list;
+  uint64_t item_off, part_off, item_bucket;
   uint64_t total;
 };
 
@@ -163,7 +164,7 @@ Plan plan_of(const Dims& D, bool bwd) {
   if (bwd) {
     p.dx = take(M * D.d * 4);
     p.g = take(M * D.d * e);
-    p.dh = take(M * D.d * 4);        // T-typed input gradients; fp32 scratch for dE rows
+    p.dh = take(M * D.d * 4);        // T-typed input gradients; fp32 partial sums for dE
     p.dbig = take(M * std::max(D.F, D.Q) * e);
     p.dout = take(M * D.d * e);
     p.delta = take(M * D.H * 4);
@@ -176,6 +177,9 @@ Plan plan_of(const Dims& D, bool bwd) {
     p.offsets = take((uint64_t)(D.V + 1) * 4);
     p.cursor = take((uint64_t)D.V * 4);
     p.list = take(M * 4);
+    p.item_off = take((uint64_t)(D.V + 1) * 4);
+    p.part_off = take((uint64_t)(D.V + 1) * 4);
+    p.item_bucket = take(nc::embed_bwd_max_pieces(M, D.V) * 4);
   }
   p.total = off;
   return p;
@@ -372,7 +376,10 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
   es.offsets = at<int32_t>(ws, P.offsets);
   es.cursor = at<int32_t>(ws, P.cursor);
   es.list = at<int32_t>(ws, P.list);
-  es.de = static_cast<float*>(dh);
+  es.item_off = at<int32_t>(ws, P.item_off);
+  es.part_off = at<int32_t>(ws, P.part_off);
+  es.item_bucket = at<int32_t>(ws, P.item_bucket);
+  es.part = static_cast<float*>(dh);     // embed_bwd_max_parts(M) * d floats <= M * d
   HIPCHECK(nc::embed_bwd(dt, W(iE), tokens, rinv0, dx, (int)M, D.d, D.V, es, G(iE), s));
   return NC_OK;
 }
