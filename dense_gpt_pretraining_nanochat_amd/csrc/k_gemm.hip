@@ -180,9 +180,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   const int tn = (t % per_group) / gsize;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  const int kps = g.K / g.splits;
-  const int kbeg = split * kps;
-  const int nk = kps / BK;
+  // split `split` takes k slabs [split * ns / splits, (split + 1) * ns / splits)
+  const int ns = g.K / BK;
+  const int sb = (int)((long)split * ns / g.splits), se = (int)((long)(split + 1) * ns / g.splits);
+  const int kbeg = sb * BK;
+  const int nk = se - sb;
 
   const T* __restrict__ A = static_cast<const T*>(g.A);
   const T* __restrict__ B = static_cast<const T*>(g.B);
@@ -361,9 +363,10 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g) {
   const int tm = first_m + (t % per_group) % gsize;
   const int tn = (t % per_group) / gsize;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int kps = g.K / g.splits;
-  const int kbeg = split * kps;
-  const int nk = kps / BK;
+  const int ns = g.K / BK;
+  const int sb = (int)((long)split * ns / g.splits), se = (int)((long)(split + 1) * ns / g.splits);
+  const int kbeg = sb * BK;
+  const int nk = se - sb;
 
   BigLoader<AK> la;
   BigLoader<BKC> lb;
@@ -522,7 +525,7 @@ hipError_t gemm(DType t, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs
                 hipStream_t stream) {
   const int bk = t == DType::BF16 ? 64 : 32;
   if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.splits <= 0) return hipErrorInvalidValue;
-  if (g.M % 16 || g.N % 16 || g.K % (bk * g.splits)) return hipErrorInvalidValue;
+  if (g.M % 16 || g.N % 16 || g.K % bk || g.K / bk < g.splits) return hipErrorInvalidValue;
   if (epi != Epi::PartialF32 && g.splits != 1) return hipErrorInvalidValue;
   return t == DType::BF16 ? dispatch<bf16>(a_kcontig, b_kcontig, epi, g, stream)
                           : dispatch<float>(a_kcontig, b_kcontig, epi, g, stream);
@@ -532,6 +535,18 @@ int gemm_tile(DType t, bool a_kcontig, bool b_kcontig, const GemmArgs& g) {
   (void)a_kcontig;
   (void)b_kcontig;
   return choose_tile(t == DType::BF16, g);
+}
+
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
 }
 
 hipError_t splitk_reduce(const float* part, int splits, size_t n, float* dst, bool accumulate,

@@ -29,6 +29,8 @@ struct GemmArgs {
   int splits;        // K slices (PartialF32 only); K % (splits * 64) == 0
   int tile;          // output tile edge: 0 = choose, 128 or 256 (256: bf16 only)
 };
+// compute units of the current device (256 when it cannot be queried)
+int device_cus();
 hipError_t gemm(DType t, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs& g,
                 hipStream_t stream);
 // Tile edge the kernel will use for these arguments (128 or 256).

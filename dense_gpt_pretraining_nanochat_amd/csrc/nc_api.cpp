@@ -93,12 +93,16 @@ uint64_t param_elems(const Dims& D) {
 
 // lm_head rows processed per chunk: bounds the fp32 logits buffer at
 // Mc * V * 4 bytes (4 GiB at V = 65,536).
-int64_t chunk_rows(const Dims& D) { return std::min<int64_t>(D.M, 16384); }
+// Rows of the lm_head / loss processed at once: the fp32 logits and the bf16
+// logit gradients of a chunk live in the workspace (65536 rows x 65536 vocab =
+// 25.8 GB), so the vocabulary products run over the whole batch in one launch.
+int64_t chunk_rows(const Dims& D) { return std::min<int64_t>(D.M, 65536); }
 
 // Split-K plan for a weight gradient dW[N1, N2] = X1^T X2 contracted over K
-// token rows (both operands read K-strided): the tile the kernel will pick,
-// and the smallest power-of-two split giving >= 2 workgroups per CU. K must
-// stay a multiple of 64 * splits.
+// token rows (both operands read K-strided). Each split takes a contiguous run
+// of whole 64-wide k slabs (runs differ by at most one slab). The split count
+// minimises an estimate of rounds-of-workgroups x slabs-per-workgroup plus the
+// fp32 partial traffic, so the last round of workgroups is not left mostly idle.
 struct WgradPlan {
   int tile;
   int splits;
@@ -108,10 +112,23 @@ WgradPlan wgrad_plan(DType dt, int64_t N1, int64_t N2, int64_t K) {
   WgradPlan p;
   p.tile = (dt == DType::BF16 && N1 >= 256 && N2 >= 256) ? 256 : 128;
   const int64_t tiles = ((N1 + p.tile - 1) / p.tile) * ((N2 + p.tile - 1) / p.tile);
-  int s = 1;
-  while (tiles * s < 512 && s < 32 && K % (64 * (2 * s)) == 0) s *= 2;
-  p.splits = s;
-  p.partial_floats = s > 1 ? (uint64_t)s * N1 * N2 : 0;
+  const int64_t ns = K / (dt == DType::BF16 ? 64 : 32);
+  const int64_t slots = (int64_t)nc::device_cus() * (p.tile == 256 ? 1 : 2);
+  const double slab_us = p.tile == 256 ? 2.2 : 0.6;           // one k slab of one tile
+  const double bytes_per_us = 5.0e6;                          // partial write + reduce read
+  int best = 1;
+  double best_cost = 1e300;
+  for (int s = 1; s <= 32 && s <= ns; ++s) {
+    const int64_t rounds = (tiles * s + slots - 1) / slots;
+    double cost = (double)rounds * (double)((ns + s - 1) / s) * slab_us;
+    if (s > 1) cost += (double)s * N1 * N2 * 8.0 / bytes_per_us + 4.0;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  p.splits = best;
+  p.partial_floats = best > 1 ? (uint64_t)best * N1 * N2 : 0;
   return p;
 }
 
@@ -532,10 +549,10 @@ int nc_op_wgrad(int32_t dtype, const void* X1, const void* X2, float* dW, float*
                 int32_t M, int32_t N1, int32_t N2, int32_t splits, void* stream) {
   if (bad_dtype(dtype)) return NC_ERR_ARG;
   if (!X1 || !X2 || !dW || (splits > 1 && !partial)) return NC_ERR_NULL;
-  if (M <= 0 || N1 <= 0 || N2 <= 0 || N1 % 16 || N2 % 16 || splits < 1 || M % (64 * splits))
+  if (M <= 0 || N1 <= 0 || N2 <= 0 || N1 % 16 || N2 % 16 || splits < 1 || M % 64 ||
+      M / 64 < splits)
     return NC_ERR_ARG;
-  WgradPlan p;
-  p.tile = 0;
+  WgradPlan p = wgrad_plan(dt_of(dtype), N1, N2, M);   // same tile choice as the step
   p.splits = splits;
   HIPCHECK(wgrad(dt_of(dtype), X1, X2, dW, partial, M, N1, N2, p, static_cast<hipStream_t>(stream)));
   return NC_OK;

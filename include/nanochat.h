@@ -168,7 +168,9 @@ int nc_op_gemm(int32_t dtype, int32_t a_kcontig, int32_t b_kcontig, int32_t epil
 
 /* Weight-gradient contraction dW[N1,N2] = X1^T X2 over M rows (X1 [M,N1],
  * X2 [M,N2], type T), split over `splits` K slices with a fixed-order fp32
- * reduction through `partial` (splits*N1*N2 floats; unused when splits = 1). */
+ * reduction through `partial` (splits*N1*N2 floats; unused when splits = 1).
+ * Slice i covers the 64-row slabs [i*S/splits, (i+1)*S/splits), S = M/64 for
+ * bf16 (M/32 for fp32); M must be a multiple of 64 and splits <= M/64. */
 int nc_op_wgrad(int32_t dtype, const void* X1, const void* X2, float* dW, float* partial,
                 int32_t M, int32_t N1, int32_t N2, int32_t splits, void* stream);
 

@@ -117,10 +117,11 @@ def test_transpose(dtype, R, C):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("splits", [1, 2, 4])
-def test_wgrad_splitk(dtype, splits):
-    rng = np.random.default_rng(splits)
-    M, N1, N2 = 1024, 272, 192
+@pytest.mark.parametrize("splits", [1, 2, 3, 4, 7])
+@pytest.mark.parametrize("M,N1,N2", [(1024, 272, 192), (1600, 512, 256)])
+def test_wgrad_splitk(dtype, splits, M, N1, N2):
+    # splits 3 and 7 do not divide the slab count: slices differ by one slab
+    rng = np.random.default_rng(splits + N1)
     X1, X1_64 = _as(rng.standard_normal((M, N1)), dtype)
     X2, X2_64 = _as(rng.standard_normal((M, N2)), dtype)
     dW = torch.zeros((N1, N2), dtype=torch.float32, device="cuda")
