@@ -334,6 +334,27 @@ struct BigLoader {
   }
 };
 
+// Extra epilogue operand (the fp32 residual for AddF32, the saved activation
+// for Relu2Bwd), read ahead of use: 4 consecutive values per chunk.
+template <Epi EPI> struct EpiIn { typedef f32x4 type; };
+template <> struct EpiIn<Epi::Relu2Bwd> { typedef bf16x4 type; };
+
+template <Epi EPI>
+__device__ __forceinline__ void epilogue4_in(const GemmArgs& g, int split, int m, int n, f32x4 v,
+                                             typename EpiIn<EPI>::type in) {
+  const size_t off = (size_t)m * g.ldc + n;
+  if constexpr (EPI == Epi::AddF32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off) = in + v;
+  } else if constexpr (EPI == Epi::Relu2Bwd) {
+    bf16x4 w;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r] = from_f32<bf16>(v[r] * 2.f * sqrtf(to_f32(in[r])));
+    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.C) + off) = w;
+  } else {
+    epilogue4<bf16, EPI>(g, split, m, n, v);
+  }
+}
+
 template <Epi EPI, bool AK, bool BKC>
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int BM = 256, BN = 256, BK = 64;
@@ -435,7 +456,28 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g) {
   // the lane holds C[m][n..n+3] for m = 32i + l32, n = 32j + 8q + 4*lh; each
   // wavefront writes one 32 x 64 fp32 block at a time into its own LDS region,
   // then reads it back as 16-lane row segments (256 contiguous bytes per row).
+  // An epilogue that reads memory (the residual for AddF32, the saved
+  // activation for Relu2Bwd) keeps one register per staged chunk and refills
+  // it with the next 32-row block's chunk as soon as it has been used.
   constexpr int RS = TN + 4;                                   // padded row, floats
+  constexpr int CPR = TN / 4;                                  // 16-byte chunks per row
+  constexpr int CH = 32 * CPR / 64;                            // chunks per lane per block
+  constexpr bool READS = EPI == Epi::AddF32 || EPI == Epi::Relu2Bwd;
+  typedef typename EpiIn<EPI>::type In;
+  In pre[CH];
+  auto fetch1 = [&](int i, int u) -> In {
+    const int c = lane + 64 * u;
+    const int m = min(m0 + wm * TM + i * 32 + c / CPR, g.M - 1);
+    const int n = min(n0 + wn * TN + (c % CPR) * 4, g.N - 4);
+    if constexpr (EPI == Epi::Relu2Bwd)
+      return *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(g.C2) + (size_t)m * g.ldc2 + n);
+    else
+      return *reinterpret_cast<const f32x4*>(static_cast<const float*>(g.C) + (size_t)m * g.ldc + n);
+  };
+  if constexpr (READS) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) pre[u] = fetch1(0, u);
+  }
   __syncthreads();                                             // slabs no longer needed
   float* wl = reinterpret_cast<float*>(smem) + wave * 32 * RS;
 #pragma unroll
@@ -448,11 +490,18 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g) {
         *reinterpret_cast<f32x4*>(wl + l32 * RS + j * 32 + q * 8 + lh * 4) = v;
       }
 #pragma unroll
-    for (int c = lane; c < 32 * (TN / 4); c += 64) {
-      const int r = c / (TN / 4), cc = (c % (TN / 4)) * 4;
+    for (int u = 0; u < CH; ++u) {
+      const int c = lane + 64 * u;
+      const int r = c / CPR, cc = (c % CPR) * 4;
       const int m = m0 + wm * TM + i * 32 + r, n = n0 + wn * TN + cc;
       const f32x4 v = *reinterpret_cast<const f32x4*>(wl + r * RS + cc);
-      if (m < g.M && n < g.N) epilogue4<bf16, EPI>(g, split, m, n, v);
+      if constexpr (READS) {
+        const In x = pre[u];
+        if (i + 1 < FM) pre[u] = fetch1(i + 1, u);
+        if (m < g.M && n < g.N) epilogue4_in<EPI>(g, split, m, n, v, x);
+      } else {
+        if (m < g.M && n < g.N) epilogue4<bf16, EPI>(g, split, m, n, v);
+      }
     }
   }
 }
