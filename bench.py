@@ -2,6 +2,8 @@
 depth-20 dense GPT on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload C4] [--no-cpu-baseline]
+    python bench.py --kernel-only      # 3 launches of the roofline kernel + a 1 GiB copy
+                                       # (for hardware-counter passes)
 
 Prints one JSON line: tokens/s for the whole step (inputs resident in HBM),
 milliseconds per step, MFU against the dense bf16 matrix-core peak, the
@@ -12,6 +14,7 @@ workload on this host's cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -43,7 +46,30 @@ def _args():
     ap.add_argument("--workload", default="C4", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="launch only the roofline kernel (3x) and a 1 GiB device copy (3x)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_mlp_up_c4_traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "dense_gpt_pretraining_nanochat_amd", "csrc", "k_gemm.hip")
+
+
+def measured_traffic(shape):
+    """HBM bytes per launch of the roofline kernel from the stored counter
+    passes (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
+    for a copy of known size), or None when the kernel source has changed
+    since the counters were taken or the shape differs."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(GEMM_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != sha or list(t.get("shape", [])) != list(shape):
+        return None
+    return int(t["fetch_bytes"] + t["write_bytes"])
 
 
 def dominant_kernel_roofline(cfg, nc, torch, reps=20):
@@ -58,25 +84,53 @@ def dominant_kernel_roofline(cfg, nc, torch, reps=20):
     A = torch.randn(M, d, device="cuda").to(et)
     B = (torch.randn(F, d, device="cuda") * 0.02).to(et)
     U = torch.empty(M, F, device="cuda", dtype=et)
-    Aout = torch.empty(M, F, device="cuda", dtype=et)
     s = torch.cuda.current_stream()
     for _ in range(3):
-        nc.nc_op_gemm(cfg.dtype, 1, 1, nc.EPI_RELU2, A, B, U, Aout, M, F, d, d, d, F, stream=s)
+        nc.nc_op_gemm(cfg.dtype, 1, 1, nc.EPI_RELU2, A, B, U, None, M, F, d, d, d, F, stream=s)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(s)
     for _ in range(reps):
-        nc.nc_op_gemm(cfg.dtype, 1, 1, nc.EPI_RELU2, A, B, U, Aout, M, F, d, d, d, F, stream=s)
+        nc.nc_op_gemm(cfg.dtype, 1, 1, nc.EPI_RELU2, A, B, U, None, M, F, d, d, d, F, stream=s)
     ev1.record(s)
     ev1.synchronize()
     sec = ev0.elapsed_time(ev1) / 1e3 / reps
     flops = 2.0 * M * F * d
     peak = PEAK_BF16_TFLOPS if bf else PEAK_F32_TFLOPS
     ach = flops / sec / 1e12
-    del A, B, U, Aout
-    return {"kernel": "gemm_kernel<bf16,NT,Relu2> (MLP up-projection, fwd)",
+    del A, B, U
+    return {"kernel": "gemm_bf16_kernel<Relu2, A k-contiguous, B k-contiguous> "
+                      "(MLP up-projection, forward)",
             "shape": [M, F, d], "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
             "unit": "TFLOP/s", "frac": round(ach / peak, 4), "avg_us": round(sec * 1e6, 2),
-            "flops_per_launch": flops, "traffic": None}
+            "flops_per_launch": flops, "traffic": measured_traffic([M, F, d])}
+
+
+def kernel_only(a):
+    """Three launches of the roofline kernel at the workload's shape, then three
+    1 GiB device-to-device copies (the counter calibration), nothing else."""
+    import torch
+
+    import dense_gpt_pretraining_nanochat_amd as nc
+    from dense_gpt_pretraining_nanochat_amd.config import PRESETS
+    c = PRESETS[a.workload]
+    cfg = nc.nc_config_from_depth(c.depth, c.vocab_size, c.seq_len, c.batch, c.dtype)
+    M, d = c.batch * c.seq_len, 64 * c.depth
+    F = 4 * d
+    et = torch.bfloat16 if cfg.dtype == nc.NC_BF16 else torch.float32
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    A = torch.randn(M, d, device="cuda", generator=gen).to(et)
+    B = (torch.randn(F, d, device="cuda", generator=gen) * 0.02).to(et)
+    U = torch.empty(M, F, device="cuda", dtype=et)
+    for _ in range(3):
+        nc.nc_op_gemm(cfg.dtype, 1, 1, nc.EPI_RELU2, A, B, U, None, M, F, d, d, d, F)
+    src = torch.ones(256 * 1024 * 1024, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"kernel_only": a.workload, "gemm_shape": [M, F, d],
+                      "copy_bytes": src.numel() * 4}), flush=True)
 
 
 def cpu_baseline(workload, ntok):
@@ -111,8 +165,11 @@ def main():
     a = _args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(the step runs on a single GPU; see the sharding notes)", file=sys.stderr)
         sys.exit(2)
+    if a.kernel_only:
+        kernel_only(a)
+        return
     import numpy as np
     import torch
 
