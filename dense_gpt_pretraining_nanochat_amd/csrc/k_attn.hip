@@ -43,7 +43,7 @@ constexpr int BQ = 32;        // query tokens per workgroup (fwd, dQ) / per step
 constexpr int BKV = 64;       // keys per tile (fwd, dQ)
 constexpr int BKW = 128;      // keys per dK/dV workgroup (4 wavefronts x 32)
 constexpr int QCH = 512;      // query tokens per dK/dV work item (partial sums per chunk)
-constexpr int kMaxHeadsPerWG = 8;     // forward
+constexpr int kMaxHeadsPerWG = 4;     // forward: 4-wavefront workgroups, two per CU
 constexpr int kMaxHeadsPerWGdQ = 4;   // dQ keeps Q, dO and dQ tiles in registers
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -112,7 +112,10 @@ struct AttnTypes {
   static constexpr int VEC = Vec16<T>::N;
   static constexpr int KB = 4 * VEC;           // contraction per fragment
   static constexpr int NS = D / KB;            // fragments along the head dim
-  static constexpr int KSTR = D + VEC;         // LDS row stride: 16-byte pad
+  static constexpr int KSTR = D + VEC;         // LDS row stride for 16-byte reads: 16-byte pad
+  // row stride for transpose reads: a 32-byte pad puts the four rows of one
+  // 16-lane read 32 bytes apart in the banks (conflict-free)
+  static constexpr int VSTR = sizeof(T) == 2 ? D + 2 * VEC : D + VEC;
   static constexpr int DC = D / VEC;           // 16-byte chunks per 128-wide row
   typedef typename Vec16<T>::type V;
   typedef T T4 __attribute__((ext_vector_type(4)));
@@ -121,7 +124,7 @@ struct AttnTypes {
 // A tile of R rows of 128 values, two sources (e.g. K and V, or Q and dO),
 // staged row-major into two LDS arrays. bf16 prefetches into registers (up to
 // PF chunks per thread); fp32 stages synchronously.
-template <typename T, int R, int PF>
+template <typename T, int R, int PF, int S0 = AttnTypes<T>::KSTR, int S1 = AttnTypes<T>::KSTR>
 struct PairStager {
   typedef AttnTypes<T> A;
   static constexpr int CHUNKS = 2 * R * A::DC;
@@ -133,7 +136,7 @@ struct PairStager {
   }
   __device__ __forceinline__ static T* dst_of(T* d0, T* d1, int c) {
     const int which = c / (R * A::DC), r = (c / A::DC) % R, dc = c % A::DC;
-    return (which ? d1 : d0) + r * A::KSTR + dc * A::VEC;
+    return (which ? d1 + r * S1 : d0 + r * S0) + dc * A::VEC;
   }
   __device__ __forceinline__ void load(const T* s0, const T* s1, size_t ld, int tid, int nthr) {
 #pragma unroll
@@ -176,15 +179,28 @@ constexpr bool kPrefetch(int esz) { return esz == 2; }
 // --------------------------------------------------------------------------
 // forward
 // --------------------------------------------------------------------------
+// Softmax without a running maximum. The query and key head vectors arrive
+// RMS-normalised (QK-norm), so |q|, |k| <= sqrt(128) and every scaled score
+// q.k / sqrt(128) is at most sqrt(128) = 11.31 (Cauchy-Schwarz). Subtracting
+// the fixed bound kScoreMax2 (log2 domain, with margin for bf16 rounding of
+// q and k) instead of the row maximum keeps every exponent <= 0 and >= -33,
+// so p = 2^(s - bound) neither overflows nor underflows in fp32, and the
+// output sum_u p_u v_u / sum_u p_u is the softmax exactly (up to rounding).
+// That removes the per-tile maximum, its shuffles and the rescaling of the
+// output accumulators; per score the vector work is one FMA, one exp2, one
+// add and half a conversion.
+constexpr float kScoreMax2 = 17.0f;   // > sqrt(128) * log2(e) = 16.32
+
 template <typename T>
 __global__ __launch_bounds__(kMaxHeadsPerWG * 64) void attn_fwd_kernel(
     const T* __restrict__ qkv, int ldq, int Tn, int H, int hpg, T* __restrict__ o,
     float* __restrict__ lse) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
-  constexpr int TILE = BKV * A::KSTR;
-  __shared__ __align__(16) T Ks[2 * TILE];
-  __shared__ __align__(16) T Vs[2 * TILE];
+  constexpr int KT = BKV * A::KSTR;            // K tile: row-major, read with 16-byte reads
+  constexpr int VT = BKV * A::VSTR;            // V tile: row-major, read with transpose reads
+  __shared__ __align__(16) T Ks[2 * KT];
+  __shared__ __align__(16) T Vs[2 * VT];
 
   const int ngroups = (H + hpg - 1) / hpg;
   const QBlock qbk = qblock_of(blockIdx.x, Tn / BQ, ngroups);
@@ -209,31 +225,33 @@ __global__ __launch_bounds__(kMaxHeadsPerWG * 64) void attn_fwd_kernel(
   f32x4 oacc[8][2];
 #pragma unroll
   for (int i = 0; i < 8; ++i) oacc[i][0] = oacc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+  float lsum[2] = {0.f, 0.f};                  // this lane's share of the row sums
   const float sc = kLog2e / sqrtf((float)D);
 
   constexpr bool PFT = kPrefetch(sizeof(T));
-  PairStager<T, BKV, PFT ? 8 : 1> stg;
+  typedef PairStager<T, BKV, PFT ? 8 : 1, A::KSTR, A::VSTR> Stager;
+  Stager stg;
   const int ntiles = (tq0 + BQ + BKV - 1) / BKV;
   if (PFT) {
     stg.load(kbase + row0 * ldq, vbase + row0 * ldq, ldq, tid, nthr);
     stg.store(Ks, Vs, tid, nthr);
   } else {
-    PairStager<T, BKV, 1>::copy(kbase + row0 * ldq, vbase + row0 * ldq, ldq, Ks, Vs, tid, nthr);
+    Stager::copy(kbase + row0 * ldq, vbase + row0 * ldq, ldq, Ks, Vs, tid, nthr);
   }
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     const int kv0 = it * BKV;
-    const T* K = Ks + (it & 1) * TILE;
-    const T* Vv = Vs + (it & 1) * TILE;
-    T* Kn = Ks + ((it + 1) & 1) * TILE;
-    T* Vn = Vs + ((it + 1) & 1) * TILE;
+    const T* K = Ks + (it & 1) * KT;
+    const T* Vv = Vs + (it & 1) * VT;
+    T* Kn = Ks + ((it + 1) & 1) * KT;
+    T* Vn = Vs + ((it + 1) & 1) * VT;
     const bool more = it + 1 < ntiles;
     if (PFT && more)
       stg.load(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq, ldq, tid, nthr);
 
     if (active) {
+      // S^T = K Q^T: lane (lg, l16) holds keys kv0 + 16 kt + 4 lg + r of query c*16 + l16
       f32x4 st[4][2];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) st[kt][0] = st[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -246,43 +264,17 @@ __global__ __launch_bounds__(kMaxHeadsPerWG * 64) void attn_fwd_kernel(
           Mma<T>::run(st[kt][1], kf, qf[1][s]);
         }
       const bool diag = kv0 + BKV > tq0;
-      float tmax[2] = {-INFINITY, -INFINITY};
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float v = st[kt][c][r] * sc;
-            if (diag && kv0 + kt * 16 + lg * 4 + r > tq0 + c * 16 + l16) v = -INFINITY;
-            st[kt][c][r] = v;
-            tmax[c] = fmaxf(tmax[c], v);
-          }
-      float alpha[2];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const float mnew = fmaxf(mrow[c], group4_max(tmax[c]));
-        alpha[c] = exp2f(mrow[c] - mnew);
-        mrow[c] = mnew;
-      }
-      float psum[2] = {0.f, 0.f};
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = exp2f(st[kt][c][r] - mrow[c]);
+            float p = __builtin_amdgcn_exp2f(fmaf(st[kt][c][r], sc, -kScoreMax2));
+            if (diag && kv0 + kt * 16 + lg * 4 + r > tq0 + c * 16 + l16) p = 0.f;
             st[kt][c][r] = p;
-            psum[c] += p;
+            lsum[c] += p;
           }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) lrow[c] = lrow[c] * alpha[c] + group4_sum(psum[c]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        oacc[i][0] *= alpha[0];
-        oacc[i][1] *= alpha[1];
-      }
       constexpr int NPT = CFrag<T>::NPT;
 #pragma unroll
       for (int kk = 0; kk < 4 / NPT; ++kk) {
@@ -295,7 +287,7 @@ __global__ __launch_bounds__(kMaxHeadsPerWG * 64) void attn_fwd_kernel(
         const V pb0 = CFrag<T>::pack(t0), pb1 = CFrag<T>::pack(t1);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const V va = CFrag<T>::read(Vv, A::KSTR, kk * 16 * NPT, dt * 16, lane);
+          const V va = CFrag<T>::read(Vv, A::VSTR, kk * 16 * NPT, dt * 16, lane);
           Mma<T>::run(oacc[dt][0], va, pb0);
           Mma<T>::run(oacc[dt][1], va, pb1);
         }
@@ -306,8 +298,8 @@ __global__ __launch_bounds__(kMaxHeadsPerWG * 64) void attn_fwd_kernel(
         stg.store(Kn, Vn, tid, nthr);
       } else {
         __syncthreads();   // single-buffered fp32 path: wait for readers first
-        PairStager<T, BKV, 1>::copy(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq,
-                                    ldq, Kn, Vn, tid, nthr);
+        Stager::copy(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq, ldq, Kn,
+                     Vn, tid, nthr);
       }
     }
     __syncthreads();
@@ -316,7 +308,8 @@ __global__ __launch_bounds__(kMaxHeadsPerWG * 64) void attn_fwd_kernel(
   const int ldo = H * D;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    const float inv = 1.0f / lrow[c];
+    const float l = group4_sum(lsum[c]);
+    const float inv = 1.0f / l;
     const int t = tq0 + c * 16 + l16;
     T* dst = o + (row0 + t) * ldo + h * D;
 #pragma unroll
@@ -326,7 +319,7 @@ __global__ __launch_bounds__(kMaxHeadsPerWG * 64) void attn_fwd_kernel(
       for (int r = 0; r < 4; ++r) w[r] = from_f32<T>(oacc[dt][c][r] * inv);
       *reinterpret_cast<typename A::T4*>(dst + dt * 16 + lg * 4) = w;
     }
-    if (lg == 0) lse[((size_t)qbk.b * H + h) * Tn + t] = (mrow[c] + log2f(lrow[c])) * kLn2;
+    if (lg == 0) lse[((size_t)qbk.b * H + h) * Tn + t] = (kScoreMax2 + log2f(l)) * kLn2;
   }
 }
 
@@ -406,13 +399,14 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64) void attn_bwd_dq_kernel(
   const T* vbase = qkv + (H + 1) * D;
 
   constexpr bool PFT = kPrefetch(sizeof(T));
-  PairStager<T, BKV, PFT ? 8 : 1> stg;
+  typedef PairStager<T, BKV, PFT ? 8 : 1> Stager;
+  Stager stg;
   const int ntiles = (tq0 + BQ + BKV - 1) / BKV;
   if (PFT) {
     stg.load(kbase + row0 * ldq, vbase + row0 * ldq, ldq, tid, nthr);
     stg.store(Ks, Vs, tid, nthr);
   } else {
-    PairStager<T, BKV, 1>::copy(kbase + row0 * ldq, vbase + row0 * ldq, ldq, Ks, Vs, tid, nthr);
+    Stager::copy(kbase + row0 * ldq, vbase + row0 * ldq, ldq, Ks, Vs, tid, nthr);
   }
   __syncthreads();
 

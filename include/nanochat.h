@@ -195,7 +195,12 @@ int nc_op_rope_qknorm_fwd(int32_t dtype, void* qkv, int32_t B, int32_t T, int32_
  * the forward call. */
 int nc_op_rope_qknorm_bwd(int32_t dtype, void* dqkv, const void* qkv, int32_t B, int32_t T,
                           int32_t H, const float* rinv_qk, const float* cs, void* stream);
-/* o [B*T, H*128] (T), lse [B, H, T] fp32 from qkv [B*T, d+256]. */
+/* o [B*T, H*128] (T), lse [B, H, T] fp32 from qkv [B*T, d+256].
+ * Precondition: every query and key head vector has RMS <= 1 (as the rotary
+ * + QK-norm step leaves them; RMSNorm output satisfies it for any eps >= 0),
+ * so scaled scores are bounded by sqrt(128): the softmax subtracts that fixed
+ * bound instead of a running row maximum. Unnormalised inputs with scores
+ * above ~60 overflow. */
 int nc_op_attn_fwd(int32_t dtype, const void* qkv, int32_t B, int32_t T, int32_t H, void* o,
                    float* lse, void* stream);
 /* Bytes of scratch nc_op_attn_bwd needs (fp32 partial dK/dV sums per
