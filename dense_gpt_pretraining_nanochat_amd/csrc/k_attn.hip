@@ -43,7 +43,7 @@ constexpr int BQ = 32;        // query tokens per workgroup (fwd, dQ) / per step
 constexpr int BKV = 64;       // keys per tile (fwd, dQ)
 constexpr int BKW = 128;      // keys per dK/dV workgroup (4 wavefronts x 32)
 constexpr int QCH = 512;      // query tokens per dK/dV work item (partial sums per chunk)
-constexpr int kMaxHeadsPerWG = 4;     // forward: 4-wavefront workgroups, two per CU
+constexpr int kMaxHeadsPerWG = 4;     // forward: 4-wavefront workgroups
 constexpr int kMaxHeadsPerWGdQ = 4;   // dQ keeps Q, dO and dQ tiles in registers
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -420,7 +420,9 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64) void attn_bwd_dq_kernel(
     if (PFT && more)
       stg.load(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq, ldq, tid, nthr);
 
-    if (active) {
+    // (inactive wavefronts run on zero Q/dO fragments, which gives dS = 0;
+    // no branch here keeps the accumulators in place)
+    {
       f32x4 st[4][2], dpt[4][2];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64) void attn_bwd_dq_kernel(
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float p = exp2f(st[kt][c][r] * sc - lse2[c]);
+            float p = __builtin_amdgcn_exp2f(fmaf(st[kt][c][r], sc, -lse2[c]));
             if (diag && kv0 + kt * 16 + lg * 4 + r > tq0 + c * 16 + l16) p = 0.f;
             st[kt][c][r] = p * (dpt[kt][c][r] - dl[c]);       // dS
           }
@@ -595,7 +597,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
       }
     }
 
-    if (kact) {
+    // (a wavefront whose keys lie past T works on zero K/V fragments and
+    // stores nothing: no branch here keeps the accumulators in place)
+    {
     // S[row][key] and dP[row][key]: 2 row tiles x 2 key tiles
     f32x4 sa[2][2], dpa[2][2];
 #pragma unroll
@@ -621,7 +625,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int rl = c * 16 + lg * 4 + r;     // local query row
-          float p = exp2f(sa[c][kt][r] * sc - lse_s[rl]);
+          float p = __builtin_amdgcn_exp2f(fmaf(sa[c][kt][r], sc, -lse_s[rl]));
           if (diag && key0 + kt * 16 + l16 > tq0 + rl) p = 0.f;
           pa[kt][c][r] = p;
           dsa[kt][c][r] = p * (dpa[c][kt][r] - dl_s[rl]);
