@@ -40,11 +40,14 @@ namespace {
 
 constexpr int D = 128;
 constexpr int BQ = 32;        // query tokens per workgroup (fwd, dQ) / per step (dK/dV)
-constexpr int BKV = 64;       // keys per tile (fwd, dQ)
+constexpr int BKV = 64;       // keys per tile (fwd)
+constexpr int BKVQ = 32;      // keys per tile (dQ)
 constexpr int BKW = 128;      // keys per dK/dV workgroup (4 wavefronts x 32)
 constexpr int QCH = 512;      // query tokens per dK/dV work item (partial sums per chunk)
-constexpr int kMaxHeadsPerWG = 4;     // forward: 4-wavefront workgroups
-constexpr int kMaxHeadsPerWGdQ = 4;   // dQ keeps Q, dO and dQ tiles in registers
+// Forward and dQ: 4-wavefront workgroups compiled for two wavefronts per SIMD
+// (<= 256 registers), so two workgroups share a CU.
+constexpr int kMaxHeadsPerWG = 4;     // forward
+constexpr int kMaxHeadsPerWGdQ = 4;   // dQ keeps Q, dO and dQ tiles in registers, 32-key tiles
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -192,7 +195,7 @@ constexpr bool kPrefetch(int esz) { return esz == 2; }
 constexpr float kScoreMax2 = 17.0f;   // > sqrt(128) * log2(e) = 16.32
 
 template <typename T>
-__global__ __launch_bounds__(kMaxHeadsPerWG * 64) void attn_fwd_kernel(
+__global__ __launch_bounds__(kMaxHeadsPerWG * 64, 2) void attn_fwd_kernel(
     const T* __restrict__ qkv, int ldq, int Tn, int H, int hpg, T* __restrict__ o,
     float* __restrict__ lse) {
   typedef AttnTypes<T> A;
@@ -359,12 +362,13 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o
 // backward, dQ: shaped like the forward (one wavefront per head, 32 rows)
 // --------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64, 2) void attn_bwd_dq_kernel(
     const T* __restrict__ qkv, int ldq, const T* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, int Tn, int H, int hpg, T* __restrict__ dqkv, int ldd) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
-  constexpr int TILE = BKV * A::KSTR;
+  constexpr int BK = BKVQ;                      // keys per tile
+  constexpr int TILE = BK * A::KSTR;
   __shared__ __align__(16) T Ks[2 * TILE];
   __shared__ __align__(16) T Vs[2 * TILE];
 
@@ -399,9 +403,9 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64) void attn_bwd_dq_kernel(
   const T* vbase = qkv + (H + 1) * D;
 
   constexpr bool PFT = kPrefetch(sizeof(T));
-  typedef PairStager<T, BKV, PFT ? 8 : 1> Stager;
+  typedef PairStager<T, BK, PFT ? 4 : 1> Stager;
   Stager stg;
-  const int ntiles = (tq0 + BQ + BKV - 1) / BKV;
+  const int ntiles = (tq0 + BQ + BK - 1) / BK;
   if (PFT) {
     stg.load(kbase + row0 * ldq, vbase + row0 * ldq, ldq, tid, nthr);
     stg.store(Ks, Vs, tid, nthr);
@@ -411,26 +415,26 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64) void attn_bwd_dq_kernel(
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
-    const int kv0 = it * BKV;
+    const int kv0 = it * BK;
     const T* K = Ks + (it & 1) * TILE;
     const T* Vv = Vs + (it & 1) * TILE;
     T* Kn = Ks + ((it + 1) & 1) * TILE;
     T* Vn = Vs + ((it + 1) & 1) * TILE;
     const bool more = it + 1 < ntiles;
     if (PFT && more)
-      stg.load(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq, ldq, tid, nthr);
+      stg.load(kbase + (row0 + kv0 + BK) * ldq, vbase + (row0 + kv0 + BK) * ldq, ldq, tid, nthr);
 
     // (inactive wavefronts run on zero Q/dO fragments, which gives dS = 0;
     // no branch here keeps the accumulators in place)
     {
-      f32x4 st[4][2], dpt[4][2];
+      f32x4 st[BK / 16][2], dpt[BK / 16][2];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < BK / 16; ++kt)
         st[kt][0] = st[kt][1] = dpt[kt][0] = dpt[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < A::NS; ++s)
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
+        for (int kt = 0; kt < BK / 16; ++kt) {
           const V kf = *reinterpret_cast<const V*>(K + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
           const V vf = *reinterpret_cast<const V*>(Vv + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
           Mma<T>::run(st[kt][0], kf, qf[0][s]);
@@ -438,9 +442,9 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64) void attn_bwd_dq_kernel(
           Mma<T>::run(dpt[kt][0], vf, df[0][s]);
           Mma<T>::run(dpt[kt][1], vf, df[1][s]);
         }
-      const bool diag = kv0 + BKV > tq0;
+      const bool diag = kv0 + BK > tq0;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < BK / 16; ++kt)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -451,7 +455,7 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64) void attn_bwd_dq_kernel(
           }
       constexpr int NPT = CFrag<T>::NPT;
 #pragma unroll
-      for (int kk = 0; kk < 4 / NPT; ++kk) {
+      for (int kk = 0; kk < BK / 16 / NPT; ++kk) {
         f32x4 t0[NPT], t1[NPT];
 #pragma unroll
         for (int q = 0; q < NPT; ++q) {
@@ -472,7 +476,7 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64) void attn_bwd_dq_kernel(
         stg.store(Kn, Vn, tid, nthr);
       } else {
         __syncthreads();
-        PairStager<T, BKV, 1>::copy(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq,
+        PairStager<T, BK, 1>::copy(kbase + (row0 + kv0 + BK) * ldq, vbase + (row0 + kv0 + BK) * ldq,
                                     ldq, Kn, Vn, tid, nthr);
       }
     }
