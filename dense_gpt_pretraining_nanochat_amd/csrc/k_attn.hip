@@ -39,10 +39,12 @@ namespace nc {
 namespace {
 
 constexpr int D = 128;
-constexpr int BQ = 32;        // query tokens per workgroup (fwd, dQ) / per step (dK/dV)
+constexpr int BQ = 32;        // query tokens per workgroup (fwd, dQ)
+constexpr int BQK = 64;       // query tokens per step (dK/dV)
 constexpr int BKV = 64;       // keys per tile (fwd)
 constexpr int BKVQ = 32;      // keys per tile (dQ)
-constexpr int BKW = 128;      // keys per dK/dV workgroup (4 wavefronts x 32)
+constexpr int BKW = 128;      // keys per dK/dV workgroup (8 wavefronts x 16)
+constexpr int DKW_THREADS = 512;
 constexpr int QCH = 512;      // query tokens per dK/dV work item (partial sums per chunk)
 // Forward and dQ: 4-wavefront workgroups compiled for two wavefronts per SIMD
 // (<= 256 registers), so two workgroups share a CU.
@@ -520,15 +522,16 @@ __device__ inline void dkv_item(int Tn, int i, int* kblk, int* chunk) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
+__global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
     const T* __restrict__ qkv, int ldq, const T* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, int B, int Tn, int H, float* __restrict__ part) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
-  constexpr int TILE = BQ * A::KSTR;
+  constexpr int SQ = BQK;                      // query rows per step
+  constexpr int TILE = SQ * A::KSTR;
   __shared__ __align__(16) T Qs[2 * TILE];
   __shared__ __align__(16) T Os[2 * TILE];
-  __shared__ float stat_s[2][2 * BQ];          // lse (log2 domain), then delta
+  __shared__ float stat_s[2][2 * SQ];          // lse (log2 domain), then delta
 
   // items are numbered item-major, batch-minor: early (long) key blocks start first
   const int b = blockIdx.x % B;
@@ -541,41 +544,43 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const size_t row0 = (size_t)b * Tn;
   const int ldo = H * D;
-  const int key0 = kv0 + wave * 32;            // this wave's 32 keys: key0 + 16*kt + l16
-  // T is a multiple of 64, so a wave's 32 keys are either all inside or all past T
+  const int key0 = kv0 + wave * 16;            // this wave's 16 keys: key0 + l16
+  // T is a multiple of 64, so a wave's 16 keys are either all inside or all past T
   const bool kact = key0 < Tn;
 
-  V kf[2][A::NS], vf[2][A::NS];
+  V kf[1][A::NS], vf[1][A::NS];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+  for (int kt = 0; kt < 1; ++kt)
 #pragma unroll
     for (int s = 0; s < A::NS; ++s) {
       const size_t r = row0 + key0 + kt * 16 + l16;
       kf[kt][s] = kact ? *reinterpret_cast<const V*>(qkv + r * ldq + H * D + s * A::KB + lg * A::VEC) : V{};
       vf[kt][s] = kact ? *reinterpret_cast<const V*>(qkv + r * ldq + (H + 1) * D + s * A::KB + lg * A::VEC) : V{};
     }
-  f32x4 dk[8][2], dv[8][2];
+  f32x4 dk[8][1], dv[8][1];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dk[i][0] = dk[i][1] = dv[i][0] = dv[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 8; ++i) dk[i][0] = dv[i][0] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sc = kLog2e / sqrtf((float)D);
   constexpr int NPT = CFrag<T>::NPT;
 
-  // iteration space: query blocks tq0 = q0, q0+32, ... < q1 and heads h
-  const int nqb = (q1 - q0) / BQ;
+  // iteration space: query blocks tq0 = q0, q0+SQ, ... < q1 and heads h
+  const int nqb = (q1 - q0) / SQ;
   const int niter = nqb * H;
   constexpr bool PFT = kPrefetch(sizeof(T));
-  auto qsrc = [&](int i) { return qkv + (row0 + q0 + (i / H) * BQ) * ldq + (i % H) * D; };
-  auto osrc = [&](int i) { return dout + (row0 + q0 + (i / H) * BQ) * ldo + (i % H) * D; };
+  auto qsrc = [&](int i) { return qkv + (row0 + q0 + (i / H) * SQ) * ldq + (i % H) * D; };
+  auto osrc = [&](int i) { return dout + (row0 + q0 + (i / H) * SQ) * ldo + (i % H) * D; };
+  // lse (log2 domain) or delta of step i for thread tid < 2 * SQ
+  auto stat_of = [&](int i) -> float {
+    const int h = i % H, t = q0 + (i / H) * SQ + (tid % SQ);
+    const size_t idx = ((size_t)b * H + h) * Tn + t;
+    return tid < SQ ? lse[idx] * kLog2e : delta[idx];
+  };
   auto stats = [&](int i, int buf) {
-    if (tid < 2 * BQ) {
-      const int h = i % H, t = q0 + (i / H) * BQ + (tid % BQ);
-      const size_t idx = ((size_t)b * H + h) * Tn + t;
-      stat_s[buf][tid] = tid < BQ ? lse[idx] * kLog2e : delta[idx];
-    }
+    if (tid < 2 * SQ) stat_s[buf][tid] = stat_of(i);
   };
   // Q and dO rows have different strides: staged chunk by chunk from either source
-  for (int c = tid; c < 2 * BQ * A::DC; c += 256) {
-    const int which = c / (BQ * A::DC), r = (c / A::DC) % BQ, dc = c % A::DC;
+  for (int c = tid; c < 2 * SQ * A::DC; c += DKW_THREADS) {
+    const int which = c / (SQ * A::DC), r = (c / A::DC) % SQ, dc = c % A::DC;
     const T* src = which ? osrc(0) + (size_t)r * ldo : qsrc(0) + (size_t)r * ldq;
     *reinterpret_cast<V*>((which ? Os : Qs) + r * A::KSTR + dc * A::VEC) =
         *reinterpret_cast<const V*>(src + dc * A::VEC);
@@ -584,18 +589,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   __syncthreads();
 
   for (int it = 0; it < niter; ++it) {
-    const int tq0 = q0 + (it / H) * BQ;
+    const int tq0 = q0 + (it / H) * SQ;
     const T* Q = Qs + (it & 1) * TILE;
     const T* O = Os + (it & 1) * TILE;
     const float* lse_s = stat_s[it & 1];
-    const float* dl_s = stat_s[it & 1] + BQ;
+    const float* dl_s = stat_s[it & 1] + SQ;
     const bool more = it + 1 < niter;
-    typename A::V pre[PFT ? 4 : 1];
+    constexpr int NPRE = 2 * SQ * A::DC / DKW_THREADS;
+    typename A::V pre[PFT ? NPRE : 1];
+    // next step's lse / delta, requested now and stored after this step's math
+    const float stat_next = (more && tid < 2 * SQ) ? stat_of(it + 1) : 0.f;
     if (PFT && more) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + i * 256;         // 4 * 256 = 2 * BQ * DC chunks
-        const int which = c / (BQ * A::DC), r = (c / A::DC) % BQ, dc = c % A::DC;
+      for (int i = 0; i < NPRE; ++i) {
+        const int c = tid + i * DKW_THREADS;   // NPRE * threads = 2 * SQ * DC chunks
+        const int which = c / (SQ * A::DC), r = (c / A::DC) % SQ, dc = c % A::DC;
         const T* src = which ? osrc(it + 1) + (size_t)r * ldo : qsrc(it + 1) + (size_t)r * ldq;
         pre[i] = *reinterpret_cast<const V*>(src + dc * A::VEC);
       }
@@ -605,27 +613,28 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     // stores nothing: no branch here keeps the accumulators in place)
     {
     // S[row][key] and dP[row][key]: 2 row tiles x 2 key tiles
-    f32x4 sa[2][2], dpa[2][2];
+    constexpr int NC = SQ / 16;                // 16-row query tiles per step
+    f32x4 sa[NC][1], dpa[NC][1];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) sa[c][0] = sa[c][1] = dpa[c][0] = dpa[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NC; ++c) sa[c][0] = dpa[c][0] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < A::NS; ++s)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < NC; ++c) {
         const V qa = *reinterpret_cast<const V*>(Q + (c * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
         const V da = *reinterpret_cast<const V*>(O + (c * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < 1; ++kt) {
           Mma<T>::run(sa[c][kt], qa, kf[kt][s]);
           Mma<T>::run(dpa[c][kt], da, vf[kt][s]);
         }
       }
-    const bool diag = tq0 < key0 + 32;
-    f32x4 pa[2][2], dsa[2][2];   // [kt][c]
+    const bool diag = tq0 < key0 + 16;
+    f32x4 pa[1][NC], dsa[1][NC];   // [kt][c]
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 1; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int rl = c * 16 + lg * 4 + r;     // local query row
@@ -636,9 +645,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
         }
     // dV^T[d][key] += dO^T[d][rows] P[rows][key];  dK^T += Q^T dS
 #pragma unroll
-    for (int kk = 0; kk < 2 / NPT; ++kk)
+    for (int kk = 0; kk < NC / NPT; ++kk)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 1; ++kt) {
         const V pb = CFrag<T>::pack(pa[kt] + kk * NPT);
         const V sb = CFrag<T>::pack(dsa[kt] + kk * NPT);
 #pragma unroll
@@ -656,21 +665,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
       T* On = Os + ((it + 1) & 1) * TILE;
       if (PFT) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = tid + i * 256;
-          const int which = c / (BQ * A::DC), r = (c / A::DC) % BQ, dc = c % A::DC;
+        for (int i = 0; i < NPRE; ++i) {
+          const int c = tid + i * DKW_THREADS;
+          const int which = c / (SQ * A::DC), r = (c / A::DC) % SQ, dc = c % A::DC;
           *reinterpret_cast<V*>((which ? On : Qn) + r * A::KSTR + dc * A::VEC) = pre[i];
         }
       } else {
         __syncthreads();
-        for (int c = tid; c < 2 * BQ * A::DC; c += 256) {
-          const int which = c / (BQ * A::DC), r = (c / A::DC) % BQ, dc = c % A::DC;
+        for (int c = tid; c < 2 * SQ * A::DC; c += DKW_THREADS) {
+          const int which = c / (SQ * A::DC), r = (c / A::DC) % SQ, dc = c % A::DC;
           const T* src = which ? osrc(it + 1) + (size_t)r * ldo : qsrc(it + 1) + (size_t)r * ldq;
           *reinterpret_cast<V*>((which ? On : Qn) + r * A::KSTR + dc * A::VEC) =
               *reinterpret_cast<const V*>(src + dc * A::VEC);
         }
       }
-      stats(it + 1, (it + 1) & 1);
+      if (tid < 2 * SQ) stat_s[(it + 1) & 1][tid] = stat_next;
     }
     __syncthreads();
   }
@@ -678,7 +687,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   // fp32 partial sums of this query chunk: part[chunk][token][0..127 dK, 128..255 dV]
   const size_t M = (size_t)B * Tn;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < 1; ++kt) {
     float* dst = part + ((size_t)chunk * M + row0 + key0 + kt * 16 + l16) * (2 * D);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -761,7 +770,7 @@ hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const f
   dim3 gq(B * (T / BQ) * ng), bq(64 * waves);
   int items = 0;
   for (int kb = 0; kb < (T + BKW - 1) / BKW; ++kb) items += dkv_chunks(T, kb);
-  dim3 gk(B * items), bk(256);
+  dim3 gk(B * items), bk(DKW_THREADS);
   const size_t M = (size_t)B * T;
   dim3 gr((unsigned)((M + 3) / 4)), br(256);
   if (t == DType::BF16) {
