@@ -16,20 +16,20 @@
 // k0+j, columns n0+4q..n0+4q+3, and output lane i receives rows k0..k0+3 of
 // column n0+i - one matrix-core fragment.
 //
-// Forward (flash style, online softmax in the log2 domain): a workgroup owns
-// 32 query tokens and up to 8 heads, one wavefront per head. Each K/V tile of
-// 64 keys is staged once and read by every head's wavefront; the next tile is
-// prefetched into registers while the current one is in use (two LDS
-// buffers, one barrier per tile). A wavefront computes S^T = K Q^T so each lane
-// column is one query row: the softmax statistics stay in the lane and P^T
-// feeds O^T += V^T P^T straight from registers.
+// Forward (flash style): a workgroup owns 64 query tokens of two heads, one
+// wavefront per (head, 32 tokens). Each K/V tile of 64 keys is staged once
+// and read by all four wavefronts; the next tile is prefetched into registers
+// while the current one is in use (two LDS buffers, one barrier per tile). A
+// wavefront computes S^T = K Q^T so each lane column is one query row: the
+// softmax sums stay in the lane and P^T feeds O^T += V^T P^T straight from
+// registers. The softmax needs no running maximum (see kScoreMax2).
 //
 // Backward: dK/dV of a 128-key block are summed over all heads and one chunk
-// of up to 512 later query tokens by one workgroup (32 keys per wavefront,
+// of up to 512 later query tokens by one workgroup (16 keys per wavefront,
 // accumulators in registers), which keeps the work items even under the
 // causal mask; a second pass adds the chunk partials in a fixed order. dQ
-// comes from a kernel shaped like the forward. No atomics anywhere, so the
-// results are bitwise reproducible.
+// comes from a kernel shaped like the forward (32-key tiles). No atomics
+// anywhere, so the results are bitwise reproducible.
 #include <math.h>
 
 #include "common.h"
@@ -39,7 +39,8 @@ namespace nc {
 namespace {
 
 constexpr int D = 128;
-constexpr int BQ = 32;        // query tokens per workgroup (fwd, dQ)
+constexpr int BQ = 32;        // query tokens per wavefront (fwd, dQ)
+constexpr int FQB = 64;       // query tokens per fwd / dQ workgroup (2 heads x 2 x 32)
 constexpr int BQK = 64;       // query tokens per step (dK/dV)
 constexpr int BKV = 64;       // keys per tile (fwd)
 constexpr int BKVQ = 32;      // keys per tile (dQ)
@@ -48,8 +49,6 @@ constexpr int DKW_THREADS = 512;
 constexpr int QCH = 512;      // query tokens per dK/dV work item (partial sums per chunk)
 // Forward and dQ: 4-wavefront workgroups compiled for two wavefronts per SIMD
 // (<= 256 registers), so two workgroups share a CU.
-constexpr int kMaxHeadsPerWG = 4;     // forward
-constexpr int kMaxHeadsPerWGdQ = 4;   // dQ keeps Q, dO and dQ tiles in registers, 32-key tiles
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -197,9 +196,8 @@ constexpr bool kPrefetch(int esz) { return esz == 2; }
 constexpr float kScoreMax2 = 17.0f;   // > sqrt(128) * log2(e) = 16.32
 
 template <typename T>
-__global__ __launch_bounds__(kMaxHeadsPerWG * 64, 2) void attn_fwd_kernel(
-    const T* __restrict__ qkv, int ldq, int Tn, int H, int hpg, T* __restrict__ o,
-    float* __restrict__ lse) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+    const T* __restrict__ qkv, int ldq, int Tn, int H, T* __restrict__ o, float* __restrict__ lse) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
   constexpr int KT = BKV * A::KSTR;            // K tile: row-major, read with 16-byte reads
@@ -207,13 +205,15 @@ __global__ __launch_bounds__(kMaxHeadsPerWG * 64, 2) void attn_fwd_kernel(
   __shared__ __align__(16) T Ks[2 * KT];
   __shared__ __align__(16) T Vs[2 * VT];
 
-  const int ngroups = (H + hpg - 1) / hpg;
-  const QBlock qbk = qblock_of(blockIdx.x, Tn / BQ, ngroups);
-  const int tq0 = qbk.qb * BQ;
+  // workgroup: 64 query tokens x 2 heads; wavefront w: head 2*pair + (w & 1),
+  // query tokens tq0 .. tq0 + 31 with tq0 = block start + 32 * (w >> 1)
+  const QBlock qbk = qblock_of(blockIdx.x, Tn / FQB, (H + 1) / 2);
+  const int tb0 = qbk.qb * FQB;
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int h = qbk.hg * hpg + wave;
-  const bool active = wave < hpg && h < H;
+  const int h = 2 * qbk.hg + (wave & 1);
+  const int tq0 = tb0 + BQ * (wave >> 1);
+  const bool active = h < H;
   const size_t row0 = (size_t)qbk.b * Tn;
   const T* kbase = qkv + H * D;
   const T* vbase = qkv + (H + 1) * D;
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kMaxHeadsPerWG * 64, 2) void attn_fwd_kernel(
   constexpr bool PFT = kPrefetch(sizeof(T));
   typedef PairStager<T, BKV, PFT ? 8 : 1, A::KSTR, A::VSTR> Stager;
   Stager stg;
-  const int ntiles = (tq0 + BQ + BKV - 1) / BKV;
+  const int ntiles = (tb0 + FQB + BKV - 1) / BKV;
   if (PFT) {
     stg.load(kbase + row0 * ldq, vbase + row0 * ldq, ldq, tid, nthr);
     stg.store(Ks, Vs, tid, nthr);
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kMaxHeadsPerWG * 64, 2) void attn_fwd_kernel(
     if (PFT && more)
       stg.load(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq, ldq, tid, nthr);
 
-    if (active) {
+    if (active && kv0 < tq0 + BQ) {          // tiles past this wave's queries: nothing to add
       // S^T = K Q^T: lane (lg, l16) holds keys kv0 + 16 kt + 4 lg + r of query c*16 + l16
       f32x4 st[4][2];
 #pragma unroll
@@ -364,9 +364,9 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o
 // backward, dQ: shaped like the forward (one wavefront per head, 32 rows)
 // --------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64, 2) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     const T* __restrict__ qkv, int ldq, const T* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, int Tn, int H, int hpg, T* __restrict__ dqkv, int ldd) {
+    const float* __restrict__ delta, int Tn, int H, T* __restrict__ dqkv, int ldd) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
   constexpr int BK = BKVQ;                      // keys per tile
@@ -374,13 +374,14 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64, 2) void attn_bwd_dq_kernel(
   __shared__ __align__(16) T Ks[2 * TILE];
   __shared__ __align__(16) T Vs[2 * TILE];
 
-  const int ngroups = (H + hpg - 1) / hpg;
-  const QBlock qbk = qblock_of(blockIdx.x, Tn / BQ, ngroups);
-  const int tq0 = qbk.qb * BQ;
+  // workgroup: 64 query tokens x 2 heads, as in the forward
+  const QBlock qbk = qblock_of(blockIdx.x, Tn / FQB, (H + 1) / 2);
+  const int tb0 = qbk.qb * FQB;
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int h = qbk.hg * hpg + wave;
-  const bool active = wave < hpg && h < H;
+  const int h = 2 * qbk.hg + (wave & 1);
+  const int tq0 = tb0 + BQ * (wave >> 1);
+  const bool active = h < H;
   const size_t row0 = (size_t)qbk.b * Tn;
   const int ldo = H * D;
 
@@ -407,7 +408,7 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64, 2) void attn_bwd_dq_kernel(
   constexpr bool PFT = kPrefetch(sizeof(T));
   typedef PairStager<T, BK, PFT ? 4 : 1> Stager;
   Stager stg;
-  const int ntiles = (tq0 + BQ + BK - 1) / BK;
+  const int ntiles = (tb0 + FQB + BK - 1) / BK;
   if (PFT) {
     stg.load(kbase + row0 * ldq, vbase + row0 * ldq, ldq, tid, nthr);
     stg.store(Ks, Vs, tid, nthr);
@@ -427,8 +428,8 @@ __global__ __launch_bounds__(kMaxHeadsPerWGdQ * 64, 2) void attn_bwd_dq_kernel(
       stg.load(kbase + (row0 + kv0 + BK) * ldq, vbase + (row0 + kv0 + BK) * ldq, ldq, tid, nthr);
 
     // (inactive wavefronts run on zero Q/dO fragments, which gives dS = 0;
-    // no branch here keeps the accumulators in place)
-    {
+    // tiles past this wavefront's queries are skipped: a wave-uniform branch)
+    if (kv0 < tq0 + BQ) {
       f32x4 st[BK / 16][2], dpt[BK / 16][2];
 #pragma unroll
       for (int kt = 0; kt < BK / 16; ++kt)
@@ -719,28 +720,18 @@ __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(const float* __res
   *reinterpret_cast<T4*>(dqkv + row * ldd + H * D + lane * 4) = w;
 }
 
-// heads per workgroup <= maxw; at least 4 wavefronts so K/V staging has enough threads
-inline void head_groups(int H, int maxw, int* hpg, int* ng, int* waves) {
-  *ng = (H + maxw - 1) / maxw;
-  *hpg = (H + *ng - 1) / *ng;
-  *ng = (H + *hpg - 1) / *hpg;
-  *waves = *hpg < 4 ? 4 : *hpg;
-}
-
 }  // namespace
 
 hipError_t attn_fwd(DType t, const void* qkv, int ldq, int B, int T, int H, void* o, float* lse,
                     hipStream_t s) {
   if (T % BKV || H < 1 || H > 16) return hipErrorInvalidValue;
-  int hpg, ng, waves;
-  head_groups(H, kMaxHeadsPerWG, &hpg, &ng, &waves);
-  dim3 grid(B * (T / BQ) * ng), block(64 * waves);
+  dim3 grid(B * (T / FQB) * ((H + 1) / 2)), block(256);
   if (t == DType::BF16)
     hipLaunchKernelGGL(attn_fwd_kernel<bf16>, grid, block, 0, s, static_cast<const bf16*>(qkv), ldq, T,
-                       H, hpg, static_cast<bf16*>(o), lse);
+                       H, static_cast<bf16*>(o), lse);
   else
     hipLaunchKernelGGL(attn_fwd_kernel<float>, grid, block, 0, s, static_cast<const float*>(qkv), ldq,
-                       T, H, hpg, static_cast<float*>(o), lse);
+                       T, H, static_cast<float*>(o), lse);
   return hipGetLastError();
 }
 
@@ -765,9 +756,7 @@ hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const f
                     const float* delta, int B, int T, int H, void* dqkv, int ldd, float* scratch,
                     hipStream_t s) {
   if (T % BKV || H < 1 || H > 16) return hipErrorInvalidValue;
-  int hpg, ng, waves;
-  head_groups(H, kMaxHeadsPerWGdQ, &hpg, &ng, &waves);
-  dim3 gq(B * (T / BQ) * ng), bq(64 * waves);
+  dim3 gq(B * (T / FQB) * ((H + 1) / 2)), bq(256);
   int items = 0;
   for (int kb = 0; kb < (T + BKW - 1) / BKW; ++kb) items += dkv_chunks(T, kb);
   dim3 gk(B * items), bk(DKW_THREADS);
@@ -779,14 +768,14 @@ hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const f
     bf16* g = static_cast<bf16*>(dqkv);
     hipLaunchKernelGGL(attn_bwd_dkv_kernel<bf16>, gk, bk, 0, s, q, ldq, d, lse, delta, B, T, H, scratch);
     hipLaunchKernelGGL(attn_dkv_reduce_kernel<bf16>, gr, br, 0, s, scratch, B, T, H, g, ldd);
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<bf16>, gq, bq, 0, s, q, ldq, d, lse, delta, T, H, hpg, g, ldd);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<bf16>, gq, bq, 0, s, q, ldq, d, lse, delta, T, H, g, ldd);
   } else {
     const float* q = static_cast<const float*>(qkv);
     const float* d = static_cast<const float*>(dout);
     float* g = static_cast<float*>(dqkv);
     hipLaunchKernelGGL(attn_bwd_dkv_kernel<float>, gk, bk, 0, s, q, ldq, d, lse, delta, B, T, H, scratch);
     hipLaunchKernelGGL(attn_dkv_reduce_kernel<float>, gr, br, 0, s, scratch, B, T, H, g, ldd);
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<float>, gq, bq, 0, s, q, ldq, d, lse, delta, T, H, hpg, g, ldd);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<float>, gq, bq, 0, s, q, ldq, d, lse, delta, T, H, g, ldd);
   }
   return hipGetLastError();
 }
