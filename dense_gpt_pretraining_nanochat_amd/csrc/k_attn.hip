@@ -32,6 +32,8 @@
 // anywhere, so the results are bitwise reproducible.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -196,7 +198,7 @@ constexpr bool kPrefetch(int esz) { return esz == 2; }
 constexpr float kScoreMax2 = 17.0f;   // > sqrt(128) * log2(e) = 16.32
 
 template <typename T>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void attn_fwd_kernel(
     const T* __restrict__ qkv, int ldq, int Tn, int H, T* __restrict__ o, float* __restrict__ lse) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   // query tokens tq0 .. tq0 + 31 with tq0 = block start + 32 * (w >> 1)
   const QBlock qbk = qblock_of(blockIdx.x, Tn / FQB, (H + 1) / 2);
   const int tb0 = qbk.qb * FQB;
-  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int h = 2 * qbk.hg + (wave & 1);
   const int tq0 = tb0 + BQ * (wave >> 1);
@@ -234,80 +236,86 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(
   const float sc = kLog2e / sqrtf((float)D);
 
   constexpr bool PFT = kPrefetch(sizeof(T));
+  constexpr int NT = 256;                       // threads per workgroup
   typedef PairStager<T, BKV, PFT ? 8 : 1, A::KSTR, A::VSTR> Stager;
   Stager stg;
-  const int ntiles = (tb0 + FQB + BKV - 1) / BKV;
+  const int ntiles = (tb0 + FQB + BKV - 1) / BKV;   // the last tile is the diagonal one
   if (PFT) {
-    stg.load(kbase + row0 * ldq, vbase + row0 * ldq, ldq, tid, nthr);
-    stg.store(Ks, Vs, tid, nthr);
+    stg.load(kbase + row0 * ldq, vbase + row0 * ldq, ldq, tid, NT);
+    stg.store(Ks, Vs, tid, NT);
   } else {
-    Stager::copy(kbase + row0 * ldq, vbase + row0 * ldq, ldq, Ks, Vs, tid, nthr);
+    Stager::copy(kbase + row0 * ldq, vbase + row0 * ldq, ldq, Ks, Vs, tid, NT);
   }
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  // One K/V tile: S^T = K Q^T (lane (lg, l16) holds keys kv0 + 16 kt + 4 lg + r
+  // of query c*16 + l16), p = 2^(s*scale - bound), O^T += V^T P^T. Wavefronts
+  // without a head (odd H) run on zero queries and store nothing. Only the
+  // last tile needs the causal mask.
+  auto tile = [&](auto masked, const T* K, const T* Vv, int kv0) {
+    constexpr bool MASKED = decltype(masked)::value;
+    f32x4 st[4][2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) st[kt][0] = st[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < A::NS; ++s)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const V kf = *reinterpret_cast<const V*>(K + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
+        Mma<T>::run(st[kt][0], kf, qf[0][s]);
+        Mma<T>::run(st[kt][1], kf, qf[1][s]);
+      }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float p = __builtin_amdgcn_exp2f(fmaf(st[kt][c][r], sc, -kScoreMax2));
+          if constexpr (MASKED) {
+            if (kv0 + kt * 16 + lg * 4 + r > tq0 + c * 16 + l16) p = 0.f;
+          }
+          st[kt][c][r] = p;
+          lsum[c] += p;
+        }
+    constexpr int NPT = CFrag<T>::NPT;
+#pragma unroll
+    for (int kk = 0; kk < 4 / NPT; ++kk) {
+      f32x4 t0[NPT], t1[NPT];
+#pragma unroll
+      for (int q = 0; q < NPT; ++q) {
+        t0[q] = st[kk * NPT + q][0];
+        t1[q] = st[kk * NPT + q][1];
+      }
+      const V pb0 = CFrag<T>::pack(t0), pb1 = CFrag<T>::pack(t1);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const V va = CFrag<T>::read(Vv, A::VSTR, kk * 16 * NPT, dt * 16, lane);
+        Mma<T>::run(oacc[dt][0], va, pb0);
+        Mma<T>::run(oacc[dt][1], va, pb1);
+      }
+    }
+  };
+
+  for (int it = 0; it + 1 < ntiles; ++it) {
     const int kv0 = it * BKV;
-    const T* K = Ks + (it & 1) * KT;
-    const T* Vv = Vs + (it & 1) * VT;
     T* Kn = Ks + ((it + 1) & 1) * KT;
     T* Vn = Vs + ((it + 1) & 1) * VT;
-    const bool more = it + 1 < ntiles;
-    if (PFT && more)
-      stg.load(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq, ldq, tid, nthr);
-
-    if (active && kv0 < tq0 + BQ) {          // tiles past this wave's queries: nothing to add
-      // S^T = K Q^T: lane (lg, l16) holds keys kv0 + 16 kt + 4 lg + r of query c*16 + l16
-      f32x4 st[4][2];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) st[kt][0] = st[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < A::NS; ++s)
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const V kf = *reinterpret_cast<const V*>(K + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
-          Mma<T>::run(st[kt][0], kf, qf[0][s]);
-          Mma<T>::run(st[kt][1], kf, qf[1][s]);
-        }
-      const bool diag = kv0 + BKV > tq0;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float p = __builtin_amdgcn_exp2f(fmaf(st[kt][c][r], sc, -kScoreMax2));
-            if (diag && kv0 + kt * 16 + lg * 4 + r > tq0 + c * 16 + l16) p = 0.f;
-            st[kt][c][r] = p;
-            lsum[c] += p;
-          }
-      constexpr int NPT = CFrag<T>::NPT;
-#pragma unroll
-      for (int kk = 0; kk < 4 / NPT; ++kk) {
-        f32x4 t0[NPT], t1[NPT];
-#pragma unroll
-        for (int q = 0; q < NPT; ++q) {
-          t0[q] = st[kk * NPT + q][0];
-          t1[q] = st[kk * NPT + q][1];
-        }
-        const V pb0 = CFrag<T>::pack(t0), pb1 = CFrag<T>::pack(t1);
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const V va = CFrag<T>::read(Vv, A::VSTR, kk * 16 * NPT, dt * 16, lane);
-          Mma<T>::run(oacc[dt][0], va, pb0);
-          Mma<T>::run(oacc[dt][1], va, pb1);
-        }
-      }
-    }
-    if (more) {
-      if (PFT) {
-        stg.store(Kn, Vn, tid, nthr);
-      } else {
-        __syncthreads();   // single-buffered fp32 path: wait for readers first
-        Stager::copy(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq, ldq, Kn,
-                     Vn, tid, nthr);
-      }
+    if (PFT)
+      stg.load(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq, ldq, tid, NT);
+    tile(std::false_type{}, Ks + (it & 1) * KT, Vs + (it & 1) * VT, kv0);
+    if (PFT) {
+      stg.store(Kn, Vn, tid, NT);
+    } else {
+      __syncthreads();   // single-buffered fp32 path: wait for readers first
+      Stager::copy(kbase + (row0 + kv0 + BKV) * ldq, vbase + (row0 + kv0 + BKV) * ldq, ldq, Kn,
+                   Vn, tid, NT);
     }
     __syncthreads();
+  }
+  {
+    const int it = ntiles - 1;
+    tile(std::true_type{}, Ks + (it & 1) * KT, Vs + (it & 1) * VT, it * BKV);
   }
   if (!active) return;
   const int ldo = H * D;
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   // workgroup: 64 query tokens x 2 heads, as in the forward
   const QBlock qbk = qblock_of(blockIdx.x, Tn / FQB, (H + 1) / 2);
   const int tb0 = qbk.qb * FQB;
-  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int h = 2 * qbk.hg + (wave & 1);
   const int tq0 = tb0 + BQ * (wave >> 1);
@@ -406,84 +414,98 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   const T* vbase = qkv + (H + 1) * D;
 
   constexpr bool PFT = kPrefetch(sizeof(T));
+  constexpr int NT = 256;                       // threads per workgroup
   typedef PairStager<T, BK, PFT ? 4 : 1> Stager;
   Stager stg;
+  // tiles 0 .. ntiles - 3 lie below every query of the block; the last two
+  // (keys tb0 .. tb0 + 63) need the causal mask
   const int ntiles = (tb0 + FQB + BK - 1) / BK;
   if (PFT) {
-    stg.load(kbase + row0 * ldq, vbase + row0 * ldq, ldq, tid, nthr);
-    stg.store(Ks, Vs, tid, nthr);
+    stg.load(kbase + row0 * ldq, vbase + row0 * ldq, ldq, tid, NT);
+    stg.store(Ks, Vs, tid, NT);
   } else {
-    Stager::copy(kbase + row0 * ldq, vbase + row0 * ldq, ldq, Ks, Vs, tid, nthr);
+    Stager::copy(kbase + row0 * ldq, vbase + row0 * ldq, ldq, Ks, Vs, tid, NT);
   }
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  // One K/V tile: S^T and dP^T, dS = P (dP - delta), dQ += dS K. Inactive
+  // wavefronts run on zero Q/dO fragments, which gives dS = 0.
+  auto tile = [&](auto masked, const T* K, const T* Vv, int kv0) {
+    constexpr bool MASKED = decltype(masked)::value;
+    f32x4 st[BK / 16][2], dpt[BK / 16][2];
+#pragma unroll
+    for (int kt = 0; kt < BK / 16; ++kt)
+      st[kt][0] = st[kt][1] = dpt[kt][0] = dpt[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < A::NS; ++s)
+#pragma unroll
+      for (int kt = 0; kt < BK / 16; ++kt) {
+        const V kf = *reinterpret_cast<const V*>(K + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
+        const V vf = *reinterpret_cast<const V*>(Vv + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
+        Mma<T>::run(st[kt][0], kf, qf[0][s]);
+        Mma<T>::run(st[kt][1], kf, qf[1][s]);
+        Mma<T>::run(dpt[kt][0], vf, df[0][s]);
+        Mma<T>::run(dpt[kt][1], vf, df[1][s]);
+      }
+#pragma unroll
+    for (int kt = 0; kt < BK / 16; ++kt)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float p = __builtin_amdgcn_exp2f(fmaf(st[kt][c][r], sc, -lse2[c]));
+          if constexpr (MASKED) {
+            if (kv0 + kt * 16 + lg * 4 + r > tq0 + c * 16 + l16) p = 0.f;
+          }
+          st[kt][c][r] = p * (dpt[kt][c][r] - dl[c]);       // dS
+        }
+    constexpr int NPT = CFrag<T>::NPT;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16 / NPT; ++kk) {
+      f32x4 t0[NPT], t1[NPT];
+#pragma unroll
+      for (int q = 0; q < NPT; ++q) {
+        t0[q] = st[kk * NPT + q][0];
+        t1[q] = st[kk * NPT + q][1];
+      }
+      const V b0 = CFrag<T>::pack(t0), b1 = CFrag<T>::pack(t1);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const V ka = CFrag<T>::read(K, A::KSTR, kk * 16 * NPT, dt * 16, lane);   // K^T
+        Mma<T>::run(dq[dt][0], ka, b0);
+        Mma<T>::run(dq[dt][1], ka, b1);
+      }
+    }
+  };
+  auto next = [&](int it) {                      // stage tile it + 1, then barrier
     const int kv0 = it * BK;
-    const T* K = Ks + (it & 1) * TILE;
-    const T* Vv = Vs + (it & 1) * TILE;
     T* Kn = Ks + ((it + 1) & 1) * TILE;
     T* Vn = Vs + ((it + 1) & 1) * TILE;
-    const bool more = it + 1 < ntiles;
-    if (PFT && more)
-      stg.load(kbase + (row0 + kv0 + BK) * ldq, vbase + (row0 + kv0 + BK) * ldq, ldq, tid, nthr);
-
-    // (inactive wavefronts run on zero Q/dO fragments, which gives dS = 0;
-    // tiles past this wavefront's queries are skipped: a wave-uniform branch)
-    if (kv0 < tq0 + BQ) {
-      f32x4 st[BK / 16][2], dpt[BK / 16][2];
-#pragma unroll
-      for (int kt = 0; kt < BK / 16; ++kt)
-        st[kt][0] = st[kt][1] = dpt[kt][0] = dpt[kt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < A::NS; ++s)
-#pragma unroll
-        for (int kt = 0; kt < BK / 16; ++kt) {
-          const V kf = *reinterpret_cast<const V*>(K + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
-          const V vf = *reinterpret_cast<const V*>(Vv + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
-          Mma<T>::run(st[kt][0], kf, qf[0][s]);
-          Mma<T>::run(st[kt][1], kf, qf[1][s]);
-          Mma<T>::run(dpt[kt][0], vf, df[0][s]);
-          Mma<T>::run(dpt[kt][1], vf, df[1][s]);
-        }
-      const bool diag = kv0 + BK > tq0;
-#pragma unroll
-      for (int kt = 0; kt < BK / 16; ++kt)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float p = __builtin_amdgcn_exp2f(fmaf(st[kt][c][r], sc, -lse2[c]));
-            if (diag && kv0 + kt * 16 + lg * 4 + r > tq0 + c * 16 + l16) p = 0.f;
-            st[kt][c][r] = p * (dpt[kt][c][r] - dl[c]);       // dS
-          }
-      constexpr int NPT = CFrag<T>::NPT;
-#pragma unroll
-      for (int kk = 0; kk < BK / 16 / NPT; ++kk) {
-        f32x4 t0[NPT], t1[NPT];
-#pragma unroll
-        for (int q = 0; q < NPT; ++q) {
-          t0[q] = st[kk * NPT + q][0];
-          t1[q] = st[kk * NPT + q][1];
-        }
-        const V b0 = CFrag<T>::pack(t0), b1 = CFrag<T>::pack(t1);
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const V ka = CFrag<T>::read(K, A::KSTR, kk * 16 * NPT, dt * 16, lane);   // K^T
-          Mma<T>::run(dq[dt][0], ka, b0);
-          Mma<T>::run(dq[dt][1], ka, b1);
-        }
-      }
-    }
-    if (more) {
-      if (PFT) {
-        stg.store(Kn, Vn, tid, nthr);
-      } else {
-        __syncthreads();
-        PairStager<T, BK, 1>::copy(kbase + (row0 + kv0 + BK) * ldq, vbase + (row0 + kv0 + BK) * ldq,
-                                    ldq, Kn, Vn, tid, nthr);
-      }
+    if (PFT) {
+      stg.store(Kn, Vn, tid, NT);
+    } else {
+      __syncthreads();
+      Stager::copy(kbase + (row0 + kv0 + BK) * ldq, vbase + (row0 + kv0 + BK) * ldq, ldq, Kn, Vn,
+                   tid, NT);
     }
     __syncthreads();
+  };
+
+  for (int it = 0; it + 2 < ntiles; ++it) {
+    const int kv0 = it * BK;
+    if (PFT) stg.load(kbase + (row0 + kv0 + BK) * ldq, vbase + (row0 + kv0 + BK) * ldq, ldq, tid, NT);
+    tile(std::false_type{}, Ks + (it & 1) * TILE, Vs + (it & 1) * TILE, kv0);
+    next(it);
+  }
+  {
+    const int it = ntiles - 2, kv0 = it * BK;   // keys tb0 .. tb0 + 31
+    if (PFT) stg.load(kbase + (row0 + kv0 + BK) * ldq, vbase + (row0 + kv0 + BK) * ldq, ldq, tid, NT);
+    tile(std::true_type{}, Ks + (it & 1) * TILE, Vs + (it & 1) * TILE, kv0);
+    next(it);
+  }
+  {
+    const int it = ntiles - 1, kv0 = it * BK;   // keys tb0 + 32 .. tb0 + 63: none for the lower half
+    if (kv0 < tq0 + BQ) tile(std::true_type{}, Ks + (it & 1) * TILE, Vs + (it & 1) * TILE, kv0);
   }
   if (!active) return;
   const float scale = 1.0f / sqrtf((float)D);
