@@ -93,7 +93,7 @@ hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const f
 
 // ---- cross-entropy -----------------------------------------------------------
 // rows of fp32 logits [R, V]: per-row loss (fp32) and dlogits (T) = (softmax(z)-onehot)*(1-(z/c)^2)*w
-hipError_t softcap_ce(DType t, const float* logits, const int32_t* tgt, int R, int V, float cap,
+hipError_t softcap_ce(DType t, const void* logits, const int32_t* tgt, int R, int V, float cap,
                       float w, float* loss_rows, void* dlogits, uint32_t* status, hipStream_t s);
 hipError_t loss_mean(const float* loss_rows, int M, float* out, uint32_t* status, hipStream_t s);
 

@@ -91,11 +91,10 @@ uint64_t param_elems(const Dims& D) {
   return align_up(t.back().offset + (uint64_t)(t.back().rows * t.back().cols), 128);
 }
 
-// lm_head rows processed per chunk: bounds the fp32 logits buffer at
-// Mc * V * 4 bytes (4 GiB at V = 65,536).
-// Rows of the lm_head / loss processed at once: the fp32 logits and the bf16
-// logit gradients of a chunk live in the workspace (65536 rows x 65536 vocab =
-// 25.8 GB), so the vocabulary products run over the whole batch in one launch.
+// Rows of the lm_head / loss processed at once: the logits and the logit
+// gradients of a chunk (both in the activation type) live in the workspace
+// (65536 rows x 65536 vocab x 2 x 2 bytes = 17 GB in bf16 mode), so the
+// vocabulary products run over the whole batch in one launch.
 int64_t chunk_rows(const Dims& D) { return std::min<int64_t>(D.M, 65536); }
 
 // Split-K plan for a weight gradient dW[N1, N2] = X1^T X2 contracted over K
@@ -162,7 +161,7 @@ Plan plan_of(const Dims& D, bool bwd) {
   p.xf = take(M * D.d * e);
   p.rinvf = take(M * 4);
   p.loss_rows = take(M * 4);
-  p.logits = take(Mc * D.V * 4);
+  p.logits = take(Mc * D.V * e);
   p.dlog = take(Mc * D.V * e);
   const int nsets = bwd ? D.L : 1;
   for (int l = 0; l < nsets; ++l) {
@@ -291,7 +290,7 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
   void* xf = at<char>(ws, P.xf);
   float* rinvf = at<float>(ws, P.rinvf);
   float* loss_rows = at<float>(ws, P.loss_rows);
-  float* logits = at<float>(ws, P.logits);
+  void* logits = at<char>(ws, P.logits);
   void* dlog = at<char>(ws, P.dlog);
 
   HIPCHECK(nc::fill_zero(status, 256, s));
@@ -329,7 +328,7 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
   for (int64_t r0 = 0; r0 < M; r0 += Mc) {
     const int64_t mc = std::min<int64_t>(Mc, M - r0);
     const char* xfc = static_cast<const char*>(xf) + r0 * D.d * e;
-    HIPCHECK(gemm_simple(dt, true, true, Epi::StoreF32, xfc, W(iU), logits, nullptr, mc, D.V,
+    HIPCHECK(gemm_simple(dt, true, true, Epi::StoreT, xfc, W(iU), logits, nullptr, mc, D.V,
                          D.d, D.d, D.d, D.V, 0, s));
     HIPCHECK(nc::softcap_ce(dt, logits, targets + r0, (int)mc, D.V, cfg->softcap, w,
                             loss_rows + r0, bwd ? dlog : nullptr, status, s));
@@ -640,7 +639,7 @@ int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* do
   return NC_OK;
 }
 
-int nc_op_softcap_ce(int32_t dtype, const float* logits, const int32_t* targets, int32_t R,
+int nc_op_softcap_ce(int32_t dtype, const void* logits, const int32_t* targets, int32_t R,
                      int32_t V, float cap, float w, float* loss_rows, void* dlogits,
                      uint32_t* status, void* stream) {
   if (bad_dtype(dtype)) return NC_ERR_ARG;

@@ -211,9 +211,10 @@ uint64_t nc_op_attn_bwd_scratch_bytes(int32_t B, int32_t T);
 int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* dout,
                    const float* lse, float* delta, int32_t B, int32_t T, int32_t H, void* dqkv,
                    float* scratch, void* stream);
-/* Per-row loss and (if dlogits != NULL) w-scaled logit gradient (T) from fp32
- * logits [R, V]; status: device word for range flags (may not be NULL). */
-int nc_op_softcap_ce(int32_t dtype, const float* logits, const int32_t* targets, int32_t R,
+/* Per-row loss and (if dlogits != NULL) w-scaled logit gradient (T) from
+ * logits [R, V] of type T; status: device word for range flags (may not be
+ * NULL). */
+int nc_op_softcap_ce(int32_t dtype, const void* logits, const int32_t* targets, int32_t R,
                      int32_t V, float cap, float w, float* loss_rows, void* dlogits,
                      uint32_t* status, void* stream);
 

@@ -271,9 +271,7 @@ def test_attention_fwd_bwd(dtype, B, T, H):
 @pytest.mark.parametrize("R,V", [(64, 512), (16, 65536), (33, 8192), (8, 384)])
 def test_softcap_ce(dtype, R, V):
     rng = np.random.default_rng(R + V)
-    logits64 = rng.standard_normal((R, V)) * 8.0
-    logits = dev(logits64.astype(np.float32))
-    logits64 = host64(logits)
+    logits, logits64 = _as(rng.standard_normal((R, V)) * 8.0, dtype)   # logits in the dtype
     tgt = rng.integers(0, V, R).astype(np.int32)
     tgt[0] = V - 1
     w = 1.0 / (4 * R)
