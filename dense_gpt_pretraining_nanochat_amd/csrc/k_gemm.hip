@@ -256,18 +256,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
 // bf16 main-line contraction kernel, any operand order.
 // 256x256 tile, 8 wavefronts (2 x 4), 128x64 per wavefront computed with
 // v_mfma_f32_32x32x16_bf16 (4 x 2 tiles of 32x32, 128 fp32 accumulators).
-// Operand slabs are staged in LDS exactly as they sit in memory:
-//   K-contiguous operand: [256 rows][64 k] (+16-byte pad), fragments read with
-//     ds_read_b128 (lane l: row l%32, k = 8*(l/32)..+7);
-//   K-strided operand:    [64 k][256 rows] (+64-byte pad), fragments read with
-//     two LDS transpose reads (ds_read_b64_tr_b16): in each 16-lane group,
-//     source lane 4j+q names k row kb+j, columns c0+4q..+3, and output lane i
-//     receives k rows kb..kb+3 of column c0+i - so the same fragment layout
-//     comes out without any transpose pass in memory.
-// Fragments are double-buffered one 16-wide k step ahead (scheduling fences
-// keep the next step's reads ahead of this step's MFMAs). Global loads are
-// branch-free: indices past the matrix edge are clamped, which only feeds
-// output rows/columns that the epilogue never stores.
+//
+// Operand slabs of 32 k values go from global memory straight into LDS
+// (global_load_lds_dwordx4: no staging registers, no LDS store instructions)
+// through a ring of four stages, three slabs ahead of the matrix cores. Each
+// slab is laid out as it sits in memory, with 16-byte chunks XOR-swizzled so
+// that both read shapes are bank-conflict free:
+//   K-contiguous operand: [256 rows][32 k] (64-byte rows); chunk c of row r is
+//     stored at slot c ^ ((r >> 2) & 3). Fragments: ds_read_b128 (lane l: row
+//     l%32, k = 8*(l/32)..+7 of the 16-wide step).
+//   K-strided operand:    [32 k][256 rows] (512-byte rows); chunk c of k row
+//     kr is stored at slot c ^ 4*(kr & 3). Fragments: two LDS transpose reads
+//     (ds_read_b64_tr_b16): in each 16-lane group, source lane 4j+q names k
+//     row kb+j, columns c0+4q..+3, and output lane i receives k rows
+//     kb..kb+3 of column c0+i - the same fragment layout, no transpose pass.
+// Each lane's global source is chosen so that its fixed LDS destination
+// (instruction base + 16 * lane) receives the swizzled chunk. The barrier of
+// each stage sits between its two 16-wide k steps: the next stage's first
+// fragments are read while this stage's second-step MFMAs run. Waits on the
+// direct loads are explicit (vmcnt) and precede that barrier; a ring slot is
+// refilled only after every wavefront has passed the barrier that follows its
+// last read of that slot. Indices past the matrix edge are clamped, which
+// only feeds output rows/columns that the epilogue never stores.
 // MFMA 32x32 output layout: lane l, value r holds row 8*(r/4) + 4*(l/32) + r%4,
 // column l%32 of the (B-rows x A-rows) product, i.e. C[m = l%32][n = ...].
 // ---------------------------------------------------------------------------
@@ -275,59 +285,70 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-template <bool KC>
-struct BigSlab {
-  // K-contiguous: 256 x (64 + 8); K-strided: 64 x (256 + 32)
-  static constexpr int STRIDE = KC ? 72 : 288;
-  static constexpr int SIZE = KC ? 256 * 72 : 64 * 288;
-};
+constexpr int kBK = 32;                        // k values per slab
+constexpr int kStages = 4;                     // slabs in the LDS ring
+constexpr int kSlab = 256 * kBK;               // elements per operand slab (both layouts)
 
-// Global->register->LDS staging of one 256 x 64 operand slab by 512 threads.
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0, expcnt 6:4,
+// lgkmcnt 11:8): wait until at most n vector-memory ops (and no LDS ops) of
+// this wavefront are outstanding.
+#define NC_WAIT_VM_LGKM0(n) __builtin_amdgcn_s_waitcnt(0x3070 | (n))
+
+// Transposed LDS read through a restrict-qualified pointer. Once inlined, the
+// read carries alias-scope information, so the compiler's wait insertion does
+// not treat it as possibly reading the in-flight direct loads (which would put
+// a full vmcnt(0) drain in front of it). Ordering against those loads comes
+// from the explicit waits and barrier of each ring stage.
+__device__ __forceinline__ s16x4 lds_read_tr16(lds_s16x4* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+}
+
+// Direct global->LDS staging of one 256 x 32 operand slab: wavefront w moves
+// 2 KB with two 1 KB instructions.
 template <bool KC>
-struct BigLoader {
-  static constexpr int NL = 4;                 // 2048 16-byte chunks / 512 threads
-  const bf16* src[NL];
-  int dst[NL];
-  size_t kstep;                                // element offset of one 64-wide k step
-  bf16x8 reg[NL];
+struct DmaOperand {
+  const bf16* src[2];                          // per lane, slab 0
+  size_t kstep;                                // element offset of one slab
+  int dst[2];                                  // instruction base in the slab (elements)
   // rows: extent of the row (output) dimension; r0: first row of this tile
-  __device__ __forceinline__ void init(const bf16* base, int ld, int rows, int r0, int kbeg,
-                                       int tid) {
+  __device__ __forceinline__ void init(const bf16* A, int ld, int rows, int r0, int kbeg,
+                                       int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int c = tid + 512 * i;
+    for (int j = 0; j < 2; ++j) {
       if constexpr (KC) {
-        const int row = c >> 3, col = (c & 7) * 8;
-        src[i] = base + (size_t)min(r0 + row, rows - 1) * ld + kbeg + col;
-        dst[i] = row * BigSlab<KC>::STRIDE + col;
+        const int R0 = 32 * wave + 16 * j, R = R0 + lane / 4;
+        const int c = (lane % 4) ^ ((R >> 2) & 3);
+        src[j] = A + (size_t)min(r0 + R, rows - 1) * ld + kbeg + c * 8;
+        dst[j] = R0 * kBK;
       } else {
-        const int kr = c >> 5, col = (c & 31) * 8;
-        src[i] = base + (size_t)(kbeg + kr) * ld + min(r0 + col, rows - 8);
-        dst[i] = kr * BigSlab<KC>::STRIDE + col;
+        const int K0 = 4 * wave + 2 * j, kr = K0 + lane / 32;
+        const int c = (lane % 32) ^ (4 * (kr & 3));
+        src[j] = A + (size_t)(kbeg + kr) * ld + min(r0 + c * 8, rows - 8);
+        dst[j] = K0 * 256;
       }
     }
-    kstep = KC ? 64 : (size_t)64 * ld;
+    kstep = KC ? kBK : (size_t)kBK * ld;
   }
-  __device__ __forceinline__ void load(int it) {
+  __device__ __forceinline__ void issue(bf16* slab, int st) const {
 #pragma unroll
-    for (int i = 0; i < NL; ++i) reg[i] = *reinterpret_cast<const bf16x8*>(src[i] + it * kstep);
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + (size_t)st * kstep),
+                                       (lds_void*)(slab + dst[j]), 16, 0, 0);
   }
-  __device__ __forceinline__ void store(bf16* lds) const {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) *reinterpret_cast<bf16x8*>(lds + dst[i]) = reg[i];
-  }
-  // fragment of 32 rows starting at row `r` for k step `ks` (16 wide)
-  __device__ __forceinline__ static bf16x8 frag(const bf16* lds, int r, int ks, int lane) {
+  // fragment of 32 rows starting at row `r` for k step `ks` (0 or 1)
+  __device__ __forceinline__ static bf16x8 frag(const bf16* S, int r, int ks, int lane) {
     if constexpr (KC) {
-      return *reinterpret_cast<const bf16x8*>(lds + (r + (lane & 31)) * BigSlab<KC>::STRIDE +
-                                               ks * 16 + (lane >> 5) * 8);
+      const int row = r + (lane & 31), c = (2 * ks + (lane >> 5)) ^ ((row >> 2) & 3);
+      return *reinterpret_cast<const bf16x8*>(S + row * kBK + c * 8);
     } else {
       const int q = lane >> 4, sl = lane & 15;
-      const bf16* p = lds + (ks * 16 + (q >> 1) * 8 + (sl >> 2)) * BigSlab<KC>::STRIDE + r +
-                      (q & 1) * 16 + 4 * (sl & 3);
-      const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-      const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * BigSlab<KC>::STRIDE));
+      const int kr = ks * 16 + (q >> 1) * 8 + (sl >> 2);
+      const int col = (r + (q & 1) * 16 + 4 * (sl & 3)) ^ (32 * (kr & 3));
+      const s16x4 a = lds_read_tr16((lds_s16x4*)(S + kr * 256 + col));
+      // k row kr + 4 has the same (kr & 3): same swizzle
+      const s16x4 b = lds_read_tr16((lds_s16x4*)(S + (kr + 4) * 256 + col));
       const s16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
       return __builtin_bit_cast(bf16x8, ab);
     }
@@ -357,11 +378,11 @@ __device__ __forceinline__ void epilogue4_in(const GemmArgs& g, int split, int m
 
 template <Epi EPI, bool AK, bool BKC>
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int BM = 256, BN = 256, BK = 64;
+  constexpr int BM = 256, BN = 256;
   constexpr int WM = 2, WN = 4, TM = BM / WM, TN = BN / WN;   // 128 x 64 per wave
   constexpr int FM = TM / 32, FN = TN / 32;                   // 4 x 2 MFMA tiles
-  constexpr int SA = BigSlab<AK>::SIZE, SB = BigSlab<BKC>::SIZE;
-  __shared__ __align__(16) bf16 smem[2 * (SA + SB)];
+  constexpr int STAGE = 2 * kSlab;                            // A slab then B slab
+  __shared__ __align__(16) bf16 smem[kStages * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -384,15 +405,30 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g) {
   const int tm = first_m + (t % per_group) % gsize;
   const int tn = (t % per_group) / gsize;
   const int m0 = tm * BM, n0 = tn * BN;
-  const int ns = g.K / BK;
+  // split `split` takes the 64-wide k slabs [split * ns / splits, (split + 1) * ns / splits)
+  const int ns = g.K / 64;
   const int sb = (int)((long)split * ns / g.splits), se = (int)((long)(split + 1) * ns / g.splits);
-  const int kbeg = sb * BK;
-  const int nk = se - sb;
+  const int kbeg = sb * 64;
+  const int nk = 2 * (se - sb);                                // 32-wide stages
 
-  BigLoader<AK> la;
-  BigLoader<BKC> lb;
-  la.init(static_cast<const bf16*>(g.A), g.lda, g.M, m0, kbeg, tid);
-  lb.init(static_cast<const bf16*>(g.B), g.ldb, g.N, n0, kbeg, tid);
+  DmaOperand<AK> da;
+  DmaOperand<BKC> db;
+  da.init(static_cast<const bf16*>(g.A), g.lda, g.M, m0, kbeg, wave, lane);
+  db.init(static_cast<const bf16*>(g.B), g.ldb, g.N, n0, kbeg, wave, lane);
+  auto issue = [&](int st) {
+    bf16* S = smem + (st % kStages) * STAGE;
+    da.issue(S, st);
+    db.issue(S + kSlab, st);
+  };
+  // stage st has landed in every wavefront's view and this wavefront's LDS
+  // reads are complete; stages issued after st (at most two) stay in flight
+  auto land = [&](int st) {
+    const int after = min(kStages - 2, nk - 1 - st);
+    if (after >= 2) NC_WAIT_VM_LGKM0(8);                      // 4 loads per stage per wave
+    else if (after == 1) NC_WAIT_VM_LGKM0(4);
+    else NC_WAIT_VM_LGKM0(0);
+    __builtin_amdgcn_s_barrier();
+  };
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -402,54 +438,44 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  bf16* As0 = smem;
-  bf16* Bs0 = smem + SA;
-  bf16* As1 = smem + SA + SB;
-  bf16* Bs1 = As1 + SA;
-  la.load(0);
-  lb.load(0);
-  la.store(As0);
-  lb.store(Bs0);
-  __syncthreads();
-
   const int ar = wm * TM, br = wn * TN;
+  bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st)
+    if (st < nk) issue(st);
+  land(0);
+  if (kStages - 1 < nk) issue(kStages - 1);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) fa0[i] = DmaOperand<AK>::frag(smem, ar + i * 32, 0, lane);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) fb0[j] = DmaOperand<BKC>::frag(smem + kSlab, br + j * 32, 0, lane);
+
   for (int it = 0; it < nk; ++it) {
-    const bool odd = it & 1;
-    const bf16* As = odd ? As1 : As0;
-    const bf16* Bs = odd ? Bs1 : Bs0;
-    const bool more = it + 1 < nk;
-    if (more) {
-      la.load(it + 1);
-      lb.load(it + 1);
+    const bf16* S = smem + (it % kStages) * STAGE;
+    // this stage's second-step fragments, read under the first-step MFMAs
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa1[i] = DmaOperand<AK>::frag(S, ar + i * 32, 1, lane);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb1[j] = DmaOperand<BKC>::frag(S + kSlab, br + j * 32, 1, lane);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
+    if (it + 1 < nk) {
+      land(it + 1);                                            // also: this slot fully read
+      if (it + kStages < nk) issue(it + kStages);               // refills this stage's slot
+      const bf16* Sn = smem + ((it + 1) % kStages) * STAGE;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa0[i] = DmaOperand<AK>::frag(Sn, ar + i * 32, 0, lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) fb0[j] = DmaOperand<BKC>::frag(Sn + kSlab, br + j * 32, 0, lane);
     }
-    bf16x8 fa[2][FM], fb[2][FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fa[0][i] = BigLoader<AK>::frag(As, ar + i * 32, 0, lane);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb[0][j] = BigLoader<BKC>::frag(Bs, br + j * 32, 0, lane);
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int cur = s & 1, nxt = cur ^ 1;
-      if (s + 1 < BK / 16) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) fa[nxt][i] = BigLoader<AK>::frag(As, ar + i * 32, s + 1, lane);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) fb[nxt][j] = BigLoader<BKC>::frag(Bs, br + j * 32, s + 1, lane);
-      }
-      // keep the next step's LDS reads ahead of this step's MFMAs
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][j], fa[cur][i], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (more) {
-      la.store(odd ? As0 : As1);
-      lb.store(odd ? Bs0 : Bs1);
-    }
-    __syncthreads();
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[j], fa1[i], acc[i][j], 0, 0, 0);
   }
 
   // Epilogue, staged through LDS so that global accesses cover whole rows:
