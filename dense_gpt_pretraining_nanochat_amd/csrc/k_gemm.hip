@@ -305,6 +305,11 @@ __device__ __forceinline__ s16x4 lds_read_tr16(lds_s16x4* __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
 }
 
+// 16-byte chunk swizzles: K-contiguous slab (chunk slot of row `row`) and
+// K-strided slab (chunk offset of k row `kr`, in 8-element chunks).
+__device__ __forceinline__ int kc_swz(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int ks_swz(int kr) { return 4 * (kr & 3); }
+
 // Direct global->LDS staging of one 256 x 32 operand slab: wavefront w moves
 // 2 KB with two 1 KB instructions.
 template <bool KC>
@@ -319,12 +324,12 @@ struct DmaOperand {
     for (int j = 0; j < 2; ++j) {
       if constexpr (KC) {
         const int R0 = 32 * wave + 16 * j, R = R0 + lane / 4;
-        const int c = (lane % 4) ^ ((R >> 2) & 3);
+        const int c = (lane % 4) ^ kc_swz(R);
         src[j] = A + (size_t)min(r0 + R, rows - 1) * ld + kbeg + c * 8;
         dst[j] = R0 * kBK;
       } else {
         const int K0 = 4 * wave + 2 * j, kr = K0 + lane / 32;
-        const int c = (lane % 32) ^ (4 * (kr & 3));
+        const int c = (lane % 32) ^ ks_swz(kr);
         src[j] = A + (size_t)(kbeg + kr) * ld + min(r0 + c * 8, rows - 8);
         dst[j] = K0 * 256;
       }
@@ -340,12 +345,12 @@ struct DmaOperand {
   // fragment of 32 rows starting at row `r` for k step `ks` (0 or 1)
   __device__ __forceinline__ static bf16x8 frag(const bf16* S, int r, int ks, int lane) {
     if constexpr (KC) {
-      const int row = r + (lane & 31), c = (2 * ks + (lane >> 5)) ^ ((row >> 2) & 3);
+      const int row = r + (lane & 31), c = (2 * ks + (lane >> 5)) ^ kc_swz(row);
       return *reinterpret_cast<const bf16x8*>(S + row * kBK + c * 8);
     } else {
       const int q = lane >> 4, sl = lane & 15;
       const int kr = ks * 16 + (q >> 1) * 8 + (sl >> 2);
-      const int col = (r + (q & 1) * 16 + 4 * (sl & 3)) ^ (32 * (kr & 3));
+      const int col = (r + (q & 1) * 16 + 4 * (sl & 3)) ^ (8 * ks_swz(kr));
       const s16x4 a = lds_read_tr16((lds_s16x4*)(S + kr * 256 + col));
       // k row kr + 4 has the same (kr & 3): same swizzle
       const s16x4 b = lds_read_tr16((lds_s16x4*)(S + (kr + 4) * 256 + col));
@@ -445,38 +450,74 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g) {
     if (st < nk) issue(st);
   land(0);
   if (kStages - 1 < nk) issue(kStages - 1);
+  // No scalar loads outstanding from here on: LDS reads are then the only
+  // traffic on lgkmcnt (and return in order), so the loop's waits can be
+  // partial. The empty asm makes the epilogue's arguments live in scalar
+  // registers here, so their loads are not scheduled into the loop.
+  asm volatile("" ::"s"(g.C), "s"(g.C2), "s"(g.ldc), "s"(g.ldc2));
+  __builtin_amdgcn_s_waitcnt(0xC07F);                          // lgkmcnt 0, vmcnt/expcnt free
 #pragma unroll
   for (int i = 0; i < FM; ++i) fa0[i] = DmaOperand<AK>::frag(smem, ar + i * 32, 0, lane);
 #pragma unroll
   for (int j = 0; j < FN; ++j) fb0[j] = DmaOperand<BKC>::frag(smem + kSlab, br + j * 32, 0, lane);
 
-  for (int it = 0; it < nk; ++it) {
-    const bf16* S = smem + (it % kStages) * STAGE;
-    // this stage's second-step fragments, read under the first-step MFMAs
-#pragma unroll
-    for (int i = 0; i < FM; ++i) fa1[i] = DmaOperand<AK>::frag(S, ar + i * 32, 1, lane);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) fb1[j] = DmaOperand<BKC>::frag(S + kSlab, br + j * 32, 1, lane);
+  // MFMAs of one 16-wide k step; `from` skips the first ones (in i-major order)
+  auto mfma_step = [&](const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN], int from = 0) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb0[j], fa0[i], acc[i][j], 0, 0, 0);
-    if (it + 1 < nk) {
-      land(it + 1);                                            // also: this slot fully read
-      if (it + kStages < nk) issue(it + kStages);               // refills this stage's slot
-      const bf16* Sn = smem + ((it + 1) % kStages) * STAGE;
+        if (i * FN + j >= from)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  };
+  auto mfma_first = [&](const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN]) {
+    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0], fa[0], acc[0][0], 0, 0, 0);
+  };
+  auto read_step = [&](const bf16* S, int ks, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa0[i] = DmaOperand<AK>::frag(Sn, ar + i * 32, 0, lane);
+    for (int i = 0; i < FM; ++i) fa[i] = DmaOperand<AK>::frag(S, ar + i * 32, ks, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb0[j] = DmaOperand<BKC>::frag(Sn + kSlab, br + j * 32, 0, lane);
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb1[j], fa1[i], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < FN; ++j) fb[j] = DmaOperand<BKC>::frag(S + kSlab, br + j * 32, ks, lane);
+  };
+  // Every stage but the last: its second-step fragments are read under its
+  // first-step MFMAs, the next stage lands, and the next stage's first-step
+  // fragments are read under this stage's second-step MFMAs. The steady-state
+  // loop (a slot to refill every stage, two stages in flight behind the one
+  // landing) is straight-line code: with a branch around the landing the
+  // compiler cannot see that its wait (lgkmcnt 0) already covers the
+  // second-step fragments, and adds a full LDS wait that stalls the
+  // second-step MFMAs on the next stage's reads.
+  // Scheduling fences keep each phase's LDS reads ahead of the MFMAs they
+  // are meant to overlap. The compiler's wait before the first step-0 MFMA
+  // is a full LDS wait whenever direct loads are in flight; one MFMA goes
+  // first so that this wait covers only the step-0 fragments (read a whole
+  // MFMA step earlier), not the step-1 reads issued right after it.
+  int it = 0;
+  for (; it + kStages < nk; ++it) {
+    mfma_first(fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_step(smem + (it % kStages) * STAGE, 1, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(fa0, fb0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    NC_WAIT_VM_LGKM0(8);                                       // stage it+1 landed, this slot read
+    __builtin_amdgcn_s_barrier();
+    issue(it + kStages);                                       // refills this stage's slot
+    read_step(smem + ((it + 1) % kStages) * STAGE, 0, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  for (; it + 1 < nk; ++it) {                                  // the last three: nothing to issue
+    read_step(smem + (it % kStages) * STAGE, 1, fa1, fb1);
+    mfma_step(fa0, fb0);
+    land(it + 1);
+    read_step(smem + ((it + 1) % kStages) * STAGE, 0, fa0, fb0);
+    mfma_step(fa1, fb1);
+  }
+  read_step(smem + ((nk - 1) % kStages) * STAGE, 1, fa1, fb1);
+  mfma_step(fa0, fb0);
+  mfma_step(fa1, fb1);
 
   // Epilogue, staged through LDS so that global accesses cover whole rows:
   // the lane holds C[m][n..n+3] for m = 32i + l32, n = 32j + 8q + 4*lh; each
