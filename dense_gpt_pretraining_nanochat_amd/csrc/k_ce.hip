@@ -11,13 +11,16 @@
 // with w = 1 / (number of positions in the batch).
 //
 // Logits arrive in the step's activation type (bf16 in bf16 mode, like every
-// other inter-kernel activation). One workgroup per row holds the whole row in
-// fp32 registers (up to 64 values per thread at V = 65,536), so each logit is
-// read once from HBM and each gradient written once (4 bytes per logit in
-// bf16 mode). Because
-// |z| <= c, exp(z - c) never overflows and needs no running maximum. tanh is
-// evaluated from one exponential (see tanh_fast) to keep the pass bound by
-// memory rather than by transcendental throughput.
+// other inter-kernel activation). One workgroup per row keeps the row's raw
+// logits in registers (16-byte chunks: 32 registers per thread at V = 65,536
+// in bf16), so each logit is read once from HBM and each gradient written once
+// (4 bytes per logit in bf16 mode). The capped values are recomputed in the
+// gradient pass instead of being kept in fp32: the kernel then fits in 64
+// registers and two rows are in flight per compute unit, so one row's loads
+// overlap another's reduction and stores. Because |z| <= c, exp(z - c) never
+// overflows and needs no running maximum. tanh is evaluated from one
+// exponential and a hardware reciprocal (see capped_unit) to keep the pass
+// bound by memory rather than by arithmetic.
 #include <math.h>
 
 #include "common.h"
@@ -26,42 +29,54 @@
 namespace nc {
 namespace {
 
-constexpr int kMaxChunks = 16;   // float4 chunks per thread: 16 * 4 * 1024 = 65,536
+constexpr int kCeThreads = 1024;
+constexpr int kCeMaxV = 65536;
 
-// tanh(x) = sign(x) (1 - e) / (1 + e) with e = exp(-2|x|): one exponential and
-// one reciprocal; e in (0, 1] so nothing overflows.
-__device__ __forceinline__ float tanh_fast(float x) {
-  const float e = __expf(-2.0f * fabsf(x));
-  return copysignf((1.0f - e) * __frcp_rn(1.0f + e), x);
+// Capped logit in units of the cap, t = tanh(l / c) = z / c, from one base-2
+// exponential and one hardware reciprocal: tanh(x) = sign(x) (1 - e) / (1 + e)
+// with e = exp(-2|x|) = exp2(k1 |l|), k1 = -2 log2(e) / c; e in (0, 1] so
+// nothing overflows.
+struct CapConsts {
+  float k1;        // -2 log2(e) / c
+  float k2;        // c log2(e): exp(z - c) = exp2(k2 t - k2)
+};
+__device__ __forceinline__ float capped_unit(float l, const CapConsts& q) {
+  const float e = __builtin_amdgcn_exp2f(q.k1 * fabsf(l));
+  return copysignf((1.0f - e) * __builtin_amdgcn_rcpf(1.0f + e), l);
+}
+// exp(z - c) for z = c t
+__device__ __forceinline__ float shifted_exp(float t, const CapConsts& q) {
+  return __builtin_amdgcn_exp2f(fmaf(q.k2, t, -q.k2));
 }
 
-template <typename T>
-__global__ __launch_bounds__(1024) void softcap_ce_kernel(const T* __restrict__ logits,
-                                                          const int32_t* __restrict__ tgt, int V,
-                                                          int nch, float cap, float w,
-                                                          float* __restrict__ loss_rows,
-                                                          T* __restrict__ dl,
-                                                          uint32_t* status) {
+// CB: bytes per chunk (16, or 8 when a bf16 row is only 8-byte aligned).
+template <typename T, int CB>
+__global__ __launch_bounds__(kCeThreads, sizeof(T) == 2 && CB == 16 ? 8 : 4) void softcap_ce_kernel(
+    const T* __restrict__ logits, const int32_t* __restrict__ tgt, int V, int nch, float cap,
+    float w, float* __restrict__ loss_rows, T* __restrict__ dl, uint32_t* status) {
+  constexpr int E = CB / (int)sizeof(T);                       // logits per chunk
+  constexpr int NCH = kCeMaxV / (kCeThreads * E);              // chunks per thread, at most
+  typedef T TV __attribute__((ext_vector_type(E)));
   __shared__ float red[16];
   const int row = blockIdx.x;
   const int tid = threadIdx.x, nt = blockDim.x;
   const T* src = logits + (size_t)row * V;
-  typedef T T4 __attribute__((ext_vector_type(4)));
-  const float inv_cap = 1.0f / cap;
+  const CapConsts q = {-2.0f * 1.44269504088896341f / cap, cap * 1.44269504088896341f};
 
-  // t = tanh(l / c) = z / c is kept per logit; exp(z - c) = exp(c (t - 1))
-  f32x4 tz[kMaxChunks];
+  // every chunk that starts inside the row is whole (V is a multiple of E)
+  TV raw[NCH];
   float se = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
-    const int c = (i * nt + tid) * 4;
-    if (i < nch && c < V) {
-      const T4 l = *reinterpret_cast<const T4*>(src + c);
+  for (int i = 0; i < NCH; ++i) {
+    const int c = (i * nt + tid) * E;
+    if (i < nch && c < V) raw[i] = *reinterpret_cast<const TV*>(src + c);
+  }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        tz[i][e] = tanh_fast(to_f32(l[e]) * inv_cap);
-        se += __expf(cap * (tz[i][e] - 1.0f));
-      }
+  for (int i = 0; i < NCH; ++i) {
+    const int c = (i * nt + tid) * E;
+    if (i < nch && c < V) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) se += shifted_exp(capped_unit(to_f32(raw[i][e]), q), q);
     }
   }
   const float sum = block_sum(se, red);
@@ -72,44 +87,52 @@ __global__ __launch_bounds__(1024) void softcap_ce_kernel(const T* __restrict__ 
     t = t < 0 ? 0 : V - 1;
   }
   if (tid == 0) {
-    const float zt = cap * tanh_fast(to_f32(src[t]) * inv_cap);
+    const float zt = cap * capped_unit(to_f32(src[t]), q);
     loss_rows[row] = cap + logf(sum) - zt;
   }
   if (dl == nullptr) return;                       // loss only
   T* dst = dl + (size_t)row * V;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
-    const int c = (i * nt + tid) * 4;
+  for (int i = 0; i < NCH; ++i) {
+    const int c = (i * nt + tid) * E;
     if (i < nch && c < V) {
-      float g[4];
+      TV v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float tc = tz[i][e];
-        const float p = __expf(cap * (tc - 1.0f)) * inv_sum - (c + e == t ? 1.0f : 0.0f);
-        g[e] = w * p * (1.0f - tc * tc);
+      for (int e = 0; e < E; ++e) {
+        const float tc = capped_unit(to_f32(raw[i][e]), q);
+        const float p = shifted_exp(tc, q) * inv_sum - (c + e == t ? 1.0f : 0.0f);
+        v[e] = from_f32<T>(w * p * fmaf(-tc, tc, 1.0f));
       }
-      T4 v = {from_f32<T>(g[0]), from_f32<T>(g[1]), from_f32<T>(g[2]), from_f32<T>(g[3])};
-      *reinterpret_cast<T4*>(dst + c) = v;
+      *reinterpret_cast<TV*>(dst + c) = v;
     }
   }
+}
+
+template <typename T, int CB>
+hipError_t launch_ce(const void* logits, const int32_t* tgt, int R, int V, float cap, float w,
+                     float* loss_rows, void* dlogits, uint32_t* status, hipStream_t s) {
+  constexpr int E = CB / (int)sizeof(T);
+  int nt = ((V / E + 63) / 64) * 64;
+  if (nt > kCeThreads) nt = kCeThreads;
+  const int nch = (V + E * nt - 1) / (E * nt);
+  if (nch > kCeMaxV / (kCeThreads * E)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((softcap_ce_kernel<T, CB>), dim3(R), dim3(nt), 0, s,
+                     static_cast<const T*>(logits), tgt, V, nch, cap, w, loss_rows,
+                     static_cast<T*>(dlogits), status);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t softcap_ce(DType t, const void* logits, const int32_t* tgt, int R, int V, float cap,
                       float w, float* loss_rows, void* dlogits, uint32_t* status, hipStream_t s) {
-  if (V % 4 || V > 65536 || R <= 0) return hipErrorInvalidValue;
-  int nt = ((V / 4 + 63) / 64) * 64;
-  if (nt > 1024) nt = 1024;
-  const int nch = (V + 4 * nt - 1) / (4 * nt);
-  if (nch > kMaxChunks) return hipErrorInvalidValue;
-  if (t == DType::BF16)
-    hipLaunchKernelGGL(softcap_ce_kernel<bf16>, dim3(R), dim3(nt), 0, s, static_cast<const bf16*>(logits), tgt, V, nch, cap, w,
-                       loss_rows, static_cast<bf16*>(dlogits), status);
-  else
-    hipLaunchKernelGGL(softcap_ce_kernel<float>, dim3(R), dim3(nt), 0, s, static_cast<const float*>(logits), tgt, V, nch, cap, w,
-                       loss_rows, static_cast<float*>(dlogits), status);
-  return hipGetLastError();
+  if (V % 4 || V > kCeMaxV || V <= 0 || R <= 0) return hipErrorInvalidValue;
+  if (t == DType::BF16) {
+    if (V % 8 == 0)
+      return launch_ce<bf16, 16>(logits, tgt, R, V, cap, w, loss_rows, dlogits, status, s);
+    return launch_ce<bf16, 8>(logits, tgt, R, V, cap, w, loss_rows, dlogits, status, s);
+  }
+  return launch_ce<float, 16>(logits, tgt, R, V, cap, w, loss_rows, dlogits, status, s);
 }
 
 }  // namespace nc
