@@ -652,20 +652,28 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
           Mma<T>::run(dpa[c][kt], da, vf[kt][s]);
         }
       }
-    const bool diag = tq0 < key0 + 16;
+    // only steps that reach the wavefront's keys need the causal mask: a
+    // uniform branch picks the unmasked code for all the others
     f32x4 pa[1][NC], dsa[1][NC];   // [kt][c]
+    auto softmax = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int kt = 0; kt < 1; ++kt)
+        for (int kt = 0; kt < 1; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rl = c * 16 + lg * 4 + r;     // local query row
-          float p = __builtin_amdgcn_exp2f(fmaf(sa[c][kt][r], sc, -lse_s[rl]));
-          if (diag && key0 + kt * 16 + l16 > tq0 + rl) p = 0.f;
-          pa[kt][c][r] = p;
-          dsa[kt][c][r] = p * (dpa[c][kt][r] - dl_s[rl]);
-        }
+          for (int r = 0; r < 4; ++r) {
+            const int rl = c * 16 + lg * 4 + r;     // local query row
+            float p = __builtin_amdgcn_exp2f(fmaf(sa[c][kt][r], sc, -lse_s[rl]));
+            if constexpr (MASKED) {
+              if (key0 + kt * 16 + l16 > tq0 + rl) p = 0.f;
+            }
+            pa[kt][c][r] = p;
+            dsa[kt][c][r] = p * (dpa[c][kt][r] - dl_s[rl]);
+          }
+    };
+    if (tq0 < key0 + 16) softmax(std::true_type{});
+    else softmax(std::false_type{});
     // dV^T[d][key] += dO^T[d][rows] P[rows][key];  dK^T += Q^T dS
 #pragma unroll
     for (int kk = 0; kk < NC / NPT; ++kk)
