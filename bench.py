@@ -72,10 +72,12 @@ def measured_traffic(shape):
     return int(t["fetch_bytes"] + t["write_bytes"])
 
 
-def dominant_kernel_roofline(cfg, nc, torch, reps=20):
+def dominant_kernel_roofline(cfg, nc, torch, reps=20, warm=25):
     """Times the MLP up-projection GEMM (tokens x 4d x d, relu^2 epilogue;
     the largest single contraction of the step) on its own, with HIP events
-    on the stream it is launched on."""
+    on the stream it is launched on. A burst of this kernel right after the
+    step runs slower for its first ~15 launches while the clocks settle, so
+    `warm` untimed launches come first."""
     M = cfg.batch * cfg.seq_len
     d = 64 * cfg.depth
     F = 4 * d
@@ -85,7 +87,7 @@ def dominant_kernel_roofline(cfg, nc, torch, reps=20):
     B = (torch.randn(F, d, device="cuda") * 0.02).to(et)
     U = torch.empty(M, F, device="cuda", dtype=et)
     s = torch.cuda.current_stream()
-    for _ in range(3):
+    for _ in range(warm):
         nc.nc_op_gemm(cfg.dtype, 1, 1, nc.EPI_RELU2, A, B, U, None, M, F, d, d, d, F, stream=s)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(s)
@@ -102,7 +104,8 @@ def dominant_kernel_roofline(cfg, nc, torch, reps=20):
                       "(MLP up-projection, forward)",
             "shape": [M, F, d], "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
             "unit": "TFLOP/s", "frac": round(ach / peak, 4), "avg_us": round(sec * 1e6, 2),
-            "flops_per_launch": flops, "traffic": measured_traffic([M, F, d])}
+            "flops_per_launch": flops, "warmup_launches": warm, "timed_launches": reps,
+            "traffic": measured_traffic([M, F, d])}
 
 
 def kernel_only(a):
