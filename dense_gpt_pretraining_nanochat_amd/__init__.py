@@ -40,6 +40,18 @@ class NcTensorInfo(ctypes.Structure):
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
 
 
+class NcOptimConfig(ctypes.Structure):
+    _fields_ = [("lr_adamw", ctypes.c_float), ("beta1", ctypes.c_float),
+                ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+                ("wd_adamw", ctypes.c_float), ("lr_muon", ctypes.c_float),
+                ("momentum", ctypes.c_float), ("wd_muon", ctypes.c_float),
+                ("max_grad_norm", ctypes.c_float), ("ns_steps", ctypes.c_int32),
+                ("step", ctypes.c_int32)]
+
+    def __repr__(self):
+        return ("NcOptimConfig(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")")
+
+
 class NcError(RuntimeError):
     def __init__(self, code, func, hip=0):
         self.code = code
@@ -60,6 +72,10 @@ _SIGS = {
     "nc_init_params": [_U64, _CFG, _P, _P],
     "nc_forward_loss": [_CFG, _P, _P, _P, _P, _U64, _P, _P],
     "nc_forward_backward": [_CFG, _P, _P, _P, _P, _P, _U64, _P, _P],
+    "nc_forward_backward_accumulate": [_CFG, _P, _P, _P, _P, _P, _U64, _P, _P],
+    "nc_optimizer_state_bytes": [_CFG, ctypes.POINTER(_U64)],
+    "nc_optimizer_workspace_bytes": [_CFG, ctypes.POINTER(_U64)],
+    "nc_optimizer_step": [_CFG, ctypes.POINTER(NcOptimConfig), _P, _P, _P, _P, _U64, _P, _P],
     "nc_read_device_status": [_P, ctypes.POINTER(ctypes.c_uint32), _P],
     "nc_status_string": [ctypes.c_int],
     "nc_last_hip_error": [],
@@ -184,6 +200,38 @@ def nc_forward_backward(cfg, params, tokens, targets, grads, ws, loss, stream=No
                                      _ptr(loss), _stream(stream)), "nc_forward_backward")
 
 
+def nc_forward_backward_accumulate(cfg, params, tokens, targets, grads, ws, loss, stream=None):
+    _check(lib().nc_forward_backward_accumulate(ctypes.byref(cfg), _ptr(params), _ptr(tokens),
+                                                _ptr(targets), _ptr(grads), _ptr(ws),
+                                                ws.numel() * ws.element_size(), _ptr(loss),
+                                                _stream(stream)), "nc_forward_backward_accumulate")
+
+
+def nc_optimizer_state_bytes(cfg) -> int:
+    n = _U64()
+    _check(lib().nc_optimizer_state_bytes(ctypes.byref(cfg), ctypes.byref(n)), "nc_optimizer_state_bytes")
+    return n.value
+
+
+def nc_optimizer_workspace_bytes(cfg) -> int:
+    n = _U64()
+    _check(lib().nc_optimizer_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)),
+           "nc_optimizer_workspace_bytes")
+    return n.value
+
+
+def nc_optim_config(lr_adamw, beta1, beta2, eps, wd_adamw, lr_muon, momentum, wd_muon,
+                    max_grad_norm, ns_steps, step) -> NcOptimConfig:
+    return NcOptimConfig(lr_adamw, beta1, beta2, eps, wd_adamw, lr_muon, momentum, wd_muon,
+                         max_grad_norm, ns_steps, step)
+
+
+def nc_optimizer_step(cfg, optim, params, grads, state, ows, grad_norm, stream=None):
+    _check(lib().nc_optimizer_step(ctypes.byref(cfg), ctypes.byref(optim), _ptr(params), _ptr(grads),
+                                   _ptr(state), _ptr(ows), ows.numel() * ows.element_size(),
+                                   _ptr(grad_norm), _stream(stream)), "nc_optimizer_step")
+
+
 def nc_read_device_status(ws, stream=None) -> int:
     f = ctypes.c_uint32()
     _check(lib().nc_read_device_status(_ptr(ws), ctypes.byref(f), _stream(stream)),
@@ -283,6 +331,26 @@ class Step:
     def forward_backward(self, tokens, targets):
         nc_forward_backward(self.cfg, self.params, tokens, targets, self.grads, self.ws, self.loss)
         return self.loss
+
+    def forward_backward_accumulate(self, tokens, targets):
+        nc_forward_backward_accumulate(self.cfg, self.params, tokens, targets, self.grads, self.ws,
+                                       self.loss)
+        return self.loss
+
+    def optimizer_step(self, optim: NcOptimConfig):
+        """One optimizer step on params from grads; optimizer state and
+        scratch are allocated (zeroed) on first use. Returns the pre-clip
+        gradient norm as a one-element device tensor."""
+        import torch
+        if getattr(self, "opt_state", None) is None:
+            self.opt_state = torch.zeros(nc_optimizer_state_bytes(self.cfg) // 4, dtype=torch.float32,
+                                         device=self.device)
+            self.opt_ws = torch.empty(nc_optimizer_workspace_bytes(self.cfg), dtype=torch.uint8,
+                                      device=self.device)
+            self.grad_norm = torch.zeros(1, dtype=torch.float32, device=self.device)
+        nc_optimizer_step(self.cfg, optim, self.params, self.grads, self.opt_state, self.opt_ws,
+                          self.grad_norm)
+        return self.grad_norm
 
     def token_losses(self):
         import torch

@@ -281,7 +281,8 @@ __global__ __launch_bounds__(256) void embed_sort_kernel(const int32_t* __restri
 // dE[v] = rinv * (S - y * mean(S * y)), y = E[v] * rinv; all threads call it
 template <typename T>
 __device__ __forceinline__ void embed_finish_row(const T* __restrict__ E, int v, int d, float r,
-                                                 f32x4 S, bool active, float* __restrict__ dE) {
+                                                 f32x4 S, bool active, float* __restrict__ dE,
+                                                 bool accumulate) {
   __shared__ float red[16];
   const int c = threadIdx.x * 4;
   float y[4] = {0.f, 0.f, 0.f, 0.f};
@@ -296,7 +297,9 @@ __device__ __forceinline__ void embed_finish_row(const T* __restrict__ E, int v,
     f32x4 o;
 #pragma unroll
     for (int k = 0; k < 4; ++k) o[k] = r * (S[k] - y[k] * dot);
-    *reinterpret_cast<f32x4*>(dE + (size_t)v * d + c) = o;
+    f32x4* dst = reinterpret_cast<f32x4*>(dE + (size_t)v * d + c);
+    if (accumulate) o += *dst;
+    *dst = o;
   }
 }
 
@@ -306,7 +309,8 @@ template <typename T>
 __global__ __launch_bounds__(512) void embed_sum_kernel(const T* __restrict__ E,
                                                         const float* __restrict__ rinv0,
                                                         const float* __restrict__ dx, int d, int V,
-                                                        EmbedBwdScratch ws, float* __restrict__ dE) {
+                                                        EmbedBwdScratch ws, float* __restrict__ dE,
+                                                        bool accumulate) {
   __shared__ int32_t rows[kSeg];
   const int i = blockIdx.x;
   if (i >= ws.item_off[V]) return;
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(512) void embed_sum_kernel(const T* __restrict__ E,
   }
   for (; s < cnt; ++s) acc += *reinterpret_cast<const f32x4*>(dx + (size_t)rows[s] * d + c);
   if (n <= kSeg) {
-    embed_finish_row(E, v, d, rinv0[rows[0]], acc, active, dE);
+    embed_finish_row(E, v, d, rinv0[rows[0]], acc, active, dE, accumulate);
   } else if (active) {
     *reinterpret_cast<f32x4*>(ws.part + (size_t)(ws.part_off[v] + j) * d + c) = acc;
   }
@@ -342,14 +346,15 @@ template <typename T>
 __global__ __launch_bounds__(512) void embed_finish_kernel(const T* __restrict__ E,
                                                            const float* __restrict__ rinv0, int d,
                                                            EmbedBwdScratch ws,
-                                                           float* __restrict__ dE) {
+                                                           float* __restrict__ dE,
+                                                           bool accumulate) {
   const int v = blockIdx.x;
   const int tid = threadIdx.x;
   const int beg = ws.offsets[v], n = ws.offsets[v + 1] - beg;
   const bool active = tid * 4 < d;
   const size_t c = active ? (size_t)tid * 4 : 0;
-  if (n == 0) {
-    if (active) *reinterpret_cast<f32x4*>(dE + (size_t)v * d + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (n == 0) {                                  // unused id: dE row is 0 (nothing to add)
+    if (active && !accumulate) *reinterpret_cast<f32x4*>(dE + (size_t)v * d + c) = f32x4{0.f, 0.f, 0.f, 0.f};
     return;
   }
   if (n <= kSeg) return;
@@ -365,7 +370,7 @@ __global__ __launch_bounds__(512) void embed_finish_kernel(const T* __restrict__
     for (int u = 0; u < 4; ++u) acc += t[u];
   }
   for (; k < items; ++k) acc += *reinterpret_cast<const f32x4*>(p + (size_t)k * d);
-  embed_finish_row(E, v, d, rinv0[ws.list[beg]], acc, active, dE);
+  embed_finish_row(E, v, d, rinv0[ws.list[beg]], acc, active, dE, accumulate);
 }
 
 __global__ __launch_bounds__(1024) void loss_mean_kernel(const float* __restrict__ loss_rows,
@@ -444,7 +449,7 @@ uint64_t embed_bwd_max_parts(int64_t M) { return 2 * (uint64_t)(M / kSeg) + 1; }
 
 hipError_t embed_bwd(DType t, const void* E, const int32_t* tok, const float* rinv0,
                      const float* dx, int M, int d, int V, EmbedBwdScratch ws, float* dE,
-                     hipStream_t s) {
+                     bool accumulate, hipStream_t s) {
   if (d % 4 || d > 2048 || M <= 0 || V <= 0) return hipErrorInvalidValue;
   hipError_t e = fill_zero(ws.counts, sizeof(int32_t) * (V + 1), s);
   if (e != hipSuccess) return e;
@@ -459,13 +464,15 @@ hipError_t embed_bwd(DType t, const void* E, const int32_t* tok, const float* ri
   if (t == DType::BF16) {
     const bf16* Eb = static_cast<const bf16*>(E);
     hipLaunchKernelGGL(embed_sum_kernel<bf16>, dim3(pieces), dim3(nthr), 0, s, Eb, rinv0, dx, d, V,
-                       ws, dE);
-    hipLaunchKernelGGL(embed_finish_kernel<bf16>, dim3(V), dim3(nthr), 0, s, Eb, rinv0, d, ws, dE);
+                       ws, dE, accumulate);
+    hipLaunchKernelGGL(embed_finish_kernel<bf16>, dim3(V), dim3(nthr), 0, s, Eb, rinv0, d, ws, dE,
+                       accumulate);
   } else {
     const float* Ef = static_cast<const float*>(E);
     hipLaunchKernelGGL(embed_sum_kernel<float>, dim3(pieces), dim3(nthr), 0, s, Ef, rinv0, dx, d,
-                       V, ws, dE);
-    hipLaunchKernelGGL(embed_finish_kernel<float>, dim3(V), dim3(nthr), 0, s, Ef, rinv0, d, ws, dE);
+                       V, ws, dE, accumulate);
+    hipLaunchKernelGGL(embed_finish_kernel<float>, dim3(V), dim3(nthr), 0, s, Ef, rinv0, d, ws, dE,
+                       accumulate);
   }
   return hipGetLastError();
 }

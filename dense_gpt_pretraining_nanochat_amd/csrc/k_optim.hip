@@ -1,0 +1,239 @@
+// Optimizer step kernels: the global gradient norm and clip factor, AdamW for
+// the embedding and lm_head, and the elementwise parts of Muon for the block
+// matrices (momentum, normalisation, the Newton-Schulz linear combinations
+// and the final update). Muon's matrix products run on the GEMM kernels.
+//
+// The pairing of Muon with AdamW follows the followin.io release article
+// (paragraph after the architecture list); clipping by global norm, the
+// wmrh.cn tutorial, section 5.1. The update rules themselves are the public
+// descriptions of AdamW (decoupled weight decay, with Adam's bias correction)
+// and of Muon (Nesterov momentum, then a quintic Newton-Schulz iteration
+// X <- a X + (b A + c A^2) X with A = X X^T); the pages do not define them.
+//
+// Every reduction has a fixed grid and a fixed summation order, so a step is
+// bitwise reproducible.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace nc {
+namespace {
+
+constexpr int kOptThreads = 256;
+
+// fp64 block sum (thread 0 holds the result)
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  double s = 0.0;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  return s;
+}
+
+// partial[r * gridDim.x + blockIdx.x] = sum of squares of this block's share
+// of range r (grid-stride in fp64)
+__global__ __launch_bounds__(kOptThreads) void sumsq_ranges_kernel(const float* __restrict__ x,
+                                                                   OptRanges rg,
+                                                                   double* __restrict__ partial) {
+  __shared__ double red[kOptThreads / 64];
+  const int r = blockIdx.y;
+  const float* p = x + rg.off[r];
+  const size_t n = rg.cnt[r];
+  double s = 0.0;
+  for (size_t i = blockIdx.x * (size_t)kOptThreads + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * kOptThreads) {
+    const double v = p[i];
+    s += v * v;
+  }
+  s = block_sum_f64(s, red);
+  if (threadIdx.x == 0) partial[(size_t)r * gridDim.x + blockIdx.x] = s;
+}
+
+// norm_scale[0] = sqrt(sum of partials), norm_scale[1] = clip factor
+__global__ __launch_bounds__(kOptThreads) void norm_finish_kernel(const double* __restrict__ partial,
+                                                                  int n, float max_norm,
+                                                                  float* __restrict__ norm_scale) {
+  __shared__ double red[kOptThreads / 64];
+  // fixed order: thread t sums t, t + 256, ...; then the block sum in wave order
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n; i += kOptThreads) s += partial[i];
+  s = block_sum_f64(s, red);
+  if (threadIdx.x == 0) {
+    const double norm = sqrt(s);
+    norm_scale[0] = (float)norm;
+    norm_scale[1] = max_norm > 0.f ? (float)fmin(1.0, (double)max_norm / (norm + 1e-6)) : 1.0f;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kOptThreads) void adamw_kernel(T* __restrict__ p,
+                                                            const float* __restrict__ g,
+                                                            float* __restrict__ m,
+                                                            float* __restrict__ v, size_t n,
+                                                            AdamWArgs a,
+                                                            const float* __restrict__ norm_scale) {
+  const float s = norm_scale[1];
+  for (size_t i = blockIdx.x * (size_t)kOptThreads + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * kOptThreads) {
+    const float gi = g[i] * s;
+    const float mi = a.beta1 * m[i] + (1.0f - a.beta1) * gi;
+    const float vi = a.beta2 * v[i] + (1.0f - a.beta2) * gi * gi;
+    m[i] = mi;
+    v[i] = vi;
+    const float mh = mi * a.bc1, vh = vi * a.bc2;
+    const float pi = to_f32(p[i]) * a.decay - a.lr * mh / (sqrtf(vh) + a.eps);
+    p[i] = from_f32<T>(pi);
+  }
+}
+
+// buf = mu buf + s g;  u = s g + mu buf;  partial[block] = sum of u^2 (fp64)
+__global__ __launch_bounds__(kOptThreads) void muon_momentum_kernel(
+    const float* __restrict__ g, float* __restrict__ buf, float* __restrict__ u, size_t n,
+    float mu, const float* __restrict__ norm_scale, double* __restrict__ partial) {
+  __shared__ double red[kOptThreads / 64];
+  const float s = norm_scale[1];
+  double acc = 0.0;
+  for (size_t i = blockIdx.x * (size_t)kOptThreads + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * kOptThreads) {
+    const float gi = g[i] * s;
+    const float bi = mu * buf[i] + gi;
+    buf[i] = bi;
+    const float ui = gi + mu * bi;
+    u[i] = ui;
+    acc += (double)ui * ui;
+  }
+  acc = block_sum_f64(acc, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = acc;
+}
+
+// x = T(u / (||u||_F + 1e-7)), ||u|| from the momentum kernel's partials
+template <typename T>
+__global__ __launch_bounds__(kOptThreads) void muon_normalize_kernel(
+    const float* __restrict__ u, size_t n, const double* __restrict__ partial, int nparts,
+    T* __restrict__ x) {
+  __shared__ double red[kOptThreads / 64];
+  __shared__ float inv_s;
+  double s = 0.0;
+  for (int i = threadIdx.x; i < nparts; i += kOptThreads) s += partial[i];
+  s = block_sum_f64(s, red);
+  if (threadIdx.x == 0) inv_s = (float)(1.0 / (sqrt(s) + 1e-7));
+  __syncthreads();
+  const float inv = inv_s;
+  for (size_t i = blockIdx.x * (size_t)kOptThreads + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * kOptThreads)
+    x[i] = from_f32<T>(u[i] * inv);
+}
+
+// y (fp32) = alpha * x (type T)
+template <typename T>
+__global__ __launch_bounds__(kOptThreads) void scale_to_f32_kernel(const T* __restrict__ x,
+                                                                   size_t n, float alpha,
+                                                                   float* __restrict__ y) {
+  for (size_t i = blockIdx.x * (size_t)kOptThreads + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * kOptThreads)
+    y[i] = alpha * to_f32(x[i]);
+}
+
+// y (type T) = alpha * x (fp32)
+template <typename T>
+__global__ __launch_bounds__(kOptThreads) void scale_from_f32_kernel(const float* __restrict__ x,
+                                                                     size_t n, float alpha,
+                                                                     T* __restrict__ y) {
+  for (size_t i = blockIdx.x * (size_t)kOptThreads + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * kOptThreads)
+    y[i] = from_f32<T>(alpha * x[i]);
+}
+
+// p = p * decay - coef * x  (x fp32 in the parameter's layout)
+template <typename T>
+__global__ __launch_bounds__(kOptThreads) void muon_update_kernel(T* __restrict__ p,
+                                                                  const float* __restrict__ x,
+                                                                  size_t n, float decay, float coef) {
+  for (size_t i = blockIdx.x * (size_t)kOptThreads + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * kOptThreads)
+    p[i] = from_f32<T>(to_f32(p[i]) * decay - coef * x[i]);
+}
+
+int grid_for(size_t n, int cap = 4096) {
+  const size_t want = (n + kOptThreads - 1) / kOptThreads;
+  return (int)(want < (size_t)cap ? (want > 0 ? want : 1) : cap);
+}
+
+}  // namespace
+
+hipError_t grad_norm(const float* grads, const OptRanges& rg, double* partial, float max_norm,
+                     float* norm_scale, hipStream_t s) {
+  if (rg.n <= 0 || rg.n > kOptMaxRanges) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sumsq_ranges_kernel, dim3(kNormBlocksPerRange, rg.n), dim3(kOptThreads), 0, s,
+                     grads, rg, partial);
+  hipLaunchKernelGGL(norm_finish_kernel, dim3(1), dim3(kOptThreads), 0, s, partial,
+                     rg.n * kNormBlocksPerRange, max_norm, norm_scale);
+  return hipGetLastError();
+}
+
+hipError_t adamw(DType t, void* p, const float* g, float* m, float* v, size_t n, const AdamWArgs& a,
+                 const float* norm_scale, hipStream_t s) {
+  if (t == DType::BF16)
+    hipLaunchKernelGGL(adamw_kernel<bf16>, dim3(grid_for(n)), dim3(kOptThreads), 0, s,
+                       static_cast<bf16*>(p), g, m, v, n, a, norm_scale);
+  else
+    hipLaunchKernelGGL(adamw_kernel<float>, dim3(grid_for(n)), dim3(kOptThreads), 0, s,
+                       static_cast<float*>(p), g, m, v, n, a, norm_scale);
+  return hipGetLastError();
+}
+
+hipError_t muon_momentum(const float* g, float* buf, float* u, size_t n, float mu,
+                         const float* norm_scale, double* partial, hipStream_t s) {
+  hipLaunchKernelGGL(muon_momentum_kernel, dim3(kMuonParts), dim3(kOptThreads), 0, s, g, buf, u, n,
+                     mu, norm_scale, partial);
+  return hipGetLastError();
+}
+
+hipError_t muon_normalize(DType t, const float* u, size_t n, const double* partial, void* x,
+                          hipStream_t s) {
+  if (t == DType::BF16)
+    hipLaunchKernelGGL(muon_normalize_kernel<bf16>, dim3(grid_for(n)), dim3(kOptThreads), 0, s, u, n,
+                       partial, kMuonParts, static_cast<bf16*>(x));
+  else
+    hipLaunchKernelGGL(muon_normalize_kernel<float>, dim3(grid_for(n)), dim3(kOptThreads), 0, s, u,
+                       n, partial, kMuonParts, static_cast<float*>(x));
+  return hipGetLastError();
+}
+
+hipError_t scale_to_f32(DType t, const void* x, size_t n, float alpha, float* y, hipStream_t s) {
+  if (t == DType::BF16)
+    hipLaunchKernelGGL(scale_to_f32_kernel<bf16>, dim3(grid_for(n)), dim3(kOptThreads), 0, s,
+                       static_cast<const bf16*>(x), n, alpha, y);
+  else
+    hipLaunchKernelGGL(scale_to_f32_kernel<float>, dim3(grid_for(n)), dim3(kOptThreads), 0, s,
+                       static_cast<const float*>(x), n, alpha, y);
+  return hipGetLastError();
+}
+
+hipError_t scale_from_f32(DType t, const float* x, size_t n, float alpha, void* y, hipStream_t s) {
+  if (t == DType::BF16)
+    hipLaunchKernelGGL(scale_from_f32_kernel<bf16>, dim3(grid_for(n)), dim3(kOptThreads), 0, s, x,
+                       n, alpha, static_cast<bf16*>(y));
+  else
+    hipLaunchKernelGGL(scale_from_f32_kernel<float>, dim3(grid_for(n)), dim3(kOptThreads), 0, s, x,
+                       n, alpha, static_cast<float*>(y));
+  return hipGetLastError();
+}
+
+hipError_t muon_update(DType t, void* p, const float* x, size_t n, float decay, float coef,
+                       hipStream_t s) {
+  if (t == DType::BF16)
+    hipLaunchKernelGGL(muon_update_kernel<bf16>, dim3(grid_for(n)), dim3(kOptThreads), 0, s,
+                       static_cast<bf16*>(p), x, n, decay, coef);
+  else
+    hipLaunchKernelGGL(muon_update_kernel<float>, dim3(grid_for(n)), dim3(kOptThreads), 0, s,
+                       static_cast<float*>(p), x, n, decay, coef);
+  return hipGetLastError();
+}
+
+}  // namespace nc

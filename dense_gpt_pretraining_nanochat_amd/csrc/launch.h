@@ -67,7 +67,7 @@ uint64_t embed_bwd_max_pieces(int64_t M, int V);
 uint64_t embed_bwd_max_parts(int64_t M);
 hipError_t embed_bwd(DType t, const void* E, const int32_t* tok, const float* rinv0,
                      const float* dx, int M, int d, int V, EmbedBwdScratch ws, float* dE,
-                     hipStream_t s);
+                     bool accumulate, hipStream_t s);
 
 // ---- rotary + QK-norm -------------------------------------------------------
 hipError_t rope_table(int T, int half, double base, float* cs, hipStream_t s);  // [T, half] cos, then sin
@@ -97,6 +97,39 @@ hipError_t softcap_ce(DType t, const void* logits, const int32_t* tgt, int R, in
                       float w, float* loss_rows, void* dlogits, uint32_t* status, hipStream_t s);
 hipError_t loss_mean(const float* loss_rows, int M, float* out, uint32_t* status, hipStream_t s);
 
+// ---- optimizer step -------------------------------------------------------------
+constexpr int kOptMaxRanges = 160;        // tensors of one parameter buffer, at most
+constexpr int kNormBlocksPerRange = 64;   // fixed grid: the norm is bitwise reproducible
+constexpr int kMuonParts = 256;           // blocks (and fp64 partials) of the momentum kernel
+struct OptRanges {                        // element ranges of a flat fp32 buffer
+  uint64_t off[kOptMaxRanges];
+  uint64_t cnt[kOptMaxRanges];
+  int n;
+};
+struct AdamWArgs {
+  float lr, beta1, beta2, eps;
+  float decay;                            // 1 - lr * weight_decay
+  float bc1, bc2;                         // 1 / (1 - beta^step)
+};
+// norm_scale[0] = ||grads over the ranges||_2, norm_scale[1] = min(1, max_norm / (norm + 1e-6))
+// (1 when max_norm <= 0); partial holds n * kNormBlocksPerRange doubles
+hipError_t grad_norm(const float* grads, const OptRanges& rg, double* partial, float max_norm,
+                     float* norm_scale, hipStream_t s);
+// AdamW on n elements; the gradient is scaled by norm_scale[1]
+hipError_t adamw(DType t, void* p, const float* g, float* m, float* v, size_t n, const AdamWArgs& a,
+                 const float* norm_scale, hipStream_t s);
+// buf = mu buf + s g, u = s g + mu buf (s = norm_scale[1]); kMuonParts fp64 partials of ||u||^2
+hipError_t muon_momentum(const float* g, float* buf, float* u, size_t n, float mu,
+                         const float* norm_scale, double* partial, hipStream_t s);
+// x (T) = u / (||u||_F + 1e-7)
+hipError_t muon_normalize(DType t, const float* u, size_t n, const double* partial, void* x,
+                          hipStream_t s);
+// y (fp32) = alpha * x (T);  y (T) = alpha * x (fp32)
+hipError_t scale_to_f32(DType t, const void* x, size_t n, float alpha, float* y, hipStream_t s);
+hipError_t scale_from_f32(DType t, const float* x, size_t n, float alpha, void* y, hipStream_t s);
+// p (T) = p * decay - coef * x (fp32)
+hipError_t muon_update(DType t, void* p, const float* x, size_t n, float decay, float coef,
+                       hipStream_t s);
 // ---- init and utilities -----------------------------------------------------
 struct InitSeg {
   size_t begin, end;   // element range [begin, end)

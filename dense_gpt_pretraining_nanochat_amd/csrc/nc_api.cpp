@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "launch.h"
@@ -220,7 +221,7 @@ P* at(void* base, uint64_t off) {
 // dW[N1,N2] = X1^T X2 over M rows (X1 [M, N1], X2 [M, N2]), both operands read
 // K-strided, split over K with a fixed-order fp32 reduction.
 hipError_t wgrad(DType dt, const void* X1, const void* X2, float* dW, float* partial, int64_t M,
-                 int N1, int N2, const WgradPlan& p, hipStream_t s) {
+                 int N1, int N2, const WgradPlan& p, hipStream_t s, bool accumulate = false) {
   nc::GemmArgs g{};
   g.A = X1;
   g.B = X2;
@@ -234,12 +235,12 @@ hipError_t wgrad(DType dt, const void* X1, const void* X2, float* dW, float* par
   g.tile = p.tile;
   if (p.splits == 1) {
     g.C = dW;
-    return nc::gemm(dt, false, false, Epi::StoreF32, g, s);
+    return nc::gemm(dt, false, false, accumulate ? Epi::AddF32 : Epi::StoreF32, g, s);
   }
   g.C = partial;
   hipError_t e = nc::gemm(dt, false, false, Epi::PartialF32, g, s);
   if (e != hipSuccess) return e;
-  return nc::splitk_reduce(partial, p.splits, (size_t)N1 * N2, dW, false, s);
+  return nc::splitk_reduce(partial, p.splits, (size_t)N1 * N2, dW, accumulate, s);
 }
 
 hipError_t gemm_simple(DType dt, bool ak, bool bk, Epi epi, const void* A, const void* B, void* C,
@@ -263,7 +264,7 @@ hipError_t gemm_simple(DType dt, bool ak, bool bk, Epi epi, const void* A, const
 
 int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
              const int32_t* targets, float* grads, void* ws, uint64_t ws_bytes, float* loss_dev,
-             void* stream, bool bwd) {
+             void* stream, bool bwd, bool accumulate = false) {
   int rc = validate(cfg);
   if (rc) return rc;
   if (!params || !tokens || !targets || !ws || !loss_dev || (bwd && !grads)) return NC_ERR_NULL;
@@ -338,7 +339,7 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
                            static_cast<char*>(dxf) + r0 * D.d * e, nullptr, mc, D.d, D.V, D.V,
                            D.d, D.d, 0, s));
       // dU (+)= dlog^T . xf_chunk: both operands contracted over their rows
-      HIPCHECK(gemm_simple(dt, false, false, r0 == 0 ? Epi::StoreF32 : Epi::AddF32, dlog, xfc,
+      HIPCHECK(gemm_simple(dt, false, false, (r0 == 0 && !accumulate) ? Epi::StoreF32 : Epi::AddF32, dlog, xfc,
                            G(iU), nullptr, D.V, D.d, (int)mc, D.V, D.d, D.d, 0, s));
     }
   }
@@ -366,15 +367,15 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
     void* h2 = at<char>(ws, A.h2);
     void* a = at<char>(ws, A.a);
     // MLP: x_out = x_mid + relu(h2 Wfc^T)^2 Wpr^T
-    HIPCHECK(wgrad(dt, g, a, G(base + 3), partial, M, D.d, D.F, pPR, s));
+    HIPCHECK(wgrad(dt, g, a, G(base + 3), partial, M, D.d, D.F, pPR, s, accumulate));
     HIPCHECK(gemm_simple(dt, true, false, Epi::Relu2Bwd, g, W(base + 3), dbig, a, M, D.F, D.d,
                          D.d, D.F, D.F, D.F, s));
-    HIPCHECK(wgrad(dt, dbig, h2, G(base + 2), partial, M, D.F, D.d, pFC, s));
+    HIPCHECK(wgrad(dt, dbig, h2, G(base + 2), partial, M, D.F, D.d, pFC, s, accumulate));
     HIPCHECK(gemm_simple(dt, true, false, Epi::StoreT, dbig, W(base + 2), dh, nullptr, M, D.d,
                          D.F, D.F, D.d, D.d, 0, s));
     HIPCHECK(nc::rmsnorm_bwd(dt, dh, h2, at<float>(ws, A.rinv2), Mi, D.d, dx, true, g, s));
     // attention: x_mid = x_in + o Wo^T
-    HIPCHECK(wgrad(dt, g, o, G(base + 1), partial, M, D.d, D.d, pO, s));
+    HIPCHECK(wgrad(dt, g, o, G(base + 1), partial, M, D.d, D.d, pO, s, accumulate));
     HIPCHECK(gemm_simple(dt, true, false, Epi::StoreT, g, W(base + 1), dout, nullptr, M, D.d, D.d,
                          D.d, D.d, D.d, 0, s));
     HIPCHECK(nc::attn_bwd_delta(dt, o, dout, D.B, D.T, D.H, delta, s));
@@ -382,7 +383,7 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
                           D.Q, at<float>(ws, P.attn_part), s));
     HIPCHECK(nc::rope_qknorm_bwd(dt, dbig, D.Q, qkv, D.Q, Mi, D.T, D.H, cs,
                                  at<float>(ws, A.rqk), s));
-    HIPCHECK(wgrad(dt, dbig, h, G(base + 0), partial, M, D.Q, D.d, pQ, s));
+    HIPCHECK(wgrad(dt, dbig, h, G(base + 0), partial, M, D.Q, D.d, pQ, s, accumulate));
     HIPCHECK(gemm_simple(dt, true, false, Epi::StoreT, dbig, W(base + 0), dh, nullptr, M, D.d,
                          D.Q, D.Q, D.d, D.d, 0, s));
     HIPCHECK(nc::rmsnorm_bwd(dt, dh, h, at<float>(ws, A.rinv1), Mi, D.d, dx, true, g, s));
@@ -396,7 +397,7 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
   es.part_off = at<int32_t>(ws, P.part_off);
   es.item_bucket = at<int32_t>(ws, P.item_bucket);
   es.part = static_cast<float*>(dh);     // embed_bwd_max_parts(M) * d floats <= M * d
-  HIPCHECK(nc::embed_bwd(dt, W(iE), tokens, rinv0, dx, (int)M, D.d, D.V, es, G(iE), s));
+  HIPCHECK(nc::embed_bwd(dt, W(iE), tokens, rinv0, dx, (int)M, D.d, D.V, es, G(iE), accumulate, s));
   return NC_OK;
 }
 
@@ -497,6 +498,200 @@ int nc_forward_backward(const nc_config* cfg, const void* params, const int32_t*
                         const int32_t* targets, float* grads, void* ws, uint64_t ws_bytes,
                         float* loss_dev, void* stream) {
   return run_step(cfg, params, tokens, targets, grads, ws, ws_bytes, loss_dev, stream, true);
+}
+
+int nc_forward_backward_accumulate(const nc_config* cfg, const void* params, const int32_t* tokens,
+                                   const int32_t* targets, float* grads, void* ws,
+                                   uint64_t ws_bytes, float* loss_dev, void* stream) {
+  return run_step(cfg, params, tokens, targets, grads, ws, ws_bytes, loss_dev, stream, true, true);
+}
+
+// ---------------------------------------------------------------- optimizer
+
+namespace {
+
+// Quintic Newton-Schulz coefficients of Muon's public description.
+constexpr float kNsA = 3.4445f, kNsB = -4.7750f, kNsC = 2.0315f;
+
+struct OptPlan {
+  uint64_t norm_partial, norm_scale, muon_partial;
+  uint64_t u, x0, x, a, cf, bt, df, xf;
+  uint64_t total;
+};
+
+OptPlan opt_plan_of(const Dims& D) {
+  OptPlan P{};
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t o = off;
+    off = align_up(off + bytes, kAlign);
+    return o;
+  };
+  const uint64_t big = (uint64_t)D.F * D.d;     // largest block matrix (Wfc, Wpr)
+  const uint64_t sq = (uint64_t)D.d * D.d;      // r x r with r = d, the short side of every one
+  P.norm_partial = take(sizeof(double) * nc::kOptMaxRanges * nc::kNormBlocksPerRange);
+  P.norm_scale = take(4 * sizeof(float));
+  P.muon_partial = take(sizeof(double) * nc::kMuonParts);
+  P.u = take(4 * big);
+  P.x0 = take(D.esz * big);
+  P.x = take(D.esz * big);
+  P.a = take(D.esz * sq);
+  P.cf = take(4 * sq);
+  P.bt = take(D.esz * sq);
+  P.df = take(4 * big);
+  P.xf = take(4 * big);
+  P.total = off;
+  return P;
+}
+
+int validate_optim(const nc_optim_config* o) {
+  if (!o) return NC_ERR_NULL;
+  auto finite_nonneg = [](float v) { return v >= 0.f && v < 1e30f; };
+  if (!finite_nonneg(o->lr_adamw) || !finite_nonneg(o->lr_muon)) return NC_ERR_ARG;
+  if (!(o->beta1 >= 0.f && o->beta1 < 1.f) || !(o->beta2 >= 0.f && o->beta2 < 1.f)) return NC_ERR_ARG;
+  if (!(o->eps > 0.f) || !finite_nonneg(o->wd_adamw) || !finite_nonneg(o->wd_muon)) return NC_ERR_ARG;
+  if (!(o->momentum >= 0.f && o->momentum < 1.f)) return NC_ERR_ARG;
+  if (!(o->max_grad_norm < 1e30f)) return NC_ERR_ARG;
+  if (o->ns_steps < 0 || o->ns_steps > 16 || o->step < 1) return NC_ERR_ARG;
+  return NC_OK;
+}
+
+hipError_t gemm_args(DType dt, bool ak, bool bk, Epi epi, const void* A, const void* B, void* C,
+                     int M, int N, int K, int lda, int ldb, int ldc, hipStream_t s) {
+  nc::GemmArgs g{};
+  g.A = A;
+  g.B = B;
+  g.C = C;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.ldc = ldc;
+  g.splits = 1;
+  return nc::gemm(dt, ak, bk, epi, g, s);
+}
+
+// One Muon step on the [R, C] matrix p (gradient g, momentum buf).
+int muon_matrix(const Dims& D, const OptPlan& P, void* ows, const nc_optim_config* o, void* p,
+                const float* g, float* buf, int R, int C, hipStream_t s) {
+  const DType dt = D.dt;
+  const size_t n = (size_t)R * C;
+  const bool tall = R > C;
+  const int r = tall ? C : R, c = tall ? R : C;   // the iteration runs on X [r, c], r <= c
+  const float* norm_scale = at<float>(ows, P.norm_scale);
+  double* mpart = at<double>(ows, P.muon_partial);
+  float* u = at<float>(ows, P.u);
+  float* df = at<float>(ows, P.df);
+  float* xf = at<float>(ows, P.xf);
+  const float decay = 1.0f - o->lr_muon * o->wd_muon;
+  const float scale = std::sqrt(std::max(1.0f, (float)R / (float)C));
+  HIPCHECK(nc::muon_momentum(g, buf, u, n, o->momentum, norm_scale, mpart, s));
+  if (o->ns_steps == 0) {
+    HIPCHECK(nc::muon_normalize(DType::F32, u, n, mpart, xf, s));
+    HIPCHECK(nc::muon_update(dt, p, xf, n, decay, o->lr_muon * scale, s));
+    return NC_OK;
+  }
+  void* x0 = at<char>(ows, P.x0);
+  HIPCHECK(nc::muon_normalize(dt, u, n, mpart, x0, s));
+  void* X = x0;
+  if (tall) {
+    X = at<char>(ows, P.x);
+    HIPCHECK(nc::transpose(dt, x0, R, C, C, X, R, s));
+  }
+  void* A = at<char>(ows, P.a);
+  float* cf = at<float>(ows, P.cf);
+  void* bt = at<char>(ows, P.bt);
+  const size_t rr = (size_t)r * r, rc = (size_t)r * c;
+  for (int k = 0; k < o->ns_steps; ++k) {
+    // A = X X^T;  cf = (b/c) A + A A^T (= (b A + c A^2) / c, A symmetric)
+    HIPCHECK(gemm_args(dt, true, true, Epi::StoreT, X, X, A, r, r, c, c, c, r, s));
+    HIPCHECK(nc::scale_to_f32(dt, A, rr, kNsB / kNsC, cf, s));
+    HIPCHECK(gemm_args(dt, true, true, Epi::AddF32, A, A, cf, r, r, r, r, r, r, s));
+    HIPCHECK(nc::scale_from_f32(dt, cf, rr, 1.0f, bt, s));
+    // df = (a/c) X + cf X, so that the next iterate is c * df
+    HIPCHECK(nc::scale_to_f32(dt, X, rc, kNsA / kNsC, df, s));
+    HIPCHECK(gemm_args(dt, true, false, Epi::AddF32, bt, X, df, r, c, r, r, c, c, s));
+    if (k + 1 < o->ns_steps) HIPCHECK(nc::scale_from_f32(dt, df, rc, kNsC, X, s));
+  }
+  const float* fin = df;
+  if (tall) {
+    HIPCHECK(nc::transpose(DType::F32, df, r, c, c, xf, r, s));
+    fin = xf;
+  }
+  HIPCHECK(nc::muon_update(dt, p, fin, n, decay, o->lr_muon * scale * kNsC, s));
+  return NC_OK;
+}
+
+}  // namespace
+
+int nc_optimizer_state_bytes(const nc_config* cfg, uint64_t* bytes) {
+  const int rc = validate(cfg);
+  if (rc) return rc;
+  if (!bytes) return NC_ERR_NULL;
+  *bytes = 2 * sizeof(float) * param_elems(dims_of(cfg));
+  return NC_OK;
+}
+
+int nc_optimizer_workspace_bytes(const nc_config* cfg, uint64_t* bytes) {
+  const int rc = validate(cfg);
+  if (rc) return rc;
+  if (!bytes) return NC_ERR_NULL;
+  *bytes = opt_plan_of(dims_of(cfg)).total;
+  return NC_OK;
+}
+
+int nc_optimizer_step(const nc_config* cfg, const nc_optim_config* optim, void* params,
+                      const float* grads, float* state, void* ows, uint64_t ows_bytes,
+                      float* grad_norm_dev, void* stream) {
+  int rc = validate(cfg);
+  if (rc) return rc;
+  rc = validate_optim(optim);
+  if (rc) return rc;
+  if (!params || !grads || !state || !ows || !grad_norm_dev) return NC_ERR_NULL;
+  if (misaligned(params) || misaligned(grads) || misaligned(state) || misaligned(ows) ||
+      misaligned(grad_norm_dev))
+    return NC_ERR_ALIGN;
+  const Dims D = dims_of(cfg);
+  const OptPlan P = opt_plan_of(D);
+  if (ows_bytes < P.total) return NC_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const auto lay = layout_of(D);
+  const uint64_t N = param_elems(D);
+  if ((int)lay.size() > nc::kOptMaxRanges) return NC_ERR_UNSUPPORTED;
+  // global norm and clip factor
+  nc::OptRanges rg{};
+  rg.n = (int)lay.size();
+  for (int i = 0; i < rg.n; ++i) {
+    rg.off[i] = lay[i].offset;
+    rg.cnt[i] = (uint64_t)(lay[i].rows * lay[i].cols);
+  }
+  float* norm_scale = at<float>(ows, P.norm_scale);
+  HIPCHECK(nc::grad_norm(grads, rg, at<double>(ows, P.norm_partial), optim->max_grad_norm,
+                         norm_scale, s));
+  HIPCHECK(hipMemcpyAsync(grad_norm_dev, norm_scale, sizeof(float), hipMemcpyDeviceToDevice, s));
+  float* m1 = state;          // AdamW first moment, or Muon momentum
+  float* m2 = state + N;      // AdamW second moment (E and U only)
+  nc::AdamWArgs aa;
+  aa.lr = optim->lr_adamw;
+  aa.beta1 = optim->beta1;
+  aa.beta2 = optim->beta2;
+  aa.eps = optim->eps;
+  aa.decay = 1.0f - optim->lr_adamw * optim->wd_adamw;
+  aa.bc1 = (float)(1.0 / (1.0 - std::pow((double)optim->beta1, (double)optim->step)));
+  aa.bc2 = (float)(1.0 / (1.0 - std::pow((double)optim->beta2, (double)optim->step)));
+  for (const auto& t : lay) {
+    void* p = static_cast<char*>(params) + t.offset * D.esz;
+    const float* g = grads + t.offset;
+    const size_t n = (size_t)(t.rows * t.cols);
+    if (t.layer < 0) {                                   // E or U: AdamW
+      HIPCHECK(nc::adamw(D.dt, p, g, m1 + t.offset, m2 + t.offset, n, aa, norm_scale, s));
+    } else {                                             // block matrices: Muon
+      rc = muon_matrix(D, P, ows, optim, p, g, m1 + t.offset, (int)t.rows, (int)t.cols, s);
+      if (rc) return rc;
+    }
+  }
+  return NC_OK;
 }
 
 int nc_read_device_status(const void* ws, uint32_t* flags, void* stream) {

@@ -141,6 +141,69 @@ int nc_forward_backward(const nc_config* cfg, const void* params, const int32_t*
                         const int32_t* targets, float* grads, void* ws, uint64_t ws_bytes,
                         float* loss_dev, void* stream);
 
+/* As nc_forward_backward, but ADDS d(mean loss)/d(params) to grads instead of
+ * overwriting it, for gradient accumulation over several batches (wmrh.cn
+ * tutorial, section 4.1: gradient accumulation). The caller zeroes grads
+ * before the first batch and scales as it wants (each call adds the gradient
+ * of that batch's mean loss). */
+int nc_forward_backward_accumulate(const nc_config* cfg, const void* params,
+                                   const int32_t* tokens, const int32_t* targets, float* grads,
+                                   void* ws, uint64_t ws_bytes, float* loss_dev, void* stream);
+
+/* ---- optimizer step --------------------------------------------------------
+ * Muon for the block matrices (Wqkv, Wo, Wfc, Wpr of every layer) and AdamW
+ * for the embedding E and the lm_head U (followin.io release article,
+ * paragraph after the architecture list: Muon + AdamW, after modded-nanoGPT;
+ * vnrom.net, section "Cấu trúc thư mục và module chính": the optimizer module
+ * implements AdamW with Muon), after clipping the gradient by its global norm
+ * (wmrh.cn tutorial, section 5.1). The pages do not define the update rules;
+ * they follow the public descriptions:
+ *   AdamW (decoupled weight decay, Adam's bias correction), per element:
+ *     m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2
+ *     p = p (1 - lr wd) - lr (m / (1-b1^step)) / (sqrt(v / (1-b2^step)) + eps)
+ *   Muon, per [R, C] matrix:
+ *     buf = mu buf + g;  u = g + mu buf  (Nesterov)
+ *     X = u / (||u||_F + 1e-7), transposed when R > C, then ns_steps times
+ *     X = a X + (b A + c A^2) X with A = X X^T, (a, b, c) = (3.4445, -4.7750,
+ *     2.0315), transposed back
+ *     p = p (1 - lr wd) - lr max(1, R/C)^(1/2) X
+ *   clipping: g is scaled by min(1, max_norm / (||g||_2 + 1e-6)), the norm
+ *   over every parameter's gradient; max_norm <= 0 disables it.
+ * In bf16 mode the Newton-Schulz products take bf16 operands (fp32
+ * accumulation) and parameters are rounded back to bf16; in fp32 mode
+ * everything is fp32. */
+typedef struct {
+  float lr_adamw;      /* AdamW learning rate (E, U), >= 0                       */
+  float beta1, beta2;  /* AdamW moment decay rates, in [0, 1)                    */
+  float eps;           /* AdamW denominator guard, > 0                           */
+  float wd_adamw;      /* AdamW decoupled weight decay, >= 0                     */
+  float lr_muon;       /* Muon learning rate (block matrices), >= 0              */
+  float momentum;      /* Muon momentum mu, in [0, 1)                            */
+  float wd_muon;       /* Muon decoupled weight decay, >= 0                      */
+  float max_grad_norm; /* clip threshold; <= 0 disables clipping                 */
+  int32_t ns_steps;    /* Newton-Schulz iterations, 0..16 (5 in the description) */
+  int32_t step;        /* 1-based index of this step (AdamW bias correction)     */
+} nc_optim_config;
+
+/* Bytes of optimizer state: 2 * nc_param_count fp32 values in the parameter
+ * layout. The first half holds AdamW's first moment for E and U and Muon's
+ * momentum for the matrices, the second half AdamW's second moment (used for
+ * E and U only). The caller zeroes it before the first step. */
+int nc_optimizer_state_bytes(const nc_config* cfg, uint64_t* bytes);
+
+/* Bytes of scratch nc_optimizer_step needs (norm partials and the
+ * Newton-Schulz buffers of the largest matrix). */
+int nc_optimizer_workspace_bytes(const nc_config* cfg, uint64_t* bytes);
+
+/* One optimizer step: updates params (in place, dtype of cfg) and state from
+ * grads (fp32, not modified); writes the pre-clip global gradient norm (fp32)
+ * to *grad_norm_dev. Hyperparameters out of range give NC_ERR_ARG; ows must
+ * hold nc_optimizer_workspace_bytes bytes and may not be shared with a
+ * concurrent call. Deterministic: a fixed-order norm reduction and no atomics. */
+int nc_optimizer_step(const nc_config* cfg, const nc_optim_config* optim, void* params,
+                      const float* grads, float* state, void* ows, uint64_t ows_bytes,
+                      float* grad_norm_dev, void* stream);
+
 /* Copies the workspace status word to *flags (synchronises on the stream)
  * and clears nothing; each forward call resets it. */
 int nc_read_device_status(const void* ws, uint32_t* flags, void* stream);

@@ -117,3 +117,38 @@ def test_workspace_grows_with_batch_and_depth():
     assert nc.nc_workspace_bytes(c4, True) < 64 * 2 ** 30     # fits easily in 288 GB
     off = nc.nc_token_losses_offset(c4, True)
     assert off % 256 == 0 and off + 4 * 65536 <= nc.nc_workspace_bytes(c4, True)
+
+
+def _optim(**kw):
+    base = dict(lr_adamw=0.01, beta1=0.8, beta2=0.95, eps=1e-10, wd_adamw=0.0, lr_muon=0.02,
+                momentum=0.95, wd_muon=0.0, max_grad_norm=1.0, ns_steps=5, step=1)
+    base.update(kw)
+    return nc.nc_optim_config(**base)
+
+
+def test_optimizer_sizes_and_argument_checks():
+    """State is two fp32 values per parameter element; invalid hyperparameters,
+    NULL, misaligned and short-workspace calls fail before any launch."""
+    L = nc.lib()
+    cfg = _cfg("C1")
+    n = nc.nc_param_count(cfg)
+    assert nc.nc_optimizer_state_bytes(cfg) == 2 * 4 * n
+    ows = nc.nc_optimizer_workspace_bytes(cfg)
+    assert ows > 0
+    a = 1 << 20
+    p = ctypes.c_void_p
+
+    def step(o, params=p(a), ws_bytes=ows, grads=p(a)):
+        return L.nc_optimizer_step(ctypes.byref(cfg), ctypes.byref(o), params, grads, p(a), p(a),
+                                   ws_bytes, p(a), None)
+
+    assert step(_optim(), params=None) == -3
+    assert step(_optim(), grads=p(a + 64)) == -4
+    assert step(_optim(), ws_bytes=ows - 1) == -5
+    for bad in (dict(step=0), dict(beta1=1.0), dict(beta2=-0.1), dict(eps=0.0), dict(momentum=1.0),
+                dict(ns_steps=17), dict(ns_steps=-1), dict(lr_muon=-1.0), dict(wd_adamw=-0.5)):
+        assert step(_optim(**bad)) == -7, bad
+    # the state size grows with depth; the workspace with the largest matrix
+    big = nc.nc_config_from_depth(20, 65536, 2048, 32, "bf16")
+    assert nc.nc_optimizer_state_bytes(big) == 2 * 4 * nc.nc_param_count(big)
+    assert nc.nc_optimizer_workspace_bytes(big) > ows
