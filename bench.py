@@ -46,6 +46,8 @@ def _args():
     ap.add_argument("--workload", default="C4", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--no-optimizer", action="store_true",
+                    help="skip the separate timing of the optimizer step")
     ap.add_argument("--kernel-only", action="store_true",
                     help="launch only the roofline kernel (3x) and a 1 GiB device copy (3x)")
     return ap.parse_args()
@@ -106,6 +108,43 @@ def dominant_kernel_roofline(cfg, nc, torch, reps=20, warm=25):
             "unit": "TFLOP/s", "frac": round(ach / peak, 4), "avg_us": round(sec * 1e6, 2),
             "flops_per_launch": flops, "warmup_launches": warm, "timed_launches": reps,
             "traffic": measured_traffic([M, F, d])}
+
+
+def ns_flops(c):
+    """Matrix-core FLOPs of Muon's Newton-Schulz iterations for one optimizer
+    step: per matrix [R, C] with r = min, c = max, each iteration is
+    X X^T (2 r r c), A A^T (2 r^3) and B X (2 r r c)."""
+    d = 64 * c.depth
+    mats = [(d + 256, d), (d, d), (4 * d, d), (d, 4 * d)]
+    per_layer = sum(4 * min(R, C) ** 2 * max(R, C) + 2 * min(R, C) ** 3 for R, C in mats)
+    return 5 * c.depth * per_layer
+
+
+def optimizer_timing(step, nc, torch, c, reps=5):
+    """One optimizer step (global-norm clip, AdamW on E and U, Muon with 5
+    Newton-Schulz iterations on every block matrix) on the step's gradient,
+    timed with HIP events on the stream it runs on."""
+    o = nc.nc_optim_config(0.004, 0.8, 0.95, 1e-10, 0.0, 0.02, 0.95, 0.0, 1.0, 5, 1)
+    s = torch.cuda.current_stream()
+    saved = step.params.clone()
+    for k in range(2):
+        o.step = k + 1
+        step.optimizer_step(o)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(s)
+    for k in range(reps):
+        o.step = k + 3
+        step.optimizer_step(o)
+    ev1.record(s)
+    ev1.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    step.params.copy_(saved)
+    fl = ns_flops(c)
+    return {"ms_per_step": round(ms, 3), "newton_schulz_flops": fl,
+            "newton_schulz_tflops_if_all_time": round(fl / (ms / 1e3) / 1e12, 1),
+            "state_bytes": int(step.opt_state.numel() * 4),
+            "what": "clip + AdamW(E, U) + Muon(5 Newton-Schulz steps) over all 502M parameters; "
+                    "not part of the timed training step"}
 
 
 def kernel_only(a):
@@ -230,6 +269,9 @@ def main():
         "device_status": status,
         "wall_s_timed": round(wall, 3),
     }
+    if not a.no_optimizer:
+        out["optimizer"] = optimizer_timing(step, nc, torch, c)
+        step.opt_state = step.opt_ws = None
     del step
     torch.cuda.empty_cache()
     out["roofline"] = dominant_kernel_roofline(cfg, nc, torch)

@@ -144,8 +144,22 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, int split, int m, i
   }
 }
 
+// Arguments of batch item b: A and B advance by sa / sb elements of T, C by
+// sc elements of its own type (T or fp32, by epilogue).
+template <typename T, Epi EPI>
+__device__ __forceinline__ GemmArgs batch_item(const GemmArgs& g0, int b) {
+  GemmArgs g = g0;
+  if (b == 0) return g;
+  constexpr size_t csz = (EPI == Epi::StoreT || EPI == Epi::Relu2 || EPI == Epi::Relu2Bwd)
+                             ? sizeof(T) : sizeof(float);
+  g.A = static_cast<const char*>(g0.A) + (size_t)b * g0.sa * sizeof(T);
+  g.B = static_cast<const char*>(g0.B) + (size_t)b * g0.sb * sizeof(T);
+  g.C = static_cast<char*>(g0.C) + (size_t)b * g0.sc * csz;
+  return g;
+}
+
 template <typename T, bool AK, bool BKC, Epi EPI, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g0) {
   constexpr int NTHR = WM * WN * 64;
   constexpr int VEC = Vec16<T>::N;
   constexpr int KB = 4 * VEC;                 // k per matrix-core fragment
@@ -163,13 +177,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   const int wm = wave % WM, wn = wave / WM;
 
   // ---- tile scheduling --------------------------------------------------
-  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int tiles_m = (g0.M + BM - 1) / BM, tiles_n = (g0.N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
-  const int total = ntiles * g.splits;
+  const int per_item = ntiles * g0.splits;
+  const int total = per_item * (g0.batch > 1 ? g0.batch : 1);
   int bid = blockIdx.x;
   const int nb = gridDim.x;                  // a multiple of 8
   bid = (bid & 7) * (nb >> 3) + (bid >> 3);  // contiguous logical range per XCD
   if (bid >= total) return;
+  const int item = bid / per_item;
+  bid -= item * per_item;
+  const GemmArgs g = batch_item<T, EPI>(g0, item);
   const int split = bid / ntiles;
   int t = bid - split * ntiles;
   constexpr int GROUP = 8;
@@ -382,7 +400,7 @@ __device__ __forceinline__ void epilogue4_in(const GemmArgs& g, int split, int m
 }
 
 template <Epi EPI, bool AK, bool BKC>
-__global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g) {
+__global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
   constexpr int BM = 256, BN = 256;
   constexpr int WM = 2, WN = 4, TM = BM / WM, TN = BN / WN;   // 128 x 64 per wave
   constexpr int FM = TM / 32, FN = TN / 32;                   // 4 x 2 MFMA tiles
@@ -394,13 +412,17 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g) {
   const int l32 = lane & 31, lh = lane >> 5;
   const int wm = wave % WM, wn = wave / WM;
 
-  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int tiles_m = (g0.M + BM - 1) / BM, tiles_n = (g0.N + BN - 1) / BN;
   const int ntiles = tiles_m * tiles_n;
-  const int total = ntiles * g.splits;
+  const int per_item = ntiles * g0.splits;
+  const int total = per_item * (g0.batch > 1 ? g0.batch : 1);
   int bid = blockIdx.x;
   const int nb = gridDim.x;
   bid = (bid & 7) * (nb >> 3) + (bid >> 3);
   if (bid >= total) return;
+  const int item = bid / per_item;
+  bid -= item * per_item;
+  const GemmArgs g = batch_item<bf16, EPI>(g0, item);
   const int split = bid / ntiles;
   const int t = bid - split * ntiles;
   constexpr int GROUP = 8;
@@ -585,7 +607,8 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
 
 template <typename T, bool AK, bool BKC, Epi EPI, int BM, int BN, int WM, int WN>
 hipError_t launch_tiles(const GemmArgs& g, hipStream_t s) {
-  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.splits;
+  const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.splits *
+                    (g.batch > 1 ? g.batch : 1);
   const int grid = (tiles + 7) / 8 * 8;
   hipLaunchKernelGGL((gemm_kernel<T, AK, BKC, EPI, BM, BN, WM, WN>), dim3(grid), dim3(WM * WN * 64), 0,
                      s, g);
@@ -597,7 +620,8 @@ hipError_t launch_tiles(const GemmArgs& g, hipStream_t s) {
 int choose_tile(bool bf16, const GemmArgs& g) {
   if (!bf16 || g.tile == 128) return 128;
   if (g.tile == 256) return 256;
-  const long big_tiles = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.splits;
+  const long big_tiles = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.splits *
+                        (g.batch > 1 ? g.batch : 1);
   return (g.M >= 256 && g.N >= 256 && big_tiles >= 256) ? 256 : 128;
 }
 
@@ -605,7 +629,8 @@ template <typename T, bool AK, bool BKC, Epi EPI>
 hipError_t launch(const GemmArgs& g, hipStream_t s) {
   if constexpr (std::is_same<T, bf16>::value) {
     if (choose_tile(true, g) == 256) {
-      const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.splits;
+      const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.splits *
+                        (g.batch > 1 ? g.batch : 1);
       const int grid = (tiles + 7) / 8 * 8;
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, AK, BKC>), dim3(grid), dim3(512), 0, s, g);
       return hipGetLastError();
@@ -643,6 +668,11 @@ hipError_t gemm(DType t, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs
   if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.splits <= 0) return hipErrorInvalidValue;
   if (g.M % 16 || g.N % 16 || g.K % bk || g.K / bk < g.splits) return hipErrorInvalidValue;
   if (epi != Epi::PartialF32 && g.splits != 1) return hipErrorInvalidValue;
+  if (g.batch < 0 || (g.batch > 1 && (epi == Epi::PartialF32 || epi == Epi::Relu2Bwd)))
+    return hipErrorInvalidValue;
+  if ((long)((g.M + 127) / 128) * ((g.N + 127) / 128) * g.splits * (g.batch > 1 ? g.batch : 1) >
+      (1L << 30))
+    return hipErrorInvalidValue;
   return t == DType::BF16 ? dispatch<bf16>(a_kcontig, b_kcontig, epi, g, stream)
                           : dispatch<float>(a_kcontig, b_kcontig, epi, g, stream);
 }

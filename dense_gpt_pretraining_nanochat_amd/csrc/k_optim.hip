@@ -42,13 +42,24 @@ __global__ __launch_bounds__(kOptThreads) void sumsq_ranges_kernel(const float* 
                                                                    double* __restrict__ partial) {
   __shared__ double red[kOptThreads / 64];
   const int r = blockIdx.y;
-  const float* p = x + rg.off[r];
-  const size_t n = rg.cnt[r];
+  const f32x4* p = reinterpret_cast<const f32x4*>(x + rg.off[r]);   // ranges are 16-byte aligned
+  const size_t n4 = rg.cnt[r] / 4;                                    // and multiples of 4
+  const size_t stride = (size_t)gridDim.x * kOptThreads;
   double s = 0.0;
-  for (size_t i = blockIdx.x * (size_t)kOptThreads + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * kOptThreads) {
-    const double v = p[i];
-    s += v * v;
+  size_t i = blockIdx.x * (size_t)kOptThreads + threadIdx.x;
+  for (; i + 3 * stride < n4; i += 4 * stride) {      // four 16-byte loads in flight
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s += (double)v[u][e] * v[u][e];
+  }
+  for (; i < n4; i += stride) {
+    const f32x4 v = p[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += (double)v[e] * v[e];
   }
   s = block_sum_f64(s, red);
   if (threadIdx.x == 0) partial[(size_t)r * gridDim.x + blockIdx.x] = s;
@@ -91,24 +102,31 @@ __global__ __launch_bounds__(kOptThreads) void adamw_kernel(T* __restrict__ p,
   }
 }
 
-// buf = mu buf + s g;  u = s g + mu buf;  partial[block] = sum of u^2 (fp64)
+// Item y of a batch of matrices (gradient and momentum at stride `gs`, u
+// packed): buf = mu buf + s g;  u = s g + mu buf;  partial[y][block] = the
+// block's share of ||u||^2 (fp64)
 __global__ __launch_bounds__(kOptThreads) void muon_momentum_kernel(
-    const float* __restrict__ g, float* __restrict__ buf, float* __restrict__ u, size_t n,
-    float mu, const float* __restrict__ norm_scale, double* __restrict__ partial) {
+    const float* __restrict__ g, float* __restrict__ buf, size_t gs, float* __restrict__ u,
+    size_t n, float mu, const float* __restrict__ norm_scale, double* __restrict__ partial) {
   __shared__ double red[kOptThreads / 64];
   const float s = norm_scale[1];
+  const size_t y = blockIdx.y;
+  const f32x4* gy = reinterpret_cast<const f32x4*>(g + y * gs);
+  f32x4* by = reinterpret_cast<f32x4*>(buf + y * gs);
+  f32x4* uy = reinterpret_cast<f32x4*>(u + y * n);
   double acc = 0.0;
-  for (size_t i = blockIdx.x * (size_t)kOptThreads + threadIdx.x; i < n;
+  for (size_t i = blockIdx.x * (size_t)kOptThreads + threadIdx.x; i < n / 4;
        i += (size_t)gridDim.x * kOptThreads) {
-    const float gi = g[i] * s;
-    const float bi = mu * buf[i] + gi;
-    buf[i] = bi;
-    const float ui = gi + mu * bi;
-    u[i] = ui;
-    acc += (double)ui * ui;
+    const f32x4 gi = gy[i] * s;
+    const f32x4 bi = mu * by[i] + gi;
+    by[i] = bi;
+    const f32x4 ui = gi + mu * bi;
+    uy[i] = ui;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc += (double)ui[e] * ui[e];
   }
   acc = block_sum_f64(acc, red);
-  if (threadIdx.x == 0) partial[blockIdx.x] = acc;
+  if (threadIdx.x == 0) partial[y * gridDim.x + blockIdx.x] = acc;
 }
 
 // x = T(u / (||u||_F + 1e-7)), ||u|| from the momentum kernel's partials
@@ -118,6 +136,10 @@ __global__ __launch_bounds__(kOptThreads) void muon_normalize_kernel(
     T* __restrict__ x) {
   __shared__ double red[kOptThreads / 64];
   __shared__ float inv_s;
+  const size_t y = blockIdx.y;                   // batch item: u, x packed, partials per item
+  u += y * n;
+  x += y * n;
+  partial += y * nparts;
   double s = 0.0;
   for (int i = threadIdx.x; i < nparts; i += kOptThreads) s += partial[i];
   s = block_sum_f64(s, red);
@@ -151,9 +173,11 @@ __global__ __launch_bounds__(kOptThreads) void scale_from_f32_kernel(const float
 
 // p = p * decay - coef * x  (x fp32 in the parameter's layout)
 template <typename T>
-__global__ __launch_bounds__(kOptThreads) void muon_update_kernel(T* __restrict__ p,
+__global__ __launch_bounds__(kOptThreads) void muon_update_kernel(T* __restrict__ p, size_t ps,
                                                                   const float* __restrict__ x,
                                                                   size_t n, float decay, float coef) {
+  p += blockIdx.y * ps;                          // batch item: p at stride ps, x packed
+  x += blockIdx.y * n;
   for (size_t i = blockIdx.x * (size_t)kOptThreads + threadIdx.x; i < n;
        i += (size_t)gridDim.x * kOptThreads)
     p[i] = from_f32<T>(to_f32(p[i]) * decay - coef * x[i]);
@@ -169,6 +193,8 @@ int grid_for(size_t n, int cap = 4096) {
 hipError_t grad_norm(const float* grads, const OptRanges& rg, double* partial, float max_norm,
                      float* norm_scale, hipStream_t s) {
   if (rg.n <= 0 || rg.n > kOptMaxRanges) return hipErrorInvalidValue;
+  for (int i = 0; i < rg.n; ++i)
+    if (rg.off[i] % 4 || rg.cnt[i] % 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL(sumsq_ranges_kernel, dim3(kNormBlocksPerRange, rg.n), dim3(kOptThreads), 0, s,
                      grads, rg, partial);
   hipLaunchKernelGGL(norm_finish_kernel, dim3(1), dim3(kOptThreads), 0, s, partial,
@@ -187,21 +213,23 @@ hipError_t adamw(DType t, void* p, const float* g, float* m, float* v, size_t n,
   return hipGetLastError();
 }
 
-hipError_t muon_momentum(const float* g, float* buf, float* u, size_t n, float mu,
-                         const float* norm_scale, double* partial, hipStream_t s) {
-  hipLaunchKernelGGL(muon_momentum_kernel, dim3(kMuonParts), dim3(kOptThreads), 0, s, g, buf, u, n,
-                     mu, norm_scale, partial);
+hipError_t muon_momentum(const float* g, float* buf, size_t gs, float* u, size_t n, int items,
+                         float mu, const float* norm_scale, double* partial, hipStream_t s) {
+  if (n % 4 || gs % 4 || items < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(muon_momentum_kernel, dim3(kMuonParts, items), dim3(kOptThreads), 0, s, g, buf,
+                     gs, u, n, mu, norm_scale, partial);
   return hipGetLastError();
 }
 
-hipError_t muon_normalize(DType t, const float* u, size_t n, const double* partial, void* x,
-                          hipStream_t s) {
+hipError_t muon_normalize(DType t, const float* u, size_t n, int items, const double* partial,
+                          void* x, hipStream_t s) {
+  const dim3 grid(grid_for(n, 1024), items);
   if (t == DType::BF16)
-    hipLaunchKernelGGL(muon_normalize_kernel<bf16>, dim3(grid_for(n)), dim3(kOptThreads), 0, s, u, n,
-                       partial, kMuonParts, static_cast<bf16*>(x));
+    hipLaunchKernelGGL(muon_normalize_kernel<bf16>, grid, dim3(kOptThreads), 0, s, u, n, partial,
+                       kMuonParts, static_cast<bf16*>(x));
   else
-    hipLaunchKernelGGL(muon_normalize_kernel<float>, dim3(grid_for(n)), dim3(kOptThreads), 0, s, u,
-                       n, partial, kMuonParts, static_cast<float*>(x));
+    hipLaunchKernelGGL(muon_normalize_kernel<float>, grid, dim3(kOptThreads), 0, s, u, n, partial,
+                       kMuonParts, static_cast<float*>(x));
   return hipGetLastError();
 }
 
@@ -225,14 +253,15 @@ hipError_t scale_from_f32(DType t, const float* x, size_t n, float alpha, void* 
   return hipGetLastError();
 }
 
-hipError_t muon_update(DType t, void* p, const float* x, size_t n, float decay, float coef,
-                       hipStream_t s) {
+hipError_t muon_update(DType t, void* p, size_t ps, const float* x, size_t n, int items, float decay,
+                       float coef, hipStream_t s) {
+  const dim3 grid(grid_for(n, 1024), items);
   if (t == DType::BF16)
-    hipLaunchKernelGGL(muon_update_kernel<bf16>, dim3(grid_for(n)), dim3(kOptThreads), 0, s,
-                       static_cast<bf16*>(p), x, n, decay, coef);
+    hipLaunchKernelGGL(muon_update_kernel<bf16>, grid, dim3(kOptThreads), 0, s,
+                       static_cast<bf16*>(p), ps, x, n, decay, coef);
   else
-    hipLaunchKernelGGL(muon_update_kernel<float>, dim3(grid_for(n)), dim3(kOptThreads), 0, s,
-                       static_cast<float*>(p), x, n, decay, coef);
+    hipLaunchKernelGGL(muon_update_kernel<float>, grid, dim3(kOptThreads), 0, s,
+                       static_cast<float*>(p), ps, x, n, decay, coef);
   return hipGetLastError();
 }
 

@@ -28,6 +28,8 @@ struct GemmArgs {
   int lda, ldb, ldc, ldc2;
   int splits;        // K slices (PartialF32 only); K % (splits * 64) == 0
   int tile;          // output tile edge: 0 = choose, 128 or 256 (256: bf16 only)
+  int batch;         // independent products of this shape (0 or 1: one)
+  int64_t sa, sb, sc;  // element strides between batch items of A, B and C (C2 is not batched)
 };
 // compute units of the current device (256 when it cannot be queried)
 int device_cus();
@@ -118,18 +120,20 @@ hipError_t grad_norm(const float* grads, const OptRanges& rg, double* partial, f
 // AdamW on n elements; the gradient is scaled by norm_scale[1]
 hipError_t adamw(DType t, void* p, const float* g, float* m, float* v, size_t n, const AdamWArgs& a,
                  const float* norm_scale, hipStream_t s);
-// buf = mu buf + s g, u = s g + mu buf (s = norm_scale[1]); kMuonParts fp64 partials of ||u||^2
-hipError_t muon_momentum(const float* g, float* buf, float* u, size_t n, float mu,
-                         const float* norm_scale, double* partial, hipStream_t s);
-// x (T) = u / (||u||_F + 1e-7)
-hipError_t muon_normalize(DType t, const float* u, size_t n, const double* partial, void* x,
-                          hipStream_t s);
+// For `items` matrices of n elements (g and buf at stride gs, u packed):
+// buf = mu buf + s g, u = s g + mu buf (s = norm_scale[1]); kMuonParts fp64
+// partials of ||u||^2 per item. n and gs are multiples of 4.
+hipError_t muon_momentum(const float* g, float* buf, size_t gs, float* u, size_t n, int items,
+                         float mu, const float* norm_scale, double* partial, hipStream_t s);
+// x (T) = u / (||u||_F + 1e-7), per item (u, x packed)
+hipError_t muon_normalize(DType t, const float* u, size_t n, int items, const double* partial,
+                          void* x, hipStream_t s);
 // y (fp32) = alpha * x (T);  y (T) = alpha * x (fp32)
 hipError_t scale_to_f32(DType t, const void* x, size_t n, float alpha, float* y, hipStream_t s);
 hipError_t scale_from_f32(DType t, const float* x, size_t n, float alpha, void* y, hipStream_t s);
-// p (T) = p * decay - coef * x (fp32)
-hipError_t muon_update(DType t, void* p, const float* x, size_t n, float decay, float coef,
-                       hipStream_t s);
+// p (T) = p * decay - coef * x (fp32), per item (p at stride ps, x packed)
+hipError_t muon_update(DType t, void* p, size_t ps, const float* x, size_t n, int items, float decay,
+                       float coef, hipStream_t s);
 // ---- init and utilities -----------------------------------------------------
 struct InitSeg {
   size_t begin, end;   // element range [begin, end)

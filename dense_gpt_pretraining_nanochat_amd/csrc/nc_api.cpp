@@ -519,6 +519,8 @@ struct OptPlan {
   uint64_t total;
 };
 
+// Muon runs each matrix kind (Wqkv, Wo, Wfc, Wpr) for all layers at once,
+// so its buffers hold `depth` matrices of the largest kind.
 OptPlan opt_plan_of(const Dims& D) {
   OptPlan P{};
   uint64_t off = 0;
@@ -527,11 +529,11 @@ OptPlan opt_plan_of(const Dims& D) {
     off = align_up(off + bytes, kAlign);
     return o;
   };
-  const uint64_t big = (uint64_t)D.F * D.d;     // largest block matrix (Wfc, Wpr)
-  const uint64_t sq = (uint64_t)D.d * D.d;      // r x r with r = d, the short side of every one
+  const uint64_t big = (uint64_t)D.L * D.F * D.d;    // all layers' Wfc (or Wpr)
+  const uint64_t sq = (uint64_t)D.L * D.d * D.d;     // r x r per layer, r = d (every short side)
   P.norm_partial = take(sizeof(double) * nc::kOptMaxRanges * nc::kNormBlocksPerRange);
   P.norm_scale = take(4 * sizeof(float));
-  P.muon_partial = take(sizeof(double) * nc::kMuonParts);
+  P.muon_partial = take(sizeof(double) * nc::kMuonParts * D.L);
   P.u = take(4 * big);
   P.x0 = take(D.esz * big);
   P.x = take(D.esz * big);
@@ -556,8 +558,10 @@ int validate_optim(const nc_optim_config* o) {
   return NC_OK;
 }
 
-hipError_t gemm_args(DType dt, bool ak, bool bk, Epi epi, const void* A, const void* B, void* C,
-                     int M, int N, int K, int lda, int ldb, int ldc, hipStream_t s) {
+// `batch` products of one shape, items at strides sa, sb, sc (elements)
+hipError_t gemm_batched(DType dt, bool ak, bool bk, Epi epi, const void* A, const void* B, void* C,
+                        int M, int N, int K, int lda, int ldb, int ldc, int batch, int64_t sa,
+                        int64_t sb, int64_t sc, hipStream_t s) {
   nc::GemmArgs g{};
   g.A = A;
   g.B = B;
@@ -569,13 +573,20 @@ hipError_t gemm_args(DType dt, bool ak, bool bk, Epi epi, const void* A, const v
   g.ldb = ldb;
   g.ldc = ldc;
   g.splits = 1;
+  g.batch = batch;
+  g.sa = sa;
+  g.sb = sb;
+  g.sc = sc;
   return nc::gemm(dt, ak, bk, epi, g, s);
 }
 
-// One Muon step on the [R, C] matrix p (gradient g, momentum buf).
-int muon_matrix(const Dims& D, const OptPlan& P, void* ows, const nc_optim_config* o, void* p,
-                const float* g, float* buf, int R, int C, hipStream_t s) {
+// One Muon step on every layer's [R, C] matrix of one kind: params, grads and
+// momentum of layer l sit at element offset first + l * stride.
+int muon_kind(const Dims& D, const OptPlan& P, void* ows, const nc_optim_config* o, void* params,
+              const float* grads, float* m1, uint64_t first, uint64_t stride, int R, int C,
+              hipStream_t s) {
   const DType dt = D.dt;
+  const int L = D.L;
   const size_t n = (size_t)R * C;
   const bool tall = R > C;
   const int r = tall ? C : R, c = tall ? R : C;   // the iteration runs on X [r, c], r <= c
@@ -584,42 +595,46 @@ int muon_matrix(const Dims& D, const OptPlan& P, void* ows, const nc_optim_confi
   float* u = at<float>(ows, P.u);
   float* df = at<float>(ows, P.df);
   float* xf = at<float>(ows, P.xf);
+  void* p = static_cast<char*>(params) + first * D.esz;
   const float decay = 1.0f - o->lr_muon * o->wd_muon;
   const float scale = std::sqrt(std::max(1.0f, (float)R / (float)C));
-  HIPCHECK(nc::muon_momentum(g, buf, u, n, o->momentum, norm_scale, mpart, s));
+  HIPCHECK(nc::muon_momentum(grads + first, m1 + first, stride, u, n, L, o->momentum, norm_scale,
+                             mpart, s));
   if (o->ns_steps == 0) {
-    HIPCHECK(nc::muon_normalize(DType::F32, u, n, mpart, xf, s));
-    HIPCHECK(nc::muon_update(dt, p, xf, n, decay, o->lr_muon * scale, s));
+    HIPCHECK(nc::muon_normalize(DType::F32, u, n, L, mpart, xf, s));
+    HIPCHECK(nc::muon_update(dt, p, stride, xf, n, L, decay, o->lr_muon * scale, s));
     return NC_OK;
   }
-  void* x0 = at<char>(ows, P.x0);
-  HIPCHECK(nc::muon_normalize(dt, u, n, mpart, x0, s));
-  void* X = x0;
+  char* x0 = at<char>(ows, P.x0);
+  HIPCHECK(nc::muon_normalize(dt, u, n, L, mpart, x0, s));
+  char* X = x0;
   if (tall) {
     X = at<char>(ows, P.x);
-    HIPCHECK(nc::transpose(dt, x0, R, C, C, X, R, s));
+    for (int l = 0; l < L; ++l)
+      HIPCHECK(nc::transpose(dt, x0 + l * n * D.esz, R, C, C, X + l * n * D.esz, R, s));
   }
   void* A = at<char>(ows, P.a);
   float* cf = at<float>(ows, P.cf);
   void* bt = at<char>(ows, P.bt);
-  const size_t rr = (size_t)r * r, rc = (size_t)r * c;
+  const int64_t rr = (int64_t)r * r, rc = (int64_t)r * c;
   for (int k = 0; k < o->ns_steps; ++k) {
     // A = X X^T;  cf = (b/c) A + A A^T (= (b A + c A^2) / c, A symmetric)
-    HIPCHECK(gemm_args(dt, true, true, Epi::StoreT, X, X, A, r, r, c, c, c, r, s));
-    HIPCHECK(nc::scale_to_f32(dt, A, rr, kNsB / kNsC, cf, s));
-    HIPCHECK(gemm_args(dt, true, true, Epi::AddF32, A, A, cf, r, r, r, r, r, r, s));
-    HIPCHECK(nc::scale_from_f32(dt, cf, rr, 1.0f, bt, s));
+    HIPCHECK(gemm_batched(dt, true, true, Epi::StoreT, X, X, A, r, r, c, c, c, r, L, rc, rc, rr, s));
+    HIPCHECK(nc::scale_to_f32(dt, A, rr * L, kNsB / kNsC, cf, s));
+    HIPCHECK(gemm_batched(dt, true, true, Epi::AddF32, A, A, cf, r, r, r, r, r, r, L, rr, rr, rr, s));
+    HIPCHECK(nc::scale_from_f32(dt, cf, rr * L, 1.0f, bt, s));
     // df = (a/c) X + cf X, so that the next iterate is c * df
-    HIPCHECK(nc::scale_to_f32(dt, X, rc, kNsA / kNsC, df, s));
-    HIPCHECK(gemm_args(dt, true, false, Epi::AddF32, bt, X, df, r, c, r, r, c, c, s));
-    if (k + 1 < o->ns_steps) HIPCHECK(nc::scale_from_f32(dt, df, rc, kNsC, X, s));
+    HIPCHECK(nc::scale_to_f32(dt, X, rc * L, kNsA / kNsC, df, s));
+    HIPCHECK(gemm_batched(dt, true, false, Epi::AddF32, bt, X, df, r, c, r, r, c, c, L, rr, rc, rc, s));
+    if (k + 1 < o->ns_steps) HIPCHECK(nc::scale_from_f32(dt, df, rc * L, kNsC, X, s));
   }
   const float* fin = df;
   if (tall) {
-    HIPCHECK(nc::transpose(DType::F32, df, r, c, c, xf, r, s));
+    for (int l = 0; l < L; ++l)
+      HIPCHECK(nc::transpose(DType::F32, df + l * n, r, c, c, xf + l * n, r, s));
     fin = xf;
   }
-  HIPCHECK(nc::muon_update(dt, p, fin, n, decay, o->lr_muon * scale * kNsC, s));
+  HIPCHECK(nc::muon_update(dt, p, stride, fin, n, L, decay, o->lr_muon * scale * kNsC, s));
   return NC_OK;
 }
 
@@ -680,16 +695,20 @@ int nc_optimizer_step(const nc_config* cfg, const nc_optim_config* optim, void* 
   aa.decay = 1.0f - optim->lr_adamw * optim->wd_adamw;
   aa.bc1 = (float)(1.0 / (1.0 - std::pow((double)optim->beta1, (double)optim->step)));
   aa.bc2 = (float)(1.0 / (1.0 - std::pow((double)optim->beta2, (double)optim->step)));
-  for (const auto& t : lay) {
+  for (const auto& t : lay) {                            // E and U: AdamW
+    if (t.layer >= 0) continue;
     void* p = static_cast<char*>(params) + t.offset * D.esz;
-    const float* g = grads + t.offset;
-    const size_t n = (size_t)(t.rows * t.cols);
-    if (t.layer < 0) {                                   // E or U: AdamW
-      HIPCHECK(nc::adamw(D.dt, p, g, m1 + t.offset, m2 + t.offset, n, aa, norm_scale, s));
-    } else {                                             // block matrices: Muon
-      rc = muon_matrix(D, P, ows, optim, p, g, m1 + t.offset, (int)t.rows, (int)t.cols, s);
-      if (rc) return rc;
-    }
+    HIPCHECK(nc::adamw(D.dt, p, grads + t.offset, m1 + t.offset, m2 + t.offset,
+                       (size_t)(t.rows * t.cols), aa, norm_scale, s));
+  }
+  // block matrices: Muon, one kind (same shape in every layer) at a time
+  const uint64_t stride = D.L > 1 ? lay[1 + 4].offset - lay[1].offset : 0;
+  for (int k = 0; k < 4; ++k) {
+    const auto& t = lay[1 + k];
+    for (int l = 1; l < D.L; ++l)
+      if (lay[1 + 4 * l + k].offset != t.offset + l * stride) return NC_ERR_UNSUPPORTED;
+    rc = muon_kind(D, P, ows, optim, params, grads, m1, t.offset, stride, (int)t.rows, (int)t.cols, s);
+    if (rc) return rc;
   }
   return NC_OK;
 }

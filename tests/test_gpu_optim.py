@@ -153,3 +153,29 @@ def test_optimizer_is_deterministic():
     b = _run_steps("C2", OC, nsteps=1)
     assert np.array_equal(a[4][0], b[4][0])
     assert a[6] == b[6]
+
+
+def test_optimizer_step_depth12_bf16():
+    """d = 768 with 12 layers: the batched Newton-Schulz products B X
+    (768 x 3072 per layer, 12 layers) take the 256-tile kernel."""
+    depth, V = 12, 1024
+    cfg = nc.nc_config_from_depth(depth, V, 64, 1, "bf16")
+    ocfg = oracle.OracleConfig(depth=depth, vocab=V, seq_len=64, batch=1)
+    n = oracle.param_count(ocfg, padded=True)
+    flat = inputs.make_params(oracle.layout(ocfg), n, 4242, "bf16", depth)
+    p0 = inputs.as_float64(flat, "bf16")
+    step = nc.Step(cfg)
+    step.params.copy_(torch.from_numpy(flat.view(np.int16)).view(torch.bfloat16).cuda())
+    g = _grads(ocfg, n, 77)
+    kw = dict(OC, max_grad_norm=0.0)            # clipping disabled
+    po, _, _, onorm = ooptim.optimizer_step(ocfg, ooptim.OptimConfig(**kw), p0, g, np.zeros(n),
+                                            np.zeros(n), 1)
+    step.grads.copy_(torch.from_numpy(g.astype(np.float32)).cuda())
+    o = nc.nc_optim_config(kw["lr_adamw"], kw["beta1"], kw["beta2"], kw["eps"], kw["wd_adamw"],
+                           kw["lr_muon"], kw["momentum"], kw["wd_muon"], kw["max_grad_norm"], 5, 1)
+    gn = float(step.optimizer_step(o).item())
+    pg = host64(step.params)
+    assert abs(gn - onorm) <= 1e-5 * onorm
+    for tname, off, r, cc in oracle.layout(ocfg):
+        sl = slice(off, off + r * cc)
+        check_bf16(pg[sl] - p0[sl], po[sl] - p0[sl], tname)
