@@ -48,6 +48,8 @@ def _args():
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
     ap.add_argument("--no-optimizer", action="store_true",
                     help="skip the separate timing of the optimizer step")
+    ap.add_argument("--optimizer-only", action="store_true",
+                    help="time only optimizer steps on a seeded synthetic gradient (for traces)")
     ap.add_argument("--kernel-only", action="store_true",
                     help="launch only the roofline kernel (3x) and a 1 GiB device copy (3x)")
     return ap.parse_args()
@@ -147,6 +149,24 @@ def optimizer_timing(step, nc, torch, c, reps=5):
                     "not part of the timed training step"}
 
 
+def optimizer_only(a):
+    """Optimizer steps alone at the workload's shape: parameters from
+    nc_init_params, a seeded normal gradient, 2 untimed + --steps timed."""
+    import torch
+
+    import dense_gpt_pretraining_nanochat_amd as nc
+    from dense_gpt_pretraining_nanochat_amd.config import PRESETS, SEEDS
+    c = PRESETS[a.workload]
+    cfg = nc.nc_config_from_depth(c.depth, c.vocab_size, c.seq_len, c.batch, c.dtype)
+    step = nc.Step(cfg)
+    step.init(SEEDS[a.workload][0])
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    step.grads.normal_(0.0, 1e-3, generator=gen)
+    t = optimizer_timing(step, nc, torch, c, reps=a.steps)
+    print(json.dumps({"optimizer_only": a.workload, **t}), flush=True)
+
+
 def kernel_only(a):
     """Three launches of the roofline kernel at the workload's shape, then three
     1 GiB device-to-device copies (the counter calibration), nothing else."""
@@ -211,6 +231,9 @@ def main():
         sys.exit(2)
     if a.kernel_only:
         kernel_only(a)
+        return
+    if a.optimizer_only:
+        optimizer_only(a)
         return
     import numpy as np
     import torch
