@@ -73,6 +73,10 @@ _SIGS = {
     "nc_forward_loss": [_CFG, _P, _P, _P, _P, _U64, _P, _P],
     "nc_forward_backward": [_CFG, _P, _P, _P, _P, _P, _U64, _P, _P],
     "nc_forward_backward_accumulate": [_CFG, _P, _P, _P, _P, _P, _U64, _P, _P],
+    "nc_kv_cache_bytes": [_CFG, _I32, ctypes.POINTER(_U64)],
+    "nc_infer_workspace_bytes": [_CFG, _I32, ctypes.POINTER(_U64)],
+    "nc_prefill": [_CFG, _P, _P, _I32, _P, _I32, _P, _U64, _P, _P],
+    "nc_decode_step": [_CFG, _P, _P, _I32, _P, _I32, _P, _U64, _P, _P],
     "nc_optimizer_state_bytes": [_CFG, ctypes.POINTER(_U64)],
     "nc_optimizer_workspace_bytes": [_CFG, ctypes.POINTER(_U64)],
     "nc_optimizer_step": [_CFG, ctypes.POINTER(NcOptimConfig), _P, _P, _P, _P, _U64, _P, _P],
@@ -232,6 +236,31 @@ def nc_optimizer_step(cfg, optim, params, grads, state, ows, grad_norm, stream=N
                                    _ptr(grad_norm), _stream(stream)), "nc_optimizer_step")
 
 
+def nc_kv_cache_bytes(cfg, max_seq) -> int:
+    n = _U64()
+    _check(lib().nc_kv_cache_bytes(ctypes.byref(cfg), max_seq, ctypes.byref(n)), "nc_kv_cache_bytes")
+    return n.value
+
+
+def nc_infer_workspace_bytes(cfg, max_seq) -> int:
+    n = _U64()
+    _check(lib().nc_infer_workspace_bytes(ctypes.byref(cfg), max_seq, ctypes.byref(n)),
+           "nc_infer_workspace_bytes")
+    return n.value
+
+
+def nc_prefill(cfg, params, tokens, T0, kv, max_seq, ws, logits, stream=None):
+    _check(lib().nc_prefill(ctypes.byref(cfg), _ptr(params), _ptr(tokens), T0, _ptr(kv), max_seq,
+                            _ptr(ws), ws.numel() * ws.element_size(), _ptr(logits), _stream(stream)),
+           "nc_prefill")
+
+
+def nc_decode_step(cfg, params, tokens, pos, kv, max_seq, ws, logits, stream=None):
+    _check(lib().nc_decode_step(ctypes.byref(cfg), _ptr(params), _ptr(tokens), pos, _ptr(kv), max_seq,
+                                _ptr(ws), ws.numel() * ws.element_size(), _ptr(logits),
+                                _stream(stream)), "nc_decode_step")
+
+
 def nc_read_device_status(ws, stream=None) -> int:
     f = ctypes.c_uint32()
     _check(lib().nc_read_device_status(_ptr(ws), ctypes.byref(f), _stream(stream)),
@@ -301,6 +330,41 @@ def nc_op_softcap_ce(dtype, logits, targets, R, V, cap, w, loss_rows, dlogits, s
 
 
 # ---------------------------------------------------------------- buffers
+
+class Decoder:
+    """Device buffers for KV-cache inference with ``cfg.batch`` sequences of
+    up to ``max_seq`` positions: the cache, scratch and the [batch, V] fp32
+    logits. ``params`` is a parameter buffer in the training layout (for
+    example a Step's)."""
+
+    def __init__(self, cfg: NcConfig, params, max_seq: int, device="cuda"):
+        import torch
+        self.cfg, self.params, self.max_seq = cfg, params, max_seq
+        self.device = torch.device(device)
+        self.kv = torch.zeros(nc_kv_cache_bytes(cfg, max_seq), dtype=torch.uint8, device=self.device)
+        self.ws = torch.empty(nc_infer_workspace_bytes(cfg, max_seq), dtype=torch.uint8,
+                              device=self.device)
+        self.logits = torch.zeros(cfg.batch, cfg.vocab_size, dtype=torch.float32, device=self.device)
+        self.pos = 0
+
+    def prefill(self, tokens):
+        """tokens: int32 device tensor [batch, T0]; returns the logits of the
+        last prompt position."""
+        T0 = int(tokens.shape[1])
+        nc_prefill(self.cfg, self.params, tokens, T0, self.kv, self.max_seq, self.ws, self.logits)
+        self.pos = T0
+        return self.logits
+
+    def step(self, tokens):
+        """tokens: int32 device tensor [batch] at the next position."""
+        nc_decode_step(self.cfg, self.params, tokens, self.pos, self.kv, self.max_seq, self.ws,
+                       self.logits)
+        self.pos += 1
+        return self.logits
+
+    def status(self):
+        return nc_read_device_status(self.ws)
+
 
 class Step:
     """Owns the torch-allocated device buffers of one training-step shape and

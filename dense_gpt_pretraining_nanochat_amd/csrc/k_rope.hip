@@ -18,12 +18,13 @@ namespace {
 
 constexpr int kHalf = 64;   // head_dim / 2
 
-__global__ void rope_table_kernel(int T, int half, double base, float* __restrict__ cs) {
+// rows t = 0..T-1 of the table hold position t0 + t
+__global__ void rope_table_kernel(int T, int t0, int half, double base, float* __restrict__ cs) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= T * half) return;
   const int t = i / half, j = i % half;
   const double inv_freq = pow(base, -2.0 * j / (2.0 * half));
-  const double th = (double)t * inv_freq;
+  const double th = (double)(t0 + t) * inv_freq;
   cs[i] = (float)cos(th);
   cs[(size_t)T * half + i] = (float)sin(th);
 }
@@ -123,9 +124,10 @@ __global__ __launch_bounds__(256) void rope_qknorm_bwd_kernel(T* __restrict__ dq
 
 }  // namespace
 
-hipError_t rope_table(int T, int half, double base, float* cs, hipStream_t s) {
+hipError_t rope_table(int T, int half, double base, float* cs, hipStream_t s, int t0) {
   const int n = T * half;
-  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, T, half, base, cs);
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, T, t0, half, base,
+                     cs);
   return hipGetLastError();
 }
 

@@ -72,7 +72,8 @@ hipError_t embed_bwd(DType t, const void* E, const int32_t* tok, const float* ri
                      bool accumulate, hipStream_t s);
 
 // ---- rotary + QK-norm -------------------------------------------------------
-hipError_t rope_table(int T, int half, double base, float* cs, hipStream_t s);  // [T, half] cos, then sin
+// [T, half] cos, then sin, of positions t0 .. t0 + T - 1
+hipError_t rope_table(int T, int half, double base, float* cs, hipStream_t s, int t0 = 0);
 // in place on qkv[M, ldq]: H query heads at cols [0, H*128), the key head at [H*128, H*128+128)
 hipError_t rope_qknorm_fwd(DType t, void* qkv, int ldq, int M, int T, int H, const float* cs,
                            float eps, float* rinv_qk, hipStream_t s);
@@ -99,6 +100,22 @@ hipError_t softcap_ce(DType t, const void* logits, const int32_t* tgt, int R, in
                       float w, float* loss_rows, void* dlogits, uint32_t* status, hipStream_t s);
 hipError_t loss_mean(const float* loss_rows, int M, float* out, uint32_t* status, hipStream_t s);
 
+// ---- inference: KV cache, decode attention ---------------------------------------
+// Cache of one layer: [B][max_seq][256] of T (k-hat then v, 128 each).
+// Copies k-hat and v of M rows of qkv (row m = b * Tseq + t) to positions pos0 + t.
+hipError_t kv_store(DType t, const void* qkv, int ldq, int H, int M, int Tseq, int pos0, void* cache,
+                    int max_seq, hipStream_t s);
+// Attention of one new query row per batch row b (q-hat in qkv row b) over
+// cache positions 0..pos: chunks of 64 keys give fp32 partial sum_u p v and
+// sum_u p (p shifted by the fixed score bound), combined in chunk order into
+// o[b, H*128] (T). part holds B * ceil((pos+1)/64) * H * 129 floats.
+hipError_t decode_attn(DType t, const void* qkv, int ldq, int B, int H, const void* cache,
+                       int max_seq, int pos, float* part, void* o, int ldo, hipStream_t s);
+// dst[r, :] = src[(r + 1) * stride - 1, :] for r < rows, 0 for rows <= r < rows_pad (T, width d)
+hipError_t gather_last_rows(DType t, const void* src, int stride, int rows, int rows_pad, int d,
+                            void* dst, hipStream_t s);
+// out[r, v] = c * tanh(in[r, v] / c), fp32, r < rows
+hipError_t softcap_rows(const float* in, int rows, int V, float cap, float* out, hipStream_t s);
 // ---- optimizer step -------------------------------------------------------------
 constexpr int kOptMaxRanges = 160;        // tensors of one parameter buffer, at most
 constexpr int kNormBlocksPerRange = 64;   // fixed grid: the norm is bitwise reproducible

@@ -713,6 +713,199 @@ int nc_optimizer_step(const nc_config* cfg, const nc_optim_config* optim, void* 
   return NC_OK;
 }
 
+// ---------------------------------------------------------------- inference
+
+namespace {
+
+struct InferPlan {
+  uint64_t status, cs, x, rinv, h, qkv, rqk, o, lse, h2, a, xf, last, logits, part;
+  uint64_t total;
+};
+
+int pad16(int v) { return (v + 15) / 16 * 16; }
+
+// Rows: the longest prompt (batch x seq_len) or the padded decode batch,
+// whichever is larger; the status word comes first, as in the step workspace.
+InferPlan infer_plan_of(const Dims& D, int max_seq) {
+  InferPlan P{};
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t o = off;
+    off = align_up(off + std::max<uint64_t>(bytes, 1), kAlign);
+    return o;
+  };
+  const uint64_t Bp = (uint64_t)pad16(D.B);
+  const uint64_t R = std::max<uint64_t>((uint64_t)D.M, Bp), e = D.esz;
+  P.status = take(256);
+  P.cs = take((uint64_t)D.T * 64 * 2 * 4);
+  P.x = take(R * D.d * 4);
+  P.rinv = take(R * 4);
+  P.h = take(R * D.d * e);
+  P.qkv = take(R * D.Q * e);
+  P.rqk = take(R * (D.H + 1) * 4);
+  P.o = take(R * D.d * e);
+  P.lse = take((uint64_t)D.B * D.H * D.T * 4);
+  P.h2 = take(R * D.d * e);
+  P.a = take(R * D.F * e);
+  P.xf = take(R * D.d * e);
+  P.last = take(Bp * D.d * e);
+  P.logits = take(Bp * D.V * 4);
+  const uint64_t nch = ((uint64_t)max_seq + 63) / 64;
+  P.part = take((uint64_t)D.B * nch * D.H * 129 * 4);
+  P.total = off;
+  return P;
+}
+
+uint64_t kv_layer_bytes(const Dims& D, int max_seq) {
+  return (uint64_t)D.B * max_seq * 256 * D.esz;
+}
+
+// The blocks over M rows (prefill: the prompt, B x Tseq rows; decode: the
+// padded batch, one row per sequence), storing k-hat and v of the first
+// kv_rows rows at cache positions pos0 + t. cs holds the rotary table of
+// positions pos0 .. pos0 + Tseq - 1.
+int infer_blocks(const Dims& D, const nc_config* cfg, const std::vector<Tensor>& lay,
+                 const void* params, void* ws, const InferPlan& P, int64_t M, int kv_rows, int Tseq,
+                 int pos0, bool prefill, void* kv, int max_seq, hipStream_t s) {
+  const DType dt = D.dt;
+  const float eps = cfg->rms_eps;
+  auto W = [&](int idx) { return static_cast<const char*>(params) + lay[idx].offset * D.esz; };
+  float* x = at<float>(ws, P.x);
+  float* rinv = at<float>(ws, P.rinv);
+  void* h = at<char>(ws, P.h);
+  void* qkv = at<char>(ws, P.qkv);
+  void* o = at<char>(ws, P.o);
+  void* h2 = at<char>(ws, P.h2);
+  void* a = at<char>(ws, P.a);
+  const float* cs = at<float>(ws, P.cs);
+  for (int l = 0; l < D.L; ++l) {
+    const int base = 1 + 4 * l;
+    void* cache = static_cast<char*>(kv) + (uint64_t)l * kv_layer_bytes(D, max_seq);
+    HIPCHECK(nc::rmsnorm_fwd(dt, x, (int)M, D.d, eps, h, rinv, s));
+    HIPCHECK(gemm_simple(dt, true, true, Epi::StoreT, h, W(base + 0), qkv, nullptr, M, D.Q, D.d,
+                         D.d, D.d, D.Q, 0, s));
+    HIPCHECK(nc::rope_qknorm_fwd(dt, qkv, D.Q, kv_rows, Tseq, D.H, cs, eps, at<float>(ws, P.rqk), s));
+    HIPCHECK(nc::kv_store(dt, qkv, D.Q, D.H, kv_rows, Tseq, pos0, cache, max_seq, s));
+    if (prefill)
+      HIPCHECK(nc::attn_fwd(dt, qkv, D.Q, D.B, Tseq, D.H, o, at<float>(ws, P.lse), s));
+    else
+      HIPCHECK(nc::decode_attn(dt, qkv, D.Q, D.B, D.H, cache, max_seq, pos0, at<float>(ws, P.part), o,
+                               D.d, s));
+    HIPCHECK(gemm_simple(dt, true, true, Epi::AddF32, o, W(base + 1), x, nullptr, M, D.d, D.d, D.d,
+                         D.d, D.d, 0, s));
+    HIPCHECK(nc::rmsnorm_fwd(dt, x, (int)M, D.d, eps, h2, rinv, s));
+    HIPCHECK(gemm_simple(dt, true, true, Epi::Relu2, h2, W(base + 2), a, nullptr, M, D.F, D.d, D.d,
+                         D.d, D.F, 0, s));
+    HIPCHECK(gemm_simple(dt, true, true, Epi::AddF32, a, W(base + 3), x, nullptr, M, D.d, D.F, D.F,
+                         D.F, D.d, 0, s));
+  }
+  return NC_OK;
+}
+
+// Final norm, then the capped logits of the last row of every `stride` rows.
+int infer_logits(const Dims& D, const nc_config* cfg, const std::vector<Tensor>& lay,
+                 const void* params, void* ws, const InferPlan& P, int64_t M, int stride,
+                 float* logits_out, hipStream_t s) {
+  const DType dt = D.dt;
+  const int Bp = pad16(D.B);
+  void* xf = at<char>(ws, P.xf);
+  void* last = at<char>(ws, P.last);
+  float* lg = at<float>(ws, P.logits);
+  const char* U = static_cast<const char*>(params) + lay[1 + 4 * D.L].offset * D.esz;
+  HIPCHECK(nc::rmsnorm_fwd(dt, at<float>(ws, P.x), (int)M, D.d, cfg->rms_eps, xf, at<float>(ws, P.rinv), s));
+  HIPCHECK(nc::gather_last_rows(dt, xf, stride, D.B, Bp, D.d, last, s));
+  HIPCHECK(gemm_simple(dt, true, true, Epi::StoreF32, last, U, lg, nullptr, Bp, D.V, D.d, D.d, D.d,
+                       D.V, 0, s));
+  HIPCHECK(nc::softcap_rows(lg, D.B, D.V, cfg->softcap, logits_out, s));
+  return NC_OK;
+}
+
+int check_infer_args(const nc_config* cfg, const void* params, const void* tokens, const void* kv,
+                     int max_seq, const void* ws, const float* logits) {
+  const int rc = validate(cfg);
+  if (rc) return rc;
+  if (!params || !tokens || !kv || !ws || !logits) return NC_ERR_NULL;
+  if (misaligned(params) || misaligned(tokens) || misaligned(kv) || misaligned(ws) ||
+      misaligned(logits))
+    return NC_ERR_ALIGN;
+  if (max_seq < 1 || max_seq > (1 << 24)) return NC_ERR_ARG;
+  return NC_OK;
+}
+
+}  // namespace
+
+int nc_kv_cache_bytes(const nc_config* cfg, int32_t max_seq, uint64_t* bytes) {
+  const int rc = validate(cfg);
+  if (rc) return rc;
+  if (!bytes) return NC_ERR_NULL;
+  if (max_seq < 1 || max_seq > (1 << 24)) return NC_ERR_ARG;
+  const Dims D = dims_of(cfg);
+  *bytes = (uint64_t)D.L * kv_layer_bytes(D, max_seq);
+  return NC_OK;
+}
+
+int nc_infer_workspace_bytes(const nc_config* cfg, int32_t max_seq, uint64_t* bytes) {
+  const int rc = validate(cfg);
+  if (rc) return rc;
+  if (!bytes) return NC_ERR_NULL;
+  if (max_seq < 1 || max_seq > (1 << 24)) return NC_ERR_ARG;
+  *bytes = infer_plan_of(dims_of(cfg), max_seq).total;
+  return NC_OK;
+}
+
+int nc_prefill(const nc_config* cfg, const void* params, const int32_t* tokens, int32_t T0, void* kv,
+               int32_t max_seq, void* ws, uint64_t ws_bytes, float* logits, void* stream) {
+  int rc = check_infer_args(cfg, params, tokens, kv, max_seq, ws, logits);
+  if (rc) return rc;
+  if (T0 < 64 || T0 % 64 || T0 > cfg->seq_len || T0 > max_seq) return NC_ERR_ARG;
+  const Dims D = dims_of(cfg);
+  const InferPlan P = infer_plan_of(D, max_seq);
+  if (ws_bytes < P.total) return NC_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Dims Dp = D;
+  Dp.T = T0;
+  Dp.M = (int64_t)D.B * T0;
+  const auto lay = layout_of(D);
+  const char* E = static_cast<const char*>(params) + lay[0].offset * D.esz;
+  uint32_t* status = at<uint32_t>(ws, P.status);
+  HIPCHECK(nc::fill_zero(status, 256, s));
+  HIPCHECK(nc::rope_table(T0, 64, (double)cfg->rope_base, at<float>(ws, P.cs), s, 0));
+  HIPCHECK(nc::embed_norm_fwd(D.dt, E, tokens, (int)Dp.M, D.d, D.V, cfg->rms_eps, at<float>(ws, P.x),
+                              at<float>(ws, P.rinv), status, s));
+  rc = infer_blocks(Dp, cfg, lay, params, ws, P, Dp.M, (int)Dp.M, T0, 0, true, kv, max_seq, s);
+  if (rc) return rc;
+  return infer_logits(Dp, cfg, lay, params, ws, P, Dp.M, T0, logits, s);
+}
+
+int nc_decode_step(const nc_config* cfg, const void* params, const int32_t* tokens, int32_t pos,
+                   void* kv, int32_t max_seq, void* ws, uint64_t ws_bytes, float* logits,
+                   void* stream) {
+  int rc = check_infer_args(cfg, params, tokens, kv, max_seq, ws, logits);
+  if (rc) return rc;
+  if (pos < 0 || pos >= max_seq) return NC_ERR_ARG;
+  const Dims D = dims_of(cfg);
+  if (D.H > 16) return NC_ERR_UNSUPPORTED;
+  const InferPlan P = infer_plan_of(D, max_seq);
+  if (ws_bytes < P.total) return NC_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int Bp = pad16(D.B);
+  Dims Dd = D;
+  Dd.M = Bp;
+  const auto lay = layout_of(D);
+  const char* E = static_cast<const char*>(params) + lay[0].offset * D.esz;
+  uint32_t* status = at<uint32_t>(ws, P.status);
+  HIPCHECK(nc::fill_zero(status, 256, s));
+  HIPCHECK(nc::rope_table(1, 64, (double)cfg->rope_base, at<float>(ws, P.cs), s, pos));
+  // rows past the batch stay zero through the blocks (every row is independent)
+  HIPCHECK(nc::fill_zero(at<char>(ws, P.x), (size_t)Bp * D.d * 4, s));
+  HIPCHECK(nc::fill_zero(at<char>(ws, P.o), (size_t)Bp * D.d * D.esz, s));
+  HIPCHECK(nc::embed_norm_fwd(D.dt, E, tokens, D.B, D.d, D.V, cfg->rms_eps, at<float>(ws, P.x),
+                              at<float>(ws, P.rinv), status, s));
+  rc = infer_blocks(Dd, cfg, lay, params, ws, P, Bp, D.B, 1, pos, false, kv, max_seq, s);
+  if (rc) return rc;
+  return infer_logits(Dd, cfg, lay, params, ws, P, Bp, 1, logits, s);
+}
+
 int nc_read_device_status(const void* ws, uint32_t* flags, void* stream) {
   if (!ws || !flags) return NC_ERR_NULL;
   if (misaligned(ws)) return NC_ERR_ALIGN;

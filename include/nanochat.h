@@ -150,6 +150,42 @@ int nc_forward_backward_accumulate(const nc_config* cfg, const void* params,
                                    const int32_t* tokens, const int32_t* targets, float* grads,
                                    void* ws, uint64_t ws_bytes, float* loss_dev, void* stream);
 
+/* ---- inference with a KV cache -------------------------------------------
+ * An inference engine with a KV cache and a simple prefill / decode flow
+ * (followin.io release article, section "花半天用 100 美元訓練的模型， 打敗了
+ * GPT-2"; vnrom.net, section "Cấu trúc thư mục và module chính"). The model is
+ * the training step's; the mask is causal, so the logits a decoding step
+ * returns for position p equal the full-sequence forward's at p.
+ *
+ * Cache layout: for layer l, row b, position t, 256 values of dtype (the
+ * rotary + QK-normalised key head, then the value head) at element
+ * ((l * batch + b) * max_seq + t) * 256. cfg.batch is the number of sequences
+ * decoded together and cfg.seq_len the longest prompt nc_prefill accepts.
+ * Logits are fp32, softcapped (z = c tanh(l / c)), [batch, vocab_size]. */
+
+/* Bytes of the cache for cfg.batch sequences of up to max_seq positions. */
+int nc_kv_cache_bytes(const nc_config* cfg, int32_t max_seq, uint64_t* bytes);
+
+/* Bytes of scratch for nc_prefill (prompts up to cfg.seq_len) and
+ * nc_decode_step (caches of max_seq positions); the device status word sits
+ * where nc_read_device_status expects it. */
+int nc_infer_workspace_bytes(const nc_config* cfg, int32_t max_seq, uint64_t* bytes);
+
+/* Runs the prompt tokens [batch, T0] (int32; T0 a multiple of 64, at most
+ * cfg.seq_len and max_seq) through the model, fills cache positions 0..T0-1
+ * and writes the logits of position T0-1 of every row. */
+int nc_prefill(const nc_config* cfg, const void* params, const int32_t* tokens, int32_t T0, void* kv,
+               int32_t max_seq, void* ws, uint64_t ws_bytes, float* logits, void* stream);
+
+/* One decoding step: tokens [batch] (int32) at position pos (0 <= pos <
+ * max_seq; positions 0..pos-1 of the cache must hold the sequence so far)
+ * are run through the model, their keys and values stored at position pos,
+ * and the logits of position pos written. Attention reads cache positions
+ * 0..pos. Token ids outside [0, V) are clamped and flagged in the status. */
+int nc_decode_step(const nc_config* cfg, const void* params, const int32_t* tokens, int32_t pos,
+                   void* kv, int32_t max_seq, void* ws, uint64_t ws_bytes, float* logits,
+                   void* stream);
+
 /* ---- optimizer step --------------------------------------------------------
  * Muon for the block matrices (Wqkv, Wo, Wfc, Wpr of every layer) and AdamW
  * for the embedding E and the lm_head U (followin.io release article,

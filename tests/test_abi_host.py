@@ -152,3 +152,41 @@ def test_optimizer_sizes_and_argument_checks():
     big = nc.nc_config_from_depth(20, 65536, 2048, 32, "bf16")
     assert nc.nc_optimizer_state_bytes(big) == 2 * 4 * nc.nc_param_count(big)
     assert nc.nc_optimizer_workspace_bytes(big) > ows
+
+
+def test_inference_sizes_and_argument_checks():
+    """The cache holds 256 values (k-hat, v) per layer, sequence and position;
+    bad lengths, NULL, misaligned and short-workspace calls fail before any
+    launch."""
+    L = nc.lib()
+    cfg = _cfg("C1")
+    esz = 4
+    assert nc.nc_kv_cache_bytes(cfg, 100) == cfg.depth * cfg.batch * 100 * 256 * esz
+    big = nc.nc_config_from_depth(20, 65536, 2048, 32, "bf16")
+    assert nc.nc_kv_cache_bytes(big, 2048) == 20 * 32 * 2048 * 256 * 2
+    ws = nc.nc_infer_workspace_bytes(cfg, 256)
+    assert ws > 0 and nc.nc_infer_workspace_bytes(cfg, 4096) > ws
+    with pytest.raises(nc.NcError):
+        nc.nc_kv_cache_bytes(cfg, 0)
+    a = 1 << 20
+    p = ctypes.c_void_p
+
+    def prefill(T0=64, max_seq=256, ws_bytes=ws, tokens=p(a), kv=p(a)):
+        return L.nc_prefill(ctypes.byref(cfg), p(a), tokens, T0, kv, max_seq, p(a), ws_bytes, p(a),
+                            None)
+
+    def decode(pos=0, max_seq=256, ws_bytes=ws, kv=p(a)):
+        return L.nc_decode_step(ctypes.byref(cfg), p(a), p(a), pos, kv, max_seq, p(a), ws_bytes, p(a),
+                                None)
+
+    assert prefill(T0=32) == -7                 # not a multiple of 64
+    assert prefill(T0=128) == -7                # longer than cfg.seq_len
+    assert prefill(max_seq=32) == -7            # longer than the cache
+    assert prefill(tokens=None) == -3
+    assert prefill(kv=p(a + 4)) == -4
+    assert prefill(ws_bytes=ws - 1) == -5
+    assert decode(pos=256) == -7
+    assert decode(pos=-1) == -7
+    assert decode(max_seq=0) == -7
+    assert decode(kv=None) == -3
+    assert decode(ws_bytes=ws - 1) == -5
