@@ -2,6 +2,7 @@
 depth-20 dense GPT on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload C4] [--no-cpu-baseline]
+    python bench.py --decode-only --steps 256   # KV-cache prefill + decoding steps only
     python bench.py --kernel-only      # 3 launches of the roofline kernel + a 1 GiB copy
                                        # (for hardware-counter passes)
 
@@ -50,6 +51,10 @@ def _args():
                     help="skip the separate timing of the optimizer step")
     ap.add_argument("--optimizer-only", action="store_true",
                     help="time only optimizer steps on a seeded synthetic gradient (for traces)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only KV-cache inference: a 1024-token prefill, then decoding steps")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the separate timing of KV-cache decoding")
     ap.add_argument("--kernel-only", action="store_true",
                     help="launch only the roofline kernel (3x) and a 1 GiB device copy (3x)")
     return ap.parse_args()
@@ -149,6 +154,74 @@ def optimizer_timing(step, nc, torch, c, reps=5):
                     "not part of the timed training step"}
 
 
+def decode_bytes(c, pos):
+    """Algorithmic HBM bytes of one decoding step at position pos: every block
+    matrix and the lm_head read once, the batch's embedding rows, the cached
+    k-hat and v of positions 0..pos read and position pos written, per layer
+    and sequence (bf16)."""
+    d = 64 * c.depth
+    esz = 2 if c.dtype == "bf16" else 4
+    block = (d + 256) * d + d * d + 2 * 4 * d * d
+    weights = (c.depth * block + c.vocab_size * d) * esz
+    kv = c.depth * c.batch * (pos + 2) * 256 * esz
+    return weights + c.batch * d * esz + kv + c.batch * c.vocab_size * 4
+
+
+def decode_timing(nc, torch, c, params, T0=1024, nsteps=128):
+    """Prefill T0 tokens of every sequence, then `nsteps` decoding steps,
+    each timed as a whole with HIP events on the stream they run on."""
+    import numpy as np
+
+    from dense_gpt_pretraining_nanochat_amd import inputs
+    cfg = nc.nc_config_from_depth(c.depth, c.vocab_size, c.seq_len, c.batch, c.dtype)
+    max_seq = T0 + nsteps + 8
+    dec = nc.Decoder(cfg, params, max_seq)
+    tok, _ = inputs.make_tokens(c.vocab_size, T0 + nsteps + 8, c.batch, 4321, "zipf")
+    prompt = torch.from_numpy(np.ascontiguousarray(tok[:, :T0])).cuda()
+    cols = [torch.from_numpy(np.ascontiguousarray(tok[:, p])).cuda() for p in range(tok.shape[1])]
+    s = torch.cuda.current_stream()
+    dec.prefill(prompt)                                  # warm
+    for p in range(T0, T0 + 4):
+        dec.step(cols[p])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record(s)
+    dec.prefill(prompt)
+    ev[1].record(s)
+    for p in range(T0, T0 + nsteps):
+        dec.step(cols[p])
+    ev[2].record(s)
+    ev[2].synchronize()
+    pre_ms = ev[0].elapsed_time(ev[1])
+    dec_ms = ev[1].elapsed_time(ev[2]) / nsteps
+    status = dec.status()
+    by = sum(decode_bytes(c, p) for p in range(T0, T0 + nsteps)) / nsteps
+    return {"batch": c.batch, "prompt_tokens": T0, "decode_steps": nsteps,
+            "positions": [T0, T0 + nsteps - 1],
+            "prefill_ms": round(pre_ms, 3),
+            "prefill_tokens_per_s": round(c.batch * T0 / (pre_ms / 1e3), 1),
+            "decode_ms_per_step": round(dec_ms, 4),
+            "decode_tokens_per_s": round(c.batch / (dec_ms / 1e3), 1),
+            "decode_algorithmic_bytes_per_step": int(by),
+            "decode_hbm_frac": round(by / (dec_ms / 1e3) / (PEAK_HBM_GBS * 1e9), 4),
+            "device_status": status,
+            "what": "KV-cache inference at the training shape (bf16, cache of the whole "
+                    "context); not part of the timed training step"}
+
+
+def decode_only(a):
+    import torch
+
+    import dense_gpt_pretraining_nanochat_amd as nc
+    from dense_gpt_pretraining_nanochat_amd.config import PRESETS, SEEDS
+    c = PRESETS[a.workload]
+    cfg = nc.nc_config_from_depth(c.depth, c.vocab_size, c.seq_len, c.batch, c.dtype)
+    pdt = torch.bfloat16 if cfg.dtype == nc.NC_BF16 else torch.float32
+    params = torch.zeros(nc.nc_param_count(cfg), dtype=pdt, device="cuda")
+    nc.nc_init_params(SEEDS[a.workload][0], cfg, params)
+    t = decode_timing(nc, torch, c, params, T0=min(1024, c.seq_len), nsteps=a.steps)
+    print(json.dumps({"decode_only": a.workload, **t}), flush=True)
+
+
 def optimizer_only(a):
     """Optimizer steps alone at the workload's shape: parameters from
     nc_init_params, a seeded normal gradient, 2 untimed + --steps timed."""
@@ -235,6 +308,9 @@ def main():
     if a.optimizer_only:
         optimizer_only(a)
         return
+    if a.decode_only:
+        decode_only(a)
+        return
     import numpy as np
     import torch
 
@@ -295,6 +371,12 @@ def main():
     if not a.no_optimizer:
         out["optimizer"] = optimizer_timing(step, nc, torch, c)
         step.opt_state = step.opt_ws = None
+    if not a.no_decode:
+        params = step.params
+        step.ws = step.grads = None
+        torch.cuda.empty_cache()
+        out["decode"] = decode_timing(nc, torch, c, params, T0=min(1024, c.seq_len))
+        del params
     del step
     torch.cuda.empty_cache()
     out["roofline"] = dominant_kernel_roofline(cfg, nc, torch)

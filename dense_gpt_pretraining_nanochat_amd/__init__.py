@@ -85,6 +85,8 @@ _SIGS = {
     "nc_last_hip_error": [],
     "nc_op_gemm": [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P],
     "nc_op_wgrad": [_I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P],
+    "nc_op_few_rows_gemm": [_I32, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _I32, ctypes.c_float, _P],
+    "nc_op_decode_attn": [_I32, _P, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _I32, _P],
     "nc_op_transpose": [_I32, _P, _I32, _I32, _I32, _P, _I32, _P],
     "nc_op_rmsnorm_fwd": [_I32, _P, _I32, _I32, _F32, _P, _P, _P],
     "nc_op_rmsnorm_bwd": [_I32, _P, _P, _P, _I32, _I32, _P, _I32, _P, _P],
@@ -272,6 +274,16 @@ def nc_op_gemm(dtype, a_kcontig, b_kcontig, epilogue, A, B, C, C2, M, N, K, lda,
                stream=None):
     _check(lib().nc_op_gemm(_dt(dtype), int(a_kcontig), int(b_kcontig), epilogue, _ptr(A), _ptr(B),
                             _ptr(C), _ptr(C2), M, N, K, lda, ldb, ldc, _stream(stream)), "nc_op_gemm")
+
+
+def nc_op_few_rows_gemm(epilogue, W, ldw, X, ldx, C, ldc, M, N, K, cap=0.0, stream=None):
+    _check(lib().nc_op_few_rows_gemm(epilogue, _ptr(W), ldw, _ptr(X), ldx, _ptr(C), ldc, M, N, K, cap,
+                                     _stream(stream)), "nc_op_few_rows_gemm")
+
+
+def nc_op_decode_attn(dtype, qkv, ldq, B, H, cache, max_seq, pos, part, o, ldo, stream=None):
+    _check(lib().nc_op_decode_attn(_dt(dtype), _ptr(qkv), ldq, B, H, _ptr(cache), max_seq, pos,
+                                   _ptr(part), _ptr(o), ldo, _stream(stream)), "nc_op_decode_attn")
 
 
 def nc_op_wgrad(dtype, X1, X2, dW, partial, M, N1, N2, splits, stream=None):

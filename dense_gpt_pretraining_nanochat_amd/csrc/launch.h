@@ -111,6 +111,18 @@ hipError_t kv_store(DType t, const void* qkv, int ldq, int H, int M, int Tseq, i
 // o[b, H*128] (T). part holds B * ceil((pos+1)/64) * H * 129 floats.
 hipError_t decode_attn(DType t, const void* qkv, int ldq, int B, int H, const void* cache,
                        int max_seq, int pos, float* part, void* o, int ldo, hipStream_t s);
+// bf16 products with few rows: C[m, n] (epi) sum_k X[m, k] W[n, k] for m < M <=
+// kSkinnyMaxRows; W [N, K] and X [M, K] row-major bf16 (K-contiguous), N % 16 == 0,
+// K % 32 == 0, leading dimensions multiples of 8 (W, X) and 4 (C).
+enum class SkEpi {
+  StoreT,      // C (bf16) = acc
+  AddF32,      // C (float) += acc
+  Relu2,       // C (bf16) = relu(acc)^2
+  SoftcapF32,  // C (float) = cap * tanh(acc / cap)
+};
+constexpr int kSkinnyMaxRows = 32;
+hipError_t skinny_gemm(const void* W, int ldw, const void* X, int ldx, void* C, int ldc, int M, int N,
+                       int K, SkEpi epi, float cap, hipStream_t s);
 // dst[r, :] = src[(r + 1) * stride - 1, :] for r < rows, 0 for rows <= r < rows_pad (T, width d)
 hipError_t gather_last_rows(DType t, const void* src, int stride, int rows, int rows_pad, int d,
                             void* dst, hipStream_t s);

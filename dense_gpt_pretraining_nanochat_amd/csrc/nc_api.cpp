@@ -760,10 +760,30 @@ uint64_t kv_layer_bytes(const Dims& D, int max_seq) {
   return (uint64_t)D.B * max_seq * 256 * D.esz;
 }
 
-// The blocks over M rows (prefill: the prompt, B x Tseq rows; decode: the
-// padded batch, one row per sequence), storing k-hat and v of the first
-// kv_rows rows at cache positions pos0 + t. cs holds the rotary table of
-// positions pos0 .. pos0 + Tseq - 1.
+// Linear layer of the inference path: Y = X W^T under an epilogue, through
+// the few-row kernel when every row fits one of its workgroups (bf16 decoding)
+// and the tiled GEMM otherwise.
+hipError_t infer_linear(DType dt, Epi epi, const void* X, const void* W, void* C, int64_t M, int N, int K,
+                        int ldx, int ldc, hipStream_t s) {
+  if (dt == DType::BF16 && M <= nc::kSkinnyMaxRows) {
+    nc::SkEpi e;
+    switch (epi) {
+      case Epi::StoreT: e = nc::SkEpi::StoreT; break;
+      case Epi::AddF32: e = nc::SkEpi::AddF32; break;
+      case Epi::Relu2: e = nc::SkEpi::Relu2; break;
+      default: return hipErrorInvalidValue;
+    }
+    return nc::skinny_gemm(W, K, X, ldx, C, ldc, (int)M, N, K, e, 0.f, s);
+  }
+  return gemm_simple(dt, true, true, epi, X, W, C, nullptr, M, N, K, ldx, K, ldc, 0, s);
+}
+
+bool few_rows(const Dims& D, int64_t M) { return D.dt == DType::BF16 && M <= nc::kSkinnyMaxRows; }
+
+// The blocks over M rows (prefill: the prompt, B x Tseq rows; decode: one row
+// per sequence, padded to 16 when the tiled GEMM runs), storing k-hat and v
+// of the first kv_rows rows at cache positions pos0 + t. cs holds the rotary
+// table of positions pos0 .. pos0 + Tseq - 1.
 int infer_blocks(const Dims& D, const nc_config* cfg, const std::vector<Tensor>& lay,
                  const void* params, void* ws, const InferPlan& P, int64_t M, int kv_rows, int Tseq,
                  int pos0, bool prefill, void* kv, int max_seq, hipStream_t s) {
@@ -782,8 +802,7 @@ int infer_blocks(const Dims& D, const nc_config* cfg, const std::vector<Tensor>&
     const int base = 1 + 4 * l;
     void* cache = static_cast<char*>(kv) + (uint64_t)l * kv_layer_bytes(D, max_seq);
     HIPCHECK(nc::rmsnorm_fwd(dt, x, (int)M, D.d, eps, h, rinv, s));
-    HIPCHECK(gemm_simple(dt, true, true, Epi::StoreT, h, W(base + 0), qkv, nullptr, M, D.Q, D.d,
-                         D.d, D.d, D.Q, 0, s));
+    HIPCHECK(infer_linear(dt, Epi::StoreT, h, W(base + 0), qkv, M, D.Q, D.d, D.d, D.Q, s));
     HIPCHECK(nc::rope_qknorm_fwd(dt, qkv, D.Q, kv_rows, Tseq, D.H, cs, eps, at<float>(ws, P.rqk), s));
     HIPCHECK(nc::kv_store(dt, qkv, D.Q, D.H, kv_rows, Tseq, pos0, cache, max_seq, s));
     if (prefill)
@@ -791,13 +810,10 @@ int infer_blocks(const Dims& D, const nc_config* cfg, const std::vector<Tensor>&
     else
       HIPCHECK(nc::decode_attn(dt, qkv, D.Q, D.B, D.H, cache, max_seq, pos0, at<float>(ws, P.part), o,
                                D.d, s));
-    HIPCHECK(gemm_simple(dt, true, true, Epi::AddF32, o, W(base + 1), x, nullptr, M, D.d, D.d, D.d,
-                         D.d, D.d, 0, s));
+    HIPCHECK(infer_linear(dt, Epi::AddF32, o, W(base + 1), x, M, D.d, D.d, D.d, D.d, s));
     HIPCHECK(nc::rmsnorm_fwd(dt, x, (int)M, D.d, eps, h2, rinv, s));
-    HIPCHECK(gemm_simple(dt, true, true, Epi::Relu2, h2, W(base + 2), a, nullptr, M, D.F, D.d, D.d,
-                         D.d, D.F, 0, s));
-    HIPCHECK(gemm_simple(dt, true, true, Epi::AddF32, a, W(base + 3), x, nullptr, M, D.d, D.F, D.F,
-                         D.F, D.d, 0, s));
+    HIPCHECK(infer_linear(dt, Epi::Relu2, h2, W(base + 2), a, M, D.F, D.d, D.d, D.F, s));
+    HIPCHECK(infer_linear(dt, Epi::AddF32, a, W(base + 3), x, M, D.d, D.F, D.F, D.d, s));
   }
   return NC_OK;
 }
@@ -807,12 +823,22 @@ int infer_logits(const Dims& D, const nc_config* cfg, const std::vector<Tensor>&
                  const void* params, void* ws, const InferPlan& P, int64_t M, int stride,
                  float* logits_out, hipStream_t s) {
   const DType dt = D.dt;
-  const int Bp = pad16(D.B);
   void* xf = at<char>(ws, P.xf);
   void* last = at<char>(ws, P.last);
-  float* lg = at<float>(ws, P.logits);
   const char* U = static_cast<const char*>(params) + lay[1 + 4 * D.L].offset * D.esz;
   HIPCHECK(nc::rmsnorm_fwd(dt, at<float>(ws, P.x), (int)M, D.d, cfg->rms_eps, xf, at<float>(ws, P.rinv), s));
+  if (few_rows(D, D.B)) {
+    const void* rows = xf;
+    if (stride != 1) {
+      HIPCHECK(nc::gather_last_rows(dt, xf, stride, D.B, D.B, D.d, last, s));
+      rows = last;
+    }
+    HIPCHECK(nc::skinny_gemm(U, D.d, rows, D.d, logits_out, D.V, D.B, D.V, D.d, nc::SkEpi::SoftcapF32,
+                             cfg->softcap, s));
+    return NC_OK;
+  }
+  const int Bp = pad16(D.B);
+  float* lg = at<float>(ws, P.logits);
   HIPCHECK(nc::gather_last_rows(dt, xf, stride, D.B, Bp, D.d, last, s));
   HIPCHECK(gemm_simple(dt, true, true, Epi::StoreF32, last, U, lg, nullptr, Bp, D.V, D.d, D.d, D.d,
                        D.V, 0, s));
@@ -888,22 +914,27 @@ int nc_decode_step(const nc_config* cfg, const void* params, const int32_t* toke
   const InferPlan P = infer_plan_of(D, max_seq);
   if (ws_bytes < P.total) return NC_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int Bp = pad16(D.B);
+  // the few-row kernels take the batch as it is; the tiled GEMM wants rows in
+  // multiples of 16, and the rows past the batch stay zero through the blocks
+  // (every row is independent)
+  const bool few = few_rows(D, D.B);
+  const int Mr = few ? D.B : pad16(D.B);
   Dims Dd = D;
-  Dd.M = Bp;
+  Dd.M = Mr;
   const auto lay = layout_of(D);
   const char* E = static_cast<const char*>(params) + lay[0].offset * D.esz;
   uint32_t* status = at<uint32_t>(ws, P.status);
   HIPCHECK(nc::fill_zero(status, 256, s));
   HIPCHECK(nc::rope_table(1, 64, (double)cfg->rope_base, at<float>(ws, P.cs), s, pos));
-  // rows past the batch stay zero through the blocks (every row is independent)
-  HIPCHECK(nc::fill_zero(at<char>(ws, P.x), (size_t)Bp * D.d * 4, s));
-  HIPCHECK(nc::fill_zero(at<char>(ws, P.o), (size_t)Bp * D.d * D.esz, s));
+  if (!few) {
+    HIPCHECK(nc::fill_zero(at<char>(ws, P.x), (size_t)Mr * D.d * 4, s));
+    HIPCHECK(nc::fill_zero(at<char>(ws, P.o), (size_t)Mr * D.d * D.esz, s));
+  }
   HIPCHECK(nc::embed_norm_fwd(D.dt, E, tokens, D.B, D.d, D.V, cfg->rms_eps, at<float>(ws, P.x),
                               at<float>(ws, P.rinv), status, s));
-  rc = infer_blocks(Dd, cfg, lay, params, ws, P, Bp, D.B, 1, pos, false, kv, max_seq, s);
+  rc = infer_blocks(Dd, cfg, lay, params, ws, P, Mr, D.B, 1, pos, false, kv, max_seq, s);
   if (rc) return rc;
-  return infer_logits(Dd, cfg, lay, params, ws, P, Bp, 1, logits, s);
+  return infer_logits(Dd, cfg, lay, params, ws, P, Mr, 1, logits, s);
 }
 
 int nc_read_device_status(const void* ws, uint32_t* flags, void* stream) {
@@ -948,6 +979,32 @@ int nc_op_gemm(int32_t dtype, int32_t a_kcontig, int32_t b_kcontig, int32_t epil
   static const Epi map[5] = {Epi::StoreT, Epi::StoreF32, Epi::AddF32, Epi::Relu2, Epi::Relu2Bwd};
   HIPCHECK(gemm_simple(dt_of(dtype), a_kcontig != 0, b_kcontig != 0, map[epilogue], A, B, C, C2, M,
                        N, K, lda, ldb, ldc, ldc, static_cast<hipStream_t>(stream)));
+  return NC_OK;
+}
+
+int nc_op_few_rows_gemm(int32_t epilogue, const void* W, int32_t ldw, const void* X, int32_t ldx, void* C,
+                        int32_t ldc, int32_t M, int32_t N, int32_t K, float cap, void* stream) {
+  if (epilogue < 0 || epilogue > 3) return NC_ERR_ARG;
+  if (!W || !X || !C) return NC_ERR_NULL;
+  if (M < 1 || M > nc::kSkinnyMaxRows || N < 16 || N % 16 || K < 32 || K % 32) return NC_ERR_ARG;
+  if (ldw % 8 || ldx % 8 || ldc % 4 || ldw < K || ldx < K || ldc < N) return NC_ERR_ARG;
+  if (epilogue == 3 && !(cap > 0.f)) return NC_ERR_ARG;
+  static const nc::SkEpi map[4] = {nc::SkEpi::StoreT, nc::SkEpi::AddF32, nc::SkEpi::Relu2,
+                                   nc::SkEpi::SoftcapF32};
+  HIPCHECK(nc::skinny_gemm(W, ldw, X, ldx, C, ldc, M, N, K, map[epilogue], cap,
+                           static_cast<hipStream_t>(stream)));
+  return NC_OK;
+}
+
+int nc_op_decode_attn(int32_t dtype, const void* qkv, int32_t ldq, int32_t B, int32_t H, const void* cache,
+                      int32_t max_seq, int32_t pos, float* part, void* o, int32_t ldo, void* stream) {
+  if (bad_dtype(dtype)) return NC_ERR_ARG;
+  if (!qkv || !cache || !part || !o) return NC_ERR_NULL;
+  if (B < 1 || H < 1 || H > 16 || pos < 0 || pos >= max_seq || ldq < H * 128 + 256 || ldo < H * 128 ||
+      ldq % 8 || ldo % 8)
+    return NC_ERR_ARG;
+  HIPCHECK(nc::decode_attn(dt_of(dtype), qkv, ldq, B, H, cache, max_seq, pos, part, o, ldo,
+                           static_cast<hipStream_t>(stream)));
   return NC_OK;
 }
 

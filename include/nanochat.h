@@ -265,6 +265,23 @@ int nc_op_gemm(int32_t dtype, int32_t a_kcontig, int32_t b_kcontig, int32_t epil
                const void* A, const void* B, void* C, void* C2, int32_t M, int32_t N, int32_t K,
                int32_t lda, int32_t ldb, int32_t ldc, void* stream);
 
+/* bf16 product with few rows, as KV-cache decoding runs its linear layers
+ * (one row per sequence): C[m,n] (epilogue) sum_k X[m,k] W[n,k] for
+ * m < M <= 32. W [N,K] and X [M,K] bf16 row-major (K-contiguous); epilogue
+ * 0: C bf16 = acc, 1: C fp32 += acc, 2: C bf16 = relu(acc)^2, 3: C fp32 =
+ * cap * tanh(acc / cap). N % 16 == 0, K % 32 == 0, ldw and ldx multiples of
+ * 8, ldc of 4. */
+int nc_op_few_rows_gemm(int32_t epilogue, const void* W, int32_t ldw, const void* X, int32_t ldx, void* C,
+                        int32_t ldc, int32_t M, int32_t N, int32_t K, float cap, void* stream);
+
+/* Decoding attention over a KV cache (layout as nc_kv_cache_bytes
+ * describes, one layer): for each of B rows of qkv ([B, ldq], q-hat of H
+ * heads first) the attention of its query heads over cache positions 0..pos
+ * of that row, written to o [B, ldo] (H*128 per row). part is scratch of
+ * B * ceil((pos+1)/64) * H * 129 floats. */
+int nc_op_decode_attn(int32_t dtype, const void* qkv, int32_t ldq, int32_t B, int32_t H, const void* cache,
+                      int32_t max_seq, int32_t pos, float* part, void* o, int32_t ldo, void* stream);
+
 /* Weight-gradient contraction dW[N1,N2] = X1^T X2 over M rows (X1 [M,N1],
  * X2 [M,N2], type T), split over `splits` K slices with a fixed-order fp32
  * reduction through `partial` (splits*N1*N2 floats; unused when splits = 1).

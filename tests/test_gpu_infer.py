@@ -152,3 +152,94 @@ def test_depth20_cache_against_stored_oracle():
     got = np.array([losses[p] for p in sorted(losses)])
     want = ref[sorted(losses)]
     assert abs(got.mean() - want.mean()) <= 5e-3 * want.mean()
+
+
+# ------------------------------------------------- decoding kernels, one by one
+
+def _bf16_exact(rng, shape):
+    t = torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16)
+    return t.cuda(), t.double().numpy()
+
+
+@pytest.mark.parametrize("epi", [0, 1, 2, 3])
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 32])
+@pytest.mark.parametrize("N,K", [(48, 96), (1280, 1280), (208, 5120)])
+def test_few_rows_gemm(epi, M, N, K):
+    """Against an fp64 product of the same bf16 values; rows past M and the
+    padding columns of C stay untouched."""
+    rng = np.random.default_rng(M * 1000 + N + K + epi)
+    W, W64 = _bf16_exact(rng, (N, K))
+    X, X64 = _bf16_exact(rng, (M, K))
+    ref = X64 @ W64.T
+    ldc = N + 16
+    f32_out = epi in (1, 3)
+    sentinel = 7.0
+    C = torch.full((M + 3, ldc), sentinel, dtype=torch.float32 if f32_out else torch.bfloat16,
+                   device="cuda")
+    if epi == 1:
+        base = rng.standard_normal((M, N)).astype(np.float32)
+        C[:M, :N] = torch.from_numpy(base).cuda()
+        ref = ref + base
+    if epi == 2:
+        ref = np.maximum(ref, 0.0) ** 2
+    cap = 0.0
+    if epi == 3:
+        cap = 0.5 * float(np.abs(ref).max())      # so the cap bends the large values
+        ref = cap * np.tanh(ref / cap)
+    nc.nc_op_few_rows_gemm(epi, W, K, X, K, C, ldc, M, N, K, cap)
+    torch.cuda.synchronize()
+    out = C.double().cpu().numpy()
+    got = out[:M, :N]
+    scale = np.abs(ref).max()
+    if f32_out:
+        assert max_rel(got, ref) <= 1e-5, max_rel(got, ref)
+    else:
+        assert np.all(np.abs(got - ref) <= 2 ** -7 * np.abs(ref) + 1e-5 * scale)
+    assert np.all(out[M:] == sentinel) and np.all(out[:, N:] == sentinel)
+
+
+def _unit_rms(a):
+    return a / np.sqrt(np.mean(a ** 2, axis=-1, keepdims=True))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,H,pos", [(1, 1, 0), (3, 10, 63), (2, 16, 64), (5, 3, 100), (32, 10, 1000),
+                                     (4, 10, 2047)])
+def test_decode_attention(dtype, B, H, pos):
+    """One query row per sequence over cache positions 0..pos against the
+    fp64 softmax; cache rows past pos hold NaN and must not reach the result."""
+    max_seq = 2048
+    rng = np.random.default_rng(B * 100 + H * 7 + pos)
+    et = torch.bfloat16 if dtype == "bf16" else torch.float32
+    d = 128 * H
+    ldq = d + 256
+    q = _unit_rms(rng.standard_normal((B, H, 128)))
+    kh = _unit_rms(rng.standard_normal((B, max_seq, 128)))
+    v = rng.standard_normal((B, max_seq, 128))
+    qkv = np.zeros((B, ldq))
+    qkv[:, :d] = q.reshape(B, d)
+    cache = np.concatenate([kh, v], axis=-1)
+    cache[:, pos + 1:] = np.nan
+    qkv_d = torch.from_numpy(qkv).to(et).cuda()
+    cache_d = torch.from_numpy(cache).to(et).cuda()
+    q64 = qkv_d.double().cpu().numpy()[:, :d].reshape(B, H, 128)
+    c64 = cache_d.double().cpu().numpy()
+    nch = pos // 64 + 1
+    part = torch.empty(B * nch * H * 129, dtype=torch.float32, device="cuda")
+    o = torch.full((B, d + 8), 3.0, dtype=et, device="cuda")
+    nc.nc_op_decode_attn(dtype, qkv_d, ldq, B, H, cache_d, max_seq, pos, part, o, d + 8)
+    torch.cuda.synchronize()
+    got = o.double().cpu().numpy()
+    assert np.all(got[:, d:] == 3.0)
+    s = np.einsum("bhc,buc->bhu", q64, c64[:, :pos + 1, :128]) / np.sqrt(128.0)
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    p /= p.sum(axis=-1, keepdims=True)
+    ref = np.einsum("bhu,buc->bhc", p, c64[:, :pos + 1, 128:]).reshape(B, d)
+    got = got[:, :d]
+    assert np.all(np.isfinite(got))
+    if dtype == "f32":
+        assert max_rel(got, ref) <= 1e-5, max_rel(got, ref)
+    else:
+        # P is rounded to bf16 before the P V product, the output once more
+        assert np.abs(got - ref).max() <= 2e-2 * np.abs(ref).max(), np.abs(got - ref).max()
+        check_bf16(got, ref, "o")
