@@ -27,21 +27,6 @@ constexpr int kMaxHeads = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kScoreMax2 = 17.0f;   // > sqrt(128) log2(e): exponents stay <= 0
 
-template <typename T>
-__global__ __launch_bounds__(256) void kv_store_kernel(const T* __restrict__ qkv, int ldq, int H,
-                                                       int M, int Tseq, int pos0,
-                                                       T* __restrict__ cache, int max_seq) {
-  typedef typename Vec16<T>::type V;
-  constexpr int E = Vec16<T>::N;            // elements per 16-byte chunk
-  constexpr int C = kKvW / E;               // chunks per position
-  const size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x;
-  if (i >= (size_t)M * C) return;
-  const int m = (int)(i / C), c = (int)(i % C);
-  const int b = m / Tseq, t = m % Tseq;
-  *reinterpret_cast<V*>(cache + ((size_t)b * max_seq + pos0 + t) * kKvW + c * E) =
-      *reinterpret_cast<const V*>(qkv + (size_t)m * ldq + H * 128 + c * E);
-}
-
 // grid (B, chunks): partial sums of chunk `blockIdx.y` of row `blockIdx.x`
 template <typename T>
 __global__ __launch_bounds__(256) void decode_attn_partial_kernel(
@@ -201,86 +186,237 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* __rest
 // ---------------------------------------------------------------------------
 // Products with a handful of rows (decoding: one row per sequence), bf16:
 // C[m, n] (epilogue) sum_k X[m, k] W[n, k], m < M <= 32. The product is a
-// stream over W, so a workgroup owns just 16 output columns (many
-// workgroups, short dependency chains); its 8 wavefronts take interleaved
-// 32-wide k steps, so together they read each W row front to back, and
-// multiply with v_mfma_f32_16x16x32_bf16 (16 W rows as the row operand, 16
-// rows of X as the column operand). The wavefronts' partial tiles are added
-// through LDS in wavefront order (bitwise reproducible).
+// stream over W, so a workgroup owns just 16 output columns and one of S
+// slices of K (many workgroups, short dependency chains). Its 8 wavefronts
+// take interleaved 32-wide k steps of the slice, so together they read each
+// W row front to back, and multiply with v_mfma_f32_16x16x32_bf16 (16 W rows
+// as the row operand, 16 rows of X as the column operand); loads of the next
+// batch of steps are in flight while the current one is multiplied. The
+// wavefronts' tiles are added through LDS in wavefront order; with S > 1 each
+// slice stores its tile and the last slice of a column block to arrive (an
+// arrival counter) adds the S tiles in slice order. Results are therefore
+// bitwise reproducible.
+//
+// The RMS norm of X's rows can be folded in: the producer of the rows left
+// per-16-column sums of squares, the norm is applied to the fp32 accumulator
+// (Y = rinv * sum_k W x, with x rounded to bf16 unscaled).
 constexpr int kSkWaves = 8;
+constexpr int kSkU = 4;            // k steps per wavefront per batch
+constexpr int kSsqPer = 8;         // 16 x 8 = 128 column blocks: rows up to 2048 wide
 
-template <int MT, SkEpi EPI>
-__global__ __launch_bounds__(512) void skinny_kernel(const bf16* __restrict__ W, int ldw,
-                                                     const bf16* __restrict__ X, int ldx,
-                                                     void* __restrict__ Cv, int ldc, int M, int K,
-                                                     float cap) {
+template <int MT, SkEpi EPI, bool NORM>
+__global__ __launch_bounds__(512) void skinny_kernel(SkArgs g) {
   __shared__ __align__(16) float red[kSkWaves * MT * 256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float ssq_red[16][32];
+  __shared__ float rinv_s[32];
+  __shared__ int last_s;
+  // wave-uniform in a scalar register, so the step guards below are scalar branches
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  const int nsteps = K >> 5;
-  const bf16* wrow = W + (size_t)(n0 + l16) * ldw + 8 * lg;
+  const int nb = blockIdx.x, sk = blockIdx.y, S = gridDim.y;
+  const int n0 = nb * 16;
+  const int nsteps = g.K >> 5;
+  const int sb = (int)((long)sk * nsteps / S), se = (int)((long)(sk + 1) * nsteps / S);
+  const bf16* __restrict__ W = static_cast<const bf16*>(g.W);
+  const bf16* __restrict__ X = static_cast<const bf16*>(g.X);
+
+  float sq[kSsqPer];
+  if constexpr (NORM) {
+    const int m = tid & 31, grp = tid >> 5;
+#pragma unroll
+    for (int j = 0; j < kSsqPer; ++j) {
+      const int blk = grp + 16 * j;
+      sq[j] = (blk < g.nssq && m < g.M) ? g.ssq_in[blk * 32 + m] : 0.f;
+    }
+  }
+
+  const bf16* wrow = W + (size_t)(n0 + l16) * g.ldw + 8 * lg;
   f32x4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 4;
-  for (int s0 = wave; s0 < nsteps; s0 += kSkWaves * U) {
-    bf16x8 a[U], x[U][MT];
+  auto load = [&](int s0, bf16x8 (&a)[kSkU], bf16x8 (&x)[kSkU][MT]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kSkU; ++u) {
       const int s = s0 + kSkWaves * u;
-      if (s < nsteps) {
+      if (s < se) {
         a[u] = *reinterpret_cast<const bf16x8*>(wrow + 32 * s);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const int m = 16 * mt + l16;
-          x[u][mt] = m < M ? *reinterpret_cast<const bf16x8*>(X + (size_t)m * ldx + 32 * s + 8 * lg)
-                           : bf16x8{};
+          x[u][mt] = m < g.M ? *reinterpret_cast<const bf16x8*>(X + (size_t)m * g.ldx + 32 * s + 8 * lg)
+                             : bf16x8{};
         }
+      } else {
+        // never multiplied, but kept zero: a matrix instruction the compiler
+        // places under an EXEC mask still runs on every lane
+        a[u] = bf16x8{};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) x[u][mt] = bf16x8{};
       }
     }
+  };
+  auto mma = [&](int s0, const bf16x8 (&a)[kSkU], const bf16x8 (&x)[kSkU][MT]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (s0 + kSkWaves * u < nsteps)
+    for (int u = 0; u < kSkU; ++u)
+      if (s0 + kSkWaves * u < se)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], x[u][mt], acc[mt], 0, 0, 0);
+  };
+  constexpr int kBatch = kSkWaves * kSkU;   // k steps of the workgroup per batch
+  bf16x8 a0[kSkU], x0[kSkU][MT], a1[kSkU], x1[kSkU][MT];
+  int s0 = sb + wave;
+  load(s0, a0, x0);
+  for (; s0 < se; s0 += 2 * kBatch) {
+    load(s0 + kBatch, a1, x1);
+    mma(s0, a0, x0);
+    load(s0 + 2 * kBatch, a0, x0);
+    mma(s0 + kBatch, a1, x1);
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
     *reinterpret_cast<f32x4*>(red + ((wave * MT + mt) * 64 + lane) * 4) = acc[mt];
+  if constexpr (NORM) {
+    float t = 0.f;
+#pragma unroll
+    for (int j = 0; j < kSsqPer; ++j) t += sq[j];
+    ssq_red[tid >> 5][tid & 31] = t;
+  }
   __syncthreads();
-  // lane ln of tile mt holds C[16 mt + (ln & 15)][n0 + 4 (ln >> 4) + r]
-  for (int e = tid; e < MT * 64; e += 512) {
-    const int mt = e >> 6, ln = e & 63;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kSkWaves; ++w) v += *reinterpret_cast<const f32x4*>(red + ((w * MT + mt) * 64 + ln) * 4);
-    const int m = 16 * mt + (ln & 15), n = n0 + 4 * (ln >> 4);
-    if (m >= M) continue;
-    const size_t off = (size_t)m * ldc + n;
-    if constexpr (EPI == SkEpi::StoreT) {
-      *reinterpret_cast<bf16x4*>(static_cast<bf16*>(Cv) + off) =
-          bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-    } else if constexpr (EPI == SkEpi::Relu2) {
-      bf16x4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float r = fmaxf(v[i], 0.f);
-        w[i] = (bf16)(r * r);
-      }
-      *reinterpret_cast<bf16x4*>(static_cast<bf16*>(Cv) + off) = w;
-    } else if constexpr (EPI == SkEpi::AddF32) {
-      f32x4* c = reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off);
-      *c = *c + v;
-    } else {
-      const float inv = 1.0f / cap;
-      f32x4 z;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = cap * tanhf(v[i] * inv);
-      *reinterpret_cast<f32x4*>(static_cast<float*>(Cv) + off) = z;
+  if constexpr (NORM) {
+    if (tid < 32) {
+      float t = 0.f;
+      for (int grp = 0; grp < 16; ++grp) t += ssq_red[grp][tid];
+      rinv_s[tid] = 1.0f / sqrtf(t / g.K + g.eps);
     }
   }
+  // thread e < MT * 64 holds C[16 mt + (ln & 15)][n0 + 4 (ln >> 4) + r], mt = e / 64, ln = e % 64
+  const int e = tid;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (e < MT * 64) {
+#pragma unroll
+    for (int w = 0; w < kSkWaves; ++w) v += *reinterpret_cast<const f32x4*>(red + (w * MT * 64 + e) * 4);
+  }
+  if (S > 1) {
+    // Slices meet through device-coherent (agent-scope) stores and loads of
+    // the partial tiles: a store is acknowledged once it is visible to every
+    // XCD, so waiting for the acknowledgements before counting in orders the
+    // tile before the count, without a whole-L2 write-back.
+    float* slot = g.part + ((size_t)nb * S + sk) * (MT * 256);
+    if (e < MT * 64) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __hip_atomic_store(slot + e * 4 + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): every store of this thread acknowledged
+    __syncthreads();
+    if (tid == 0)
+      last_s = __hip_atomic_fetch_add(g.cnt + nb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (uint32_t)(S - 1);
+    __syncthreads();
+    if (!last_s) return;
+    if (e < MT * 64) {
+      v = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < S; ++k) {
+        const float* src = g.part + ((size_t)nb * S + k) * (MT * 256) + e * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[i] += __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (tid == 0) __hip_atomic_store(g.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (e >= MT * 64) return;
+  const int ln = e & 63;
+  const int m = 16 * (e >> 6) + (ln & 15), n = n0 + 4 * (ln >> 4);
+  const bool row = m < g.M;
+  if constexpr (NORM) v *= rinv_s[m];
+  const size_t off = (size_t)m * g.ldc + n;
+  if constexpr (EPI == SkEpi::StoreT) {
+    if (row)
+      *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.C) + off) =
+          bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  } else if constexpr (EPI == SkEpi::Relu2) {
+    bf16x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float r = fmaxf(v[i], 0.f);
+      w[i] = (bf16)(r * r);
+    }
+    if (row) *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.C) + off) = w;
+  } else if constexpr (EPI == SkEpi::AddF32) {
+    f32x4 c = v;
+    if (row) {
+      f32x4* cp = reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off);
+      c = *cp + v;
+      *cp = c;
+      if (g.xb)
+        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.xb) + off) =
+            bf16x4{(bf16)c[0], (bf16)c[1], (bf16)c[2], (bf16)c[3]};
+    }
+    if (g.ssq_out) {
+      // the 16 columns of this block for row m sit in lanes ln, ln ^ 16, ln ^ 32, ln ^ 48
+      float q = row ? c[0] * c[0] + c[1] * c[1] + c[2] * c[2] + c[3] * c[3] : 0.f;
+      q += __shfl_xor(q, 16, 64);
+      q += __shfl_xor(q, 32, 64);
+      if (row && (ln >> 4) == 0) g.ssq_out[nb * 32 + m] = q;
+    }
+  } else {
+    const float inv = 1.0f / g.cap;
+    f32x4 z;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[i] = g.cap * tanhf(v[i] * inv);
+    if (row) *reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off) = z;
+  }
+}
+
+// One workgroup per sequence: x = n(E[tok]), its bf16 copy and the
+// per-16-column sums of squares the next product folds its norm from.
+__global__ __launch_bounds__(256) void decode_embed_kernel(const bf16* __restrict__ E,
+                                                           const int32_t* __restrict__ tok, int d, int V,
+                                                           float eps, float* __restrict__ x,
+                                                           bf16* __restrict__ xb, float* __restrict__ ssq,
+                                                           uint32_t* status) {
+  __shared__ float wsum[4];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  int id = tok[m];
+  if (id < 0 || id >= V) {
+    if (tid == 0) atomicOr(status, kStatusTokenRange);
+    id = id < 0 ? 0 : V - 1;
+  }
+  const int c = 8 * tid;                 // this thread's 8 columns
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  if (c < d) {
+    const bf16x8 e8 = *reinterpret_cast<const bf16x8*>(E + (size_t)id * d + c);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = (float)e8[i];
+      ss += v[i] * v[i];
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) wsum[tid >> 6] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((wsum[0] + wsum[1] + wsum[2] + wsum[3]) / d + eps);
+  float q = 0.f;
+  if (c < d) {
+    float y[8];
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      y[i] = v[i] * r;
+      o[i] = (bf16)y[i];
+      q += y[i] * y[i];
+    }
+    const f32x4 lo = {y[0], y[1], y[2], y[3]}, hi = {y[4], y[5], y[6], y[7]};
+    *reinterpret_cast<f32x4*>(x + (size_t)m * d + c) = lo;
+    *reinterpret_cast<f32x4*>(x + (size_t)m * d + c + 4) = hi;
+    *reinterpret_cast<bf16x8*>(xb + (size_t)m * d + c) = o;
+  }
+  q += __shfl_xor(q, 1, 64);             // threads 2j, 2j + 1 hold columns 16j .. 16j + 15
+  if (c < d && (tid & 1) == 0) ssq[(tid >> 1) * 32 + m] = q;
 }
 
 template <typename T>
@@ -320,21 +456,6 @@ __global__ __launch_bounds__(256) void softcap_rows_kernel(const float* __restri
 
 }  // namespace
 
-hipError_t kv_store(DType t, const void* qkv, int ldq, int H, int M, int Tseq, int pos0, void* cache,
-                    int max_seq, hipStream_t s) {
-  if (M <= 0 || Tseq <= 0 || pos0 < 0 || pos0 + Tseq > max_seq || M % Tseq) return hipErrorInvalidValue;
-  const int per = kKvW / (t == DType::BF16 ? 8 : 4);
-  const size_t n = (size_t)M * per;
-  const dim3 grid((unsigned)((n + 255) / 256));
-  if (t == DType::BF16)
-    hipLaunchKernelGGL(kv_store_kernel<bf16>, grid, dim3(256), 0, s, static_cast<const bf16*>(qkv), ldq,
-                       H, M, Tseq, pos0, static_cast<bf16*>(cache), max_seq);
-  else
-    hipLaunchKernelGGL(kv_store_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(qkv),
-                       ldq, H, M, Tseq, pos0, static_cast<float*>(cache), max_seq);
-  return hipGetLastError();
-}
-
 hipError_t decode_attn(DType t, const void* qkv, int ldq, int B, int H, const void* cache,
                        int max_seq, int pos, float* part, void* o, int ldo, hipStream_t s) {
   if (B <= 0 || H < 1 || H > kMaxHeads || pos < 0 || pos >= max_seq) return hipErrorInvalidValue;
@@ -358,30 +479,59 @@ hipError_t decode_attn(DType t, const void* qkv, int ldq, int B, int H, const vo
   return hipGetLastError();
 }
 
-hipError_t skinny_gemm(const void* W, int ldw, const void* X, int ldx, void* C, int ldc, int M, int N,
-                       int K, SkEpi epi, float cap, hipStream_t s) {
-  if (M < 1 || M > kSkinnyMaxRows || N < 16 || N % 16 || K < 32 || K % 32 || ldw % 8 || ldx % 8 ||
-      ldc % 4 || ldw < K || ldx < K || ldc < N)
+int skinny_splits(int N, int K) {
+  const int nsteps = K / 32, nb = N / 16;
+  if (nb >= 1024) return 1;                     // the column blocks alone fill the chip
+  int S = (nsteps + kSkWaves * kSkU - 1) / (kSkWaves * kSkU);   // one batch per wavefront
+  while (nb * S < 256 && 2 * S * kSkWaves <= nsteps) S *= 2;     // at least a workgroup per CU
+  return S;
+}
+
+size_t skinny_part_bytes(int M, int N, int K) {
+  const int S = skinny_splits(N, K);
+  const int MT = M <= 16 ? 1 : 2;
+  return S > 1 ? (size_t)(N / 16) * S * MT * 256 * sizeof(float) : 0;
+}
+
+hipError_t skinny_gemm(const SkArgs& a, SkEpi epi, hipStream_t s) {
+  if (a.M < 1 || a.M > kSkinnyMaxRows || a.N < 16 || a.N % 16 || a.K < 32 || a.K % 32 || a.ldw % 8 ||
+      a.ldx % 8 || a.ldc % 4 || a.ldw < a.K || a.ldx < a.K || a.ldc < a.N)
     return hipErrorInvalidValue;
-  const dim3 grid(N / 16), block(512);
-  const bf16* w = static_cast<const bf16*>(W);
-  const bf16* x = static_cast<const bf16*>(X);
-#define NC_SKINNY(MT, E)                                                                      \
-  hipLaunchKernelGGL((skinny_kernel<MT, E>), grid, block, 0, s, w, ldw, x, ldx, C, ldc, M, K, cap)
-#define NC_SKINNY_EPI(MT)                                       \
-  switch (epi) {                                                \
-    case SkEpi::StoreT: NC_SKINNY(MT, SkEpi::StoreT); break;    \
-    case SkEpi::AddF32: NC_SKINNY(MT, SkEpi::AddF32); break;    \
-    case SkEpi::Relu2: NC_SKINNY(MT, SkEpi::Relu2); break;      \
+  if (a.ssq_in && (a.nssq < 1 || a.nssq > 16 * kSsqPer)) return hipErrorInvalidValue;
+  if ((a.xb || a.ssq_out) && epi != SkEpi::AddF32) return hipErrorInvalidValue;
+  const int S = skinny_splits(a.N, a.K);
+  if (S > 1 && (!a.part || !a.cnt)) return hipErrorInvalidValue;
+  const dim3 grid(a.N / 16, S), block(512);
+  const bool norm = a.ssq_in != nullptr;
+#define NC_SKINNY(MT, E)                                                     \
+  do {                                                                       \
+    if (norm)                                                                \
+      hipLaunchKernelGGL((skinny_kernel<MT, E, true>), grid, block, 0, s, a);  \
+    else                                                                     \
+      hipLaunchKernelGGL((skinny_kernel<MT, E, false>), grid, block, 0, s, a); \
+  } while (0)
+#define NC_SKINNY_EPI(MT)                                            \
+  switch (epi) {                                                     \
+    case SkEpi::StoreT: NC_SKINNY(MT, SkEpi::StoreT); break;         \
+    case SkEpi::AddF32: NC_SKINNY(MT, SkEpi::AddF32); break;         \
+    case SkEpi::Relu2: NC_SKINNY(MT, SkEpi::Relu2); break;           \
     case SkEpi::SoftcapF32: NC_SKINNY(MT, SkEpi::SoftcapF32); break; \
   }
-  if (M <= 16) {
+  if (a.M <= 16) {
     NC_SKINNY_EPI(1)
   } else {
     NC_SKINNY_EPI(2)
   }
 #undef NC_SKINNY_EPI
 #undef NC_SKINNY
+  return hipGetLastError();
+}
+
+hipError_t decode_embed(const void* E, const int32_t* tok, int M, int d, int V, float eps, float* x,
+                        void* xb, float* ssq, uint32_t* status, hipStream_t s) {
+  if (M < 1 || M > kSkinnyMaxRows || d % 16 || d > 2048) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_embed_kernel, dim3(M), dim3(256), 0, s, static_cast<const bf16*>(E), tok, d,
+                     V, eps, x, static_cast<bf16*>(xb), ssq, status);
   return hipGetLastError();
 }
 

@@ -50,7 +50,9 @@ __global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(T* __restrict__ qk
                                                               int Tlen, int H,
                                                               const float* __restrict__ cs,
                                                               float eps,
-                                                              float* __restrict__ rinv_qk) {
+                                                              float* __restrict__ rinv_qk,
+                                                              T* __restrict__ cache, int max_seq,
+                                                              int pos0) {
   const int sl = threadIdx.x & 15;
   const size_t w = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);   // (token, head) pair
   const int nh = H + 1;
@@ -80,7 +82,19 @@ __global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(T* __restrict__ qk
   }
   Quad<T>::store(p, ra);
   Quad<T>::store(p + kHalf, rb);
-  if (sl == 0) rinv_qk[m * nh + h] = r;
+  if (rinv_qk && sl == 0) rinv_qk[m * nh + h] = r;
+  if (cache && h == H) {
+    // KV cache row of (sequence m / Tlen, position pos0 + t): k-hat, then v
+    T* dst = cache + ((m / Tlen) * (size_t)max_seq + pos0 + t) * 256 + 4 * sl;
+    Quad<T>::store(dst, ra);
+    Quad<T>::store(dst + kHalf, rb);
+    float v[4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      Quad<T>::load(p + 128 + half * kHalf, v);
+      Quad<T>::store(dst + 128 + half * kHalf, v);
+    }
+  }
 }
 
 // dz' = r (dy - y mean(dy y)) with y the saved normalised vector, then rotate by -theta
@@ -132,15 +146,17 @@ hipError_t rope_table(int T, int half, double base, float* cs, hipStream_t s, in
 }
 
 hipError_t rope_qknorm_fwd(DType t, void* qkv, int ldq, int M, int T, int H, const float* cs,
-                           float eps, float* rinv_qk, hipStream_t s) {
+                           float eps, float* rinv_qk, hipStream_t s, void* cache, int max_seq,
+                           int pos0) {
+  if (cache && (M % T || pos0 < 0 || pos0 + T > max_seq)) return hipErrorInvalidValue;
   const size_t vecs = (size_t)M * (H + 1);
   dim3 grid((unsigned)((vecs + 15) / 16)), block(256);
   if (t == DType::BF16)
     hipLaunchKernelGGL(rope_qknorm_fwd_kernel<bf16>, grid, block, 0, s, static_cast<bf16*>(qkv), ldq,
-                       M, T, H, cs, eps, rinv_qk);
+                       M, T, H, cs, eps, rinv_qk, static_cast<bf16*>(cache), max_seq, pos0);
   else
     hipLaunchKernelGGL(rope_qknorm_fwd_kernel<float>, grid, block, 0, s, static_cast<float*>(qkv),
-                       ldq, M, T, H, cs, eps, rinv_qk);
+                       ldq, M, T, H, cs, eps, rinv_qk, static_cast<float*>(cache), max_seq, pos0);
   return hipGetLastError();
 }
 

@@ -74,9 +74,12 @@ hipError_t embed_bwd(DType t, const void* E, const int32_t* tok, const float* ri
 // ---- rotary + QK-norm -------------------------------------------------------
 // [T, half] cos, then sin, of positions t0 .. t0 + T - 1
 hipError_t rope_table(int T, int half, double base, float* cs, hipStream_t s, int t0 = 0);
-// in place on qkv[M, ldq]: H query heads at cols [0, H*128), the key head at [H*128, H*128+128)
+// in place on qkv[M, ldq]: H query heads at cols [0, H*128), the key head at [H*128, H*128+128).
+// rinv_qk may be null. With a cache ([M/T][max_seq][256]), the rotated, normalised key and the
+// value of row m also go to position pos0 + m % T of sequence m / T.
 hipError_t rope_qknorm_fwd(DType t, void* qkv, int ldq, int M, int T, int H, const float* cs,
-                           float eps, float* rinv_qk, hipStream_t s);
+                           float eps, float* rinv_qk, hipStream_t s, void* cache = nullptr,
+                           int max_seq = 0, int pos0 = 0);
 hipError_t rope_qknorm_bwd(DType t, void* dqkv, int ldd, const void* qkv, int ldq, int M, int T,
                            int H, const float* cs, const float* rinv_qk, hipStream_t s);
 
@@ -102,9 +105,6 @@ hipError_t loss_mean(const float* loss_rows, int M, float* out, uint32_t* status
 
 // ---- inference: KV cache, decode attention ---------------------------------------
 // Cache of one layer: [B][max_seq][256] of T (k-hat then v, 128 each).
-// Copies k-hat and v of M rows of qkv (row m = b * Tseq + t) to positions pos0 + t.
-hipError_t kv_store(DType t, const void* qkv, int ldq, int H, int M, int Tseq, int pos0, void* cache,
-                    int max_seq, hipStream_t s);
 // Attention of one new query row per batch row b (q-hat in qkv row b) over
 // cache positions 0..pos: chunks of 64 keys give fp32 partial sum_u p v and
 // sum_u p (p shifted by the fixed score bound), combined in chunk order into
@@ -116,13 +116,38 @@ hipError_t decode_attn(DType t, const void* qkv, int ldq, int B, int H, const vo
 // K % 32 == 0, leading dimensions multiples of 8 (W, X) and 4 (C).
 enum class SkEpi {
   StoreT,      // C (bf16) = acc
-  AddF32,      // C (float) += acc
+  AddF32,      // C (float) += acc; optionally xb (bf16) = C and ssq_out = per-16-column sums of C^2
   Relu2,       // C (bf16) = relu(acc)^2
   SoftcapF32,  // C (float) = cap * tanh(acc / cap)
 };
 constexpr int kSkinnyMaxRows = 32;
-hipError_t skinny_gemm(const void* W, int ldw, const void* X, int ldx, void* C, int ldc, int M, int N,
-                       int K, SkEpi epi, float cap, hipStream_t s);
+struct SkArgs {
+  const void* W;
+  int ldw;
+  const void* X;          // bf16 [M, K]
+  int ldx;
+  void* C;
+  int ldc;
+  int M, N, K;
+  // RMS norm of the rows of X folded in (acc scaled by 1/sqrt(ss/K + eps)), ss summed from
+  // ssq_in[j * 32 + m], j < nssq (null: no norm)
+  const float* ssq_in;
+  int nssq;
+  float eps;
+  void* xb;               // AddF32 only: bf16 copy of the new C rows, ld ldc (null: none)
+  float* ssq_out;         // AddF32 only: [N/16][32] sums of squares of the new C rows (null: none)
+  float cap;
+  float* part;            // split partials: skinny_scratch_bytes
+  uint32_t* cnt;          // N/16 arrival counters, zero on entry (left zero)
+};
+// k splits the product uses, and the partial-tile scratch they need
+int skinny_splits(int N, int K);
+size_t skinny_part_bytes(int M, int N, int K);
+hipError_t skinny_gemm(const SkArgs& a, SkEpi epi, hipStream_t s);
+// x[m] = n(E[tok[m]]) (fp32), xb[m] = bf16 copy, ssq[j * 32 + m] = sum of x[m]^2 over columns
+// 16j..16j+15; one row per sequence (M <= 32), d <= 2048
+hipError_t decode_embed(const void* E, const int32_t* tok, int M, int d, int V, float eps, float* x,
+                        void* xb, float* ssq, uint32_t* status, hipStream_t s);
 // dst[r, :] = src[(r + 1) * stride - 1, :] for r < rows, 0 for rows <= r < rows_pad (T, width d)
 hipError_t gather_last_rows(DType t, const void* src, int stride, int rows, int rows_pad, int d,
                             void* dst, hipStream_t s);

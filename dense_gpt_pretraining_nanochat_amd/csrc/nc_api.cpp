@@ -718,7 +718,9 @@ int nc_optimizer_step(const nc_config* cfg, const nc_optim_config* optim, void* 
 namespace {
 
 struct InferPlan {
-  uint64_t status, cs, x, rinv, h, qkv, rqk, o, lse, h2, a, xf, last, logits, part;
+  uint64_t status, skcnt, cs, x, rinv, h, qkv, rqk, o, lse, h2, a, xf, last, logits, part, xb, ssq,
+      skpart;
+  uint64_t sync_bytes;   // status word and few-row product counters, cleared by every call
   uint64_t total;
 };
 
@@ -736,7 +738,10 @@ InferPlan infer_plan_of(const Dims& D, int max_seq) {
   };
   const uint64_t Bp = (uint64_t)pad16(D.B);
   const uint64_t R = std::max<uint64_t>((uint64_t)D.M, Bp), e = D.esz;
-  P.status = take(256);
+  // status word, then the arrival counters of the few-row products (N/16 <= V/16)
+  P.sync_bytes = align_up(256 + (uint64_t)(D.V / 16) * 4, kAlign);
+  P.status = take(P.sync_bytes);
+  P.skcnt = P.status + 256;
   P.cs = take((uint64_t)D.T * 64 * 2 * 4);
   P.x = take(R * D.d * 4);
   P.rinv = take(R * 4);
@@ -752,6 +757,15 @@ InferPlan infer_plan_of(const Dims& D, int max_seq) {
   P.logits = take(Bp * D.V * 4);
   const uint64_t nch = ((uint64_t)max_seq + 63) / 64;
   P.part = take((uint64_t)D.B * nch * D.H * 129 * 4);
+  P.xb = take(Bp * D.d * 2);
+  P.ssq = take(128 * 32 * 4);
+  uint64_t part = 0;
+  if (D.B <= nc::kSkinnyMaxRows) {
+    const int shapes[5][2] = {{D.Q, D.d}, {D.d, D.d}, {D.F, D.d}, {D.d, D.F}, {D.V, D.d}};
+    for (const auto& nk : shapes)
+      part = std::max<uint64_t>(part, nc::skinny_part_bytes(D.B, nk[0], nk[1]));
+  }
+  P.skpart = take(part);
   P.total = off;
   return P;
 }
@@ -760,21 +774,10 @@ uint64_t kv_layer_bytes(const Dims& D, int max_seq) {
   return (uint64_t)D.B * max_seq * 256 * D.esz;
 }
 
-// Linear layer of the inference path: Y = X W^T under an epilogue, through
-// the few-row kernel when every row fits one of its workgroups (bf16 decoding)
-// and the tiled GEMM otherwise.
+// Linear layer of the prefill (and the wide-batch / fp32 decoding) path:
+// Y = X W^T under an epilogue through the tiled GEMM.
 hipError_t infer_linear(DType dt, Epi epi, const void* X, const void* W, void* C, int64_t M, int N, int K,
                         int ldx, int ldc, hipStream_t s) {
-  if (dt == DType::BF16 && M <= nc::kSkinnyMaxRows) {
-    nc::SkEpi e;
-    switch (epi) {
-      case Epi::StoreT: e = nc::SkEpi::StoreT; break;
-      case Epi::AddF32: e = nc::SkEpi::AddF32; break;
-      case Epi::Relu2: e = nc::SkEpi::Relu2; break;
-      default: return hipErrorInvalidValue;
-    }
-    return nc::skinny_gemm(W, K, X, ldx, C, ldc, (int)M, N, K, e, 0.f, s);
-  }
   return gemm_simple(dt, true, true, epi, X, W, C, nullptr, M, N, K, ldx, K, ldc, 0, s);
 }
 
@@ -803,8 +806,8 @@ int infer_blocks(const Dims& D, const nc_config* cfg, const std::vector<Tensor>&
     void* cache = static_cast<char*>(kv) + (uint64_t)l * kv_layer_bytes(D, max_seq);
     HIPCHECK(nc::rmsnorm_fwd(dt, x, (int)M, D.d, eps, h, rinv, s));
     HIPCHECK(infer_linear(dt, Epi::StoreT, h, W(base + 0), qkv, M, D.Q, D.d, D.d, D.Q, s));
-    HIPCHECK(nc::rope_qknorm_fwd(dt, qkv, D.Q, kv_rows, Tseq, D.H, cs, eps, at<float>(ws, P.rqk), s));
-    HIPCHECK(nc::kv_store(dt, qkv, D.Q, D.H, kv_rows, Tseq, pos0, cache, max_seq, s));
+    HIPCHECK(nc::rope_qknorm_fwd(dt, qkv, D.Q, kv_rows, Tseq, D.H, cs, eps, nullptr, s, cache, max_seq,
+                                 pos0));
     if (prefill)
       HIPCHECK(nc::attn_fwd(dt, qkv, D.Q, D.B, Tseq, D.H, o, at<float>(ws, P.lse), s));
     else
@@ -828,13 +831,21 @@ int infer_logits(const Dims& D, const nc_config* cfg, const std::vector<Tensor>&
   const char* U = static_cast<const char*>(params) + lay[1 + 4 * D.L].offset * D.esz;
   HIPCHECK(nc::rmsnorm_fwd(dt, at<float>(ws, P.x), (int)M, D.d, cfg->rms_eps, xf, at<float>(ws, P.rinv), s));
   if (few_rows(D, D.B)) {
-    const void* rows = xf;
-    if (stride != 1) {
-      HIPCHECK(nc::gather_last_rows(dt, xf, stride, D.B, D.B, D.d, last, s));
-      rows = last;
-    }
-    HIPCHECK(nc::skinny_gemm(U, D.d, rows, D.d, logits_out, D.V, D.B, D.V, D.d, nc::SkEpi::SoftcapF32,
-                             cfg->softcap, s));
+    HIPCHECK(nc::gather_last_rows(dt, xf, stride, D.B, D.B, D.d, last, s));
+    nc::SkArgs g{};
+    g.W = U;
+    g.ldw = D.d;
+    g.X = last;
+    g.ldx = D.d;
+    g.C = logits_out;
+    g.ldc = D.V;
+    g.M = D.B;
+    g.N = D.V;
+    g.K = D.d;
+    g.cap = cfg->softcap;
+    g.part = at<float>(ws, P.skpart);
+    g.cnt = at<uint32_t>(ws, P.skcnt);
+    HIPCHECK(nc::skinny_gemm(g, nc::SkEpi::SoftcapF32, s));
     return NC_OK;
   }
   const int Bp = pad16(D.B);
@@ -843,6 +854,66 @@ int infer_logits(const Dims& D, const nc_config* cfg, const std::vector<Tensor>&
   HIPCHECK(gemm_simple(dt, true, true, Epi::StoreF32, last, U, lg, nullptr, Bp, D.V, D.d, D.d, D.d,
                        D.V, 0, s));
   HIPCHECK(nc::softcap_rows(lg, D.B, D.V, cfg->softcap, logits_out, s));
+  return NC_OK;
+}
+
+// bf16 decoding of up to 32 sequences: every linear layer through the
+// few-row product, the block norms folded into the products that read the
+// residual stream (its producers leave a bf16 copy and per-16-column sums of
+// squares), the cache written by the rotary kernel.
+int decode_few_rows(const Dims& D, const nc_config* cfg, const std::vector<Tensor>& lay,
+                    const void* params, const int32_t* tokens, int pos, void* kv, int max_seq, void* ws,
+                    const InferPlan& P, float* logits, hipStream_t s) {
+  const float eps = cfg->rms_eps;
+  auto W = [&](int idx) { return static_cast<const char*>(params) + lay[idx].offset * D.esz; };
+  float* x = at<float>(ws, P.x);
+  void* xb = at<char>(ws, P.xb);
+  float* ssq = at<float>(ws, P.ssq);
+  void* qkv = at<char>(ws, P.qkv);
+  void* o = at<char>(ws, P.o);
+  void* a = at<char>(ws, P.a);
+  const int nssq = D.d / 16;
+  auto lin = [&](int widx, const void* X, int ldx, void* C, int ldc, int N, int K, nc::SkEpi epi,
+                 bool norm, bool emit, float cap) {
+    nc::SkArgs g{};
+    g.W = widx >= 0 ? W(widx) : nullptr;
+    g.ldw = K;
+    g.X = X;
+    g.ldx = ldx;
+    g.C = C;
+    g.ldc = ldc;
+    g.M = D.B;
+    g.N = N;
+    g.K = K;
+    if (norm) {
+      g.ssq_in = ssq;
+      g.nssq = nssq;
+      g.eps = eps;
+    }
+    if (emit) {
+      g.xb = xb;
+      g.ssq_out = ssq;
+    }
+    g.cap = cap;
+    g.part = at<float>(ws, P.skpart);
+    g.cnt = at<uint32_t>(ws, P.skcnt);
+    return nc::skinny_gemm(g, epi, s);
+  };
+  HIPCHECK(nc::decode_embed(W(0), tokens, D.B, D.d, D.V, eps, x, xb, ssq, at<uint32_t>(ws, P.status), s));
+  const float* cs = at<float>(ws, P.cs);
+  for (int l = 0; l < D.L; ++l) {
+    const int base = 1 + 4 * l;
+    void* cache = static_cast<char*>(kv) + (uint64_t)l * kv_layer_bytes(D, max_seq);
+    HIPCHECK(lin(base + 0, xb, D.d, qkv, D.Q, D.Q, D.d, nc::SkEpi::StoreT, true, false, 0.f));
+    HIPCHECK(nc::rope_qknorm_fwd(D.dt, qkv, D.Q, D.B, 1, D.H, cs, eps, nullptr, s, cache, max_seq, pos));
+    HIPCHECK(nc::decode_attn(D.dt, qkv, D.Q, D.B, D.H, cache, max_seq, pos, at<float>(ws, P.part), o, D.d,
+                             s));
+    HIPCHECK(lin(base + 1, o, D.d, x, D.d, D.d, D.d, nc::SkEpi::AddF32, false, true, 0.f));
+    HIPCHECK(lin(base + 2, xb, D.d, a, D.F, D.F, D.d, nc::SkEpi::Relu2, true, false, 0.f));
+    HIPCHECK(lin(base + 3, a, D.F, x, D.d, D.d, D.F, nc::SkEpi::AddF32, false, true, 0.f));
+  }
+  HIPCHECK(lin(1 + 4 * D.L, xb, D.d, logits, D.V, D.V, D.d, nc::SkEpi::SoftcapF32, true, false,
+               cfg->softcap));
   return NC_OK;
 }
 
@@ -894,7 +965,7 @@ int nc_prefill(const nc_config* cfg, const void* params, const int32_t* tokens, 
   const auto lay = layout_of(D);
   const char* E = static_cast<const char*>(params) + lay[0].offset * D.esz;
   uint32_t* status = at<uint32_t>(ws, P.status);
-  HIPCHECK(nc::fill_zero(status, 256, s));
+  HIPCHECK(nc::fill_zero(status, P.sync_bytes, s));
   HIPCHECK(nc::rope_table(T0, 64, (double)cfg->rope_base, at<float>(ws, P.cs), s, 0));
   HIPCHECK(nc::embed_norm_fwd(D.dt, E, tokens, (int)Dp.M, D.d, D.V, cfg->rms_eps, at<float>(ws, P.x),
                               at<float>(ws, P.rinv), status, s));
@@ -914,22 +985,20 @@ int nc_decode_step(const nc_config* cfg, const void* params, const int32_t* toke
   const InferPlan P = infer_plan_of(D, max_seq);
   if (ws_bytes < P.total) return NC_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // the few-row kernels take the batch as it is; the tiled GEMM wants rows in
-  // multiples of 16, and the rows past the batch stay zero through the blocks
-  // (every row is independent)
-  const bool few = few_rows(D, D.B);
-  const int Mr = few ? D.B : pad16(D.B);
-  Dims Dd = D;
-  Dd.M = Mr;
   const auto lay = layout_of(D);
   const char* E = static_cast<const char*>(params) + lay[0].offset * D.esz;
   uint32_t* status = at<uint32_t>(ws, P.status);
-  HIPCHECK(nc::fill_zero(status, 256, s));
+  HIPCHECK(nc::fill_zero(status, P.sync_bytes, s));
   HIPCHECK(nc::rope_table(1, 64, (double)cfg->rope_base, at<float>(ws, P.cs), s, pos));
-  if (!few) {
-    HIPCHECK(nc::fill_zero(at<char>(ws, P.x), (size_t)Mr * D.d * 4, s));
-    HIPCHECK(nc::fill_zero(at<char>(ws, P.o), (size_t)Mr * D.d * D.esz, s));
-  }
+  if (few_rows(D, D.B))
+    return decode_few_rows(D, cfg, lay, params, tokens, pos, kv, max_seq, ws, P, logits, s);
+  // the tiled GEMM wants rows in multiples of 16; the rows past the batch stay
+  // zero through the blocks (every row is independent)
+  const int Mr = pad16(D.B);
+  Dims Dd = D;
+  Dd.M = Mr;
+  HIPCHECK(nc::fill_zero(at<char>(ws, P.x), (size_t)Mr * D.d * 4, s));
+  HIPCHECK(nc::fill_zero(at<char>(ws, P.o), (size_t)Mr * D.d * D.esz, s));
   HIPCHECK(nc::embed_norm_fwd(D.dt, E, tokens, D.B, D.d, D.V, cfg->rms_eps, at<float>(ws, P.x),
                               at<float>(ws, P.rinv), status, s));
   rc = infer_blocks(Dd, cfg, lay, params, ws, P, Mr, D.B, 1, pos, false, kv, max_seq, s);
@@ -982,17 +1051,49 @@ int nc_op_gemm(int32_t dtype, int32_t a_kcontig, int32_t b_kcontig, int32_t epil
   return NC_OK;
 }
 
-int nc_op_few_rows_gemm(int32_t epilogue, const void* W, int32_t ldw, const void* X, int32_t ldx, void* C,
-                        int32_t ldc, int32_t M, int32_t N, int32_t K, float cap, void* stream) {
-  if (epilogue < 0 || epilogue > 3) return NC_ERR_ARG;
-  if (!W || !X || !C) return NC_ERR_NULL;
+int nc_op_few_rows_scratch_bytes(int32_t M, int32_t N, int32_t K, uint64_t* bytes) {
+  if (!bytes) return NC_ERR_NULL;
   if (M < 1 || M > nc::kSkinnyMaxRows || N < 16 || N % 16 || K < 32 || K % 32) return NC_ERR_ARG;
+  *bytes = align_up((uint64_t)(N / 16) * 4, kAlign) + nc::skinny_part_bytes(M, N, K);
+  return NC_OK;
+}
+
+int nc_op_few_rows_gemm(int32_t epilogue, const void* W, int32_t ldw, const void* X, int32_t ldx, void* C,
+                        int32_t ldc, int32_t M, int32_t N, int32_t K, float cap, const float* ssq_in,
+                        float eps, void* xb, float* ssq_out, void* scratch, uint64_t scratch_bytes,
+                        void* stream) {
+  if (epilogue < 0 || epilogue > 3) return NC_ERR_ARG;
+  if (!W || !X || !C || !scratch) return NC_ERR_NULL;
+  if (misaligned(scratch)) return NC_ERR_ALIGN;
+  if (M < 1 || M > nc::kSkinnyMaxRows || N < 16 || N % 16 || K < 32 || K % 32 || K > 2048 * (ssq_in ? 1 : 64))
+    return NC_ERR_ARG;
   if (ldw % 8 || ldx % 8 || ldc % 4 || ldw < K || ldx < K || ldc < N) return NC_ERR_ARG;
   if (epilogue == 3 && !(cap > 0.f)) return NC_ERR_ARG;
+  if ((xb || ssq_out) && epilogue != 1) return NC_ERR_ARG;
+  uint64_t need = 0;
+  nc_op_few_rows_scratch_bytes(M, N, K, &need);
+  if (scratch_bytes < need) return NC_ERR_WORKSPACE;
   static const nc::SkEpi map[4] = {nc::SkEpi::StoreT, nc::SkEpi::AddF32, nc::SkEpi::Relu2,
                                    nc::SkEpi::SoftcapF32};
-  HIPCHECK(nc::skinny_gemm(W, ldw, X, ldx, C, ldc, M, N, K, map[epilogue], cap,
-                           static_cast<hipStream_t>(stream)));
+  nc::SkArgs g{};
+  g.W = W;
+  g.ldw = ldw;
+  g.X = X;
+  g.ldx = ldx;
+  g.C = C;
+  g.ldc = ldc;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.ssq_in = ssq_in;
+  g.nssq = K / 16;
+  g.eps = eps;
+  g.xb = xb;
+  g.ssq_out = ssq_out;
+  g.cap = cap;
+  g.cnt = static_cast<uint32_t*>(scratch);
+  g.part = reinterpret_cast<float*>(static_cast<char*>(scratch) + align_up((uint64_t)(N / 16) * 4, kAlign));
+  HIPCHECK(nc::skinny_gemm(g, map[epilogue], static_cast<hipStream_t>(stream)));
   return NC_OK;
 }
 

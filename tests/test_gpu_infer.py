@@ -163,10 +163,11 @@ def _bf16_exact(rng, shape):
 
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
 @pytest.mark.parametrize("M", [1, 5, 16, 17, 32])
-@pytest.mark.parametrize("N,K", [(48, 96), (1280, 1280), (208, 5120)])
+@pytest.mark.parametrize("N,K", [(48, 96), (1280, 1280), (208, 5120), (4096, 256)])
 def test_few_rows_gemm(epi, M, N, K):
     """Against an fp64 product of the same bf16 values; rows past M and the
-    padding columns of C stay untouched."""
+    padding columns of C stay untouched. Covers one k slice and several
+    (the split count follows N and K)."""
     rng = np.random.default_rng(M * 1000 + N + K + epi)
     W, W64 = _bf16_exact(rng, (N, K))
     X, X64 = _bf16_exact(rng, (M, K))
@@ -186,7 +187,8 @@ def test_few_rows_gemm(epi, M, N, K):
     if epi == 3:
         cap = 0.5 * float(np.abs(ref).max())      # so the cap bends the large values
         ref = cap * np.tanh(ref / cap)
-    nc.nc_op_few_rows_gemm(epi, W, K, X, K, C, ldc, M, N, K, cap)
+    scratch = torch.zeros(nc.nc_op_few_rows_scratch_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+    nc.nc_op_few_rows_gemm(epi, W, K, X, K, C, ldc, M, N, K, scratch, cap=cap)
     torch.cuda.synchronize()
     out = C.double().cpu().numpy()
     got = out[:M, :N]
@@ -196,6 +198,46 @@ def test_few_rows_gemm(epi, M, N, K):
     else:
         assert np.all(np.abs(got - ref) <= 2 ** -7 * np.abs(ref) + 1e-5 * scale)
     assert np.all(out[M:] == sentinel) and np.all(out[:, N:] == sentinel)
+    # the arrival counters are left zero for the next call
+    assert int(scratch[:4 * (N // 16)].view(torch.int32).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("M", [3, 32])
+@pytest.mark.parametrize("N,K", [(1536, 1280), (1280, 1280), (5120, 2048)])
+def test_few_rows_gemm_norm_and_residual_outputs(M, N, K):
+    """The RMS factor comes from per-16-column sums of squares; the residual
+    epilogue also leaves a bf16 copy of the new rows and their sums of
+    squares (what the next product folds its norm from)."""
+    rng = np.random.default_rng(M + N + K)
+    W, W64 = _bf16_exact(rng, (N, K))
+    X, X64 = _bf16_exact(rng, (M, K))
+    resid = rng.standard_normal((M, K)) * 3.0
+    ss = np.zeros((K // 16, 32))
+    ss[:, :M] = (resid ** 2).reshape(M, K // 16, 16).sum(axis=-1).T
+    eps = 1e-6
+    r = 1.0 / np.sqrt(ss[:, :M].sum(axis=0) / K + eps)
+    scratch = torch.zeros(nc.nc_op_few_rows_scratch_bytes(M, N, K), dtype=torch.uint8, device="cuda")
+    C = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    ssq_in = torch.from_numpy(ss.astype(np.float32)).cuda()
+    nc.nc_op_few_rows_gemm(0, W, K, X, K, C, N, M, N, K, scratch, ssq_in=ssq_in, eps=eps)
+    ref = r[:, None] * (X64 @ W64.T)
+    torch.cuda.synchronize()
+    got = C.double().cpu().numpy()
+    assert np.all(np.abs(got - ref) <= 2 ** -7 * np.abs(ref) + 1e-5 * np.abs(ref).max())
+    # residual add with the bf16 copy and the sums of squares
+    base = rng.standard_normal((M, N)).astype(np.float32)
+    Cf = torch.from_numpy(base).cuda()
+    xb = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    ssq_out = torch.full(((N // 16), 32), -1.0, dtype=torch.float32, device="cuda")
+    nc.nc_op_few_rows_gemm(1, W, K, X, K, Cf, N, M, N, K, scratch, xb=xb, ssq_out=ssq_out)
+    torch.cuda.synchronize()
+    new = Cf.double().cpu().numpy()
+    assert max_rel(new, base + X64 @ W64.T) <= 1e-5
+    assert torch.equal(xb, Cf.to(torch.bfloat16))
+    so = ssq_out.double().cpu().numpy()
+    want = (new ** 2).reshape(M, N // 16, 16).sum(axis=-1).T
+    assert max_rel(so[:, :M], want) <= 1e-5
+    assert np.all(so[:, M:] == -1.0)
 
 
 def _unit_rms(a):
