@@ -205,7 +205,7 @@ constexpr int kSkU = 4;            // k steps per wavefront per batch
 constexpr int kSsqPer = 8;         // 16 x 8 = 128 column blocks: rows up to 2048 wide
 
 template <int MT, SkEpi EPI, bool NORM>
-__global__ __launch_bounds__(512) void skinny_kernel(SkArgs g) {
+__global__ __launch_bounds__(512, 2) void skinny_kernel(SkArgs g) {
   __shared__ __align__(16) float red[kSkWaves * MT * 256];
   __shared__ float ssq_red[16][32];
   __shared__ float rinv_s[32];
@@ -479,16 +479,19 @@ hipError_t decode_attn(DType t, const void* qkv, int ldq, int B, int H, const vo
   return hipGetLastError();
 }
 
+// Measured on MI355X at the decoding shapes (32 rows, bf16): a slice costs
+// one more round trip through memory for its partial tile, which outweighs
+// the extra parallelism until a workgroup would stream more than 2048 k
+// values (two batches per wavefront); 16-column blocks alone give 80-4096
+// workgroups.
 int skinny_splits(int N, int K) {
-  const int nsteps = K / 32, nb = N / 16;
-  if (nb >= 1024) return 1;                     // the column blocks alone fill the chip
-  int S = (nsteps + kSkWaves * kSkU - 1) / (kSkWaves * kSkU);   // one batch per wavefront
-  while (nb * S < 256 && 2 * S * kSkWaves <= nsteps) S *= 2;     // at least a workgroup per CU
-  return S;
+  (void)N;
+  const int nsteps = K / 32;
+  return (nsteps + 2 * kSkWaves * kSkU - 1) / (2 * kSkWaves * kSkU);
 }
 
-size_t skinny_part_bytes(int M, int N, int K) {
-  const int S = skinny_splits(N, K);
+size_t skinny_part_bytes(int M, int N, int K, int splits) {
+  const int S = splits > 0 ? splits : skinny_splits(N, K);
   const int MT = M <= 16 ? 1 : 2;
   return S > 1 ? (size_t)(N / 16) * S * MT * 256 * sizeof(float) : 0;
 }
@@ -499,8 +502,8 @@ hipError_t skinny_gemm(const SkArgs& a, SkEpi epi, hipStream_t s) {
     return hipErrorInvalidValue;
   if (a.ssq_in && (a.nssq < 1 || a.nssq > 16 * kSsqPer)) return hipErrorInvalidValue;
   if ((a.xb || a.ssq_out) && epi != SkEpi::AddF32) return hipErrorInvalidValue;
-  const int S = skinny_splits(a.N, a.K);
-  if (S > 1 && (!a.part || !a.cnt)) return hipErrorInvalidValue;
+  const int S = a.splits > 0 ? a.splits : skinny_splits(a.N, a.K);
+  if (S > a.K / 32 || (S > 1 && (!a.part || !a.cnt))) return hipErrorInvalidValue;
   const dim3 grid(a.N / 16, S), block(512);
   const bool norm = a.ssq_in != nullptr;
 #define NC_SKINNY(MT, E)                                                     \

@@ -1051,18 +1051,20 @@ int nc_op_gemm(int32_t dtype, int32_t a_kcontig, int32_t b_kcontig, int32_t epil
   return NC_OK;
 }
 
-int nc_op_few_rows_scratch_bytes(int32_t M, int32_t N, int32_t K, uint64_t* bytes) {
+int nc_op_few_rows_scratch_bytes(int32_t M, int32_t N, int32_t K, int32_t splits, uint64_t* bytes) {
   if (!bytes) return NC_ERR_NULL;
-  if (M < 1 || M > nc::kSkinnyMaxRows || N < 16 || N % 16 || K < 32 || K % 32) return NC_ERR_ARG;
-  *bytes = align_up((uint64_t)(N / 16) * 4, kAlign) + nc::skinny_part_bytes(M, N, K);
+  if (M < 1 || M > nc::kSkinnyMaxRows || N < 16 || N % 16 || K < 32 || K % 32 || splits < 0 ||
+      splits > K / 32)
+    return NC_ERR_ARG;
+  *bytes = align_up((uint64_t)(N / 16) * 4, kAlign) + nc::skinny_part_bytes(M, N, K, splits);
   return NC_OK;
 }
 
 int nc_op_few_rows_gemm(int32_t epilogue, const void* W, int32_t ldw, const void* X, int32_t ldx, void* C,
                         int32_t ldc, int32_t M, int32_t N, int32_t K, float cap, const float* ssq_in,
-                        float eps, void* xb, float* ssq_out, void* scratch, uint64_t scratch_bytes,
-                        void* stream) {
-  if (epilogue < 0 || epilogue > 3) return NC_ERR_ARG;
+                        float eps, void* xb, float* ssq_out, int32_t splits, void* scratch,
+                        uint64_t scratch_bytes, void* stream) {
+  if (epilogue < 0 || epilogue > 3 || splits < 0 || splits > K / 32) return NC_ERR_ARG;
   if (!W || !X || !C || !scratch) return NC_ERR_NULL;
   if (misaligned(scratch)) return NC_ERR_ALIGN;
   if (M < 1 || M > nc::kSkinnyMaxRows || N < 16 || N % 16 || K < 32 || K % 32 || K > 2048 * (ssq_in ? 1 : 64))
@@ -1071,7 +1073,7 @@ int nc_op_few_rows_gemm(int32_t epilogue, const void* W, int32_t ldw, const void
   if (epilogue == 3 && !(cap > 0.f)) return NC_ERR_ARG;
   if ((xb || ssq_out) && epilogue != 1) return NC_ERR_ARG;
   uint64_t need = 0;
-  nc_op_few_rows_scratch_bytes(M, N, K, &need);
+  nc_op_few_rows_scratch_bytes(M, N, K, splits, &need);
   if (scratch_bytes < need) return NC_ERR_WORKSPACE;
   static const nc::SkEpi map[4] = {nc::SkEpi::StoreT, nc::SkEpi::AddF32, nc::SkEpi::Relu2,
                                    nc::SkEpi::SoftcapF32};
@@ -1091,6 +1093,7 @@ int nc_op_few_rows_gemm(int32_t epilogue, const void* W, int32_t ldw, const void
   g.xb = xb;
   g.ssq_out = ssq_out;
   g.cap = cap;
+  g.splits = splits;
   g.cnt = static_cast<uint32_t*>(scratch);
   g.part = reinterpret_cast<float*>(static_cast<char*>(scratch) + align_up((uint64_t)(N / 16) * 4, kAlign));
   HIPCHECK(nc::skinny_gemm(g, map[epilogue], static_cast<hipStream_t>(stream)));

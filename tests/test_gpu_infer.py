@@ -164,10 +164,12 @@ def _bf16_exact(rng, shape):
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
 @pytest.mark.parametrize("M", [1, 5, 16, 17, 32])
 @pytest.mark.parametrize("N,K", [(48, 96), (1280, 1280), (208, 5120), (4096, 256)])
-def test_few_rows_gemm(epi, M, N, K):
+@pytest.mark.parametrize("splits", [0, 5])
+def test_few_rows_gemm(epi, M, N, K, splits):
     """Against an fp64 product of the same bf16 values; rows past M and the
     padding columns of C stay untouched. Covers one k slice and several
-    (the split count follows N and K)."""
+    (0: the count decoding picks, which gives 3 slices at K = 5120)."""
+    splits = min(splits, K // 32)
     rng = np.random.default_rng(M * 1000 + N + K + epi)
     W, W64 = _bf16_exact(rng, (N, K))
     X, X64 = _bf16_exact(rng, (M, K))
@@ -187,8 +189,9 @@ def test_few_rows_gemm(epi, M, N, K):
     if epi == 3:
         cap = 0.5 * float(np.abs(ref).max())      # so the cap bends the large values
         ref = cap * np.tanh(ref / cap)
-    scratch = torch.zeros(nc.nc_op_few_rows_scratch_bytes(M, N, K), dtype=torch.uint8, device="cuda")
-    nc.nc_op_few_rows_gemm(epi, W, K, X, K, C, ldc, M, N, K, scratch, cap=cap)
+    scratch = torch.zeros(nc.nc_op_few_rows_scratch_bytes(M, N, K, splits), dtype=torch.uint8,
+                          device="cuda")
+    nc.nc_op_few_rows_gemm(epi, W, K, X, K, C, ldc, M, N, K, scratch, cap=cap, splits=splits)
     torch.cuda.synchronize()
     out = C.double().cpu().numpy()
     got = out[:M, :N]
