@@ -13,6 +13,12 @@ seeded tokens with the same shape and id range stand in:
 Each row is one sequence of T + 1 draws; tokens are its first T entries and
 targets its last T (next-token targets).
 
+Token byte lengths (the tokenizer's table, for bits-per-byte evaluation) are
+synthetic too: ids 0..255 one byte each (the byte-level base of a BPE
+vocabulary), the last 8 ids zero (special tokens), the rest 1 + a geometric
+draw (at least 1, mean 3.8), so that a typical token spans about 4.8 bytes, the
+compression the tutorial quotes for the pages' tokenizer (section 2.1).
+
 Parameters for parity runs are N(0, std^2) per tensor, drawn with numpy's
 ``default_rng(seed)`` in float64 and rounded to float32, then to bf16 in bf16
 mode. (The library's own initialiser uses a different, counter-based
@@ -81,3 +87,12 @@ def as_float64(flat: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_bits_to_f32(flat).astype(np.float64)
     return np.asarray(flat, dtype=np.float32).astype(np.float64)
+
+
+def make_token_bytes(vocab: int, seed: int) -> np.ndarray:
+    """Synthetic byte length of every vocabulary id, int32 [vocab]."""
+    rng = np.random.default_rng(seed)
+    b = (1 + rng.geometric(1.0 / 3.8, size=vocab)).astype(np.int32)
+    b[:min(256, vocab)] = 1
+    b[max(0, vocab - 8):] = 0
+    return b

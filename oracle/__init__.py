@@ -22,9 +22,11 @@ from .model import (OracleConfig, layout, param_count, unpack, forward_loss,
                     rope, rope_bwd, causal_mqa, causal_mqa_bwd, softcap_ce_rows,
                     row_forward)
 from .rng import splitmix64_stream, init_params
+from .eval import bits_per_byte, bits_per_byte_from_losses
 
 __all__ = [
     "OracleConfig", "layout", "param_count", "unpack", "forward_loss",
     "forward_backward", "rmsnorm", "rmsnorm_bwd", "rope_tables", "rope",
     "rope_bwd", "causal_mqa", "causal_mqa_bwd", "softcap_ce_rows", "row_forward", "splitmix64_stream", "init_params",
+    "bits_per_byte", "bits_per_byte_from_losses",
 ]
