@@ -154,6 +154,27 @@ def optimizer_timing(step, nc, torch, c, reps=5):
                     "not part of the timed training step"}
 
 
+def bpb_timing(step, nc, torch, c, tok_d, tgt_d, reps=3):
+    """Bits-per-byte evaluation of the step's batch (the forward pass, the loss
+    and an fp64 byte-weighted reduction) with a synthetic byte table."""
+    from dense_gpt_pretraining_nanochat_amd import inputs
+    tb = torch.from_numpy(inputs.make_token_bytes(c.vocab_size, 7)).cuda()
+    s = torch.cuda.current_stream()
+    step.eval_bpb(tok_d, tgt_d, tb)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(s)
+    for _ in range(reps):
+        r = step.eval_bpb(tok_d, tgt_d, tb)
+    ev1.record(s)
+    ev1.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    v = r.cpu().tolist()
+    return {"ms_per_batch": round(ms, 3), "tokens_per_s": round(c.batch * c.seq_len / (ms / 1e3), 1),
+            "bits_per_byte": v[2], "bytes": int(v[1]),
+            "what": "forward + loss + byte-weighted fp64 reduction over the timed batch "
+                    "(synthetic byte table); not part of the timed training step"}
+
+
 def decode_bytes(c, pos):
     """Algorithmic HBM bytes of one decoding step at position pos: every block
     matrix and the lm_head read once, the batch's embedding rows, the cached
@@ -368,6 +389,7 @@ def main():
         "device_status": status,
         "wall_s_timed": round(wall, 3),
     }
+    out["eval_bpb"] = bpb_timing(step, nc, torch, c, tok_d, tgt_d)
     if not a.no_optimizer:
         out["optimizer"] = optimizer_timing(step, nc, torch, c)
         step.opt_state = step.opt_ws = None

@@ -73,6 +73,7 @@ _SIGS = {
     "nc_forward_loss": [_CFG, _P, _P, _P, _P, _U64, _P, _P],
     "nc_forward_backward": [_CFG, _P, _P, _P, _P, _P, _U64, _P, _P],
     "nc_forward_backward_accumulate": [_CFG, _P, _P, _P, _P, _P, _U64, _P, _P],
+    "nc_eval_bpb": [_CFG, _P, _P, _P, _P, _P, _U64, _P, _P, _P],
     "nc_kv_cache_bytes": [_CFG, _I32, ctypes.POINTER(_U64)],
     "nc_infer_workspace_bytes": [_CFG, _I32, ctypes.POINTER(_U64)],
     "nc_prefill": [_CFG, _P, _P, _I32, _P, _I32, _P, _U64, _P, _P],
@@ -238,6 +239,12 @@ def nc_optimizer_step(cfg, optim, params, grads, state, ows, grad_norm, stream=N
     _check(lib().nc_optimizer_step(ctypes.byref(cfg), ctypes.byref(optim), _ptr(params), _ptr(grads),
                                    _ptr(state), _ptr(ows), ows.numel() * ows.element_size(),
                                    _ptr(grad_norm), _stream(stream)), "nc_optimizer_step")
+
+
+def nc_eval_bpb(cfg, params, tokens, targets, token_bytes, ws, loss, bpb, stream=None):
+    _check(lib().nc_eval_bpb(ctypes.byref(cfg), _ptr(params), _ptr(tokens), _ptr(targets), _ptr(token_bytes),
+                             _ptr(ws), ws.numel() * ws.element_size(), _ptr(loss), _ptr(bpb),
+                             _stream(stream)), "nc_eval_bpb")
 
 
 def nc_kv_cache_bytes(cfg, max_seq) -> int:
@@ -424,6 +431,15 @@ class Step:
         nc_forward_backward_accumulate(self.cfg, self.params, tokens, targets, self.grads, self.ws,
                                        self.loss)
         return self.loss
+
+    def eval_bpb(self, tokens, targets, token_bytes):
+        """Bits per byte of the batch: a float64 device tensor (nats, bytes,
+        bits per byte); the mean loss lands in ``loss``."""
+        import torch
+        if getattr(self, "bpb", None) is None:
+            self.bpb = torch.zeros(3, dtype=torch.float64, device=self.device)
+        nc_eval_bpb(self.cfg, self.params, tokens, targets, token_bytes, self.ws, self.loss, self.bpb)
+        return self.bpb
 
     def optimizer_step(self, optim: NcOptimConfig):
         """One optimizer step on params from grads; optimizer state and

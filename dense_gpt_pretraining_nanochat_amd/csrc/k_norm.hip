@@ -387,6 +387,46 @@ __global__ __launch_bounds__(1024) void loss_mean_kernel(const float* __restrict
   }
 }
 
+// Bits per byte of a batch: the summed loss of the positions whose target has
+// a nonzero byte length, those lengths summed, and their ratio in bits, all in
+// fp64 and a fixed order (one workgroup). Targets are clamped as the loss
+// kernel clamps them.
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  const int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x % kWave) == 0) red[w] = v;
+  __syncthreads();
+  double s = 0.0;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  return s;
+}
+
+__global__ __launch_bounds__(1024) void bpb_kernel(const float* __restrict__ loss_rows,
+                                                   const int32_t* __restrict__ targets, int M,
+                                                   const int32_t* __restrict__ token_bytes, int V,
+                                                   double* __restrict__ out) {
+  __shared__ double red[16];
+  double nats = 0.0, bytes = 0.0;
+  for (int i = threadIdx.x; i < M; i += 1024) {
+    int t = targets[i];
+    t = t < 0 ? 0 : (t >= V ? V - 1 : t);
+    const int b = token_bytes[t];
+    if (b > 0) {
+      nats += (double)loss_rows[i];
+      bytes += (double)b;
+    }
+  }
+  nats = block_sum_f64(nats, red);
+  bytes = block_sum_f64(bytes, red);
+  if (threadIdx.x == 0) {
+    out[0] = nats;
+    out[1] = bytes;
+    out[2] = bytes > 0.0 ? nats / (0.69314718055994530942 * bytes) : __builtin_nan("");
+  }
+}
+
 __global__ void fill_zero_kernel(uint32_t* __restrict__ p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
@@ -479,6 +519,13 @@ hipError_t embed_bwd(DType t, const void* E, const int32_t* tok, const float* ri
 
 hipError_t loss_mean(const float* loss_rows, int M, float* out, uint32_t* status, hipStream_t s) {
   hipLaunchKernelGGL(loss_mean_kernel, dim3(1), dim3(1024), 0, s, loss_rows, M, out, status);
+  return hipGetLastError();
+}
+
+hipError_t bits_per_byte(const float* loss_rows, const int32_t* targets, int M, const int32_t* token_bytes,
+                         int V, double* out, hipStream_t s) {
+  if (M < 1 || V < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bpb_kernel, dim3(1), dim3(1024), 0, s, loss_rows, targets, M, token_bytes, V, out);
   return hipGetLastError();
 }
 

@@ -102,6 +102,10 @@ hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const f
 hipError_t softcap_ce(DType t, const void* logits, const int32_t* tgt, int R, int V, float cap,
                       float w, float* loss_rows, void* dlogits, uint32_t* status, hipStream_t s);
 hipError_t loss_mean(const float* loss_rows, int M, float* out, uint32_t* status, hipStream_t s);
+// out[0] = sum of loss_rows[i] over i with token_bytes[targets[i]] > 0, out[1] = sum of those
+// lengths, out[2] = out[0] / (ln 2 * out[1]) (NaN when out[1] = 0); fp64, fixed order
+hipError_t bits_per_byte(const float* loss_rows, const int32_t* targets, int M, const int32_t* token_bytes,
+                         int V, double* out, hipStream_t s);
 
 // ---- inference: KV cache, decode attention ---------------------------------------
 // Cache of one layer: [B][max_seq][256] of T (k-hat then v, 128 each).

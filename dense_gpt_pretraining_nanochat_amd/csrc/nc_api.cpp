@@ -494,6 +494,22 @@ int nc_forward_loss(const nc_config* cfg, const void* params, const int32_t* tok
   return run_step(cfg, params, tokens, targets, nullptr, ws, ws_bytes, loss_dev, stream, false);
 }
 
+int nc_eval_bpb(const nc_config* cfg, const void* params, const int32_t* tokens, const int32_t* targets,
+                const int32_t* token_bytes, void* ws, uint64_t ws_bytes, float* loss_dev, double* bpb_dev,
+                void* stream) {
+  int rc = validate(cfg);
+  if (rc) return rc;
+  if (!token_bytes || !bpb_dev) return NC_ERR_NULL;
+  if (misaligned(token_bytes) || misaligned(bpb_dev)) return NC_ERR_ALIGN;
+  rc = run_step(cfg, params, tokens, targets, nullptr, ws, ws_bytes, loss_dev, stream, false);
+  if (rc) return rc;
+  const Dims D = dims_of(cfg);
+  const Plan P = plan_of(D, false);
+  HIPCHECK(nc::bits_per_byte(at<float>(ws, P.loss_rows), targets, (int)D.M, token_bytes, D.V, bpb_dev,
+                             static_cast<hipStream_t>(stream)));
+  return NC_OK;
+}
+
 int nc_forward_backward(const nc_config* cfg, const void* params, const int32_t* tokens,
                         const int32_t* targets, float* grads, void* ws, uint64_t ws_bytes,
                         float* loss_dev, void* stream) {

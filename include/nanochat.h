@@ -134,6 +134,19 @@ int nc_forward_loss(const nc_config* cfg, const void* params, const int32_t* tok
                     const int32_t* targets, void* ws, uint64_t ws_bytes, float* loss_dev,
                     void* stream);
 
+/* Bits per byte of a batch (harness page, module list in "Cấu trúc thư mục
+ * và module chính": the loss-evaluation module reports bits per byte). Runs
+ * the forward pass as nc_forward_loss (same workspace; mean loss to
+ * *loss_dev), then, over the positions whose target id has a nonzero byte
+ * length in token_bytes (int32 [vocab_size] on the device: the tokenizer's
+ * byte length of every id; 0 for special tokens), writes to bpb_dev (3
+ * doubles on the device): the summed loss in nats, the summed byte lengths,
+ * and their ratio in bits per byte, sum / (ln 2 * bytes) (NaN when no
+ * position counts). Sums are fp64 in a fixed order. */
+int nc_eval_bpb(const nc_config* cfg, const void* params, const int32_t* tokens, const int32_t* targets,
+                const int32_t* token_bytes, void* ws, uint64_t ws_bytes, float* loss_dev, double* bpb_dev,
+                void* stream);
+
 /* Forward, loss and backward. grads (fp32, nc_param_count elements, same
  * layout as params) is OVERWRITTEN with d(mean loss)/d(params); padding
  * elements are left untouched. */

@@ -190,3 +190,20 @@ def test_inference_sizes_and_argument_checks():
     assert decode(max_seq=0) == -7
     assert decode(kv=None) == -3
     assert decode(ws_bytes=ws - 1) == -5
+
+
+def test_eval_bpb_argument_checks():
+    """NULL and misaligned byte-table or output pointers fail before any launch."""
+    L = nc.lib()
+    cfg = _cfg("C1")
+    ws = nc.nc_workspace_bytes(cfg, 0)
+    a = 1 << 20
+    p = ctypes.c_void_p
+
+    def call(tb=p(a), out=p(a)):
+        return L.nc_eval_bpb(ctypes.byref(cfg), p(a), p(a), p(a), tb, p(a), ws, p(a), out, None)
+
+    assert call(tb=None) == -3
+    assert call(out=None) == -3
+    assert call(tb=p(a + 4)) == -4
+    assert call(out=p(a + 8)) == -4
