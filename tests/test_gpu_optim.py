@@ -179,3 +179,48 @@ def test_optimizer_step_depth12_bf16():
     for tname, off, r, cc in oracle.layout(ocfg):
         sl = slice(off, off + r * cc)
         check_bf16(pg[sl] - p0[sl], po[sl] - p0[sl], tname)
+
+
+@pytest.mark.parametrize("name", ["C1", "C2"])
+def test_three_training_iterations_match_oracle(name):
+    """Forward + backward + optimizer step, three times in a row on one
+    seeded batch, against the oracle doing the same: the parameters after
+    the third step (the whole training loop's state) and the loss of every
+    iteration. In bf16 mode each update carries the one-step bar (rel L2
+    3e-2) and the parameter differences feed the next gradients, so the sum
+    of three updates is held to three times it (rel L2 <= 0.1, cosine >=
+    0.995); fp32 mode keeps max-rel 1e-3."""
+    c, cfg, ocfg, step, p64, dseed = _setup(name)
+    tok, tgt = inputs.make_tokens(c.vocab_size, c.seq_len, c.batch, dseed, TOKEN_LAW[name])
+    kw = dict(OC, max_grad_norm=1.0)
+    oc = ooptim.OptimConfig(**kw)
+    n = oracle.param_count(ocfg, padded=True)
+    po, s1, s2 = p64.copy(), np.zeros(n), np.zeros(n)
+    olosses = []
+    for k in range(3):
+        loss, g, _ = oracle.forward_backward(ocfg, po, tok, tgt)
+        olosses.append(loss)
+        po, s1, s2, _ = ooptim.optimizer_step(ocfg, oc, po, g, s1, s2, k + 1)
+        if c.dtype == "bf16":                     # bf16 parameters: rounded once per step
+            po = inputs.as_float64(inputs.f32_to_bf16_bits(po.astype(np.float32)), "bf16")
+    glosses = []
+    for k in range(3):
+        step.grads.fill_(0)
+        glosses.append(float(step.forward_backward(dev(tok), dev(tgt)).item()))
+        o = nc.nc_optim_config(kw["lr_adamw"], kw["beta1"], kw["beta2"], kw["eps"], kw["wd_adamw"],
+                               kw["lr_muon"], kw["momentum"], kw["wd_muon"], kw["max_grad_norm"], 5,
+                               k + 1)
+        step.optimizer_step(o)
+    torch.cuda.synchronize()
+    assert step.status() == 0
+    bar = 1e-4 if c.dtype == "f32" else 5e-3
+    for gl, ol in zip(glosses, olosses):
+        assert abs(gl - ol) <= bar * ol, (glosses, olosses)
+    assert glosses[2] < glosses[0]                 # the loop learns the batch
+    pg = host64(step.params)
+    for tname, off, r, cc in oracle.layout(ocfg):
+        sl = slice(off, off + r * cc)
+        if c.dtype == "f32":
+            assert max_rel(pg[sl] - p64[sl], po[sl] - p64[sl]) <= 1e-3, tname
+        else:
+            check_bf16(pg[sl] - p64[sl], po[sl] - p64[sl], tname, cos_min=0.995, l2_max=0.1)
