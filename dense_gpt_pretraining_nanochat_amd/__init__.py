@@ -86,6 +86,9 @@ _SIGS = {
     "nc_last_hip_error": [],
     "nc_op_gemm": [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P],
     "nc_op_wgrad": [_I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P],
+    "nc_op_gemm_axpby": [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                         ctypes.c_float, ctypes.c_float, _I32, ctypes.c_int64, ctypes.c_int64,
+                         ctypes.c_int64, _I32, _P],
     "nc_op_few_rows_scratch_bytes": [_I32, _I32, _I32, _I32, ctypes.POINTER(_U64)],
     "nc_op_few_rows_gemm": [_I32, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _I32, ctypes.c_float, _P,
                             ctypes.c_float, _P, _P, _I32, _P, _U64, _P],
@@ -303,6 +306,13 @@ def nc_op_few_rows_gemm(epilogue, W, ldw, X, ldx, C, ldc, M, N, K, scratch, cap=
 def nc_op_decode_attn(dtype, qkv, ldq, B, H, cache, max_seq, pos, part, o, ldo, stream=None):
     _check(lib().nc_op_decode_attn(_dt(dtype), _ptr(qkv), ldq, B, H, _ptr(cache), max_seq, pos,
                                    _ptr(part), _ptr(o), ldo, _stream(stream)), "nc_op_decode_attn")
+
+
+def nc_op_gemm_axpby(dtype, a_kcontig, b_kcontig, out_f32, A, B, C, C2, M, N, K, lda, ldb, ldc, alpha,
+                     beta, batch=1, sa=0, sb=0, sc=0, tile=0, stream=None):
+    _check(lib().nc_op_gemm_axpby(_dt(dtype), int(a_kcontig), int(b_kcontig), int(out_f32), _ptr(A), _ptr(B),
+                                  _ptr(C), _ptr(C2), M, N, K, lda, ldb, ldc, alpha, beta, batch, sa, sb,
+                                  sc, tile, _stream(stream)), "nc_op_gemm_axpby")
 
 
 def nc_op_wgrad(dtype, X1, X2, dW, partial, M, N1, N2, splits, stream=None):

@@ -141,20 +141,35 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, int split, int m, i
 #pragma unroll
     for (int r = 0; r < 4; ++r) w[r] = from_f32<T>(v[r] * 2.f * sqrtf(to_f32(a[r])));
     *reinterpret_cast<T4*>(static_cast<T*>(g.C) + off) = w;
+  } else if constexpr (EPI == Epi::AxpbyT || EPI == Epi::AxpbyF32) {
+    const T4 x = *reinterpret_cast<const T4*>(static_cast<const T*>(g.C2) + (size_t)m * g.ldc2 + n);
+    f32x4 y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = fmaf(g.alpha, v[r], g.beta * to_f32(x[r]));
+    if constexpr (EPI == Epi::AxpbyT) {
+      T4 w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = from_f32<T>(y[r]);
+      *reinterpret_cast<T4*>(static_cast<T*>(g.C) + off) = w;
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off) = y;
+    }
   }
 }
 
-// Arguments of batch item b: A and B advance by sa / sb elements of T, C by
-// sc elements of its own type (T or fp32, by epilogue).
+// Arguments of batch item b: A, B and C2 advance by sa / sb / sc2 elements of
+// T, C by sc elements of its own type (T or fp32, by epilogue).
 template <typename T, Epi EPI>
 __device__ __forceinline__ GemmArgs batch_item(const GemmArgs& g0, int b) {
   GemmArgs g = g0;
   if (b == 0) return g;
-  constexpr size_t csz = (EPI == Epi::StoreT || EPI == Epi::Relu2 || EPI == Epi::Relu2Bwd)
+  constexpr size_t csz = (EPI == Epi::StoreT || EPI == Epi::Relu2 || EPI == Epi::Relu2Bwd ||
+                          EPI == Epi::AxpbyT)
                              ? sizeof(T) : sizeof(float);
   g.A = static_cast<const char*>(g0.A) + (size_t)b * g0.sa * sizeof(T);
   g.B = static_cast<const char*>(g0.B) + (size_t)b * g0.sb * sizeof(T);
   g.C = static_cast<char*>(g0.C) + (size_t)b * g0.sc * csz;
+  if (g0.C2) g.C2 = static_cast<char*>(g0.C2) + (size_t)b * g0.sc2 * sizeof(T);
   return g;
 }
 
@@ -382,6 +397,8 @@ struct DmaOperand {
 // for Relu2Bwd), read ahead of use: 4 consecutive values per chunk.
 template <Epi EPI> struct EpiIn { typedef f32x4 type; };
 template <> struct EpiIn<Epi::Relu2Bwd> { typedef bf16x4 type; };
+template <> struct EpiIn<Epi::AxpbyT> { typedef bf16x4 type; };
+template <> struct EpiIn<Epi::AxpbyF32> { typedef bf16x4 type; };
 
 template <Epi EPI>
 __device__ __forceinline__ void epilogue4_in(const GemmArgs& g, int split, int m, int n, f32x4 v,
@@ -394,6 +411,18 @@ __device__ __forceinline__ void epilogue4_in(const GemmArgs& g, int split, int m
 #pragma unroll
     for (int r = 0; r < 4; ++r) w[r] = from_f32<bf16>(v[r] * 2.f * sqrtf(to_f32(in[r])));
     *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.C) + off) = w;
+  } else if constexpr (EPI == Epi::AxpbyT || EPI == Epi::AxpbyF32) {
+    f32x4 y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) y[r] = fmaf(g.alpha, v[r], g.beta * to_f32(in[r]));
+    if constexpr (EPI == Epi::AxpbyT) {
+      bf16x4 w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = from_f32<bf16>(y[r]);
+      *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.C) + off) = w;
+    } else {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off) = y;
+    }
   } else {
     epilogue4<bf16, EPI>(g, split, m, n, v);
   }
@@ -551,14 +580,16 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
   constexpr int RS = TN + 4;                                   // padded row, floats
   constexpr int CPR = TN / 4;                                  // 16-byte chunks per row
   constexpr int CH = 32 * CPR / 64;                            // chunks per lane per block
-  constexpr bool READS = EPI == Epi::AddF32 || EPI == Epi::Relu2Bwd;
+  constexpr bool READS = EPI == Epi::AddF32 || EPI == Epi::Relu2Bwd || EPI == Epi::AxpbyT ||
+                        EPI == Epi::AxpbyF32;
+  constexpr bool READS_C2 = EPI == Epi::Relu2Bwd || EPI == Epi::AxpbyT || EPI == Epi::AxpbyF32;
   typedef typename EpiIn<EPI>::type In;
   In pre[CH];
   auto fetch1 = [&](int i, int u) -> In {
     const int c = lane + 64 * u;
     const int m = min(m0 + wm * TM + i * 32 + c / CPR, g.M - 1);
     const int n = min(n0 + wn * TN + (c % CPR) * 4, g.N - 4);
-    if constexpr (EPI == Epi::Relu2Bwd)
+    if constexpr (READS_C2)
       return *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(g.C2) + (size_t)m * g.ldc2 + n);
     else
       return *reinterpret_cast<const f32x4*>(static_cast<const float*>(g.C) + (size_t)m * g.ldc + n);
@@ -648,6 +679,8 @@ hipError_t dispatch_epi(Epi epi, const GemmArgs& g, hipStream_t s) {
     case Epi::Relu2: return launch<T, AK, BKC, Epi::Relu2>(g, s);
     case Epi::Relu2Bwd: return launch<T, AK, BKC, Epi::Relu2Bwd>(g, s);
     case Epi::PartialF32: return launch<T, AK, BKC, Epi::PartialF32>(g, s);
+    case Epi::AxpbyT: return launch<T, AK, BKC, Epi::AxpbyT>(g, s);
+    case Epi::AxpbyF32: return launch<T, AK, BKC, Epi::AxpbyF32>(g, s);
   }
   return hipErrorInvalidValue;
 }
@@ -668,7 +701,8 @@ hipError_t gemm(DType t, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs
   if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.splits <= 0) return hipErrorInvalidValue;
   if (g.M % 16 || g.N % 16 || g.K % bk || g.K / bk < g.splits) return hipErrorInvalidValue;
   if (epi != Epi::PartialF32 && g.splits != 1) return hipErrorInvalidValue;
-  if (g.batch < 0 || (g.batch > 1 && (epi == Epi::PartialF32 || epi == Epi::Relu2Bwd)))
+  if (g.batch < 0 || (g.batch > 1 && epi == Epi::PartialF32)) return hipErrorInvalidValue;
+  if ((epi == Epi::Relu2Bwd || epi == Epi::AxpbyT || epi == Epi::AxpbyF32) && !g.C2)
     return hipErrorInvalidValue;
   if ((long)((g.M + 127) / 128) * ((g.N + 127) / 128) * g.splits * (g.batch > 1 ? g.batch : 1) >
       (1L << 30))

@@ -151,26 +151,6 @@ __global__ __launch_bounds__(kOptThreads) void muon_normalize_kernel(
     x[i] = from_f32<T>(u[i] * inv);
 }
 
-// y (fp32) = alpha * x (type T)
-template <typename T>
-__global__ __launch_bounds__(kOptThreads) void scale_to_f32_kernel(const T* __restrict__ x,
-                                                                   size_t n, float alpha,
-                                                                   float* __restrict__ y) {
-  for (size_t i = blockIdx.x * (size_t)kOptThreads + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * kOptThreads)
-    y[i] = alpha * to_f32(x[i]);
-}
-
-// y (type T) = alpha * x (fp32)
-template <typename T>
-__global__ __launch_bounds__(kOptThreads) void scale_from_f32_kernel(const float* __restrict__ x,
-                                                                     size_t n, float alpha,
-                                                                     T* __restrict__ y) {
-  for (size_t i = blockIdx.x * (size_t)kOptThreads + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * kOptThreads)
-    y[i] = from_f32<T>(alpha * x[i]);
-}
-
 // p = p * decay - coef * x  (x fp32 in the parameter's layout)
 template <typename T>
 __global__ __launch_bounds__(kOptThreads) void muon_update_kernel(T* __restrict__ p, size_t ps,
@@ -230,26 +210,6 @@ hipError_t muon_normalize(DType t, const float* u, size_t n, int items, const do
   else
     hipLaunchKernelGGL(muon_normalize_kernel<float>, grid, dim3(kOptThreads), 0, s, u, n, partial,
                        kMuonParts, static_cast<float*>(x));
-  return hipGetLastError();
-}
-
-hipError_t scale_to_f32(DType t, const void* x, size_t n, float alpha, float* y, hipStream_t s) {
-  if (t == DType::BF16)
-    hipLaunchKernelGGL(scale_to_f32_kernel<bf16>, dim3(grid_for(n)), dim3(kOptThreads), 0, s,
-                       static_cast<const bf16*>(x), n, alpha, y);
-  else
-    hipLaunchKernelGGL(scale_to_f32_kernel<float>, dim3(grid_for(n)), dim3(kOptThreads), 0, s,
-                       static_cast<const float*>(x), n, alpha, y);
-  return hipGetLastError();
-}
-
-hipError_t scale_from_f32(DType t, const float* x, size_t n, float alpha, void* y, hipStream_t s) {
-  if (t == DType::BF16)
-    hipLaunchKernelGGL(scale_from_f32_kernel<bf16>, dim3(grid_for(n)), dim3(kOptThreads), 0, s, x,
-                       n, alpha, static_cast<bf16*>(y));
-  else
-    hipLaunchKernelGGL(scale_from_f32_kernel<float>, dim3(grid_for(n)), dim3(kOptThreads), 0, s, x,
-                       n, alpha, static_cast<float*>(y));
   return hipGetLastError();
 }
 

@@ -18,6 +18,8 @@ enum class Epi {
   Relu2,       // C (T) = a = relu(acc)^2
   Relu2Bwd,    // C (T) = acc * 2 * sqrt(C2[m,n])       (C2 holds a = relu(u)^2, type T)
   PartialF32,  // C (float) + split*M*ldc = acc over this split's K range
+  AxpbyT,      // C (T) = alpha * acc + beta * C2[m,n] (C2 of type T)
+  AxpbyF32,    // C (float) = alpha * acc + beta * C2[m,n] (C2 of type T)
 };
 struct GemmArgs {
   const void* A;
@@ -29,7 +31,8 @@ struct GemmArgs {
   int splits;        // K slices (PartialF32 only); K % (splits * 64) == 0
   int tile;          // output tile edge: 0 = choose, 128 or 256 (256: bf16 only)
   int batch;         // independent products of this shape (0 or 1: one)
-  int64_t sa, sb, sc;  // element strides between batch items of A, B and C (C2 is not batched)
+  int64_t sa, sb, sc, sc2;  // element strides between batch items of A, B, C and C2
+  float alpha, beta;        // Axpby epilogues
 };
 // compute units of the current device (256 when it cannot be queried)
 int device_cus();
@@ -187,9 +190,6 @@ hipError_t muon_momentum(const float* g, float* buf, size_t gs, float* u, size_t
 // x (T) = u / (||u||_F + 1e-7), per item (u, x packed)
 hipError_t muon_normalize(DType t, const float* u, size_t n, int items, const double* partial,
                           void* x, hipStream_t s);
-// y (fp32) = alpha * x (T);  y (T) = alpha * x (fp32)
-hipError_t scale_to_f32(DType t, const void* x, size_t n, float alpha, float* y, hipStream_t s);
-hipError_t scale_from_f32(DType t, const float* x, size_t n, float alpha, void* y, hipStream_t s);
 // p (T) = p * decay - coef * x (fp32), per item (p at stride ps, x packed)
 hipError_t muon_update(DType t, void* p, size_t ps, const float* x, size_t n, int items, float decay,
                        float coef, hipStream_t s);

@@ -531,7 +531,7 @@ constexpr float kNsA = 3.4445f, kNsB = -4.7750f, kNsC = 2.0315f;
 
 struct OptPlan {
   uint64_t norm_partial, norm_scale, muon_partial;
-  uint64_t u, x0, x, a, cf, bt, df, xf;
+  uint64_t u, x0, x, a, bt, df, xf;
   uint64_t total;
 };
 
@@ -554,7 +554,6 @@ OptPlan opt_plan_of(const Dims& D) {
   P.x0 = take(D.esz * big);
   P.x = take(D.esz * big);
   P.a = take(D.esz * sq);
-  P.cf = take(4 * sq);
   P.bt = take(D.esz * sq);
   P.df = take(4 * big);
   P.xf = take(4 * big);
@@ -596,6 +595,33 @@ hipError_t gemm_batched(DType dt, bool ak, bool bk, Epi epi, const void* A, cons
   return nc::gemm(dt, ak, bk, epi, g, s);
 }
 
+// Batched product with the alpha * acc + beta * C2 epilogue (C2 laid out as C).
+hipError_t gemm_axpby(DType dt, bool ak, bool bk, Epi epi, const void* A, const void* B, void* C,
+                      const void* C2, int M, int N, int K, int lda, int ldb, int ldc, int batch,
+                      int64_t sa, int64_t sb, int64_t sc, float alpha, float beta, hipStream_t s) {
+  nc::GemmArgs g{};
+  g.A = A;
+  g.B = B;
+  g.C = C;
+  g.C2 = const_cast<void*>(C2);
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.ldc = ldc;
+  g.ldc2 = ldc;
+  g.splits = 1;
+  g.batch = batch;
+  g.sa = sa;
+  g.sb = sb;
+  g.sc = sc;
+  g.sc2 = sc;
+  g.alpha = alpha;
+  g.beta = beta;
+  return nc::gemm(dt, ak, bk, epi, g, s);
+}
+
 // One Muon step on every layer's [R, C] matrix of one kind: params, grads and
 // momentum of layer l sit at element offset first + l * stride.
 int muon_kind(const Dims& D, const OptPlan& P, void* ows, const nc_optim_config* o, void* params,
@@ -630,19 +656,20 @@ int muon_kind(const Dims& D, const OptPlan& P, void* ows, const nc_optim_config*
       HIPCHECK(nc::transpose(dt, x0 + l * n * D.esz, R, C, C, X + l * n * D.esz, R, s));
   }
   void* A = at<char>(ows, P.a);
-  float* cf = at<float>(ows, P.cf);
   void* bt = at<char>(ows, P.bt);
+  char* Xn = tall ? x0 : at<char>(ows, P.x);       // the other iterate buffer
   const int64_t rr = (int64_t)r * r, rc = (int64_t)r * c;
   for (int k = 0; k < o->ns_steps; ++k) {
-    // A = X X^T;  cf = (b/c) A + A A^T (= (b A + c A^2) / c, A symmetric)
+    // A = X X^T;  bt = A A^T + (b/c) A  (= (b A + c A^2) / c, A symmetric)
     HIPCHECK(gemm_batched(dt, true, true, Epi::StoreT, X, X, A, r, r, c, c, c, r, L, rc, rc, rr, s));
-    HIPCHECK(nc::scale_to_f32(dt, A, rr * L, kNsB / kNsC, cf, s));
-    HIPCHECK(gemm_batched(dt, true, true, Epi::AddF32, A, A, cf, r, r, r, r, r, r, L, rr, rr, rr, s));
-    HIPCHECK(nc::scale_from_f32(dt, cf, rr * L, 1.0f, bt, s));
-    // df = (a/c) X + cf X, so that the next iterate is c * df
-    HIPCHECK(nc::scale_to_f32(dt, X, rc * L, kNsA / kNsC, df, s));
-    HIPCHECK(gemm_batched(dt, true, false, Epi::AddF32, bt, X, df, r, c, r, r, c, c, L, rr, rc, rc, s));
-    if (k + 1 < o->ns_steps) HIPCHECK(nc::scale_from_f32(dt, df, rc * L, kNsC, X, s));
+    HIPCHECK(gemm_axpby(dt, true, true, Epi::AxpbyT, A, A, bt, A, r, r, r, r, r, r, L, rr, rr, rr, 1.0f,
+                        kNsB / kNsC, s));
+    // next iterate a X + (b A + c A^2) X = c (bt X) + a X; the last one in fp32 (df)
+    const bool last = k + 1 == o->ns_steps;
+    HIPCHECK(gemm_axpby(dt, true, false, last ? Epi::AxpbyF32 : Epi::AxpbyT, bt, X,
+                        last ? static_cast<void*>(df) : static_cast<void*>(Xn), X, r, c, r, r, c, c, L,
+                        rr, rc, rc, kNsC, kNsA, s));
+    if (!last) std::swap(X, Xn);
   }
   const float* fin = df;
   if (tall) {
@@ -650,7 +677,7 @@ int muon_kind(const Dims& D, const OptPlan& P, void* ows, const nc_optim_config*
       HIPCHECK(nc::transpose(DType::F32, df + l * n, r, c, c, xf + l * n, r, s));
     fin = xf;
   }
-  HIPCHECK(nc::muon_update(dt, p, stride, fin, n, L, decay, o->lr_muon * scale * kNsC, s));
+  HIPCHECK(nc::muon_update(dt, p, stride, fin, n, L, decay, o->lr_muon * scale, s));
   return NC_OK;
 }
 
@@ -1125,6 +1152,45 @@ int nc_op_decode_attn(int32_t dtype, const void* qkv, int32_t ldq, int32_t B, in
     return NC_ERR_ARG;
   HIPCHECK(nc::decode_attn(dt_of(dtype), qkv, ldq, B, H, cache, max_seq, pos, part, o, ldo,
                            static_cast<hipStream_t>(stream)));
+  return NC_OK;
+}
+
+int nc_op_gemm_axpby(int32_t dtype, int32_t a_kcontig, int32_t b_kcontig, int32_t out_f32, const void* A,
+                     const void* B, void* C, const void* C2, int32_t M, int32_t N, int32_t K, int32_t lda,
+                     int32_t ldb, int32_t ldc, float alpha, float beta, int32_t batch, int64_t sa,
+                     int64_t sb, int64_t sc, int32_t tile, void* stream) {
+  if (bad_dtype(dtype)) return NC_ERR_ARG;
+  if (!A || !B || !C || !C2) return NC_ERR_NULL;
+  if (M <= 0 || N <= 0 || K <= 0 || M % 16 || N % 16 || K % 64 || batch < 1) return NC_ERR_ARG;
+  const int vec = dtype == NC_BF16 ? 8 : 4;
+  if (lda % vec || ldb % vec || ldc % 4) return NC_ERR_ARG;
+  if (lda < (a_kcontig ? K : M) || ldb < (b_kcontig ? K : N) || ldc < N) return NC_ERR_ARG;
+  if (sa < 0 || sb < 0 || sc < 0 || (tile != 0 && tile != 128 && tile != 256) ||
+      (tile == 256 && dtype != NC_BF16))
+    return NC_ERR_ARG;
+  nc::GemmArgs g{};
+  g.A = A;
+  g.B = B;
+  g.C = C;
+  g.C2 = const_cast<void*>(C2);
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.lda = lda;
+  g.ldb = ldb;
+  g.ldc = ldc;
+  g.ldc2 = ldc;
+  g.splits = 1;
+  g.tile = tile;
+  g.batch = batch;
+  g.sa = sa;
+  g.sb = sb;
+  g.sc = sc;
+  g.sc2 = sc;
+  g.alpha = alpha;
+  g.beta = beta;
+  HIPCHECK(nc::gemm(dt_of(dtype), a_kcontig != 0, b_kcontig != 0, out_f32 ? Epi::AxpbyF32 : Epi::AxpbyT, g,
+                    static_cast<hipStream_t>(stream)));
   return NC_OK;
 }
 

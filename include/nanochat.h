@@ -305,6 +305,17 @@ int nc_op_few_rows_gemm(int32_t epilogue, const void* W, int32_t ldw, const void
 int nc_op_decode_attn(int32_t dtype, const void* qkv, int32_t ldq, int32_t B, int32_t H, const void* cache,
                       int32_t max_seq, int32_t pos, float* part, void* o, int32_t ldo, void* stream);
 
+/* Batched contraction with a linear-combination epilogue, as the Newton-Schulz
+ * iteration of the optimizer uses it: for batch item i (operands advance by
+ * sa, sb and sc elements; C2 is laid out as C and advances with it)
+ * C = alpha * (A B^T) + beta * C2, C2 of type T, C of type T (out_f32 = 0)
+ * or fp32 (out_f32 = 1). Operand orders and size rules as nc_op_gemm; tile
+ * 0 lets the library choose, 128 or 256 (bf16 only) forces the edge. */
+int nc_op_gemm_axpby(int32_t dtype, int32_t a_kcontig, int32_t b_kcontig, int32_t out_f32, const void* A,
+                     const void* B, void* C, const void* C2, int32_t M, int32_t N, int32_t K, int32_t lda,
+                     int32_t ldb, int32_t ldc, float alpha, float beta, int32_t batch, int64_t sa,
+                     int64_t sb, int64_t sc, int32_t tile, void* stream);
+
 /* Weight-gradient contraction dW[N1,N2] = X1^T X2 over M rows (X1 [M,N1],
  * X2 [M,N2], type T), split over `splits` K slices with a fixed-order fp32
  * reduction through `partial` (splits*N1*N2 floats; unused when splits = 1).

@@ -105,6 +105,31 @@ def test_gemm_256_tiles(ak, bk, epi):
         assert np.all(np.abs(got - ref) <= 2 ** -7 * np.abs(ref) + 1e-5 * np.abs(ref).max())
 
 
+@pytest.mark.parametrize("dtype,tile", [("f32", 128), ("bf16", 128), ("bf16", 256)])
+@pytest.mark.parametrize("bk", [1, 0])
+@pytest.mark.parametrize("out_f32", [0, 1])
+def test_gemm_axpby_batched(dtype, tile, bk, out_f32):
+    """C_i = alpha A_i B_i^T + beta C2_i for three batch items, ragged edges,
+    both kernels (tile edge forced), both operand orders the optimizer uses."""
+    batch, M, N, K = 3, 272, 208, 192
+    rng = np.random.default_rng(tile + 2 * bk + out_f32 + (dtype == "bf16"))
+    A, A64 = _as(rng.standard_normal((batch, M, K)), dtype)
+    B, B64 = _as(rng.standard_normal((batch, N, K) if bk else (batch, K, N)), dtype)
+    C2, C264 = _as(rng.standard_normal((batch, M, N)), dtype)
+    alpha, beta = 2.0315, 3.4445
+    Bm = B64 if bk else np.transpose(B64, (0, 2, 1))
+    ref = alpha * np.einsum("bmk,bnk->bmn", A64, Bm) + beta * C264
+    C = torch.zeros((batch, M, N), dtype=torch.float32, device="cuda") if out_f32 else _empty((batch, M, N), dtype)
+    nc.nc_op_gemm_axpby(dtype, 1, bk, out_f32, A, B, C, C2, M, N, K, K, K if bk else N, N, alpha, beta,
+                        batch=batch, sa=M * K, sb=N * K, sc=M * N, tile=tile)
+    torch.cuda.synchronize()
+    got = host64(C)
+    if out_f32 or dtype == "f32":
+        assert max_rel(got, ref) <= 1e-5, max_rel(got, ref)
+    else:
+        assert np.all(np.abs(got - ref) <= 2 ** -7 * np.abs(ref) + 1e-5 * np.abs(ref).max())
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("R,C", [(64, 64), (192, 1280), (8192, 384), (40, 24)])
 def test_transpose(dtype, R, C):
