@@ -55,6 +55,8 @@ def _args():
                     help="time only KV-cache inference: a 1024-token prefill, then decoding steps")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the separate timing of KV-cache decoding")
+    ap.add_argument("--no-eval", action="store_true",
+                    help="skip the separate timing of the bits-per-byte evaluation")
     ap.add_argument("--kernel-only", action="store_true",
                     help="launch only the roofline kernel (3x) and a 1 GiB device copy (3x)")
     return ap.parse_args()
@@ -389,7 +391,8 @@ def main():
         "device_status": status,
         "wall_s_timed": round(wall, 3),
     }
-    out["eval_bpb"] = bpb_timing(step, nc, torch, c, tok_d, tgt_d)
+    if not a.no_eval:
+        out["eval_bpb"] = bpb_timing(step, nc, torch, c, tok_d, tgt_d)
     if not a.no_optimizer:
         out["optimizer"] = optimizer_timing(step, nc, torch, c)
         step.opt_state = step.opt_ws = None
