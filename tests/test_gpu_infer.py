@@ -95,6 +95,20 @@ def test_decode_from_empty_cache(dtype):
         _check(got[p], want[:, p], dtype, f"position {p}")
 
 
+def test_wide_batch_takes_the_tiled_path():
+    """40 sequences in bf16: more rows than the few-row kernels take, so the
+    decoding step pads to 48 rows and runs the tiled GEMM, the separate norm
+    kernels and the gathered lm_head; same bar against the oracle."""
+    B, n = 40, 72
+    cfg, ocfg, params, P = _model(2, 1024, 64, B, "bf16", 21)
+    seq, _ = inputs.make_tokens(1024, n, B, 22, "zipf")
+    want = _oracle_logits(ocfg, P, seq)
+    positions = {63, 64, 71}
+    got = _run(cfg, params, seq, 64, 96, positions)
+    for p in sorted(positions):
+        _check(got[p], want[:, p], "bf16", f"position {p}")
+
+
 def test_prefill_longest_prompt():
     """A prompt of cfg.seq_len tokens (several attention tiles) into a cache
     of exactly that many positions."""
