@@ -91,7 +91,7 @@ _SIGS = {
                          ctypes.c_int64, _I32, _P],
     "nc_op_few_rows_scratch_bytes": [_I32, _I32, _I32, _I32, ctypes.POINTER(_U64)],
     "nc_op_few_rows_gemm": [_I32, _P, _I32, _P, _I32, _P, _I32, _I32, _I32, _I32, ctypes.c_float, _P,
-                            ctypes.c_float, _P, _P, _I32, _P, _U64, _P],
+                            ctypes.c_float, _P, _P, _I32, _I32, _P, _U64, _P],
     "nc_op_decode_attn": [_I32, _P, _I32, _I32, _I32, _P, _I32, _I32, _P, _P, _I32, _P],
     "nc_op_transpose": [_I32, _P, _I32, _I32, _I32, _P, _I32, _P],
     "nc_op_rmsnorm_fwd": [_I32, _P, _I32, _I32, _F32, _P, _P, _P],
@@ -296,9 +296,10 @@ def nc_op_few_rows_scratch_bytes(M, N, K, splits=0) -> int:
 
 
 def nc_op_few_rows_gemm(epilogue, W, ldw, X, ldx, C, ldc, M, N, K, scratch, cap=0.0, ssq_in=None,
-                        eps=0.0, xb=None, ssq_out=None, splits=0, stream=None):
+                        eps=0.0, xb=None, ssq_out=None, splits=0, ntile=0, stream=None):
     _check(lib().nc_op_few_rows_gemm(epilogue, _ptr(W), ldw, _ptr(X), ldx, _ptr(C), ldc, M, N, K, cap,
-                                     _ptr(ssq_in), eps, _ptr(xb), _ptr(ssq_out), splits, _ptr(scratch),
+                                     _ptr(ssq_in), eps, _ptr(xb), _ptr(ssq_out), splits, ntile,
+                                     _ptr(scratch),
                                      scratch.numel() * scratch.element_size(), _stream(stream)),
            "nc_op_few_rows_gemm")
 

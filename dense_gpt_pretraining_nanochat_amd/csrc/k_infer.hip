@@ -204,9 +204,11 @@ constexpr int kSkWaves = 8;
 constexpr int kSkU = 4;            // k steps per wavefront per batch
 constexpr int kSsqPer = 8;         // 16 x 8 = 128 column blocks: rows up to 2048 wide
 
-template <int MT, SkEpi EPI, bool NORM>
+template <int MT, int NT, SkEpi EPI, bool NORM>
 __global__ __launch_bounds__(512, 2) void skinny_kernel(SkArgs g) {
-  __shared__ __align__(16) float red[kSkWaves * MT * 256];
+  constexpr int U = NT == 1 ? kSkU : 2;        // k steps per wavefront per batch
+  constexpr int TILES = NT * MT;               // 16 x 16 output tiles per wavefront
+  __shared__ __align__(16) float red[kSkWaves * TILES * 256];
   __shared__ float ssq_red[16][32];
   __shared__ float rinv_s[32];
   __shared__ int last_s;
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(512, 2) void skinny_kernel(SkArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
   const int nb = blockIdx.x, sk = blockIdx.y, S = gridDim.y;
-  const int n0 = nb * 16;
+  const int n0 = nb * 16 * NT;
   const int nsteps = g.K >> 5;
   const int sb = (int)((long)sk * nsteps / S), se = (int)((long)(sk + 1) * nsteps / S);
   const bf16* __restrict__ W = static_cast<const bf16*>(g.W);
@@ -231,15 +233,20 @@ __global__ __launch_bounds__(512, 2) void skinny_kernel(SkArgs g) {
   }
 
   const bf16* wrow = W + (size_t)(n0 + l16) * g.ldw + 8 * lg;
-  f32x4 acc[MT];
+  const size_t wtile = (size_t)16 * g.ldw;     // next 16 W rows
+  f32x4 acc[NT][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto load = [&](int s0, bf16x8 (&a)[kSkU], bf16x8 (&x)[kSkU][MT]) {
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int u = 0; u < kSkU; ++u) {
+    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto load = [&](int s0, bf16x8 (&a)[U][NT], bf16x8 (&x)[U][MT]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       const int s = s0 + kSkWaves * u;
       if (s < se) {
-        a[u] = *reinterpret_cast<const bf16x8*>(wrow + 32 * s);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          a[u][nt] = *reinterpret_cast<const bf16x8*>(wrow + nt * wtile + 32 * s);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const int m = 16 * mt + l16;
@@ -249,22 +256,25 @@ __global__ __launch_bounds__(512, 2) void skinny_kernel(SkArgs g) {
       } else {
         // never multiplied, but kept zero: a matrix instruction the compiler
         // places under an EXEC mask still runs on every lane
-        a[u] = bf16x8{};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) a[u][nt] = bf16x8{};
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) x[u][mt] = bf16x8{};
       }
     }
   };
-  auto mma = [&](int s0, const bf16x8 (&a)[kSkU], const bf16x8 (&x)[kSkU][MT]) {
+  auto mma = [&](int s0, const bf16x8 (&a)[U][NT], const bf16x8 (&x)[U][MT]) {
 #pragma unroll
-    for (int u = 0; u < kSkU; ++u)
+    for (int u = 0; u < U; ++u)
       if (s0 + kSkWaves * u < se)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], x[u][mt], acc[mt], 0, 0, 0);
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][nt], x[u][mt], acc[nt][mt], 0, 0, 0);
   };
-  constexpr int kBatch = kSkWaves * kSkU;   // k steps of the workgroup per batch
-  bf16x8 a0[kSkU], x0[kSkU][MT], a1[kSkU], x1[kSkU][MT];
+  constexpr int kBatch = kSkWaves * U;      // k steps of the workgroup per batch
+  bf16x8 a0[U][NT], x0[U][MT], a1[U][NT], x1[U][MT];
   int s0 = sb + wave;
   load(s0, a0, x0);
   for (; s0 < se; s0 += 2 * kBatch) {
@@ -274,8 +284,10 @@ __global__ __launch_bounds__(512, 2) void skinny_kernel(SkArgs g) {
     mma(s0 + kBatch, a1, x1);
   }
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    *reinterpret_cast<f32x4*>(red + ((wave * MT + mt) * 64 + lane) * 4) = acc[mt];
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      *reinterpret_cast<f32x4*>(red + ((wave * TILES + nt * MT + mt) * 64 + lane) * 4) = acc[nt][mt];
   if constexpr (NORM) {
     float t = 0.f;
 #pragma unroll
@@ -290,20 +302,21 @@ __global__ __launch_bounds__(512, 2) void skinny_kernel(SkArgs g) {
       rinv_s[tid] = 1.0f / sqrtf(t / g.K + g.eps);
     }
   }
-  // thread e < MT * 64 holds C[16 mt + (ln & 15)][n0 + 4 (ln >> 4) + r], mt = e / 64, ln = e % 64
+  // thread e < TILES * 64: tile (nt, mt) = e / 64, lane ln = e % 64 holds
+  // C[16 mt + (ln & 15)][n0 + 16 nt + 4 (ln >> 4) + r]
   const int e = tid;
   f32x4 v = {0.f, 0.f, 0.f, 0.f};
-  if (e < MT * 64) {
+  if (e < TILES * 64) {
 #pragma unroll
-    for (int w = 0; w < kSkWaves; ++w) v += *reinterpret_cast<const f32x4*>(red + (w * MT * 64 + e) * 4);
+    for (int w = 0; w < kSkWaves; ++w) v += *reinterpret_cast<const f32x4*>(red + (w * TILES * 64 + e) * 4);
   }
   if (S > 1) {
     // Slices meet through device-coherent (agent-scope) stores and loads of
     // the partial tiles: a store is acknowledged once it is visible to every
     // XCD, so waiting for the acknowledgements before counting in orders the
     // tile before the count, without a whole-L2 write-back.
-    float* slot = g.part + ((size_t)nb * S + sk) * (MT * 256);
-    if (e < MT * 64) {
+    float* slot = g.part + ((size_t)nb * S + sk) * (TILES * 256);
+    if (e < TILES * 64) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         __hip_atomic_store(slot + e * 4 + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -315,10 +328,10 @@ __global__ __launch_bounds__(512, 2) void skinny_kernel(SkArgs g) {
                (uint32_t)(S - 1);
     __syncthreads();
     if (!last_s) return;
-    if (e < MT * 64) {
+    if (e < TILES * 64) {
       v = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int k = 0; k < S; ++k) {
-        const float* src = g.part + ((size_t)nb * S + k) * (MT * 256) + e * 4;
+        const float* src = g.part + ((size_t)nb * S + k) * (TILES * 256) + e * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           v[i] += __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -327,9 +340,9 @@ __global__ __launch_bounds__(512, 2) void skinny_kernel(SkArgs g) {
     if (tid == 0) __hip_atomic_store(g.cnt + nb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  if (e >= MT * 64) return;
-  const int ln = e & 63;
-  const int m = 16 * (e >> 6) + (ln & 15), n = n0 + 4 * (ln >> 4);
+  if (e >= TILES * 64) return;
+  const int ln = e & 63, tile = e >> 6, nt = tile / MT, mt = tile % MT;
+  const int m = 16 * mt + (ln & 15), n = n0 + 16 * nt + 4 * (ln >> 4);
   const bool row = m < g.M;
   if constexpr (NORM) v *= rinv_s[m];
   const size_t off = (size_t)m * g.ldc + n;
@@ -360,7 +373,7 @@ __global__ __launch_bounds__(512, 2) void skinny_kernel(SkArgs g) {
       float q = row ? c[0] * c[0] + c[1] * c[1] + c[2] * c[2] + c[3] * c[3] : 0.f;
       q += __shfl_xor(q, 16, 64);
       q += __shfl_xor(q, 32, 64);
-      if (row && (ln >> 4) == 0) g.ssq_out[nb * 32 + m] = q;
+      if (row && (ln >> 4) == 0) g.ssq_out[(nb * NT + nt) * 32 + m] = q;
     }
   } else {
     const float inv = 1.0f / g.cap;
@@ -496,6 +509,17 @@ size_t skinny_part_bytes(int M, int N, int K, int splits) {
   return S > 1 ? (size_t)(N / 16) * S * MT * 256 * sizeof(float) : 0;
 }
 
+// Wider workgroups re-read X less per column; measured at the decoding shapes
+// (32 rows, weights streamed once per step): 4 tiles for the lm_head, 2 for the
+// MLP up-projection, 1 for the narrow products, whose workgroup count it would
+// halve.
+int skinny_ntile(int N, int K) {
+  (void)K;
+  if (N % 64 == 0 && N / 64 >= 512) return 4;
+  if (N % 32 == 0 && N >= 4096) return 2;
+  return 1;
+}
+
 hipError_t skinny_gemm(const SkArgs& a, SkEpi epi, hipStream_t s) {
   if (a.M < 1 || a.M > kSkinnyMaxRows || a.N < 16 || a.N % 16 || a.K < 32 || a.K % 32 || a.ldw % 8 ||
       a.ldx % 8 || a.ldc % 4 || a.ldw < a.K || a.ldx < a.K || a.ldc < a.N)
@@ -504,27 +528,38 @@ hipError_t skinny_gemm(const SkArgs& a, SkEpi epi, hipStream_t s) {
   if ((a.xb || a.ssq_out) && epi != SkEpi::AddF32) return hipErrorInvalidValue;
   const int S = a.splits > 0 ? a.splits : skinny_splits(a.N, a.K);
   if (S > a.K / 32 || (S > 1 && (!a.part || !a.cnt))) return hipErrorInvalidValue;
-  const dim3 grid(a.N / 16, S), block(512);
+  const int NT = a.ntile > 0 ? a.ntile : skinny_ntile(a.N, a.K);
+  if ((NT != 1 && NT != 2 && NT != 4) || a.N % (16 * NT)) return hipErrorInvalidValue;
+  const dim3 grid(a.N / (16 * NT), S), block(512);
   const bool norm = a.ssq_in != nullptr;
-#define NC_SKINNY(MT, E)                                                     \
-  do {                                                                       \
-    if (norm)                                                                \
-      hipLaunchKernelGGL((skinny_kernel<MT, E, true>), grid, block, 0, s, a);  \
-    else                                                                     \
-      hipLaunchKernelGGL((skinny_kernel<MT, E, false>), grid, block, 0, s, a); \
+#define NC_SKINNY(MT, NTV, E)                                                      \
+  do {                                                                             \
+    if (norm)                                                                      \
+      hipLaunchKernelGGL((skinny_kernel<MT, NTV, E, true>), grid, block, 0, s, a);   \
+    else                                                                           \
+      hipLaunchKernelGGL((skinny_kernel<MT, NTV, E, false>), grid, block, 0, s, a);  \
   } while (0)
-#define NC_SKINNY_EPI(MT)                                            \
-  switch (epi) {                                                     \
-    case SkEpi::StoreT: NC_SKINNY(MT, SkEpi::StoreT); break;         \
-    case SkEpi::AddF32: NC_SKINNY(MT, SkEpi::AddF32); break;         \
-    case SkEpi::Relu2: NC_SKINNY(MT, SkEpi::Relu2); break;           \
-    case SkEpi::SoftcapF32: NC_SKINNY(MT, SkEpi::SoftcapF32); break; \
+#define NC_SKINNY_EPI(MT, NTV)                                             \
+  switch (epi) {                                                           \
+    case SkEpi::StoreT: NC_SKINNY(MT, NTV, SkEpi::StoreT); break;          \
+    case SkEpi::AddF32: NC_SKINNY(MT, NTV, SkEpi::AddF32); break;          \
+    case SkEpi::Relu2: NC_SKINNY(MT, NTV, SkEpi::Relu2); break;            \
+    case SkEpi::SoftcapF32: NC_SKINNY(MT, NTV, SkEpi::SoftcapF32); break;  \
+  }
+#define NC_SKINNY_NT(MT)          \
+  if (NT == 1) {                  \
+    NC_SKINNY_EPI(MT, 1)          \
+  } else if (NT == 2) {           \
+    NC_SKINNY_EPI(MT, 2)          \
+  } else {                        \
+    NC_SKINNY_EPI(MT, 4)          \
   }
   if (a.M <= 16) {
-    NC_SKINNY_EPI(1)
+    NC_SKINNY_NT(1)
   } else {
-    NC_SKINNY_EPI(2)
+    NC_SKINNY_NT(2)
   }
+#undef NC_SKINNY_NT
 #undef NC_SKINNY_EPI
 #undef NC_SKINNY
   return hipGetLastError();

@@ -147,10 +147,12 @@ struct SkArgs {
   float* part;            // split partials: skinny_part_bytes
   uint32_t* cnt;          // N/16 arrival counters, zero on entry (left zero)
   int splits;             // k slices; 0 = skinny_splits(N, K)
+  int ntile;              // 16-column tiles per workgroup (1, 2 or 4); 0 = skinny_ntile(N, K)
 };
 // k splits the product uses, and the partial-tile scratch they need
 int skinny_splits(int N, int K);
 size_t skinny_part_bytes(int M, int N, int K, int splits = 0);
+int skinny_ntile(int N, int K);
 hipError_t skinny_gemm(const SkArgs& a, SkEpi epi, hipStream_t s);
 // x[m] = n(E[tok[m]]) (fp32), xb[m] = bf16 copy, ssq[j * 32 + m] = sum of x[m]^2 over columns
 // 16j..16j+15; one row per sequence (M <= 32), d <= 2048

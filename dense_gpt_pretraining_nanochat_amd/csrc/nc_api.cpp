@@ -1105,9 +1105,11 @@ int nc_op_few_rows_scratch_bytes(int32_t M, int32_t N, int32_t K, int32_t splits
 
 int nc_op_few_rows_gemm(int32_t epilogue, const void* W, int32_t ldw, const void* X, int32_t ldx, void* C,
                         int32_t ldc, int32_t M, int32_t N, int32_t K, float cap, const float* ssq_in,
-                        float eps, void* xb, float* ssq_out, int32_t splits, void* scratch,
+                        float eps, void* xb, float* ssq_out, int32_t splits, int32_t ntile, void* scratch,
                         uint64_t scratch_bytes, void* stream) {
   if (epilogue < 0 || epilogue > 3 || splits < 0 || splits > K / 32) return NC_ERR_ARG;
+  if (ntile != 0 && ntile != 1 && ntile != 2 && ntile != 4) return NC_ERR_ARG;
+  if (ntile > 0 && N % (16 * ntile)) return NC_ERR_ARG;
   if (!W || !X || !C || !scratch) return NC_ERR_NULL;
   if (misaligned(scratch)) return NC_ERR_ALIGN;
   if (M < 1 || M > nc::kSkinnyMaxRows || N < 16 || N % 16 || K < 32 || K % 32 || K > 2048 * (ssq_in ? 1 : 64))
@@ -1137,6 +1139,7 @@ int nc_op_few_rows_gemm(int32_t epilogue, const void* W, int32_t ldw, const void
   g.ssq_out = ssq_out;
   g.cap = cap;
   g.splits = splits;
+  g.ntile = ntile;
   g.cnt = static_cast<uint32_t*>(scratch);
   g.part = reinterpret_cast<float*>(static_cast<char*>(scratch) + align_up((uint64_t)(N / 16) * 4, kAlign));
   HIPCHECK(nc::skinny_gemm(g, map[epilogue], static_cast<hipStream_t>(stream)));

@@ -288,13 +288,15 @@ int nc_op_gemm(int32_t dtype, int32_t a_kcontig, int32_t b_kcontig, int32_t epil
  * leading dimension ldc) and ssq_out[j*32 + m] (sum of the squares of new C
  * row m over columns 16j..16j+15). N % 16 == 0, K % 32 == 0, ldw and ldx
  * multiples of 8, ldc of 4. splits: slices of K (1..K/32) reduced in slice
- * order, 0 = the count decoding uses. scratch: nc_op_few_rows_scratch_bytes bytes,
+ * order, 0 = the count decoding uses; ntile: 16-column tiles per workgroup
+ * (1, 2 or 4, dividing N/16), 0 = decoding's choice. scratch:
+ * nc_op_few_rows_scratch_bytes bytes,
  * 256-B aligned, its first N/16 words zero on entry (left zero). Results do
  * not depend on timing (fixed-order reductions). */
 int nc_op_few_rows_scratch_bytes(int32_t M, int32_t N, int32_t K, int32_t splits, uint64_t* bytes);
 int nc_op_few_rows_gemm(int32_t epilogue, const void* W, int32_t ldw, const void* X, int32_t ldx, void* C,
                         int32_t ldc, int32_t M, int32_t N, int32_t K, float cap, const float* ssq_in,
-                        float eps, void* xb, float* ssq_out, int32_t splits, void* scratch,
+                        float eps, void* xb, float* ssq_out, int32_t splits, int32_t ntile, void* scratch,
                         uint64_t scratch_bytes, void* stream);
 
 /* Decoding attention over a KV cache (layout as nc_kv_cache_bytes

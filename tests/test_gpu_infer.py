@@ -178,12 +178,15 @@ def _bf16_exact(rng, shape):
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
 @pytest.mark.parametrize("M", [1, 5, 16, 17, 32])
 @pytest.mark.parametrize("N,K", [(48, 96), (1280, 1280), (208, 5120), (4096, 256)])
-@pytest.mark.parametrize("splits", [0, 5])
-def test_few_rows_gemm(epi, M, N, K, splits):
+@pytest.mark.parametrize("splits,ntile", [(0, 0), (5, 1), (0, 2), (5, 4)])
+def test_few_rows_gemm(epi, M, N, K, splits, ntile):
     """Against an fp64 product of the same bf16 values; rows past M and the
     padding columns of C stay untouched. Covers one k slice and several
-    (0: the count decoding picks, which gives 3 slices at K = 5120)."""
+    (0: the count decoding picks, which gives 3 slices at K = 5120) and 1, 2
+    or 4 column tiles per workgroup (0: decoding's choice)."""
     splits = min(splits, K // 32)
+    while ntile > 1 and N % (16 * ntile):
+        ntile //= 2
     rng = np.random.default_rng(M * 1000 + N + K + epi)
     W, W64 = _bf16_exact(rng, (N, K))
     X, X64 = _bf16_exact(rng, (M, K))
@@ -205,7 +208,7 @@ def test_few_rows_gemm(epi, M, N, K, splits):
         ref = cap * np.tanh(ref / cap)
     scratch = torch.zeros(nc.nc_op_few_rows_scratch_bytes(M, N, K, splits), dtype=torch.uint8,
                           device="cuda")
-    nc.nc_op_few_rows_gemm(epi, W, K, X, K, C, ldc, M, N, K, scratch, cap=cap, splits=splits)
+    nc.nc_op_few_rows_gemm(epi, W, K, X, K, C, ldc, M, N, K, scratch, cap=cap, splits=splits, ntile=ntile)
     torch.cuda.synchronize()
     out = C.double().cpu().numpy()
     got = out[:M, :N]
@@ -221,7 +224,8 @@ def test_few_rows_gemm(epi, M, N, K, splits):
 
 @pytest.mark.parametrize("M", [3, 32])
 @pytest.mark.parametrize("N,K", [(1536, 1280), (1280, 1280), (5120, 2048)])
-def test_few_rows_gemm_norm_and_residual_outputs(M, N, K):
+@pytest.mark.parametrize("ntile", [1, 4])
+def test_few_rows_gemm_norm_and_residual_outputs(M, N, K, ntile):
     """The RMS factor comes from per-16-column sums of squares; the residual
     epilogue also leaves a bf16 copy of the new rows and their sums of
     squares (what the next product folds its norm from)."""
@@ -236,7 +240,7 @@ def test_few_rows_gemm_norm_and_residual_outputs(M, N, K):
     scratch = torch.zeros(nc.nc_op_few_rows_scratch_bytes(M, N, K), dtype=torch.uint8, device="cuda")
     C = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
     ssq_in = torch.from_numpy(ss.astype(np.float32)).cuda()
-    nc.nc_op_few_rows_gemm(0, W, K, X, K, C, N, M, N, K, scratch, ssq_in=ssq_in, eps=eps)
+    nc.nc_op_few_rows_gemm(0, W, K, X, K, C, N, M, N, K, scratch, ssq_in=ssq_in, eps=eps, ntile=ntile)
     ref = r[:, None] * (X64 @ W64.T)
     torch.cuda.synchronize()
     got = C.double().cpu().numpy()
@@ -246,7 +250,7 @@ def test_few_rows_gemm_norm_and_residual_outputs(M, N, K):
     Cf = torch.from_numpy(base).cuda()
     xb = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
     ssq_out = torch.full(((N // 16), 32), -1.0, dtype=torch.float32, device="cuda")
-    nc.nc_op_few_rows_gemm(1, W, K, X, K, Cf, N, M, N, K, scratch, xb=xb, ssq_out=ssq_out)
+    nc.nc_op_few_rows_gemm(1, W, K, X, K, Cf, N, M, N, K, scratch, xb=xb, ssq_out=ssq_out, ntile=ntile)
     torch.cuda.synchronize()
     new = Cf.double().cpu().numpy()
     assert max_rel(new, base + X64 @ W64.T) <= 1e-5
