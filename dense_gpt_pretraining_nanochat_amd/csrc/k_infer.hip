@@ -9,10 +9,16 @@
 //
 // Multi-query attention means one cached K/V head per layer serves every
 // query head: a decoding workgroup stages 64 cached keys once and scores all
-// H heads against them. Scores are bounded by sqrt(128) (QK-norm), so the
-// softmax is shifted by the same fixed bound as in training and the chunk
-// partials sum_u p v and sum_u p simply add; they are combined in chunk order
+// H heads against them (bf16: on the matrix cores; fp32: on the vector
+// units). Scores are bounded by sqrt(128) (QK-norm), so the softmax is
+// shifted by the same fixed bound as in training and the chunk partials
+// sum_u p v and sum_u p simply add; they are combined in chunk order
 // (bitwise reproducible).
+//
+// The linear layers of a decoding step have one row per sequence; the
+// few-row product below streams each weight matrix once with many small
+// workgroups, folds the block norms in, and writes what the next product
+// needs to fold its own norm (the embedding kernel starts that chain).
 #include <math.h>
 
 #include "common.h"
