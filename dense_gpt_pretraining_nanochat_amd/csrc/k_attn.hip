@@ -118,9 +118,12 @@ struct AttnTypes {
   static constexpr int VEC = Vec16<T>::N;
   static constexpr int KB = 4 * VEC;           // contraction per fragment
   static constexpr int NS = D / KB;            // fragments along the head dim
-  static constexpr int KSTR = D + VEC;         // LDS row stride for 16-byte reads: 16-byte pad
-  // row stride for transpose reads: a 32-byte pad puts the four rows of one
-  // 16-lane read 32 bytes apart in the banks (conflict-free)
+  static constexpr int KSTR = D + VEC;         // LDS row stride, 16-byte pad
+  // bf16 tiles: a 32-byte pad. Measured with the bank-conflict counter, it
+  // leaves both the 16-byte row reads and the transpose reads conflict-free
+  // (with the 16-byte pad, 25-44% of the attention kernels' LDS cycles were
+  // conflicts): the LDS serves 32 lanes of a 16-byte read, or all 64 lanes
+  // of an 8-byte one, per pass over its banks.
   static constexpr int VSTR = sizeof(T) == 2 ? D + 2 * VEC : D + VEC;
   static constexpr int DC = D / VEC;           // 16-byte chunks per 128-wide row
   typedef typename Vec16<T>::type V;
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void attn_fwd_kernel(
     const T* __restrict__ qkv, int ldq, int Tn, int H, T* __restrict__ o, float* __restrict__ lse) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
-  constexpr int KT = BKV * A::KSTR;            // K tile: row-major, read with 16-byte reads
+  constexpr int KT = BKV * A::VSTR;            // K tile: row-major, read with 16-byte reads
   constexpr int VT = BKV * A::VSTR;            // V tile: row-major, read with transpose reads
   __shared__ __align__(16) T Ks[2 * KT];
   __shared__ __align__(16) T Vs[2 * VT];
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void attn_fwd_kernel(
 
   constexpr bool PFT = kPrefetch(sizeof(T));
   constexpr int NT = 256;                       // threads per workgroup
-  typedef PairStager<T, BKV, PFT ? 8 : 1, A::KSTR, A::VSTR> Stager;
+  typedef PairStager<T, BKV, PFT ? 8 : 1, A::VSTR, A::VSTR> Stager;
   Stager stg;
   const int ntiles = (tb0 + FQB + BKV - 1) / BKV;   // the last tile is the diagonal one
   if (PFT) {
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void attn_fwd_kernel(
     for (int s = 0; s < A::NS; ++s)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const V kf = *reinterpret_cast<const V*>(K + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
+        const V kf = *reinterpret_cast<const V*>(K + (kt * 16 + l16) * A::VSTR + s * A::KB + lg * A::VEC);
         Mma<T>::run(st[kt][0], kf, qf[0][s]);
         Mma<T>::run(st[kt][1], kf, qf[1][s]);
       }
@@ -378,7 +381,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   typedef AttnTypes<T> A;
   typedef typename A::V V;
   constexpr int BK = BKVQ;                      // keys per tile
-  constexpr int TILE = BK * A::KSTR;
+  constexpr int TILE = BK * A::VSTR;
   __shared__ __align__(16) T Ks[2 * TILE];
   __shared__ __align__(16) T Vs[2 * TILE];
 
@@ -415,7 +418,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 
   constexpr bool PFT = kPrefetch(sizeof(T));
   constexpr int NT = 256;                       // threads per workgroup
-  typedef PairStager<T, BK, PFT ? 4 : 1> Stager;
+  typedef PairStager<T, BK, PFT ? 4 : 1, A::VSTR, A::VSTR> Stager;
   Stager stg;
   // tiles 0 .. ntiles - 3 lie below every query of the block; the last two
   // (keys tb0 .. tb0 + 63) need the causal mask
@@ -440,8 +443,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
     for (int s = 0; s < A::NS; ++s)
 #pragma unroll
       for (int kt = 0; kt < BK / 16; ++kt) {
-        const V kf = *reinterpret_cast<const V*>(K + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
-        const V vf = *reinterpret_cast<const V*>(Vv + (kt * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
+        const V kf = *reinterpret_cast<const V*>(K + (kt * 16 + l16) * A::VSTR + s * A::KB + lg * A::VEC);
+        const V vf = *reinterpret_cast<const V*>(Vv + (kt * 16 + l16) * A::VSTR + s * A::KB + lg * A::VEC);
         Mma<T>::run(st[kt][0], kf, qf[0][s]);
         Mma<T>::run(st[kt][1], kf, qf[1][s]);
         Mma<T>::run(dpt[kt][0], vf, df[0][s]);
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
       const V b0 = CFrag<T>::pack(t0), b1 = CFrag<T>::pack(t1);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const V ka = CFrag<T>::read(K, A::KSTR, kk * 16 * NPT, dt * 16, lane);   // K^T
+        const V ka = CFrag<T>::read(K, A::VSTR, kk * 16 * NPT, dt * 16, lane);   // K^T
         Mma<T>::run(dq[dt][0], ka, b0);
         Mma<T>::run(dq[dt][1], ka, b1);
       }
@@ -551,7 +554,10 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
   typedef AttnTypes<T> A;
   typedef typename A::V V;
   constexpr int SQ = BQK;                      // query rows per step
-  constexpr int TILE = SQ * A::KSTR;
+  // Q and dO are read both as 16-byte row fragments and with the transpose
+  // read: the 32-byte row pad keeps both patterns free of bank conflicts
+  constexpr int ST = A::VSTR;
+  constexpr int TILE = SQ * ST;
   __shared__ __align__(16) T Qs[2 * TILE];
   __shared__ __align__(16) T Os[2 * TILE];
   __shared__ float stat_s[2][2 * SQ];          // lse (log2 domain), then delta
@@ -605,7 +611,7 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
   for (int c = tid; c < 2 * SQ * A::DC; c += DKW_THREADS) {
     const int which = c / (SQ * A::DC), r = (c / A::DC) % SQ, dc = c % A::DC;
     const T* src = which ? osrc(0) + (size_t)r * ldo : qsrc(0) + (size_t)r * ldq;
-    *reinterpret_cast<V*>((which ? Os : Qs) + r * A::KSTR + dc * A::VEC) =
+    *reinterpret_cast<V*>((which ? Os : Qs) + r * ST + dc * A::VEC) =
         *reinterpret_cast<const V*>(src + dc * A::VEC);
   }
   stats(0, 0);
@@ -644,8 +650,8 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
     for (int s = 0; s < A::NS; ++s)
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const V qa = *reinterpret_cast<const V*>(Q + (c * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
-        const V da = *reinterpret_cast<const V*>(O + (c * 16 + l16) * A::KSTR + s * A::KB + lg * A::VEC);
+        const V qa = *reinterpret_cast<const V*>(Q + (c * 16 + l16) * ST + s * A::KB + lg * A::VEC);
+        const V da = *reinterpret_cast<const V*>(O + (c * 16 + l16) * ST + s * A::KB + lg * A::VEC);
 #pragma unroll
         for (int kt = 0; kt < 1; ++kt) {
           Mma<T>::run(sa[c][kt], qa, kf[kt][s]);
@@ -683,8 +689,8 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
         const V sb = CFrag<T>::pack(dsa[kt] + kk * NPT);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const V oa = CFrag<T>::read(O, A::KSTR, kk * 16 * NPT, dt * 16, lane);
-          const V qa = CFrag<T>::read(Q, A::KSTR, kk * 16 * NPT, dt * 16, lane);
+          const V oa = CFrag<T>::read(O, ST, kk * 16 * NPT, dt * 16, lane);
+          const V qa = CFrag<T>::read(Q, ST, kk * 16 * NPT, dt * 16, lane);
           Mma<T>::run(dv[dt][kt], oa, pb);
           Mma<T>::run(dk[dt][kt], qa, sb);
         }
@@ -699,14 +705,14 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
         for (int i = 0; i < NPRE; ++i) {
           const int c = tid + i * DKW_THREADS;
           const int which = c / (SQ * A::DC), r = (c / A::DC) % SQ, dc = c % A::DC;
-          *reinterpret_cast<V*>((which ? On : Qn) + r * A::KSTR + dc * A::VEC) = pre[i];
+          *reinterpret_cast<V*>((which ? On : Qn) + r * ST + dc * A::VEC) = pre[i];
         }
       } else {
         __syncthreads();
         for (int c = tid; c < 2 * SQ * A::DC; c += DKW_THREADS) {
           const int which = c / (SQ * A::DC), r = (c / A::DC) % SQ, dc = c % A::DC;
           const T* src = which ? osrc(it + 1) + (size_t)r * ldo : qsrc(it + 1) + (size_t)r * ldq;
-          *reinterpret_cast<V*>((which ? On : Qn) + r * A::KSTR + dc * A::VEC) =
+          *reinterpret_cast<V*>((which ? On : Qn) + r * ST + dc * A::VEC) =
               *reinterpret_cast<const V*>(src + dc * A::VEC);
         }
       }
