@@ -617,26 +617,32 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
   stats(0, 0);
   __syncthreads();
 
-  for (int it = 0; it < niter; ++it) {
+  // bf16: Q/dO tiles are prefetched into registers two steps ahead (one step
+  // of math does not cover the load latency), alternating between two sets
+  constexpr int NPRE = 2 * SQ * A::DC / DKW_THREADS;
+  typedef typename A::V PreSet[PFT ? NPRE : 1];
+  auto prefetch = [&](int i, PreSet& pre) {
+#pragma unroll
+    for (int j = 0; j < NPRE; ++j) {
+      const int c = tid + j * DKW_THREADS;     // NPRE * threads = 2 * SQ * DC chunks
+      const int which = c / (SQ * A::DC), r = (c / A::DC) % SQ, dc = c % A::DC;
+      const T* src = which ? osrc(i) + (size_t)r * ldo : qsrc(i) + (size_t)r * ldq;
+      pre[j] = *reinterpret_cast<const V*>(src + dc * A::VEC);
+    }
+  };
+  PreSet preA, preB;
+  if (PFT && 1 < niter) prefetch(1, preA);
+
+  auto step = [&](const int it, PreSet& pre, PreSet& pre2) {
     const int tq0 = q0 + (it / H) * SQ;
     const T* Q = Qs + (it & 1) * TILE;
     const T* O = Os + (it & 1) * TILE;
     const float* lse_s = stat_s[it & 1];
     const float* dl_s = stat_s[it & 1] + SQ;
     const bool more = it + 1 < niter;
-    constexpr int NPRE = 2 * SQ * A::DC / DKW_THREADS;
-    typename A::V pre[PFT ? NPRE : 1];
     // next step's lse / delta, requested now and stored after this step's math
     const float stat_next = (more && tid < 2 * SQ) ? stat_of(it + 1) : 0.f;
-    if (PFT && more) {
-#pragma unroll
-      for (int i = 0; i < NPRE; ++i) {
-        const int c = tid + i * DKW_THREADS;   // NPRE * threads = 2 * SQ * DC chunks
-        const int which = c / (SQ * A::DC), r = (c / A::DC) % SQ, dc = c % A::DC;
-        const T* src = which ? osrc(it + 1) + (size_t)r * ldo : qsrc(it + 1) + (size_t)r * ldq;
-        pre[i] = *reinterpret_cast<const V*>(src + dc * A::VEC);
-      }
-    }
+    if (PFT && it + 2 < niter) prefetch(it + 2, pre2);
 
     // (a wavefront whose keys lie past T works on zero K/V fragments and
     // stores nothing: no branch here keeps the accumulators in place)
@@ -719,6 +725,10 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
       if (tid < 2 * SQ) stat_s[(it + 1) & 1][tid] = stat_next;
     }
     __syncthreads();
+  };
+  for (int it = 0; it < niter; it += 2) {
+    step(it, preA, preB);
+    if (it + 1 < niter) step(it + 1, preB, preA);
   }
   if (!kact) return;
   // fp32 partial sums of this query chunk: part[chunk][token][0..127 dK, 128..255 dV]
