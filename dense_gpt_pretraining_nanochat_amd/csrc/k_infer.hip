@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void decode_attn_mfma_kernel(const bf16* __res
                                                                float* __restrict__ part) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  constexpr int KR = 72;                       // LDS row: 64 keys + 16-byte pad
+  constexpr int KR = 80;                       // LDS row: 64 keys + 32-byte pad (conflict-free)
   __shared__ __align__(16) bf16 vt[128][KR];   // V^T of the chunk: [dcol][key]
   __shared__ __align__(16) bf16 pt[16][KR];    // P^T: [head][key]
   __shared__ float lsum[4][16];
