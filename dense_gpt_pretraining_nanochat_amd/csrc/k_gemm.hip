@@ -117,9 +117,9 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, int split, int m, i
   typedef T T4 __attribute__((ext_vector_type(4)));
   if constexpr (EPI == Epi::StoreT) {
     T4 w = {from_f32<T>(v[0]), from_f32<T>(v[1]), from_f32<T>(v[2]), from_f32<T>(v[3])};
-    *reinterpret_cast<T4*>(static_cast<T*>(g.C) + off) = w;
+    __builtin_nontemporal_store(w, reinterpret_cast<T4*>(static_cast<T*>(g.C) + off));
   } else if constexpr (EPI == Epi::StoreF32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off));
   } else if constexpr (EPI == Epi::AddF32) {
     f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off);
     *p = *p + v;
@@ -133,7 +133,7 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, int split, int m, i
       const float uf = fmaxf(v[r], 0.f);
       a[r] = from_f32<T>(uf * uf);
     }
-    *reinterpret_cast<T4*>(static_cast<T*>(g.C) + off) = a;
+    __builtin_nontemporal_store(a, reinterpret_cast<T4*>(static_cast<T*>(g.C) + off));
   } else if constexpr (EPI == Epi::Relu2Bwd) {
     // d relu(u)^2 / du = 2 relu(u) = 2 sqrt(a), a = relu(u)^2 as stored by Relu2
     const T4 a = *reinterpret_cast<const T4*>(static_cast<const T*>(g.C2) + (size_t)m * g.ldc2 + n);
@@ -304,13 +304,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g0) {
 //     row kb+j, columns c0+4q..+3, and output lane i receives k rows
 //     kb..kb+3 of column c0+i - the same fragment layout, no transpose pass.
 // Each lane's global source is chosen so that its fixed LDS destination
-// (instruction base + 16 * lane) receives the swizzled chunk. The barrier of
-// each stage sits between its two 16-wide k steps: the next stage's first
-// fragments are read while this stage's second-step MFMAs run. Waits on the
-// direct loads are explicit (vmcnt) and precede that barrier; a ring slot is
-// refilled only after every wavefront has passed the barrier that follows its
-// last read of that slot. Indices past the matrix edge are clamped, which
-// only feeds output rows/columns that the epilogue never stores.
+// (instruction base + 16 * lane) receives the swizzled chunk. The main loop
+// runs the two wavefronts of each SIMD in ping-pong (one issues its MFMAs
+// while the other reads fragments and issues loads, roles swapping at every
+// barrier); waits on the direct loads are explicit (vmcnt), and a ring slot
+// is refilled only after every wavefront has passed the barrier that follows
+// its last read of that slot. Indices past the matrix edge are clamped, which
+// only feeds output rows/columns that the epilogue never stores. Final
+// outputs are written with non-temporal stores (written once, read by a
+// later kernel), so they do not push operand slabs out of L2; split-K
+// partials, read back at once by the reduction, are stored normally.
 // MFMA 32x32 output layout: lane l, value r holds row 8*(r/4) + 4*(l/32) + r%4,
 // column l%32 of the (B-rows x A-rows) product, i.e. C[m = l%32][n = ...].
 // ---------------------------------------------------------------------------
@@ -405,12 +408,12 @@ __device__ __forceinline__ void epilogue4_in(const GemmArgs& g, int split, int m
                                              typename EpiIn<EPI>::type in) {
   const size_t off = (size_t)m * g.ldc + n;
   if constexpr (EPI == Epi::AddF32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off) = in + v;
+    __builtin_nontemporal_store(in + v, reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off));
   } else if constexpr (EPI == Epi::Relu2Bwd) {
     bf16x4 w;
 #pragma unroll
     for (int r = 0; r < 4; ++r) w[r] = from_f32<bf16>(v[r] * 2.f * sqrtf(to_f32(in[r])));
-    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.C) + off) = w;
+    __builtin_nontemporal_store(w, reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.C) + off));
   } else if constexpr (EPI == Epi::AxpbyT || EPI == Epi::AxpbyF32) {
     f32x4 y;
 #pragma unroll
@@ -476,16 +479,6 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
     da.issue(S, st);
     db.issue(S + kSlab, st);
   };
-  // stage st has landed in every wavefront's view and this wavefront's LDS
-  // reads are complete; stages issued after st (at most two) stay in flight
-  auto land = [&](int st) {
-    const int after = min(kStages - 2, nk - 1 - st);
-    if (after >= 2) NC_WAIT_VM_LGKM0(8);                      // 4 loads per stage per wave
-    else if (after == 1) NC_WAIT_VM_LGKM0(4);
-    else NC_WAIT_VM_LGKM0(0);
-    __builtin_amdgcn_s_barrier();
-  };
-
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -495,80 +488,69 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int ar = wm * TM, br = wn * TN;
-  bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-#pragma unroll
-  for (int st = 0; st < kStages - 1; ++st)
-    if (st < nk) issue(st);
-  land(0);
-  if (kStages - 1 < nk) issue(kStages - 1);
-  // No scalar loads outstanding from here on: LDS reads are then the only
-  // traffic on lgkmcnt (and return in order), so the loop's waits can be
-  // partial. The empty asm makes the epilogue's arguments live in scalar
-  // registers here, so their loads are not scheduled into the loop.
-  asm volatile("" ::"s"(g.C), "s"(g.C2), "s"(g.ldc), "s"(g.ldc2));
-  __builtin_amdgcn_s_waitcnt(0xC07F);                          // lgkmcnt 0, vmcnt/expcnt free
-#pragma unroll
-  for (int i = 0; i < FM; ++i) fa0[i] = DmaOperand<AK>::frag(smem, ar + i * 32, 0, lane);
-#pragma unroll
-  for (int j = 0; j < FN; ++j) fb0[j] = DmaOperand<BKC>::frag(smem + kSlab, br + j * 32, 0, lane);
-
-  // MFMAs of one 16-wide k step; `from` skips the first ones (in i-major order)
-  auto mfma_step = [&](const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN], int from = 0) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        if (i * FN + j >= from)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-  };
-  auto mfma_first = [&](const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN]) {
-    acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[0], fa[0], acc[0][0], 0, 0, 0);
-  };
   auto read_step = [&](const bf16* S, int ks, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) fa[i] = DmaOperand<AK>::frag(S, ar + i * 32, ks, lane);
 #pragma unroll
     for (int j = 0; j < FN; ++j) fb[j] = DmaOperand<BKC>::frag(S + kSlab, br + j * 32, ks, lane);
   };
-  // Every stage but the last: its second-step fragments are read under its
-  // first-step MFMAs, the next stage lands, and the next stage's first-step
-  // fragments are read under this stage's second-step MFMAs. The steady-state
-  // loop (a slot to refill every stage, two stages in flight behind the one
-  // landing) is straight-line code: with a branch around the landing the
-  // compiler cannot see that its wait (lgkmcnt 0) already covers the
-  // second-step fragments, and adds a full LDS wait that stalls the
-  // second-step MFMAs on the next stage's reads.
-  // Scheduling fences keep each phase's LDS reads ahead of the MFMAs they
-  // are meant to overlap. The compiler's wait before the first step-0 MFMA
-  // is a full LDS wait whenever direct loads are in flight; one MFMA goes
-  // first so that this wait covers only the step-0 fragments (read a whole
-  // MFMA step earlier), not the step-1 reads issued right after it.
-  int it = 0;
-  for (; it + kStages < nk; ++it) {
-    mfma_first(fa0, fb0);
+  auto mfma_step = [&](const bf16x8 (&fa)[FM], const bf16x8 (&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  };
+  // Wait until at most `after` stages of this wavefront's direct loads are in
+  // flight (4 loads per stage) and all of its LDS reads have returned.
+  auto wait_after = [&](int after) {
+    if (after >= 2) NC_WAIT_VM_LGKM0(8);
+    else if (after == 1) NC_WAIT_VM_LGKM0(4);
+    else NC_WAIT_VM_LGKM0(0);
+  };
+  // Workgroup barrier that the scheduler moves nothing across.
+  auto barrier = [&]() {
     __builtin_amdgcn_sched_barrier(0);
-    read_step(smem + (it % kStages) * STAGE, 1, fa1, fb1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step(fa0, fb0, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    NC_WAIT_VM_LGKM0(8);                                       // stage it+1 landed, this slot read
     __builtin_amdgcn_s_barrier();
-    issue(it + kStages);                                       // refills this stage's slot
-    read_step(smem + ((it + 1) % kStages) * STAGE, 0, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
-    mfma_step(fa1, fb1);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (; it + 1 < nk; ++it) {                                  // the last three: nothing to issue
-    read_step(smem + (it % kStages) * STAGE, 1, fa1, fb1);
+  };
+
+  // Ping-pong schedule. Each stage is one memory phase (read all fragments of
+  // the stage, issue this wavefront's direct loads three stages ahead, wait)
+  // and one compute phase (its 16 MFMAs), each closed by a barrier.
+  // Wavefronts 4..7 run one phase behind 0..3; wavefronts w and w + 4 share a
+  // SIMD, so on every SIMD one wavefront issues MFMAs while the other moves
+  // data. Every wavefront passes the same number of barriers (the leading
+  // group adds one at the end, the lagging one at the start).
+  // Ring safety: the loads of stage s + 3 go into the slot of stage s - 1,
+  // which the leading group read two phases earlier and the lagging group in
+  // the phase just closed (its reads had returned before that barrier). A
+  // stage's loads from both groups have landed before the barrier that opens
+  // the leading group's memory phase for it, since each wavefront waits for
+  // its own share of stage s + 1 in its memory phase for stage s.
+  const bool lag = __builtin_amdgcn_readfirstlane(wave) >= 4;
+#pragma unroll
+  for (int st = 0; st < kStages - 1; ++st)
+    if (st < nk) issue(st);
+  // The empty asm makes the epilogue's arguments live in scalar registers
+  // here, so their loads are not scheduled into the loop.
+  asm volatile("" ::"s"(g.C), "s"(g.C2), "s"(g.ldc), "s"(g.ldc2));
+  wait_after(min(kStages - 2, nk - 1));
+  barrier();
+  if (lag) barrier();
+  bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  for (int s = 0; s < nk; ++s) {
+    const bf16* S = smem + (s % kStages) * STAGE;
+    read_step(S, 0, fa0, fb0);
+    read_step(S, 1, fa1, fb1);
+    if (s + kStages - 1 < nk) issue(s + kStages - 1);
+    wait_after(min(s + kStages - 1, nk - 1) - (s + 1));
+    barrier();
     mfma_step(fa0, fb0);
-    land(it + 1);
-    read_step(smem + ((it + 1) % kStages) * STAGE, 0, fa0, fb0);
     mfma_step(fa1, fb1);
+    barrier();
   }
-  read_step(smem + ((nk - 1) % kStages) * STAGE, 1, fa1, fb1);
-  mfma_step(fa0, fb0);
-  mfma_step(fa1, fb1);
+  if (!lag) barrier();
 
   // Epilogue, staged through LDS so that global accesses cover whole rows:
   // the lane holds C[m][n..n+3] for m = 32i + l32, n = 32j + 8q + 4*lh; each
