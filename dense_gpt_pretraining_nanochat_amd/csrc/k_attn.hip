@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void attn_fwd_kernel(
   const QBlock qbk = qblock_of(blockIdx.x, Tn / FQB, (H + 1) / 2);
   const int tb0 = qbk.qb * FQB;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int h = 2 * qbk.hg + (wave & 1);
   const int tq0 = tb0 + BQ * (wave >> 1);
   const bool active = h < H;
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
   const QBlock qbk = qblock_of(blockIdx.x, Tn / FQB, (H + 1) / 2);
   const int tb0 = qbk.qb * FQB;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int h = 2 * qbk.hg + (wave & 1);
   const int tq0 = tb0 + BQ * (wave >> 1);
   const bool active = h < H;
@@ -570,7 +570,7 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
   const int q0 = kv0 + chunk * QCH;                      // first query token of this chunk
   const int q1 = min(Tn, q0 + QCH);
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const size_t row0 = (size_t)b * Tn;
   const int ldo = H * D;
   const int key0 = kv0 + wave * 16;            // this wave's 16 keys: key0 + l16
@@ -751,7 +751,7 @@ __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(const float* __res
                                                               int B, int Tn, int H,
                                                               T* __restrict__ dqkv, int ldd) {
   const size_t M = (size_t)B * Tn;
-  const size_t row = blockIdx.x * 4ull + (threadIdx.x >> 6);
+  const size_t row = blockIdx.x * 4ull + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= M) return;
   const int lane = threadIdx.x & 63;
   const int t = (int)(row % Tn);

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void embed_norm_fwd_kernel(const T* __restrict
                                                              float* __restrict__ rinv,
                                                              uint32_t* status) {
   const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int m = blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (m >= M) return;
   int id = tok[m];
   if (id < 0 || id >= V) {
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float* __restric
                                                           float eps, T* __restrict__ y,
                                                           float* __restrict__ rinv) {
   const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int m = blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (m >= M) return;
   const float* src = x + (size_t)m * d;
   f32x4 v[kMaxVec];
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ 
                                                           int d, float* __restrict__ dx,
                                                           T* __restrict__ g) {
   const int lane = threadIdx.x & 63;
-  const int m = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int m = blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (m >= M) return;
   const size_t base = (size_t)m * d;
   float gy[kMaxVec][4];
