@@ -293,7 +293,8 @@ def test_attention_fwd_bwd(dtype, B, T, H):
 # ---------------------------------------------------------------- cross-entropy
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("R,V", [(64, 512), (16, 65536), (33, 8192), (8, 384), (5, 388), (3, 65532)])
+@pytest.mark.parametrize("R,V", [(64, 512), (16, 65536), (33, 8192), (8, 384), (5, 388), (3, 65532),
+                                 (300, 65536), (600, 1000)])
 def test_softcap_ce(dtype, R, V):
     rng = np.random.default_rng(R + V)
     logits, logits64 = _as(rng.standard_normal((R, V)) * 8.0, dtype)   # logits in the dtype
