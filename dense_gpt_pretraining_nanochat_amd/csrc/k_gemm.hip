@@ -9,16 +9,18 @@
 // the residual add, the relu^2 activation of the MLP (same list) and its
 // derivative, so no separate elementwise pass touches HBM.
 //
-// Tiling: large bf16 products use a 256x256 output tile per 512-thread
-// workgroup (8 wavefronts in a 2x4 grid, 128x64 per wavefront = 8x4 MFMA
-// tiles of 16x16; 144 KB of LDS, one workgroup per CU); small or fp32 ones a
-// 128x128 tile per 256 threads (2x2 wavefronts of 64x64). Each K step stages a
-// 128-byte-wide slab of A and B in LDS (double-buffered, one barrier per step,
-// next slab prefetched into registers while the matrix cores work). bf16 uses
-// v_mfma_f32_16x16x32_bf16, fp32 uses four v_mfma_f32_16x16x4_f32 per 16-byte
-// fragment (true fp32 products, fp32 accumulation in both cases).
-// K-strided operands are transposed in registers on their way into LDS, so
-// the matrix-core reads are always 16-byte, K-contiguous LDS reads.
+// Two kernels. Large bf16 products (at least 256 output tiles) take
+// gemm_bf16_kernel: a 256x256 output tile per 512-thread workgroup (one per
+// CU), v_mfma_f32_32x32x16_bf16, operand slabs loaded straight from global
+// memory into a 4-stage LDS ring, and a ping-pong main loop (described at the
+// kernel). Everything else, and every fp32 product, takes gemm_kernel: a
+// 128x128 tile per 256 threads (2x2 wavefronts of 64x64), each 128-byte-wide
+// K slab of A and B staged through registers into LDS (double-buffered, one
+// barrier per slab, the next slab loaded while the matrix cores work), with
+// v_mfma_f32_16x16x32_bf16 or, for fp32, four v_mfma_f32_16x16x4_f32 per
+// 16-byte fragment (true fp32 products; fp32 accumulation in every case).
+// In gemm_kernel, K-strided operands are transposed in registers on their way
+// into LDS, so its matrix-core reads are always 16-byte, K-contiguous reads.
 // Workgroup ids are remapped so each XCD (8 per chip, own L2) walks a
 // contiguous, row-grouped range of output tiles.
 #include <type_traits>
