@@ -76,11 +76,14 @@ def test_gemm(dtype, ak, bk, epi, M, N, K):
 @pytest.mark.parametrize("ak,bk", [(1, 1), (1, 0), (0, 0), (0, 1)])
 @pytest.mark.parametrize("epi", [nc.EPI_STORE_T, nc.EPI_STORE_F32, nc.EPI_ADD_F32, nc.EPI_RELU2,
                                  nc.EPI_RELU2_BWD])
-def test_gemm_256_tiles(ak, bk, epi):
+@pytest.mark.parametrize("K", [64, 128, 320])
+def test_gemm_256_tiles(ak, bk, epi, K):
     """Shapes big enough for the 256x256 bf16 tile (>= 256 tiles), ragged on
-    both output edges (M = 16 * 260, N = 16 * 257), every operand order."""
-    M, N, K = 4160, 4112, 320
-    rng = np.random.default_rng(epi + 100 + 10 * ak + 20 * bk)
+    both output edges (M = 16 * 260, N = 16 * 257), every operand order; K of
+    2, 4 and 10 slabs of 32 (the shortest main loop, one exactly as deep as
+    the 4-slab ring, and one that refills it)."""
+    M, N = 4160, 4112
+    rng = np.random.default_rng(epi + 100 + 10 * ak + 20 * bk + K)
     A, A64 = _as(rng.standard_normal((M, K) if ak else (K, M)), "bf16")
     B, B64 = _as(rng.standard_normal((N, K) if bk else (K, N)), "bf16")
     ref = (A64 if ak else A64.T) @ (B64 if bk else B64.T).T
