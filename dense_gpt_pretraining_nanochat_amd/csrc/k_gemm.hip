@@ -584,10 +584,13 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
     const int c = lane + 64 * u;
     const int m = min(m0 + wm * TM + i * 32 + c / CPR, g.M - 1);
     const int n = min(n0 + wn * TN + (c % CPR) * 4, g.N - 4);
+    // read once, right before the output replaces it: non-temporal, like the stores
     if constexpr (READS_C2)
-      return *reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(g.C2) + (size_t)m * g.ldc2 + n);
+      return __builtin_nontemporal_load(
+          reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(g.C2) + (size_t)m * g.ldc2 + n));
     else
-      return *reinterpret_cast<const f32x4*>(static_cast<const float*>(g.C) + (size_t)m * g.ldc + n);
+      return __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4*>(static_cast<const float*>(g.C) + (size_t)m * g.ldc + n));
   };
   if constexpr (READS) {
 #pragma unroll
