@@ -470,7 +470,9 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
   const GemmArgs g = batch_item<bf16, EPI>(g0, item);
   const int split = bid / ntiles;
   const int t = bid - split * ntiles;
-  constexpr int GROUP = 8;
+  // row tiles per group of the XCD's walk: 4 for the narrow (<= 5 column
+  // tiles) unsplit products, 8 otherwise (measured per shape)
+  const int GROUP = (tiles_n <= 5 && g0.splits == 1) ? 4 : 8;
   const int per_group = GROUP * tiles_n;
   const int first_m = (t / per_group) * GROUP;
   const int gsize = min(tiles_m - first_m, GROUP);
