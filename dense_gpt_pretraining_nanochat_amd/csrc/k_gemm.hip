@@ -609,6 +609,36 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
         const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         *reinterpret_cast<f32x4*>(wl + l32 * RS + j * 32 + q * 8 + lh * 4) = v;
       }
+    constexpr bool WIDE = !READS && (EPI == Epi::StoreT || EPI == Epi::Relu2);
+    if constexpr (WIDE) {
+      // bf16 outputs with no extra operand: 8 values (16 bytes) per lane and
+      // store, half the store instructions of the 4-value path below
+      constexpr int CPR8 = TN / 8, CH8 = 32 * CPR8 / 64;
+#pragma unroll
+      for (int u = 0; u < CH8; ++u) {
+        const int c = lane + 64 * u;
+        const int r = c / CPR8, cc = (c % CPR8) * 8;
+        const int m = m0 + wm * TM + i * 32 + r, n = n0 + wn * TN + cc;
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(wl + r * RS + cc);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(wl + r * RS + cc + 4);
+        if (m < g.M && n < g.N) {
+          bf16x8 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float a = v0[e], b = v1[e];
+            if constexpr (EPI == Epi::Relu2) {
+              a = fmaxf(a, 0.f); a *= a;
+              b = fmaxf(b, 0.f); b *= b;
+            }
+            w[e] = from_f32<bf16>(a);
+            w[4 + e] = from_f32<bf16>(b);
+          }
+          __builtin_nontemporal_store(
+              w, reinterpret_cast<bf16x8*>(static_cast<bf16*>(g.C) + (size_t)m * g.ldc + n));
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const int c = lane + 64 * u;
