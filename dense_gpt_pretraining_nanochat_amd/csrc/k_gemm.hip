@@ -678,9 +678,17 @@ hipError_t launch_tiles(const GemmArgs& g, hipStream_t s) {
 
 // Large bf16 products take the 256x256 tile when it still gives at least one
 // tile per CU; everything else (and fp32) the 128x128 tile.
+// The 256x256 kernel addresses each operand slab through a buffer descriptor
+// with 32-bit per-lane offsets, range-checked at 2^31 - 1 bytes: a K-contiguous
+// slab spans 256 rows of its operand's stride, so both strides must stay
+// below 2^22 elements (2^31 bytes / (256 rows * 2 bytes)). Larger strides take
+// the 128x128 kernel, which uses full-width addresses.
+bool strides_fit_256(const GemmArgs& g) { return g.lda < (1 << 22) && g.ldb < (1 << 22); }
+
 int choose_tile(bool bf16, const GemmArgs& g) {
   if (!bf16 || g.tile == 128) return 128;
   if (g.tile == 256) return 256;
+  if (!strides_fit_256(g)) return 128;
   const long big_tiles = (long)((g.M + 255) / 256) * ((g.N + 255) / 256) * g.splits *
                         (g.batch > 1 ? g.batch : 1);
   return (g.M >= 256 && g.N >= 256 && big_tiles >= 256) ? 256 : 128;
@@ -734,6 +742,7 @@ hipError_t gemm(DType t, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs
   if (g.batch < 0 || (g.batch > 1 && epi == Epi::PartialF32)) return hipErrorInvalidValue;
   if ((epi == Epi::Relu2Bwd || epi == Epi::AxpbyT || epi == Epi::AxpbyF32) && !g.C2)
     return hipErrorInvalidValue;
+  if (t == DType::BF16 && g.tile == 256 && !strides_fit_256(g)) return hipErrorInvalidValue;
   if ((long)((g.M + 127) / 128) * ((g.N + 127) / 128) * g.splits * (g.batch > 1 ? g.batch : 1) >
       (1L << 30))
     return hipErrorInvalidValue;

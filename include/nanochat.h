@@ -312,7 +312,10 @@ int nc_op_decode_attn(int32_t dtype, const void* qkv, int32_t ldq, int32_t B, in
  * sa, sb and sc elements; C2 is laid out as C and advances with it)
  * C = alpha * (A B^T) + beta * C2, C2 of type T, C of type T (out_f32 = 0)
  * or fp32 (out_f32 = 1). Operand orders and size rules as nc_op_gemm; tile
- * 0 lets the library choose, 128 or 256 (bf16 only) forces the edge. */
+ * 0 lets the library choose, 128 or 256 (bf16 only) forces the edge. The
+ * 256 edge addresses operands with 32-bit offsets: lda and ldb must be below
+ * 2^22 elements, else NC_ERR_HIP (the library's own choice falls back to the
+ * 128 edge for such strides). */
 int nc_op_gemm_axpby(int32_t dtype, int32_t a_kcontig, int32_t b_kcontig, int32_t out_f32, const void* A,
                      const void* B, void* C, const void* C2, int32_t M, int32_t N, int32_t K, int32_t lda,
                      int32_t ldb, int32_t ldc, float alpha, float beta, int32_t batch, int64_t sa,

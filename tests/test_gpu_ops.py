@@ -144,6 +144,26 @@ def test_transpose(dtype, R, C):
     assert np.array_equal(host64(out)[:, :R], x64.T)
 
 
+def test_gemm_256_rejects_wide_strides():
+    """The 256x256 kernel's slab offsets are 32-bit: a forced 256 edge with a
+    row stride of 2^22 elements is refused; the library's own choice takes
+    the 128 edge and computes the product."""
+    M, N, K, lda = 16, 16, 64, 1 << 22
+    rng = np.random.default_rng(5)
+    A = torch.zeros((M, lda), dtype=torch.bfloat16, device="cuda")
+    a, a64 = _as(rng.standard_normal((M, K)), "bf16")
+    A[:, :K] = a
+    B, B64 = _as(rng.standard_normal((N, K)), "bf16")
+    C2 = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    C = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    with pytest.raises(nc.NcError):
+        nc.nc_op_gemm_axpby("bf16", 1, 1, 1, A, B, C, C2, M, N, K, lda, K, N, 1.0, 0.0, tile=256)
+    torch.cuda.synchronize()
+    nc.nc_op_gemm_axpby("bf16", 1, 1, 1, A, B, C, C2, M, N, K, lda, K, N, 1.0, 0.0, tile=0)
+    torch.cuda.synchronize()
+    assert max_rel(host64(C), a64 @ B64.T) <= 1e-5
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("splits", [1, 2, 3, 4, 7])
 @pytest.mark.parametrize("M,N1,N2", [(1024, 272, 192), (1600, 512, 256)])
