@@ -178,15 +178,18 @@ def rope_bwd(g: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
 
 def causal_mqa(qh: np.ndarray, kh: np.ndarray, v: np.ndarray):
     """Textbook causal softmax attention with one K/V head shared by every
-    query head. qh [T,H,D], kh [T,D], v [T,D] -> (o [T,H,D], P [H,T,T])."""
+    query head. qh [T,H,D], kh [T,D], v [T,D] -> (o [T,H,D], P [H,T,T]).
+    The contractions are plain matrix products (every head against the one
+    key / value matrix)."""
     T, H, D = qh.shape
-    s = np.einsum("thd,ud->htu", qh, kh) / math.sqrt(D)
+    qt = np.ascontiguousarray(qh.transpose(1, 0, 2))          # [H, T, D]
+    s = np.matmul(qt, kh.T) / math.sqrt(D)                    # [H, T, T]: s[h,t,u] = q_t . k_u
     mask = np.triu(np.ones((T, T), dtype=bool), k=1)          # u > t
     s = np.where(mask[None], -np.inf, s)
     s = s - s.max(axis=-1, keepdims=True)
     p = np.exp(s)                                             # exact 0 where masked
     p /= p.sum(axis=-1, keepdims=True)
-    o = np.einsum("htu,ud->thd", p, v)
+    o = np.matmul(p, v).transpose(1, 0, 2)                    # o[t,h] = sum_u p[h,t,u] v_u
     return o, p
 
 
@@ -241,14 +244,16 @@ def causal_mqa_bwd(qh, kh, v, o, do):
     dv_u = sum_h sum_{t>=u} P dO, dP = dO v^T, delta = rowsum(dO * O),
     dS = P (dP - delta), dq = dS k / sqrt(D), dk = sum_h dS^T q / sqrt(D).
     Returns (dqh [T,H,D], dkh [T,D], dv [T,D])."""
-    D = qh.shape[-1]
+    T, H, D = qh.shape
     _, p = causal_mqa(qh, kh, v)                           # recompute P [H,T,T]
-    dv = np.einsum("htu,thd->ud", p, do)                   # summed over heads
-    dp = np.einsum("thd,ud->htu", do, v)
-    delta = np.einsum("thd,thd->ht", do, o)                # rowsum(P * dP)
+    dot = np.ascontiguousarray(do.transpose(1, 0, 2))      # [H, T, D]
+    qt = np.ascontiguousarray(qh.transpose(1, 0, 2))
+    dv = sum(p[h].T @ dot[h] for h in range(H))          # summed over heads and queries
+    dp = np.matmul(dot, v.T)                               # [H, T, T]
+    delta = (do * o).sum(axis=-1).T                        # [H, T] = rowsum(P * dP)
     ds = p * (dp - delta[:, :, None])
-    dqh = np.einsum("htu,ud->thd", ds, kh) / math.sqrt(D)
-    dkh = np.einsum("htu,thd->ud", ds, qh) / math.sqrt(D)
+    dqh = np.matmul(ds, kh).transpose(1, 0, 2) / math.sqrt(D)
+    dkh = sum(ds[h].T @ qt[h] for h in range(H)) / math.sqrt(D)
     return dqh, dkh, dv
 
 
