@@ -57,6 +57,8 @@ def _args():
                     help="skip the separate timing of KV-cache decoding")
     ap.add_argument("--no-eval", action="store_true",
                     help="skip the separate timing of the bits-per-byte evaluation")
+    ap.add_argument("--lm-chunk-rows", type=int, default=0,
+                    help="rows of the lm_head / loss chunk (0: the library default)")
     ap.add_argument("--kernel-only", action="store_true",
                     help="launch only the roofline kernel (3x) and a 1 GiB device copy (3x)")
     return ap.parse_args()
@@ -345,6 +347,7 @@ def main():
     c = PRESETS[a.workload]
     pseed, dseed = SEEDS[a.workload]
     cfg = nc.nc_config_from_depth(c.depth, c.vocab_size, c.seq_len, c.batch, c.dtype)
+    nc.nc_set_lm_chunk_rows(a.lm_chunk_rows)
     step = nc.Step(cfg)
     step.init(pseed)
     tok, tgt = inputs.make_tokens(c.vocab_size, c.seq_len, c.batch, dseed, TOKEN_LAW[a.workload])
@@ -389,6 +392,8 @@ def main():
         "flops_variants": {k: float(v) for k, v in flops_variants(c).items()},
         "loss": loss,
         "device_status": status,
+        "workspace_bytes": nc.nc_workspace_bytes(cfg, True),
+        "lm_chunk_rows": nc.nc_lm_chunk_rows(cfg),
         "wall_s_timed": round(wall, 3),
     }
     if not a.no_eval:

@@ -65,6 +65,8 @@ _CFG = ctypes.POINTER(NcConfig)
 _SIGS = {
     "nc_config_from_depth": [_I32, _I32, _I32, _I32, _I32, _CFG],
     "nc_validate_config": [_CFG],
+    "nc_set_lm_chunk_rows": [_I32],
+    "nc_lm_chunk_rows": [_CFG, ctypes.POINTER(_I32)],
     "nc_param_count": [_CFG, ctypes.POINTER(_U64)],
     "nc_param_layout": [_CFG, ctypes.POINTER(NcTensorInfo), _I32, ctypes.POINTER(_I32)],
     "nc_workspace_bytes": [_CFG, _I32, ctypes.POINTER(_U64)],
@@ -159,6 +161,16 @@ def nc_config_from_depth(depth, vocab_size, seq_len, batch, dtype="bf16") -> NcC
 
 def nc_validate_config(cfg) -> int:
     return lib().nc_validate_config(ctypes.byref(cfg))
+
+
+def nc_set_lm_chunk_rows(rows: int):
+    _check(lib().nc_set_lm_chunk_rows(rows), "nc_set_lm_chunk_rows")
+
+
+def nc_lm_chunk_rows(cfg) -> int:
+    n = _I32()
+    _check(lib().nc_lm_chunk_rows(ctypes.byref(cfg), ctypes.byref(n)), "nc_lm_chunk_rows")
+    return n.value
 
 
 def nc_param_count(cfg) -> int:

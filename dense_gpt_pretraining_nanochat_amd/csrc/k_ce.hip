@@ -14,13 +14,21 @@
 // other inter-kernel activation). One workgroup per row keeps the row's raw
 // logits in registers (16-byte chunks: 32 registers per thread at V = 65,536
 // in bf16), so each logit is read once from HBM and each gradient written once
-// (4 bytes per logit in bf16 mode). The capped values are recomputed in the
-// gradient pass instead of being kept in fp32: the kernel then fits in 64
-// registers and two rows are in flight per compute unit, so one row's loads
-// overlap another's reduction and stores. Because |z| <= c, exp(z - c) never
-// overflows and needs no running maximum. tanh is evaluated from one
-// exponential and a hardware reciprocal (see capped_unit) to keep the pass
-// bound by memory rather than by arithmetic.
+// (4 bytes per logit in bf16 mode). The gradient may be written in place over
+// the logits: every read of the row happens before the row's reduction
+// barrier (the target's logit reaches the other threads through LDS), every
+// write after it.
+//
+// Per logit the capped value comes from one base-2 exponential and one
+// hardware reciprocal (see capped_unit), the shifted softmax numerator from a
+// second exponential: because |z| <= c, exp(z - c) never overflows and needs
+// no running maximum. With e = exp(-2|l|/c) and r = 1/(1+e), the softcap's
+// derivative is 1 - (z/c)^2 = 4 e r^2, so the first pass also forms
+// q = exp(z - c) e r^2 and keeps it, in the activation type, in the registers
+// the raw logit occupied; the gradient pass is then one multiply per logit,
+// dl = (4 w / sum) q, plus an fp32 correction of the target's element. This
+// keeps the kernel's arithmetic (three transcendentals and about a dozen other
+// operations per logit) below its memory traffic.
 #include <math.h>
 
 #include "common.h"
@@ -50,18 +58,24 @@ __device__ __forceinline__ float shifted_exp(float t, const CapConsts& q) {
 }
 
 // CB: bytes per chunk (16, or 8 when a bf16 row is only 8-byte aligned).
-template <typename T, int CB>
+// GRAD: also write the logit gradient (dl may equal logits).
+template <typename T, int CB, bool GRAD>
 __global__ __launch_bounds__(kCeThreads, sizeof(T) == 2 && CB == 16 ? 8 : 4) void softcap_ce_kernel(
-    const T* __restrict__ logits, const int32_t* __restrict__ tgt, int V, int nch, float cap,
-    float w, float* __restrict__ loss_rows, T* __restrict__ dl, uint32_t* status) {
+    const T* logits, const int32_t* __restrict__ tgt, int V, int nch, float cap, float w,
+    float* __restrict__ loss_rows, T* dl, uint32_t* status) {
   constexpr int E = CB / (int)sizeof(T);                       // logits per chunk
   constexpr int NCH = kCeMaxV / (kCeThreads * E);              // chunks per thread, at most
   typedef T TV __attribute__((ext_vector_type(E)));
   __shared__ float red[16];
+  __shared__ float lt_s;                          // the target's logit
   const int row = blockIdx.x;
   const int tid = threadIdx.x, nt = blockDim.x;
   const T* src = logits + (size_t)row * V;
   const CapConsts q = {-2.0f * 1.44269504088896341f / cap, cap * 1.44269504088896341f};
+
+  int t = tgt[row];
+  const bool bad = t < 0 || t >= V;
+  t = t < 0 ? 0 : (t >= V ? V - 1 : t);
 
   // every chunk that starts inside the row is whole (V is a multiple of E)
   TV raw[NCH];
@@ -75,35 +89,51 @@ __global__ __launch_bounds__(kCeThreads, sizeof(T) == 2 && CB == 16 ? 8 : 4) voi
   for (int i = 0; i < NCH; ++i) {
     const int c = (i * nt + tid) * E;
     if (i < nch && c < V) {
+      // the chunk holding the target hands its logit over through LDS (no
+      // thread reads the row from memory after the barrier below)
+      if ((unsigned)(t - c) < (unsigned)E) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) se += shifted_exp(capped_unit(to_f32(raw[i][e]), q), q);
-    }
-  }
-  const float sum = block_sum(se, red);
-  const float inv_sum = 1.0f / sum;
-  int t = tgt[row];
-  if (t < 0 || t >= V) {
-    if (tid == 0) atomicOr(status, kStatusTargetRange);
-    t = t < 0 ? 0 : V - 1;
-  }
-  if (tid == 0) {
-    const float zt = cap * capped_unit(to_f32(src[t]), q);
-    loss_rows[row] = cap + logf(sum) - zt;
-  }
-  if (dl == nullptr) return;                       // loss only
-  T* dst = dl + (size_t)row * V;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = (i * nt + tid) * E;
-    if (i < nch && c < V) {
-      TV v;
+        for (int e = 0; e < E; ++e)
+          if (c + e == t) lt_s = to_f32(raw[i][e]);
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const float tc = capped_unit(to_f32(raw[i][e]), q);
-        const float p = shifted_exp(tc, q) * inv_sum - (c + e == t ? 1.0f : 0.0f);
-        v[e] = from_f32<T>(w * p * fmaf(-tc, tc, 1.0f));
+        const float l = to_f32(raw[i][e]);
+        const float u = __builtin_amdgcn_exp2f(q.k1 * fabsf(l));
+        const float r = __builtin_amdgcn_rcpf(1.0f + u);
+        const float ur = u * r;                   // (1 - u) r = r - u r
+        const float ez = shifted_exp(copysignf(r - ur, l), q);
+        se += ez;
+        if constexpr (GRAD) raw[i][e] = from_f32<T>((ez * ur) * r);
       }
-      *reinterpret_cast<TV*>(dst + c) = v;
+    }
+  }
+  const float sum = block_sum(se, red);           // barrier: the row has been read
+  const float inv_sum = 1.0f / sum;
+  const float tct = capped_unit(lt_s, q);
+  if (tid == 0) {
+    if (bad) atomicOr(status, kStatusTargetRange);
+    loss_rows[row] = cap + logf(sum) - cap * tct;
+  }
+  if constexpr (GRAD) {
+    T* dst = dl + (size_t)row * V;
+    const float sc = 4.0f * w * inv_sum;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = (i * nt + tid) * E;
+      if (i < nch && c < V) {
+        TV v;
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = from_f32<T>(sc * to_f32(raw[i][e]));
+        if (t >= c && t < c + E) {
+          // the target's element, w (p - 1) (1 - (z/c)^2), from the fp32 logit
+          const float gt = w * fmaf(shifted_exp(tct, q), inv_sum, -1.0f) * fmaf(-tct, tct, 1.0f);
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if (c + e == t) v[e] = from_f32<T>(gt);
+        }
+        *reinterpret_cast<TV*>(dst + c) = v;
+      }
     }
   }
 }
@@ -116,9 +146,14 @@ hipError_t launch_ce(const void* logits, const int32_t* tgt, int R, int V, float
   if (nt > kCeThreads) nt = kCeThreads;
   const int nch = (V + E * nt - 1) / (E * nt);
   if (nch > kCeMaxV / (kCeThreads * E)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((softcap_ce_kernel<T, CB>), dim3(R), dim3(nt), 0, s,
-                     static_cast<const T*>(logits), tgt, V, nch, cap, w, loss_rows,
-                     static_cast<T*>(dlogits), status);
+  if (dlogits)
+    hipLaunchKernelGGL((softcap_ce_kernel<T, CB, true>), dim3(R), dim3(nt), 0, s,
+                       static_cast<const T*>(logits), tgt, V, nch, cap, w, loss_rows,
+                       static_cast<T*>(dlogits), status);
+  else
+    hipLaunchKernelGGL((softcap_ce_kernel<T, CB, false>), dim3(R), dim3(nt), 0, s,
+                       static_cast<const T*>(logits), tgt, V, nch, cap, w, loss_rows,
+                       static_cast<T*>(nullptr), status);
   return hipGetLastError();
 }
 

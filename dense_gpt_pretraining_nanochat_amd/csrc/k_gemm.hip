@@ -666,6 +666,20 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
   }
 }
 
+// dst[i] (type T) = sum_s part[s * n + i] in split order
+template <typename T>
+__global__ void splitk_reduce_t_kernel(const float* __restrict__ part, int splits, size_t n4,
+                                       size_t n, T* __restrict__ dst) {
+  typedef T T4 __attribute__((ext_vector_type(4)));
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n4;
+       i += (size_t)gridDim.x * blockDim.x) {
+    f32x4 s = reinterpret_cast<const f32x4*>(part)[i];
+    for (int k = 1; k < splits; ++k) s += reinterpret_cast<const f32x4*>(part + (size_t)k * n)[i];
+    T4 w = {from_f32<T>(s[0]), from_f32<T>(s[1]), from_f32<T>(s[2]), from_f32<T>(s[3])};
+    reinterpret_cast<T4*>(dst)[i] = w;
+  }
+}
+
 template <typename T, bool AK, bool BKC, Epi EPI, int BM, int BN, int WM, int WN>
 hipError_t launch_tiles(const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.splits *
@@ -777,6 +791,22 @@ hipError_t splitk_reduce(const float* part, int splits, size_t n, float* dst, bo
   const int grid = (int)(want < 4096 ? want : 4096);
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid > 0 ? grid : 1), dim3(block), 0, stream,
                      part, splits, n4, n, dst, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t splitk_reduce_t(DType t, const float* part, int splits, size_t n, void* dst,
+                           hipStream_t stream) {
+  if (n % 4 || splits < 1) return hipErrorInvalidValue;
+  const size_t n4 = n / 4;
+  const int block = 256;
+  const size_t want = (n4 + block - 1) / block;
+  const int grid = (int)(want < 4096 ? want : 4096);
+  if (t == DType::BF16)
+    hipLaunchKernelGGL(splitk_reduce_t_kernel<bf16>, dim3(grid > 0 ? grid : 1), dim3(block), 0,
+                       stream, part, splits, n4, n, static_cast<bf16*>(dst));
+  else
+    hipLaunchKernelGGL(splitk_reduce_t_kernel<float>, dim3(grid > 0 ? grid : 1), dim3(block), 0,
+                       stream, part, splits, n4, n, static_cast<float*>(dst));
   return hipGetLastError();
 }
 

@@ -46,6 +46,9 @@ hipError_t transpose(DType t, const void* in, int R, int C, int ld_in, void* out
 // dst[i] (=|+=) sum_s part[s*n + i], s = 0..splits-1, in a fixed order.
 hipError_t splitk_reduce(const float* part, int splits, size_t n, float* dst, bool accumulate,
                          hipStream_t stream);
+// dst[i] (type of t) = sum_s part[s*n + i], s = 0..splits-1, in a fixed order.
+hipError_t splitk_reduce_t(DType t, const float* part, int splits, size_t n, void* dst,
+                           hipStream_t stream);
 
 // ---- norms and embedding --------------------------------------------------
 // x[m,:] = n(E[tok[m],:]) (fp32), rinv[m]; ids outside [0,V) are clamped and flagged.
@@ -101,7 +104,8 @@ hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const f
                     hipStream_t s);
 
 // ---- cross-entropy -----------------------------------------------------------
-// rows of fp32 logits [R, V]: per-row loss (fp32) and dlogits (T) = (softmax(z)-onehot)*(1-(z/c)^2)*w
+// rows of logits [R, V] (T): per-row loss (fp32) and dlogits (T) = (softmax(z)-onehot)*(1-(z/c)^2)*w;
+// dlogits may equal logits (the gradient then replaces them)
 hipError_t softcap_ce(DType t, const void* logits, const int32_t* tgt, int R, int V, float cap,
                       float w, float* loss_rows, void* dlogits, uint32_t* status, hipStream_t s);
 hipError_t loss_mean(const float* loss_rows, int M, float* out, uint32_t* status, hipStream_t s);

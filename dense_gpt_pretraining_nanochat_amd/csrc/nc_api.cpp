@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <vector>
 
@@ -92,11 +93,36 @@ uint64_t param_elems(const Dims& D) {
   return align_up(t.back().offset + (uint64_t)(t.back().rows * t.back().cols), 128);
 }
 
-// Rows of the lm_head / loss processed at once: the logits and the logit
-// gradients of a chunk (both in the activation type) live in the workspace
-// (65536 rows x 65536 vocab x 2 x 2 bytes = 17 GB in bf16 mode), so the
-// vocabulary products run over the whole batch in one launch.
-int64_t chunk_rows(const Dims& D) { return std::min<int64_t>(D.M, 65536); }
+// Rows of the lm_head / loss processed at once. A chunk's logits (activation
+// type; the cross-entropy kernel overwrites them with their gradient) are the
+// only [rows, V] buffer in the workspace, so its size does not grow with the
+// batch: 32,768 rows x 65,536 ids x 2 bytes = 4.3 GB in bf16 mode. Measured
+// at depth 20 (65,536 tokens): 16,384-row chunks make the step 1.5 ms slower
+// (the chunk's input-gradient product needs a 4-way split to fill the chip),
+// 32,768 rows cost 1.6 ms against one chunk of the whole batch.
+constexpr int64_t kLmChunkRowsDefault = 32768;
+std::atomic<int64_t> g_lm_chunk_rows{kLmChunkRowsDefault};
+int64_t chunk_rows(const Dims& D) { return std::min<int64_t>(D.M, g_lm_chunk_rows.load()); }
+
+// K slices for the lm_head input gradient dxf[mc, d] = dlogits . U (contraction
+// over the vocabulary): a chunk of a few thousand rows has too few output tiles
+// to fill the chip, so the product is split until there are about four tiles
+// per compute unit (fixed-order fp32 reduction into the activation type).
+int dgrad_splits(DType dt, int64_t rows, int N, int K) {
+  nc::GemmArgs g{};
+  g.M = (int)rows;
+  g.N = N;
+  g.K = K;
+  g.lda = K;
+  g.ldb = N;
+  g.splits = 1;
+  const int tile = nc::gemm_tile(dt, true, false, g);
+  const int64_t tiles = ((rows + tile - 1) / tile) * ((N + tile - 1) / tile);
+  const int bk = dt == DType::BF16 ? 64 : 32;
+  int s = 1;
+  while (tiles * s < 4 * (int64_t)nc::device_cus() && s < 8 && K / bk >= 2 * s) s *= 2;
+  return s;
+}
 
 // Split-K plan for a weight gradient dW[N1, N2] = X1^T X2 contracted over K
 // token rows (both operands read K-strided). Each split takes a contiguous run
@@ -137,7 +163,7 @@ struct LayerActs {
 };
 
 struct Plan {
-  uint64_t status, cs, x, rinv0, xf, rinvf, loss_rows, logits, dlog;
+  uint64_t status, cs, x, rinv0, xf, rinvf, loss_rows, logits;
   std::vector<LayerActs> acts;
   // backward only
   uint64_t dx, g, dh, dbig, dout, delta, partial, attn_part, counts, offsets, cursor, list;
@@ -162,8 +188,7 @@ Plan plan_of(const Dims& D, bool bwd) {
   p.xf = take(M * D.d * e);
   p.rinvf = take(M * 4);
   p.loss_rows = take(M * 4);
-  p.logits = take(Mc * D.V * e);
-  p.dlog = take(Mc * D.V * e);
+  p.logits = take(Mc * D.V * e);                // the logit gradient replaces them
   const int nsets = bwd ? D.L : 1;
   for (int l = 0; l < nsets; ++l) {
     LayerActs a;
@@ -188,6 +213,8 @@ Plan plan_of(const Dims& D, bool bwd) {
     uint64_t part = 0;
     const int64_t shapes[4][2] = {{D.Q, D.d}, {D.d, D.d}, {D.F, D.d}, {D.d, D.F}};
     for (auto& sh : shapes) part = std::max(part, wgrad_plan(D.dt, sh[0], sh[1], D.M).partial_floats);
+    const int sx = dgrad_splits(D.dt, Mc, D.d, D.V);
+    if (sx > 1) part = std::max<uint64_t>(part, (uint64_t)sx * Mc * D.d);
     p.partial = take(part * 4);
     p.attn_part = take(nc::attn_bwd_scratch_floats(D.B, D.T) * 4);
     p.counts = take((uint64_t)(D.V + 1) * 4);
@@ -292,7 +319,7 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
   float* rinvf = at<float>(ws, P.rinvf);
   float* loss_rows = at<float>(ws, P.loss_rows);
   void* logits = at<char>(ws, P.logits);
-  void* dlog = at<char>(ws, P.dlog);
+  void* dlog = logits;                           // the gradient overwrites the logits
 
   HIPCHECK(nc::fill_zero(status, 256, s));
   HIPCHECK(nc::rope_table(D.T, 64, (double)cfg->rope_base, cs, s));
@@ -325,6 +352,7 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
   // ---------------- lm_head + softcap cross-entropy, by row chunks ----------------
   const int64_t Mc = chunk_rows(D);
   void* dxf = bwd ? at<char>(ws, P.dh) : nullptr;
+  float* partial_x = bwd ? at<float>(ws, P.partial) : nullptr;
   const float w = 1.0f / (float)M;
   for (int64_t r0 = 0; r0 < M; r0 += Mc) {
     const int64_t mc = std::min<int64_t>(Mc, M - r0);
@@ -334,10 +362,28 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
     HIPCHECK(nc::softcap_ce(dt, logits, targets + r0, (int)mc, D.V, cfg->softcap, w,
                             loss_rows + r0, bwd ? dlog : nullptr, status, s));
     if (bwd) {
-      // dxf = dlog . U (U read K-strided: contraction over its rows)
-      HIPCHECK(gemm_simple(dt, true, false, Epi::StoreT, dlog, W(iU),
-                           static_cast<char*>(dxf) + r0 * D.d * e, nullptr, mc, D.d, D.V, D.V,
-                           D.d, D.d, 0, s));
+      // dxf = dlog . U (U read K-strided: contraction over its rows), split
+      // over the vocabulary when the chunk alone would not fill the chip
+      char* dxfc = static_cast<char*>(dxf) + r0 * D.d * e;
+      const int sx = dgrad_splits(dt, mc, D.d, D.V);
+      if (sx == 1) {
+        HIPCHECK(gemm_simple(dt, true, false, Epi::StoreT, dlog, W(iU), dxfc, nullptr, mc, D.d,
+                             D.V, D.V, D.d, D.d, 0, s));
+      } else {
+        nc::GemmArgs g{};
+        g.A = dlog;
+        g.B = W(iU);
+        g.C = partial_x;
+        g.M = (int)mc;
+        g.N = D.d;
+        g.K = D.V;
+        g.lda = D.V;
+        g.ldb = D.d;
+        g.ldc = D.d;
+        g.splits = sx;
+        HIPCHECK(nc::gemm(dt, true, false, Epi::PartialF32, g, s));
+        HIPCHECK(nc::splitk_reduce_t(dt, partial_x, sx, (size_t)mc * D.d, dxfc, s));
+      }
       // dU (+)= dlog^T . xf_chunk: both operands contracted over their rows
       HIPCHECK(gemm_simple(dt, false, false, (r0 == 0 && !accumulate) ? Epi::StoreF32 : Epi::AddF32, dlog, xfc,
                            G(iU), nullptr, D.V, D.d, (int)mc, D.V, D.d, D.d, 0, s));
@@ -427,6 +473,20 @@ int nc_config_from_depth(int32_t depth, int32_t vocab_size, int32_t seq_len, int
 }
 
 int nc_validate_config(const nc_config* cfg) { return validate(cfg); }
+
+int nc_set_lm_chunk_rows(int32_t rows) {
+  if (rows < 0 || rows % 64) return NC_ERR_ARG;
+  g_lm_chunk_rows.store(rows == 0 ? kLmChunkRowsDefault : rows);
+  return NC_OK;
+}
+
+int nc_lm_chunk_rows(const nc_config* cfg, int32_t* rows) {
+  const int rc = validate(cfg);
+  if (rc) return rc;
+  if (!rows) return NC_ERR_NULL;
+  *rows = (int32_t)chunk_rows(dims_of(cfg));
+  return NC_OK;
+}
 
 int nc_param_count(const nc_config* cfg, uint64_t* n) {
   const int rc = validate(cfg);

@@ -116,6 +116,18 @@ int nc_param_layout(const nc_config* cfg, nc_tensor_info* out, int32_t cap, int3
  * (saves every layer's activations) over nc_forward_loss. Host only. */
 int nc_workspace_bytes(const nc_config* cfg, int32_t with_backward, uint64_t* bytes);
 
+/* Rows of the lm_head + softcapped cross-entropy chunk. The step runs the
+ * vocabulary-wide products and the loss over row chunks of the batch, so the
+ * only [rows, vocab_size] buffer in the workspace (the chunk's logits, which
+ * the loss kernel overwrites with their gradient) does not grow with the
+ * batch. nc_set_lm_chunk_rows sets the chunk for every later call in the
+ * process (0 restores the default of 32,768 rows; otherwise a positive
+ * multiple of 64, else NC_ERR_ARG); it changes nc_workspace_bytes, so it is
+ * meant for tuning and tests, not for use while calls are in flight.
+ * nc_lm_chunk_rows reports min(batch*seq_len, chunk) for a config. Host only. */
+int nc_set_lm_chunk_rows(int32_t rows);
+int nc_lm_chunk_rows(const nc_config* cfg, int32_t* rows);
+
 /* Byte offset inside the workspace of the per-token losses (fp32 [B*T],
  * row-major like tokens), valid after a forward call until the next call on
  * the same workspace. Host only. */
@@ -367,7 +379,8 @@ int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* do
                    const float* lse, float* delta, int32_t B, int32_t T, int32_t H, void* dqkv,
                    float* scratch, void* stream);
 /* Per-row loss and (if dlogits != NULL) w-scaled logit gradient (T) from
- * logits [R, V] of type T; status: device word for range flags (may not be
+ * logits [R, V] of type T; dlogits may equal logits (the gradient then
+ * replaces them in place); status: device word for range flags (may not be
  * NULL). */
 int nc_op_softcap_ce(int32_t dtype, const void* logits, const int32_t* targets, int32_t R,
                      int32_t V, float cap, float w, float* loss_rows, void* dlogits,

@@ -119,6 +119,39 @@ def test_workspace_grows_with_batch_and_depth():
     assert off % 256 == 0 and off + 4 * 65536 <= nc.nc_workspace_bytes(c4, True)
 
 
+def test_lm_chunk_rows_bound_the_workspace():
+    """The lm_head / loss chunk keeps the only [rows, V] buffer independent of
+    the batch: at depth 20 the default 32,768-row chunk needs about 4 GiB less than
+    one chunk of the whole 65,536-token batch, and the logits part of the
+    workspace no longer grows with the batch. Bad chunk sizes are refused."""
+    c4 = _cfg("C4")
+    try:
+        assert nc.nc_lm_chunk_rows(c4) == 32768
+        small = nc.nc_workspace_bytes(c4, True)
+        nc.nc_set_lm_chunk_rows(65536)
+        assert nc.nc_lm_chunk_rows(c4) == 65536
+        whole = nc.nc_workspace_bytes(c4, True)
+        assert whole - small >= 3.5 * 2 ** 30     # 4 GiB of logits, less a larger split-K buffer
+        for bad in (100, -64, 63):
+            with pytest.raises(nc.NcError):
+                nc.nc_set_lm_chunk_rows(bad)
+        assert nc.nc_lm_chunk_rows(c4) == 65536            # a refused value changes nothing
+    finally:
+        nc.nc_set_lm_chunk_rows(0)
+    assert nc.nc_workspace_bytes(c4, True) == small
+    assert small < 33 * 2 ** 30
+    nc.nc_set_lm_chunk_rows(16384)
+    assert nc.nc_workspace_bytes(c4, True) < small
+    nc.nc_set_lm_chunk_rows(0)
+    # rows fewer than the chunk: one chunk of the whole batch
+    assert nc.nc_lm_chunk_rows(_cfg("C2")) == 4096
+    # per-layer activations grow with the batch; the logits chunk does not
+    b16 = nc.nc_workspace_bytes(nc.nc_config_from_depth(20, 65536, 2048, 16, 1), True)
+    b32 = nc.nc_workspace_bytes(nc.nc_config_from_depth(20, 65536, 2048, 32, 1), True)
+    b64 = nc.nc_workspace_bytes(nc.nc_config_from_depth(20, 65536, 2048, 64, 1), True)
+    assert abs((b64 - b32) - 2 * (b32 - b16)) <= 2 ** 26
+
+
 def _optim(**kw):
     base = dict(lr_adamw=0.01, beta1=0.8, beta2=0.95, eps=1e-10, wd_adamw=0.0, lr_muon=0.02,
                 momentum=0.95, wd_muon=0.0, max_grad_norm=1.0, ns_steps=5, step=1)

@@ -268,8 +268,11 @@ def _attn_inputs(rng, B, T, H, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("B,T,H", [(2, 64, 1), (1, 256, 3), (2, 192, 10), (1, 128, 13)])
+@pytest.mark.parametrize("B,T,H", [(2, 64, 1), (1, 256, 3), (2, 192, 10), (1, 128, 13),
+                                   (1, 1024, 2), (1, 2048, 1), (1, 2048, 10)])
 def test_attention_fwd_bwd(dtype, B, T, H):
+    """Up to T = 2048: several 512-token query chunks of the dK/dV kernel and
+    their fixed-order reduction, at the depth-20 head count too."""
     rng = np.random.default_rng(B + T + H)
     d = 128 * H
     Q = d + 256
@@ -288,7 +291,8 @@ def test_attention_fwd_bwd(dtype, B, T, H):
     else:
         check_bf16(og, oref, "o", cos_min=0.99995, l2_max=5e-3)
     # lse against the textbook value
-    s = np.einsum("bthd,bud->bhtu", z[:, :, :d].reshape(B, T, H, 128), z[:, :, d:d + 128]) / np.sqrt(128)
+    s = np.matmul(z[:, :, :d].reshape(B, T, H, 128).transpose(0, 2, 1, 3),
+                  z[:, None, :, d:d + 128].transpose(0, 1, 3, 2)) / np.sqrt(128)
     s = np.where(np.triu(np.ones((T, T), bool), 1)[None, None], -np.inf, s)
     mx = s.max(-1, keepdims=True)
     lref = (mx + np.log(np.exp(s - mx).sum(-1, keepdims=True)))[..., 0]
@@ -337,6 +341,13 @@ def test_softcap_ce(dtype, R, V):
     else:
         check_bf16(got, dref, "dlogits", cos_min=0.99999, l2_max=5e-3)
     assert int(status[0]) == 0
+    # in place: the gradient replaces the logits, bit for bit what the
+    # separate-output call wrote (the target's logit is read before any write)
+    inplace = logits.clone()
+    loss2 = torch.zeros_like(loss)
+    nc.nc_op_softcap_ce(dtype, inplace, dev(tgt), R, V, 15.0, w, loss2, inplace, status)
+    torch.cuda.synchronize()
+    assert torch.equal(inplace, dl) and torch.equal(loss2, loss)
     # out-of-range targets are clamped and flagged
     bad = tgt.copy()
     bad[1] = V + 5

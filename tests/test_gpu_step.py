@@ -171,3 +171,44 @@ def test_init_matches_oracle_generator(dtype, depth, V):
     same = np.mean(gv == rv)
     assert same >= 0.9999, same
     assert np.all(np.abs(gv - rv) <= ulp)
+
+
+@pytest.fixture
+def lm_chunk():
+    """Sets the lm_head / loss chunk rows for one test, restoring the default."""
+    yield nc.nc_set_lm_chunk_rows
+    nc.nc_set_lm_chunk_rows(0)
+
+
+@pytest.mark.parametrize("name,rows", [("C1", 64), ("C2", 1024), ("C2", 832)])
+def test_lm_head_in_row_chunks(name, rows, lm_chunk):
+    """The lm_head, the loss and their backward over several row chunks: later
+    chunks start at r0 > 0 (logits, targets, per-token losses and the input
+    gradient offset), dU is accumulated across chunks, the chunk's input
+    gradient is split over the vocabulary; with 832 rows the last of the five
+    chunks holds 768. Full-batch parity against the oracle, then accumulation
+    of a second batch on top of the first (each chunk adds into dU)."""
+    pseed, dseed = SEEDS[name]
+    c = PRESETS[name]
+    lm_chunk(rows)
+    cfg, ocfg, step, p64, tok, tgt = _setup(c.depth, c.vocab_size, c.seq_len, c.batch, c.dtype,
+                                            pseed, dseed, TOKEN_LAW[name])
+    assert nc.nc_lm_chunk_rows(cfg) == rows
+    _compare(ocfg, step, p64, tok, tgt, c.dtype)
+    # accumulate: first batch, then the same batch with rolled targets
+    tgt2 = np.roll(tgt, 1, axis=1)
+    step.grads.fill_(0)
+    step.forward_backward_accumulate(dev(tok), dev(tgt))
+    step.forward_backward_accumulate(dev(tok), dev(tgt2))
+    torch.cuda.synchronize()
+    got = host64(step.grads)
+    _, g1, _ = oracle.forward_backward(ocfg, p64, tok, tgt)
+    _, g2, _ = oracle.forward_backward(ocfg, p64, tok, tgt2)
+    ref = g1 + g2
+    for tname, off, r, cc in oracle.layout(ocfg):
+        g, o = got[off:off + r * cc], ref[off:off + r * cc]
+        if c.dtype == "f32":
+            assert max_rel(g, o) <= 1e-3, tname
+        else:
+            check_bf16(g, o, f"accumulated {tname}")
+
