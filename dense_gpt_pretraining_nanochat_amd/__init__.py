@@ -104,6 +104,7 @@ _SIGS = {
     "nc_op_attn_bwd_scratch_bytes": [_I32, _I32],
     "nc_op_attn_bwd": [_I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P],
     "nc_op_softcap_ce": [_I32, _P, _P, _I32, _I32, _F32, _F32, _P, _P, _P, _P],
+    "nc_op_attn_bwd_noalloc": [_I32, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P],
 }
 
 
@@ -375,6 +376,14 @@ def nc_op_attn_bwd(dtype, qkv, o, dout, lse, delta, B, T, H, dqkv, scratch=None,
         scratch = torch.empty(nc_op_attn_bwd_scratch_bytes(B, T), dtype=torch.uint8, device="cuda")
     _check(lib().nc_op_attn_bwd(_dt(dtype), _ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
                                 B, T, H, _ptr(dqkv), _ptr(scratch), _stream(stream)), "nc_op_attn_bwd")
+
+
+def nc_op_attn_bwd_noalloc(dtype, qkv, o, dout, lse, B, T, H, dqkv, stream=None):
+    """nc_op_attn_bwd with the library's fixed per-device scratch (no caller
+    buffers, no allocation)."""
+    _check(lib().nc_op_attn_bwd_noalloc(_dt(dtype), _ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse),
+                                        B, T, H, _ptr(dqkv), _stream(stream)),
+           "nc_op_attn_bwd_noalloc")
 
 
 def nc_op_softcap_ce(dtype, logits, targets, R, V, cap, w, loss_rows, dlogits, status, stream=None):

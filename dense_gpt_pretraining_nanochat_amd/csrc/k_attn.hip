@@ -32,6 +32,7 @@
 // anywhere, so the results are bitwise reproducible.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -824,6 +825,36 @@ hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const f
     hipLaunchKernelGGL(attn_bwd_dq_kernel<float>, gq, bq, 0, s, q, ldq, d, lse, delta, T, H, g, ldd);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fixed scratch for callers that cannot allocate device memory (code under
+// graph capture, serving loops): the delta rows and the dK/dV chunk partials
+// of one attention backward live in this file-scope array instead of a
+// caller-provided buffer. Each device holds its own copy for the life of the
+// process; in host code `scratch` only names the symbol, so its device
+// address is looked up once per device (with that device current) and that
+// address is what the kernels receive.
+static __device__ __align__(256) char scratch[kAttnFixedScratchBytes];
+
+hipError_t attn_fixed_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace nc

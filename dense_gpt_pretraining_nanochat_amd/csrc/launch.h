@@ -102,6 +102,11 @@ size_t attn_bwd_scratch_floats(int B, int T);
 hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const float* lse,
                     const float* delta, int B, int T, int H, void* dqkv, int ldd, float* scratch,
                     hipStream_t s);
+// Device address (current device) of the library's fixed attention-backward
+// scratch array of kAttnFixedScratchBytes, for the entry point that allocates
+// nothing; looked up once per device.
+constexpr size_t kAttnFixedScratchBytes = (size_t)32 << 20;
+hipError_t attn_fixed_scratch(void** ptr);
 
 // ---- cross-entropy -----------------------------------------------------------
 // rows of logits [R, V] (T): per-row loss (fp32) and dlogits (T) = (softmax(z)-onehot)*(1-(z/c)^2)*w;

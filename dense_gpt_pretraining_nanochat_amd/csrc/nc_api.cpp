@@ -1352,6 +1352,26 @@ int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* do
   return NC_OK;
 }
 
+int nc_op_attn_bwd_noalloc(int32_t dtype, const void* qkv, const void* o, const void* dout,
+                           const float* lse, int32_t B, int32_t T, int32_t H, void* dqkv,
+                           void* stream) {
+  if (bad_dtype(dtype)) return NC_ERR_ARG;
+  if (!qkv || !o || !dout || !lse || !dqkv) return NC_ERR_NULL;
+  if (B <= 0 || T < 64 || T % 64 || H < 1 || H > 16) return NC_ERR_ARG;
+  const uint64_t delta_bytes = align_up((uint64_t)B * H * T * 4, kAlign);
+  const uint64_t part_bytes = (uint64_t)nc::attn_bwd_scratch_floats(B, T) * 4;
+  if (delta_bytes + part_bytes > nc::kAttnFixedScratchBytes) return NC_ERR_WORKSPACE;
+  void* base = nullptr;
+  HIPCHECK(nc::attn_fixed_scratch(&base));
+  float* delta = static_cast<float*>(base);
+  float* part = at<float>(base, delta_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int ld = H * 128 + 256;
+  HIPCHECK(nc::attn_bwd_delta(dt_of(dtype), o, dout, B, T, H, delta, s));
+  HIPCHECK(nc::attn_bwd(dt_of(dtype), qkv, ld, dout, lse, delta, B, T, H, dqkv, ld, part, s));
+  return NC_OK;
+}
+
 int nc_op_softcap_ce(int32_t dtype, const void* logits, const int32_t* targets, int32_t R,
                      int32_t V, float cap, float w, float* loss_rows, void* dlogits,
                      uint32_t* status, void* stream) {

@@ -378,6 +378,21 @@ uint64_t nc_op_attn_bwd_scratch_bytes(int32_t B, int32_t T);
 int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* dout,
                    const float* lse, float* delta, int32_t B, int32_t T, int32_t H, void* dqkv,
                    float* scratch, void* stream);
+/* nc_op_attn_bwd without any caller scratch, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc). Same arguments and results as
+ * nc_op_attn_bwd (bitwise: the same kernels) except that delta and the dK/dV
+ * chunk partials live in a 32 MiB array inside the library, one per device,
+ * held until the process ends; the call allocates nothing. Sizes needing more
+ * than that, i.e. 4*B*H*T (rounded up to 256) + 4*B*T*256*ceil(T/512) bytes
+ * above 32 MiB (at T = 2048 and H = 10: B up to 3 fits, 4 does not), are
+ * refused with NC_ERR_WORKSPACE before anything is enqueued. Every call on a
+ * device shares that device's array and nothing in it needs clearing (each
+ * call writes what it reads); calls that overlap on one device (concurrent
+ * streams, threads) race on it and must be serialised by the caller. */
+int nc_op_attn_bwd_noalloc(int32_t dtype, const void* qkv, const void* o, const void* dout,
+                           const float* lse, int32_t B, int32_t T, int32_t H, void* dqkv,
+                           void* stream);
 /* Per-row loss and (if dlogits != NULL) w-scaled logit gradient (T) from
  * logits [R, V] of type T; dlogits may equal logits (the gradient then
  * replaces them in place); status: device word for range flags (may not be
