@@ -46,7 +46,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="C4", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--cpu-baseline-all", action="store_true",
+                    help="time only the fp64 oracle on every workload (no GPU)")
     ap.add_argument("--no-optimizer", action="store_true",
                     help="skip the separate timing of the optimizer step")
     ap.add_argument("--optimizer-only", action="store_true",
@@ -293,32 +294,73 @@ def kernel_only(a):
                       "copy_bytes": src.numel() * 4}), flush=True)
 
 
-def cpu_baseline(workload, ntok):
-    """The fp64 oracle (as it stands) on the first `ntok` tokens of one
-    sequence of the workload, forward + backward; tokens/s on this host."""
-    import numpy as np
+def host_facts():
+    """The host the oracle runs on: usable cores, CPU model, BLAS library."""
     from threadpoolctl import threadpool_info
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    b = blas[0] if blas else {}
+    return {"host_cores": cores, "cpu_model": model,
+            "blas": f"{b.get('internal_api', 'unknown')} {b.get('version', '')}".strip(),
+            "blas_threads": int(b.get("num_threads", 1))}
 
+
+def oracle_timing(workload, rows):
+    """The fp64 oracle (as it stands) forward + loss + backward on whole rows
+    of the workload's batch (same seeded params and tokens as the GPU run):
+    seconds and tokens/s on this host."""
     import oracle
     from dense_gpt_pretraining_nanochat_amd import inputs
     from dense_gpt_pretraining_nanochat_amd.config import PRESETS, SEEDS, TOKEN_LAW
     c = PRESETS[workload]
     pseed, dseed = SEEDS[workload]
-    ocfg = oracle.OracleConfig(depth=c.depth, vocab=c.vocab_size, seq_len=ntok, batch=1)
+    ocfg = oracle.OracleConfig(depth=c.depth, vocab=c.vocab_size, seq_len=c.seq_len, batch=c.batch)
     flat = inputs.make_params(oracle.layout(ocfg), oracle.param_count(ocfg, padded=True), pseed,
                               c.dtype, c.depth)
     p64 = inputs.as_float64(flat, c.dtype)
     del flat
-    tok, tgt = inputs.make_tokens(c.vocab_size, c.seq_len, 1, dseed, TOKEN_LAW[workload])
-    tok, tgt = tok[:, :ntok], tgt[:, :ntok]
+    tok, tgt = inputs.make_tokens(c.vocab_size, c.seq_len, c.batch, dseed, TOKEN_LAW[workload])
     t0 = time.perf_counter()
-    oracle.forward_backward(ocfg, p64, tok, tgt)
+    oracle.forward_backward(ocfg, p64, tok, tgt, rows=list(range(rows)), M=c.batch * c.seq_len)
     dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(ntok / dt, 3), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"{workload} model shapes, one sequence of {ntok} tokens (a causal prefix), "
-                      f"fp64 forward + loss + backward"}
+    ntok = rows * c.seq_len
+    return {"workload": workload, "rows": rows, "tokens": ntok, "seconds": round(dt, 2),
+            "tokens_per_s": round(ntok / dt, 3)}
+
+
+def cpu_baseline(workload):
+    """One full row (all seq_len tokens) of the benched workload through the
+    oracle, with the host facts."""
+    t = oracle_timing(workload, 1)
+    h = host_facts()
+    return {"value": t["tokens_per_s"], "unit": "tokens/s", "cores": h["blas_threads"],
+            "kind": "oracle", "seconds": t["seconds"],
+            "sample": f"{workload}: batch row 0, all {t['tokens']} tokens, fp64 forward + loss + "
+                      f"backward (the oracle as it stands)", **h}
+
+
+def cpu_baseline_all():
+    """The oracle on every workload: the two small ones on their whole batch,
+    the three large ones on one full row each."""
+    from dense_gpt_pretraining_nanochat_amd.config import PRESETS
+    out = []
+    for w in ("C1", "C2", "C3", "C4", "C5"):
+        rows = PRESETS[w].batch if w in ("C1", "C2") else 1
+        out.append(oracle_timing(w, rows))
+        print(json.dumps({"progress": out[-1]}), flush=True)
+    print(json.dumps({"cpu_baseline_all": out, **host_facts()}), flush=True)
 
 
 def main():
@@ -327,6 +369,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
               "(the step runs on a single GPU; see the sharding notes)", file=sys.stderr)
         sys.exit(2)
+    if a.cpu_baseline_all:
+        cpu_baseline_all()
+        return
     if a.kernel_only:
         kernel_only(a)
         return
@@ -411,7 +456,7 @@ def main():
     torch.cuda.empty_cache()
     out["roofline"] = dominant_kernel_roofline(cfg, nc, torch)
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(a.workload)
     print(json.dumps(out), flush=True)
 
 

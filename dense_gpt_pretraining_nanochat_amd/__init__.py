@@ -13,7 +13,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libnanochat.so")
+# NANOCHAT_LIB selects another build of the same library (the host-sanitizer
+# build of sanitize.py); by default the in-tree libnanochat.so
+LIB_PATH = os.environ.get("NANOCHAT_LIB") or os.path.join(_HERE, "libnanochat.so")
 
 NC_F32, NC_BF16 = 0, 1
 NC_OK = 0
@@ -38,6 +40,11 @@ class NcConfig(ctypes.Structure):
 class NcTensorInfo(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("offset", ctypes.c_uint64),
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class NcWsPiece(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("offset", ctypes.c_uint64),
+                ("bytes", ctypes.c_uint64)]
 
 
 class NcOptimConfig(ctypes.Structure):
@@ -71,6 +78,7 @@ _SIGS = {
     "nc_param_layout": [_CFG, ctypes.POINTER(NcTensorInfo), _I32, ctypes.POINTER(_I32)],
     "nc_workspace_bytes": [_CFG, _I32, ctypes.POINTER(_U64)],
     "nc_token_losses_offset": [_CFG, _I32, ctypes.POINTER(_U64)],
+    "nc_workspace_pieces": [_CFG, _I32, ctypes.POINTER(NcWsPiece), _I32, ctypes.POINTER(_I32)],
     "nc_init_params": [_U64, _CFG, _P, _P],
     "nc_forward_loss": [_CFG, _P, _P, _P, _P, _U64, _P, _P],
     "nc_forward_backward": [_CFG, _P, _P, _P, _P, _P, _U64, _P, _P],
@@ -193,6 +201,17 @@ def nc_workspace_bytes(cfg, with_backward=True) -> int:
     _check(lib().nc_workspace_bytes(ctypes.byref(cfg), int(with_backward), ctypes.byref(n)),
            "nc_workspace_bytes")
     return n.value
+
+
+def nc_workspace_pieces(cfg, with_backward=True):
+    """[(name, byte offset, bytes)] of the workspace plan, in address order."""
+    n = _I32()
+    _check(lib().nc_workspace_pieces(ctypes.byref(cfg), int(with_backward), None, 0, ctypes.byref(n)),
+           "nc_workspace_pieces")
+    arr = (NcWsPiece * n.value)()
+    _check(lib().nc_workspace_pieces(ctypes.byref(cfg), int(with_backward), arr, n.value,
+                                     ctypes.byref(n)), "nc_workspace_pieces")
+    return [(p.name.decode(), int(p.offset), int(p.bytes)) for p in arr]
 
 
 def nc_token_losses_offset(cfg, with_backward=True) -> int:

@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <string>
 #include <vector>
 
 #include "launch.h"
@@ -162,7 +163,14 @@ struct LayerActs {
   uint64_t h, rinv1, qkv, rqk, o, lse, h2, rinv2, a;
 };
 
+// A named piece of the workspace (offset and size in bytes).
+struct Piece {
+  std::string name;
+  uint64_t offset, bytes;
+};
+
 struct Plan {
+  std::vector<Piece> pieces;
   uint64_t status, cs, x, rinv0, xf, rinvf, loss_rows, logits;
   std::vector<LayerActs> acts;
   // backward only
@@ -171,59 +179,71 @@ struct Plan {
   uint64_t total;
 };
 
-Plan plan_of(const Dims& D, bool bwd) {
+// Every piece is followed by a guard of kGuard bytes that no kernel writes, so
+// a test can fill the workspace with a pattern and find any write outside the
+// pieces after a call.
+constexpr uint64_t kGuard = 256;
+
+Plan plan_of(const Dims& D, bool bwd, bool record = false) {
   Plan p{};
   uint64_t off = 0;
-  auto take = [&](uint64_t bytes) {
+  std::string prefix;
+  auto take_named = [&](const char* name, uint64_t bytes) {
     const uint64_t o = off;
-    off = align_up(off + std::max<uint64_t>(bytes, 1), kAlign);
+    if (record) {
+      if (!prefix.empty()) p.pieces.push_back({prefix + name, o, bytes});
+      else p.pieces.push_back({name, o, bytes});
+    }
+    off = align_up(off + std::max<uint64_t>(bytes, 1), kAlign) + kGuard;
     return o;
   };
   const uint64_t M = D.M, e = D.esz;
   const uint64_t Mc = chunk_rows(D);
-  p.status = take(256);
-  p.cs = take((uint64_t)D.T * 64 * 2 * 4);
-  p.x = take(M * D.d * 4);
-  p.rinv0 = take(M * 4);
-  p.xf = take(M * D.d * e);
-  p.rinvf = take(M * 4);
-  p.loss_rows = take(M * 4);
-  p.logits = take(Mc * D.V * e);                // the logit gradient replaces them
+  p.status = take_named("status", 256);
+  p.cs = take_named("rope_table", (uint64_t)D.T * 64 * 2 * 4);
+  p.x = take_named("x", M * D.d * 4);
+  p.rinv0 = take_named("rinv0", M * 4);
+  p.xf = take_named("xf", M * D.d * e);
+  p.rinvf = take_named("rinvf", M * 4);
+  p.loss_rows = take_named("loss_rows", M * 4);
+  p.logits = take_named("logits", Mc * D.V * e);                // the logit gradient replaces them
   const int nsets = bwd ? D.L : 1;
   for (int l = 0; l < nsets; ++l) {
     LayerActs a;
-    a.h = take(M * D.d * e);
-    a.rinv1 = take(M * 4);
-    a.qkv = take(M * D.Q * e);
-    a.rqk = take(M * (D.H + 1) * 4);
-    a.o = take(M * D.d * e);
-    a.lse = take(M * D.H * 4);
-    a.h2 = take(M * D.d * e);
-    a.rinv2 = take(M * 4);
-    a.a = take(M * D.F * e);
+    prefix = "h" + std::to_string(l) + ".";
+    a.h = take_named("h", M * D.d * e);
+    a.rinv1 = take_named("rinv1", M * 4);
+    a.qkv = take_named("qkv", M * D.Q * e);
+    a.rqk = take_named("rqk", M * (D.H + 1) * 4);
+    a.o = take_named("o", M * D.d * e);
+    a.lse = take_named("lse", M * D.H * 4);
+    a.h2 = take_named("h2", M * D.d * e);
+    a.rinv2 = take_named("rinv2", M * 4);
+    a.a = take_named("a", M * D.F * e);
     p.acts.push_back(a);
   }
+  prefix.clear();
   if (bwd) {
-    p.dx = take(M * D.d * 4);
-    p.g = take(M * D.d * e);
-    p.dh = take(M * D.d * 4);        // T-typed input gradients; fp32 partial sums for dE
-    p.dbig = take(M * std::max(D.F, D.Q) * e);
-    p.dout = take(M * D.d * e);
-    p.delta = take(M * D.H * 4);
+    p.dx = take_named("dx", M * D.d * 4);
+    p.g = take_named("g", M * D.d * e);
+    p.dh = take_named("dh", M * D.d * 4);        // T-typed input gradients; fp32 partial sums for dE
+    p.dbig = take_named("dbig", M * std::max(D.F, D.Q) * e);
+    p.dout = take_named("dout", M * D.d * e);
+    p.delta = take_named("delta", M * D.H * 4);
     uint64_t part = 0;
     const int64_t shapes[4][2] = {{D.Q, D.d}, {D.d, D.d}, {D.F, D.d}, {D.d, D.F}};
     for (auto& sh : shapes) part = std::max(part, wgrad_plan(D.dt, sh[0], sh[1], D.M).partial_floats);
     const int sx = dgrad_splits(D.dt, Mc, D.d, D.V);
     if (sx > 1) part = std::max<uint64_t>(part, (uint64_t)sx * Mc * D.d);
-    p.partial = take(part * 4);
-    p.attn_part = take(nc::attn_bwd_scratch_floats(D.B, D.T) * 4);
-    p.counts = take((uint64_t)(D.V + 1) * 4);
-    p.offsets = take((uint64_t)(D.V + 1) * 4);
-    p.cursor = take((uint64_t)D.V * 4);
-    p.list = take(M * 4);
-    p.item_off = take((uint64_t)(D.V + 1) * 4);
-    p.part_off = take((uint64_t)(D.V + 1) * 4);
-    p.item_bucket = take(nc::embed_bwd_max_pieces(M, D.V) * 4);
+    p.partial = take_named("partial", part * 4);
+    p.attn_part = take_named("attn_part", nc::attn_bwd_scratch_floats(D.B, D.T) * 4);
+    p.counts = take_named("counts", (uint64_t)(D.V + 1) * 4);
+    p.offsets = take_named("offsets", (uint64_t)(D.V + 1) * 4);
+    p.cursor = take_named("cursor", (uint64_t)D.V * 4);
+    p.list = take_named("list", M * 4);
+    p.item_off = take_named("item_off", (uint64_t)(D.V + 1) * 4);
+    p.part_off = take_named("part_off", (uint64_t)(D.V + 1) * 4);
+    p.item_bucket = take_named("item_bucket", nc::embed_bwd_max_pieces(M, D.V) * 4);
   }
   p.total = off;
   return p;
@@ -518,6 +538,22 @@ int nc_workspace_bytes(const nc_config* cfg, int32_t with_backward, uint64_t* by
   if (rc) return rc;
   if (!bytes) return NC_ERR_NULL;
   *bytes = plan_of(dims_of(cfg), with_backward != 0).total;
+  return NC_OK;
+}
+
+int nc_workspace_pieces(const nc_config* cfg, int32_t with_backward, nc_ws_piece* out, int32_t cap,
+                        int32_t* n) {
+  const int rc = validate(cfg);
+  if (rc) return rc;
+  if (!n || (cap > 0 && !out)) return NC_ERR_NULL;
+  const Plan P = plan_of(dims_of(cfg), with_backward != 0, true);
+  *n = (int32_t)P.pieces.size();
+  for (int i = 0; i < (int)P.pieces.size() && i < cap; ++i) {
+    memset(out[i].name, 0, sizeof(out[i].name));
+    snprintf(out[i].name, sizeof(out[i].name), "%s", P.pieces[i].name.c_str());
+    out[i].offset = P.pieces[i].offset;
+    out[i].bytes = P.pieces[i].bytes;
+  }
   return NC_OK;
 }
 

@@ -116,6 +116,22 @@ int nc_param_layout(const nc_config* cfg, nc_tensor_info* out, int32_t cap, int3
  * (saves every layer's activations) over nc_forward_loss. Host only. */
 int nc_workspace_bytes(const nc_config* cfg, int32_t with_backward, uint64_t* bytes);
 
+/* One piece of the workspace plan: what it holds, where it starts and how
+ * many bytes it spans. Every piece is followed by at least 256 bytes that no
+ * kernel writes (guard bytes), so a caller or test can fill a workspace with a
+ * pattern and check after a call that nothing outside the pieces changed. */
+typedef struct {
+  char name[32];
+  uint64_t offset;
+  uint64_t bytes;
+} nc_ws_piece;
+
+/* Writes up to `cap` pieces of the workspace plan of nc_forward_backward
+ * (with_backward != 0) or nc_forward_loss, in address order, and sets *n to
+ * their total number. Host only. */
+int nc_workspace_pieces(const nc_config* cfg, int32_t with_backward, nc_ws_piece* out, int32_t cap,
+                        int32_t* n);
+
 /* Rows of the lm_head + softcapped cross-entropy chunk. The step runs the
  * vocabulary-wide products and the loss over row chunks of the batch, so the
  * only [rows, vocab_size] buffer in the workspace (the chunk's logits, which

@@ -119,6 +119,26 @@ def test_workspace_grows_with_batch_and_depth():
     assert off % 256 == 0 and off + 4 * 65536 <= nc.nc_workspace_bytes(c4, True)
 
 
+@pytest.mark.parametrize("name", list(PRESETS))
+@pytest.mark.parametrize("bwd", [True, False])
+def test_workspace_pieces_are_guarded(name, bwd):
+    """The workspace plan: pieces in address order, 256-byte aligned, each
+    followed by at least 256 guard bytes inside the workspace; the per-token
+    losses sit where nc_token_losses_offset says."""
+    cfg = _cfg(name)
+    pieces = nc.nc_workspace_pieces(cfg, bwd)
+    total = nc.nc_workspace_bytes(cfg, bwd)
+    assert pieces[0][:2] == ("status", 0)
+    for (n0, o0, b0), (n1, o1, b1) in zip(pieces, pieces[1:]):
+        assert o0 % 256 == 0 and o1 >= o0 + b0 + 256, (n0, n1)
+    assert pieces[-1][1] + pieces[-1][2] + 256 <= total
+    names = [p[0] for p in pieces]
+    assert len(set(names)) == len(names)
+    assert dict((n, o) for n, o, _ in pieces)["loss_rows"] == nc.nc_token_losses_offset(cfg, bwd)
+    L = PRESETS[name].depth
+    assert sum(n.startswith("h") and "." in n for n in names) == (9 * L if bwd else 9)
+
+
 def test_lm_chunk_rows_bound_the_workspace():
     """The lm_head / loss chunk keeps the only [rows, V] buffer independent of
     the batch: at depth 20 the default 32,768-row chunk needs about 4 GiB less than

@@ -212,3 +212,33 @@ def test_lm_head_in_row_chunks(name, rows, lm_chunk):
         else:
             check_bf16(g, o, f"accumulated {tname}")
 
+
+
+@pytest.mark.parametrize("name,rows,bwd", [("C1", 64, True), ("C2", 1024, True), ("C2", 0, False)])
+def test_workspace_guards_untouched(name, rows, bwd, lm_chunk):
+    """Canaries: the whole workspace is filled with 0xA5, a step runs, and every
+    byte outside the pieces of nc_workspace_pieces (the 256-byte guards after
+    each piece and the alignment gaps) still holds 0xA5."""
+    pseed, dseed = SEEDS[name]
+    c = PRESETS[name]
+    lm_chunk(rows)
+    cfg, ocfg, step, p64, tok, tgt = _setup(c.depth, c.vocab_size, c.seq_len, c.batch, c.dtype,
+                                            pseed, dseed, TOKEN_LAW[name])
+    if not bwd:
+        step = nc.Step(cfg, with_backward=False)
+        step.params.copy_(torch.zeros_like(step.params))
+    pieces = nc.nc_workspace_pieces(cfg, bwd)
+    ws = step.ws
+    assert ws.numel() == nc.nc_workspace_bytes(cfg, bwd)
+    ws.fill_(0xA5)
+    if bwd:
+        step.forward_backward(dev(tok), dev(tgt))
+    else:
+        step.forward_loss(dev(tok), dev(tgt))
+    torch.cuda.synchronize()
+    outside = torch.ones(ws.numel(), dtype=torch.bool, device="cuda")
+    for _, off, nbytes in pieces:
+        outside[off:off + nbytes] = False
+    assert int(outside.sum().item()) >= 256 * len(pieces)
+    changed = (ws[outside] != 0xA5).nonzero()
+    assert changed.numel() == 0, [p for p in pieces if p[1] <= int(changed[0]) < p[1] + p[2] + 512]
