@@ -86,6 +86,35 @@ def measured_traffic(shape):
     return int(t["fetch_bytes"] + t["write_bytes"])
 
 
+def roofline_after_steps(cfg, nc, torch, step, tok_d, tgt_d, reps=5):
+    """The roofline kernel under the step's conditions (clocks, caches): one
+    launch timed right after each of `reps` training steps, HIP events on the
+    stream it is launched on."""
+    M = cfg.batch * cfg.seq_len
+    d = 64 * cfg.depth
+    F = 4 * d
+    et = torch.bfloat16 if cfg.dtype == nc.NC_BF16 else torch.float32
+    A = torch.randn(M, d, device="cuda").to(et)
+    B = (torch.randn(F, d, device="cuda") * 0.02).to(et)
+    U = torch.empty(M, F, device="cuda", dtype=et)
+    s = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        step.forward_backward(tok_d, tgt_d)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        nc.nc_op_gemm(cfg.dtype, 1, 1, nc.EPI_RELU2, A, B, U, None, M, F, d, d, d, F, stream=s)
+        e1.record(s)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+    del A, B, U
+    sec = sum(times) / len(times)
+    ach = 2.0 * M * F * d / sec / 1e12
+    return {"avg_us": round(sec * 1e6, 2), "achieved": round(ach, 2),
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "launches": reps,
+            "how": "one launch timed right after each training step (the step's clocks and caches)"}
+
+
 def dominant_kernel_roofline(cfg, nc, torch, reps=20, warm=25):
     """Times the MLP up-projection GEMM (tokens x 4d x d, relu^2 epilogue;
     the largest single contraction of the step) on its own, with HIP events
@@ -441,6 +470,7 @@ def main():
         "lm_chunk_rows": nc.nc_lm_chunk_rows(cfg),
         "wall_s_timed": round(wall, 3),
     }
+    in_step = roofline_after_steps(cfg, nc, torch, step, tok_d, tgt_d)
     if not a.no_eval:
         out["eval_bpb"] = bpb_timing(step, nc, torch, c, tok_d, tgt_d)
     if not a.no_optimizer:
@@ -455,6 +485,8 @@ def main():
     del step
     torch.cuda.empty_cache()
     out["roofline"] = dominant_kernel_roofline(cfg, nc, torch)
+    if in_step:
+        out["roofline"]["after_step"] = in_step
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(a.workload)
     print(json.dumps(out), flush=True)
