@@ -269,10 +269,12 @@ def _attn_inputs(rng, B, T, H, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("B,T,H", [(2, 64, 1), (1, 256, 3), (2, 192, 10), (1, 128, 13),
-                                   (1, 1024, 2), (1, 2048, 1), (1, 2048, 10)])
+                                   (1, 1024, 2), (1, 2048, 10), (1, 2560, 2), (1, 4160, 1)])
 def test_attention_fwd_bwd(dtype, B, T, H):
-    """Up to T = 2048: several 512-token query chunks of the dK/dV kernel and
-    their fixed-order reduction, at the depth-20 head count too."""
+    """Up to T = 2048 at the depth-20 head count (one dK/dV work item per key
+    block), and beyond: T = 2560 and 4160 give key blocks with two and three
+    2048-token query chunks, whose partials meet in the fixed-order reduction
+    (the last chunk and, at 4160, the last key block ragged)."""
     rng = np.random.default_rng(B + T + H)
     d = 128 * H
     Q = d + 256

@@ -76,10 +76,10 @@ def test_noalloc_attn_bwd_matches_scratch_version(dtype):
 
 
 def test_noalloc_attn_bwd_refuses_sizes_beyond_the_array():
-    """B = 4 sequences of 2048 tokens at 10 heads need 34 MB of scratch (> 32
-    MiB): refused on the host, nothing enqueued. B = 3 (25 MB) runs and
-    matches the scratch version bitwise."""
-    B, T, H = 4, 2048, 10
+    """B = 16 sequences of 2048 tokens at 10 heads need 34.9 MB of scratch
+    (> 32 MiB): refused on the host, nothing enqueued. B = 15 (32.7 MB) runs
+    and matches the scratch version bitwise."""
+    B, T, H = 16, 2048, 10
     M, Q = B * T, 128 * H + 256
     qkv = torch.zeros((M, Q), dtype=torch.bfloat16, device="cuda")
     o = torch.zeros((M, 128 * H), dtype=torch.bfloat16, device="cuda")
@@ -90,7 +90,7 @@ def test_noalloc_attn_bwd_refuses_sizes_beyond_the_array():
     assert e.value.code == -5
     assert int(torch.count_nonzero(dq).item()) == 0
     rng = np.random.default_rng(9)
-    B = 3
+    B = 15
     qkv, o, lse, do = _inputs(rng, B, T, H, "bf16")
     dq_ref = _reference("bf16", qkv, o, do, lse, B, T, H)
     dq = torch.zeros_like(dq_ref)
