@@ -27,8 +27,9 @@
 // Backward: dK/dV of a 128-key block are summed over all heads and one chunk
 // of up to 2048 later query tokens by one workgroup (16 keys per wavefront,
 // accumulators in registers); the work items are issued longest first (early
-// key blocks), which balances them under the causal mask, and a second pass
-// adds the chunk partials in a fixed order. dQ
+// key blocks), which balances them under the causal mask; with one chunk per
+// key block (T <= 2048) the workgroup writes dK and dV itself, otherwise a
+// second pass adds the chunk partials in a fixed order. dQ
 // comes from a kernel shaped like the forward (32-key tiles). No atomics
 // anywhere, so the results are bitwise reproducible.
 #include <math.h>
@@ -554,10 +555,14 @@ __device__ inline void dkv_item(int Tn, int i, int* kblk, int* chunk) {
   *chunk = i;
 }
 
-template <typename T>
+// DIRECT (one query chunk per key block, T <= QCH): dK (scaled by 1/sqrt(D))
+// and dV go straight into the key and value columns of dqkv; otherwise each
+// chunk leaves an fp32 partial for attn_dkv_reduce_kernel.
+template <typename T, bool DIRECT>
 __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
     const T* __restrict__ qkv, int ldq, const T* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, int B, int Tn, int H, float* __restrict__ part) {
+    const float* __restrict__ delta, int B, int Tn, int H, float* __restrict__ part,
+    T* __restrict__ dqkv, int ldd) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
   constexpr int SQ = BQK;                      // query rows per step
@@ -738,6 +743,23 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
     if (it + 1 < niter) step(it + 1, preB, preA);
   }
   if (!kact) return;
+  if constexpr (DIRECT) {
+    const float scale = 1.0f / sqrtf((float)D);
+    typedef T T4 __attribute__((ext_vector_type(4)));
+    T* dst = dqkv + (row0 + key0 + l16) * ldd + H * D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      T4 wk, wv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        wk[r] = from_f32<T>(dk[dt][0][r] * scale);
+        wv[r] = from_f32<T>(dv[dt][0][r]);
+      }
+      *reinterpret_cast<T4*>(dst + dt * 16 + lg * 4) = wk;
+      *reinterpret_cast<T4*>(dst + D + dt * 16 + lg * 4) = wv;
+    }
+    return;
+  }
   // fp32 partial sums of this query chunk: part[chunk][token][0..127 dK, 128..255 dV]
   const size_t M = (size_t)B * Tn;
 #pragma unroll
@@ -813,21 +835,34 @@ hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const f
   int items = 0;
   for (int kb = 0; kb < (T + BKW - 1) / BKW; ++kb) items += dkv_chunks(T, kb);
   dim3 gk(B * items), bk(DKW_THREADS);
+  const bool direct = dkv_chunks(T, 0) == 1;     // every key block in one work item
   const size_t M = (size_t)B * T;
   dim3 gr((unsigned)((M + 3) / 4)), br(256);
   if (t == DType::BF16) {
     const bf16* q = static_cast<const bf16*>(qkv);
     const bf16* d = static_cast<const bf16*>(dout);
     bf16* g = static_cast<bf16*>(dqkv);
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<bf16>, gk, bk, 0, s, q, ldq, d, lse, delta, B, T, H, scratch);
-    hipLaunchKernelGGL(attn_dkv_reduce_kernel<bf16>, gr, br, 0, s, scratch, B, T, H, g, ldd);
+    if (direct) {
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<bf16, true>), gk, bk, 0, s, q, ldq, d, lse, delta, B, T,
+                         H, scratch, g, ldd);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<bf16, false>), gk, bk, 0, s, q, ldq, d, lse, delta, B,
+                         T, H, scratch, g, ldd);
+      hipLaunchKernelGGL(attn_dkv_reduce_kernel<bf16>, gr, br, 0, s, scratch, B, T, H, g, ldd);
+    }
     hipLaunchKernelGGL(attn_bwd_dq_kernel<bf16>, gq, bq, 0, s, q, ldq, d, lse, delta, T, H, g, ldd);
   } else {
     const float* q = static_cast<const float*>(qkv);
     const float* d = static_cast<const float*>(dout);
     float* g = static_cast<float*>(dqkv);
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<float>, gk, bk, 0, s, q, ldq, d, lse, delta, B, T, H, scratch);
-    hipLaunchKernelGGL(attn_dkv_reduce_kernel<float>, gr, br, 0, s, scratch, B, T, H, g, ldd);
+    if (direct) {
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<float, true>), gk, bk, 0, s, q, ldq, d, lse, delta, B,
+                         T, H, scratch, g, ldd);
+    } else {
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<float, false>), gk, bk, 0, s, q, ldq, d, lse, delta,
+                         B, T, H, scratch, g, ldd);
+      hipLaunchKernelGGL(attn_dkv_reduce_kernel<float>, gr, br, 0, s, scratch, B, T, H, g, ldd);
+    }
     hipLaunchKernelGGL(attn_bwd_dq_kernel<float>, gq, bq, 0, s, q, ldq, d, lse, delta, T, H, g, ldd);
   }
   return hipGetLastError();
