@@ -389,7 +389,8 @@ def nc_op_attn_bwd_scratch_bytes(B, T) -> int:
 
 def nc_op_attn_bwd(dtype, qkv, o, dout, lse, delta, B, T, H, dqkv, scratch=None, stream=None):
     """scratch: a device buffer of nc_op_attn_bwd_scratch_bytes(B, T) bytes
-    (allocated here through torch when not given)."""
+    (allocated here through torch when not given; that size is 0, and the
+    pointer null, when T <= 2048)."""
     if scratch is None:
         import torch
         scratch = torch.empty(nc_op_attn_bwd_scratch_bytes(B, T), dtype=torch.uint8, device="cuda")

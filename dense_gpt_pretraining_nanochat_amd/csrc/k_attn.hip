@@ -824,7 +824,8 @@ hipError_t attn_bwd_delta(DType t, const void* o, const void* dout, int B, int T
 }
 
 size_t attn_bwd_scratch_floats(int B, int T) {
-  return (size_t)dkv_chunks(T, 0) * B * T * 2 * D;
+  const int nch = dkv_chunks(T, 0);
+  return nch > 1 ? (size_t)nch * B * T * 2 * D : 0;   // one chunk: dK/dV written directly
 }
 
 hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const float* lse,

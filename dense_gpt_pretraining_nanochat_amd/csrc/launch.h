@@ -98,6 +98,7 @@ hipError_t attn_bwd_delta(DType t, const void* o, const void* dout, int B, int T
                           float* delta, hipStream_t s);
 // writes dq into dqkv[:, 0:H*128], dk and dv into the next two 128-col blocks;
 // scratch holds attn_bwd_scratch_floats(B, T) floats of partial dK/dV sums
+// (none, and scratch may be null, when T <= 2048: dK/dV are written directly)
 size_t attn_bwd_scratch_floats(int B, int T);
 hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const float* lse,
                     const float* delta, int B, int T, int H, void* dqkv, int ldd, float* scratch,

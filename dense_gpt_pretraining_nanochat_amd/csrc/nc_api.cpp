@@ -1379,8 +1379,9 @@ int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* do
                    const float* lse, float* delta, int32_t B, int32_t T, int32_t H, void* dqkv,
                    float* scratch, void* stream) {
   if (bad_dtype(dtype)) return NC_ERR_ARG;
-  if (!qkv || !o || !dout || !lse || !delta || !dqkv || !scratch) return NC_ERR_NULL;
+  if (!qkv || !o || !dout || !lse || !delta || !dqkv) return NC_ERR_NULL;
   if (B <= 0 || T < 64 || T % 64 || H < 1 || H > 16) return NC_ERR_ARG;
+  if (!scratch && nc::attn_bwd_scratch_floats(B, T) > 0) return NC_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int ld = H * 128 + 256;
   HIPCHECK(nc::attn_bwd_delta(dt_of(dtype), o, dout, B, T, H, delta, s));

@@ -386,11 +386,14 @@ int nc_op_rope_qknorm_bwd(int32_t dtype, void* dqkv, const void* qkv, int32_t B,
  * above ~60 overflow. */
 int nc_op_attn_fwd(int32_t dtype, const void* qkv, int32_t B, int32_t T, int32_t H, void* o,
                    float* lse, void* stream);
-/* Bytes of scratch nc_op_attn_bwd needs (fp32 partial dK/dV sums per
- * 2048-token query chunk); 0 for invalid sizes. Host only. */
+/* Bytes of scratch nc_op_attn_bwd needs: fp32 partial dK/dV sums per
+ * 2048-token query chunk when T > 2048; 0 when T <= 2048 (each key block's
+ * dK/dV are then summed and written by one workgroup) and for invalid sizes.
+ * Host only. */
 uint64_t nc_op_attn_bwd_scratch_bytes(int32_t B, int32_t T);
 /* dqkv [B*T, d+256] (T) from qkv, o, dout [B*T, H*128], lse; delta scratch
- * [B, H, T] fp32; scratch of nc_op_attn_bwd_scratch_bytes(B, T) bytes. */
+ * [B, H, T] fp32; scratch of nc_op_attn_bwd_scratch_bytes(B, T) bytes (may be
+ * NULL when that is 0). */
 int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* dout,
                    const float* lse, float* delta, int32_t B, int32_t T, int32_t H, void* dqkv,
                    float* scratch, void* stream);
@@ -400,9 +403,10 @@ int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* do
  * nc_op_attn_bwd (bitwise: the same kernels) except that delta and the dK/dV
  * chunk partials live in a 32 MiB array inside the library, one per device,
  * held until the process ends; the call allocates nothing. Sizes needing more
- * than that, i.e. 4*B*H*T (rounded up to 256) + 4*B*T*256*ceil(T/2048) bytes
- * above 32 MiB (at T = 2048 and H = 10: B up to 15 fits, 16 does not), are
- * refused with NC_ERR_WORKSPACE before anything is enqueued. Every call on a
+ * than that, i.e. 4*B*H*T (rounded up to 256) plus, when T > 2048,
+ * 4*B*T*256*ceil(T/2048) bytes above 32 MiB (at T = 2048 and H = 10: B up to
+ * 409; at T = 4096 and H = 10: B up to 3), are refused with NC_ERR_WORKSPACE
+ * before anything is enqueued. Every call on a
  * device shares that device's array and nothing in it needs clearing (each
  * call writes what it reads); calls that overlap on one device (concurrent
  * streams, threads) race on it and must be serialised by the caller. */

@@ -100,6 +100,13 @@ def test_argument_checks_before_any_launch():
     assert L.nc_op_gemm(1, 1, 1, 0, p(a), p(a), p(a), None, 16, 16, 48, 64, 64, 16, None) == -7
     assert L.nc_op_gemm(1, 1, 1, 4, p(a), p(a), p(a), None, 16, 16, 64, 64, 64, 16, None) == -3
     assert L.nc_op_attn_fwd(1, p(a), 1, 96, 1, p(a), p(a), None) == -7
+    # attention backward scratch: none up to 2048 tokens (dK/dV written
+    # directly), one fp32 partial per 2048-query chunk beyond; a null scratch
+    # is refused only where scratch is needed
+    assert nc.nc_op_attn_bwd_scratch_bytes(32, 2048) == 0
+    assert nc.nc_op_attn_bwd_scratch_bytes(1, 2112) == 2 * 2112 * 256 * 4
+    assert nc.nc_op_attn_bwd_scratch_bytes(2, 4160) == 3 * 2 * 4160 * 256 * 4
+    assert L.nc_op_attn_bwd(1, p(a), p(a), p(a), p(a), p(a), 1, 2112, 2, p(a), None, None) == -3
 
 
 def test_status_strings():

@@ -46,8 +46,8 @@ def _reference(dtype, qkv, o, do, lse, B, T, H):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_noalloc_attn_bwd_matches_scratch_version(dtype):
     rng = np.random.default_rng(7 if dtype == "bf16" else 8)
-    first = (2, 1024, 10)            # 2 x 1024 tokens, 10 heads: 2 query chunks per key block
-    second = (1, 192, 3)             # smaller: the fixed array keeps the first call's contents
+    first = (1, 2560, 2)             # 2560 tokens: two 2048-query chunks for the first key blocks
+    second = (1, 192, 3)             # smaller, dK/dV written directly; the array keeps old contents
     outs = []
     for (B, T, H) in (first, second):
         qkv, o, lse, do = _inputs(rng, B, T, H, dtype)
@@ -76,10 +76,11 @@ def test_noalloc_attn_bwd_matches_scratch_version(dtype):
 
 
 def test_noalloc_attn_bwd_refuses_sizes_beyond_the_array():
-    """B = 16 sequences of 2048 tokens at 10 heads need 34.9 MB of scratch
-    (> 32 MiB): refused on the host, nothing enqueued. B = 15 (32.7 MB) runs
-    and matches the scratch version bitwise."""
-    B, T, H = 16, 2048, 10
+    """B = 4 sequences of 4096 tokens at 10 heads need 34.2 MB of scratch
+    (delta and two query chunks of dK/dV partials; > 32 MiB): refused on the
+    host, nothing enqueued. B = 3 (25.7 MB) runs and matches the scratch
+    version bitwise."""
+    B, T, H = 4, 4096, 10
     M, Q = B * T, 128 * H + 256
     qkv = torch.zeros((M, Q), dtype=torch.bfloat16, device="cuda")
     o = torch.zeros((M, 128 * H), dtype=torch.bfloat16, device="cuda")
@@ -90,7 +91,7 @@ def test_noalloc_attn_bwd_refuses_sizes_beyond_the_array():
     assert e.value.code == -5
     assert int(torch.count_nonzero(dq).item()) == 0
     rng = np.random.default_rng(9)
-    B = 15
+    B = 3
     qkv, o, lse, do = _inputs(rng, B, T, H, "bf16")
     dq_ref = _reference("bf16", qkv, o, do, lse, B, T, H)
     dq = torch.zeros_like(dq_ref)
