@@ -610,14 +610,18 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
   constexpr bool PFT = kPrefetch(sizeof(T));
   auto qsrc = [&](int i) { return qkv + (row0 + q0 + (i / H) * SQ) * ldq + (i % H) * D; };
   auto osrc = [&](int i) { return dout + (row0 + q0 + (i / H) * SQ) * ldo + (i % H) * D; };
-  // lse (log2 domain) or delta of step i for thread tid < 2 * SQ
-  auto stat_of = [&](int i) -> float {
+  // Per-row statistics of step i: threads tid < SQ hold lse, SQ <= tid < 2 SQ
+  // delta. Every thread loads an in-range element (of either array), so the
+  // load needs no branch; lse goes to the log2 domain only when it is stored.
+  // (A load under a branch, or a use right after it, makes the compiler wait
+  // for every load in flight, the tile prefetch included.)
+  const float* stat_src = (tid & SQ) ? delta : lse;
+  auto stat_raw = [&](int i) -> float {
     const int h = i % H, t = q0 + (i / H) * SQ + (tid % SQ);
-    const size_t idx = ((size_t)b * H + h) * Tn + t;
-    return tid < SQ ? lse[idx] * kLog2e : delta[idx];
+    return stat_src[((size_t)b * H + h) * Tn + t];
   };
-  auto stats = [&](int i, int buf) {
-    if (tid < 2 * SQ) stat_s[buf][tid] = stat_of(i);
+  auto stat_put = [&](int buf, float raw) {
+    if (tid < 2 * SQ) stat_s[buf][tid] = tid < SQ ? raw * kLog2e : raw;
   };
   // Q and dO rows have different strides: staged chunk by chunk from either source
   for (int c = tid; c < 2 * SQ * A::DC; c += DKW_THREADS) {
@@ -626,7 +630,7 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
     *reinterpret_cast<V*>((which ? Os : Qs) + r * ST + dc * A::VEC) =
         *reinterpret_cast<const V*>(src + dc * A::VEC);
   }
-  stats(0, 0);
+  stat_put(0, stat_raw(0));
   __syncthreads();
 
   // bf16: Q/dO tiles are prefetched into registers two steps ahead (one step
@@ -643,7 +647,8 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
     }
   };
   PreSet preA, preB;
-  if (PFT && 1 < niter) prefetch(1, preA);
+  // prefetches past the last step reload the last step's tile (in range, never used)
+  if (PFT) prefetch(min(1, niter - 1), preA);
 
   auto step = [&](const int it, PreSet& pre, PreSet& pre2) {
     const int tq0 = q0 + (it / H) * SQ;
@@ -653,8 +658,8 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
     const float* dl_s = stat_s[it & 1] + SQ;
     const bool more = it + 1 < niter;
     // next step's lse / delta, requested now and stored after this step's math
-    const float stat_next = (more && tid < 2 * SQ) ? stat_of(it + 1) : 0.f;
-    if (PFT && it + 2 < niter) prefetch(it + 2, pre2);
+    const float stat_next = stat_raw(more ? it + 1 : it);
+    if (PFT) prefetch(min(it + 2, niter - 1), pre2);
 
     // (a wavefront whose keys lie past T works on zero K/V fragments and
     // stores nothing: no branch here keeps the accumulators in place)
@@ -715,33 +720,39 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
       }
     }
 
-    if (more) {
-      T* Qn = Qs + ((it + 1) & 1) * TILE;
-      T* On = Os + ((it + 1) & 1) * TILE;
-      if (PFT) {
+    T* Qn = Qs + ((it + 1) & 1) * TILE;
+    T* On = Os + ((it + 1) & 1) * TILE;
+    if (PFT) {
+      // unconditional: after the last step the other buffer is no longer read
+      // (its readers finished before the previous barrier)
 #pragma unroll
-        for (int i = 0; i < NPRE; ++i) {
-          const int c = tid + i * DKW_THREADS;
-          const int which = c / (SQ * A::DC), r = (c / A::DC) % SQ, dc = c % A::DC;
-          *reinterpret_cast<V*>((which ? On : Qn) + r * ST + dc * A::VEC) = pre[i];
-        }
-      } else {
-        __syncthreads();
-        for (int c = tid; c < 2 * SQ * A::DC; c += DKW_THREADS) {
-          const int which = c / (SQ * A::DC), r = (c / A::DC) % SQ, dc = c % A::DC;
-          const T* src = which ? osrc(it + 1) + (size_t)r * ldo : qsrc(it + 1) + (size_t)r * ldq;
-          *reinterpret_cast<V*>((which ? On : Qn) + r * ST + dc * A::VEC) =
-              *reinterpret_cast<const V*>(src + dc * A::VEC);
-        }
+      for (int i = 0; i < NPRE; ++i) {
+        const int c = tid + i * DKW_THREADS;
+        const int which = c / (SQ * A::DC), r = (c / A::DC) % SQ, dc = c % A::DC;
+        *reinterpret_cast<V*>((which ? On : Qn) + r * ST + dc * A::VEC) = pre[i];
       }
-      if (tid < 2 * SQ) stat_s[(it + 1) & 1][tid] = stat_next;
+      stat_put((it + 1) & 1, stat_next);
+    } else if (more) {
+      __syncthreads();
+      for (int c = tid; c < 2 * SQ * A::DC; c += DKW_THREADS) {
+        const int which = c / (SQ * A::DC), r = (c / A::DC) % SQ, dc = c % A::DC;
+        const T* src = which ? osrc(it + 1) + (size_t)r * ldo : qsrc(it + 1) + (size_t)r * ldq;
+        *reinterpret_cast<V*>((which ? On : Qn) + r * ST + dc * A::VEC) =
+            *reinterpret_cast<const V*>(src + dc * A::VEC);
+      }
+      stat_put((it + 1) & 1, stat_next);
     }
     __syncthreads();
   };
-  for (int it = 0; it < niter; it += 2) {
+  // two steps per iteration (the prefetch register sets alternate), the odd
+  // last step after the loop: no branch inside the loop body, so the compiler
+  // tracks the loads in flight across the back edge exactly
+  int it = 0;
+  for (; it + 1 < niter; it += 2) {
     step(it, preA, preB);
-    if (it + 1 < niter) step(it + 1, preB, preA);
+    step(it + 1, preB, preA);
   }
+  if (it < niter) step(it, preA, preB);
   if (!kact) return;
   if constexpr (DIRECT) {
     const float scale = 1.0f / sqrtf((float)D);
