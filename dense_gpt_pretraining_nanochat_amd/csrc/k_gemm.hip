@@ -471,8 +471,10 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
   const int split = bid / ntiles;
   const int t = bid - split * ntiles;
   // row tiles per group of the XCD's walk: 4 for the narrow (<= 5 column
-  // tiles) unsplit products, 8 otherwise (measured per shape)
-  const int GROUP = (tiles_n <= 5 && g0.splits == 1) ? 4 : 8;
+  // tiles) unsplit products, 6 for the vocabulary-wide lm_head output (its
+  // 640 KB A panels: six stay in a 4 MB L2 while the B panels stream; 2.5 %
+  // faster than 8 at 32,768 x 65,536 x 1,280), 8 otherwise (measured per shape)
+  const int GROUP = (tiles_n <= 5 && g0.splits == 1) ? 4 : (tiles_n >= 64 ? 6 : 8);
   const int per_group = GROUP * tiles_n;
   const int first_m = (t / per_group) * GROUP;
   const int gsize = min(tiles_m - first_m, GROUP);
