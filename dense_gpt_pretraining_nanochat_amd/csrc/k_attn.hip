@@ -608,8 +608,12 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
   const int nqb = (q1 - q0) / SQ;
   const int niter = nqb * H;
   constexpr bool PFT = kPrefetch(sizeof(T));
-  auto qsrc = [&](int i) { return qkv + (row0 + q0 + (i / H) * SQ) * ldq + (i % H) * D; };
-  auto osrc = [&](int i) { return dout + (row0 + q0 + (i / H) * SQ) * ldo + (i % H) * D; };
+  // Query blocks are visited from the last one down: the workgroups of one
+  // batch row (one XCD) that run together then read the same Q/dO tiles at
+  // about the same time, and the later ones find them in L2.
+  auto qblk = [&](int i) { return q0 + (nqb - 1 - i / H) * SQ; };
+  auto qsrc = [&](int i) { return qkv + (row0 + qblk(i)) * ldq + (i % H) * D; };
+  auto osrc = [&](int i) { return dout + (row0 + qblk(i)) * ldo + (i % H) * D; };
   // Per-row statistics of step i: threads tid < SQ hold lse, SQ <= tid < 2 SQ
   // delta. Every thread loads an in-range element (of either array), so the
   // load needs no branch; lse goes to the log2 domain only when it is stored.
@@ -617,7 +621,7 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
   // for every load in flight, the tile prefetch included.)
   const float* stat_src = (tid & SQ) ? delta : lse;
   auto stat_raw = [&](int i) -> float {
-    const int h = i % H, t = q0 + (i / H) * SQ + (tid % SQ);
+    const int h = i % H, t = qblk(i) + (tid % SQ);
     return stat_src[((size_t)b * H + h) * Tn + t];
   };
   auto stat_put = [&](int buf, float raw) {
@@ -651,7 +655,7 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
   if (PFT) prefetch(min(1, niter - 1), preA);
 
   auto step = [&](const int it, PreSet& pre, PreSet& pre2) {
-    const int tq0 = q0 + (it / H) * SQ;
+    const int tq0 = qblk(it);
     const T* Q = Qs + (it & 1) * TILE;
     const T* O = Os + (it & 1) * TILE;
     const float* lse_s = stat_s[it & 1];
