@@ -470,11 +470,14 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
   const GemmArgs g = batch_item<bf16, EPI>(g0, item);
   const int split = bid / ntiles;
   const int t = bid - split * ntiles;
-  // row tiles per group of the XCD's walk: 4 for the narrow (<= 5 column
-  // tiles) unsplit products, 6 for the vocabulary-wide lm_head output (its
-  // 640 KB A panels: six stay in a 4 MB L2 while the B panels stream; 2.5 %
-  // faster than 8 at 32,768 x 65,536 x 1,280), 8 otherwise (measured per shape)
-  const int GROUP = (tiles_n <= 5 && g0.splits == 1) ? 4 : (tiles_n >= 64 ? 6 : 8);
+  // row tiles per group of the XCD's walk (measured per shape, in the step):
+  // 4 for the narrow (<= 5 column tiles) unsplit products; 6 for the narrow
+  // split-K products (6 x 5 tiles: a whole group is resident on the XCD's 32
+  // compute units, so each A panel and each slice of B is fetched once per
+  // group; the weight gradients 3-4 % and the lm_head input gradient 8 %
+  // faster than with 8) and for the vocabulary-wide lm_head output (six
+  // 640 KB A panels stay in a 4 MB L2 while the B panels stream); 8 otherwise
+  const int GROUP = (tiles_n <= 5 && g0.splits == 1) ? 4 : ((tiles_n >= 64 || tiles_n <= 5) ? 6 : 8);
   const int per_group = GROUP * tiles_n;
   const int first_m = (t / per_group) * GROUP;
   const int gsize = min(tiles_m - first_m, GROUP);
