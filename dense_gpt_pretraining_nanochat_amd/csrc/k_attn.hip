@@ -26,7 +26,9 @@
 //
 // Backward: dK/dV of a 128-key block are summed over all heads and one chunk
 // of up to 2048 later query tokens by one workgroup (16 keys per wavefront,
-// accumulators in registers); the work items are issued longest first (early
+// accumulators in registers, query blocks visited from the last one down so
+// that the key blocks of a batch row running together share the Q/dO tiles
+// in L2); the work items are issued longest first (early
 // key blocks), which balances them under the causal mask; with one chunk per
 // key block (T <= 2048) the workgroup writes dK and dV itself, otherwise a
 // second pass adds the chunk partials in a fixed order. dQ
@@ -535,8 +537,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 }
 
 // --------------------------------------------------------------------------
-// backward, dK and dV: one workgroup per 128-key block, 4 wavefronts x 32
-// keys, looping over every later 32-token query block and every head.
+// backward, dK and dV: one workgroup per 128-key block (and query chunk), 8
+// wavefronts x 16 keys, looping over the chunk's 64-token query blocks (from
+// the last one down) and, inside each, every head.
 // --------------------------------------------------------------------------
 __host__ __device__ inline int dkv_chunks(int Tn, int kblk) {
   return (Tn - kblk * BKW + QCH - 1) / QCH;
