@@ -238,6 +238,17 @@ __global__ __launch_bounds__(512, 2) void skinny_kernel(SkArgs g) {
     }
   }
 
+  // The residual tile this thread adds to (AddF32) is read now, alongside the
+  // first operand loads, so its latency is not paid again in the epilogue;
+  // this workgroup is the only writer of these elements.
+  f32x4 cres = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (EPI == SkEpi::AddF32) {
+    if (tid < TILES * 64) {
+      const int ln = tid & 63, tile = tid >> 6, nt = tile / MT, mt = tile % MT;
+      const int m = 16 * mt + (ln & 15), n = n0 + 16 * nt + 4 * (ln >> 4);
+      if (m < g.M) cres = *reinterpret_cast<const f32x4*>(static_cast<const float*>(g.C) + (size_t)m * g.ldc + n);
+    }
+  }
   const bf16* wrow = W + (size_t)(n0 + l16) * g.ldw + 8 * lg;
   const size_t wtile = (size_t)16 * g.ldw;     // next 16 W rows
   f32x4 acc[NT][MT];
@@ -368,7 +379,7 @@ __global__ __launch_bounds__(512, 2) void skinny_kernel(SkArgs g) {
     f32x4 c = v;
     if (row) {
       f32x4* cp = reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off);
-      c = *cp + v;
+      c = cres + v;
       *cp = c;
       if (g.xb)
         *reinterpret_cast<bf16x4*>(static_cast<bf16*>(g.xb) + off) =
