@@ -184,6 +184,11 @@ struct QBlock {
   int b, qb, hg;
 };
 __device__ __forceinline__ QBlock qblock_of(int bid, int nqb, int ngroups) {
+  // the hardware deals workgroups to the 8 XCDs round-robin; remapped, each
+  // XCD takes a contiguous range (whole batch rows), so the workgroups running
+  // on one XCD share their row's K/V tiles in its L2
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
   const int per_b = nqb * ngroups;
   QBlock q;
   q.b = bid / per_b;
