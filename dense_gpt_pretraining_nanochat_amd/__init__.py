@@ -74,6 +74,7 @@ _SIGS = {
     "nc_validate_config": [_CFG],
     "nc_set_lm_chunk_rows": [_I32],
     "nc_lm_chunk_rows": [_CFG, ctypes.POINTER(_I32)],
+    "nc_set_gemm_persistent": [_I32],
     "nc_param_count": [_CFG, ctypes.POINTER(_U64)],
     "nc_param_layout": [_CFG, ctypes.POINTER(NcTensorInfo), _I32, ctypes.POINTER(_I32)],
     "nc_workspace_bytes": [_CFG, _I32, ctypes.POINTER(_U64)],
@@ -174,6 +175,12 @@ def nc_validate_config(cfg) -> int:
 
 def nc_set_lm_chunk_rows(rows: int):
     _check(lib().nc_set_lm_chunk_rows(rows), "nc_set_lm_chunk_rows")
+
+
+def nc_set_gemm_persistent(on):
+    """on: True/False (or the raw 0/1 the C call takes; anything else is refused)."""
+    v = int(on) if isinstance(on, bool) else on
+    _check(lib().nc_set_gemm_persistent(v), "nc_set_gemm_persistent")
 
 
 def nc_lm_chunk_rows(cfg) -> int:

@@ -23,6 +23,7 @@
 // into LDS, so its matrix-core reads are always 16-byte, K-contiguous reads.
 // Workgroup ids are remapped so each XCD (8 per chip, own L2) walks a
 // contiguous, row-grouped range of output tiles.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -442,6 +443,28 @@ __device__ __forceinline__ void epilogue4_in(const GemmArgs& g, int split, int m
   }
 }
 
+// Staging of one wavefront's 32 x 64 fp32 accumulator block for the epilogue:
+// row r, 16-byte chunk c (0..15) at chunk slot c ^ ((r >> 1) & 15) of a 256-byte
+// row, so the column writes (32 rows, one chunk) and the row reads (2 or 4 rows,
+// consecutive chunks) both touch 32 distinct 16-byte bank groups per 32 lanes.
+// The accesses go through restrict-qualified pointers: like the transposed ring
+// reads, they then carry alias-scope information, and the compiler's wait
+// insertion does not make them wait for the direct loads of the next tile that
+// are in flight into other ring slots.
+__device__ __forceinline__ int stg_off(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 15)) << 2); }
+__device__ __forceinline__ void stg_put(float* __restrict__ p, f32x4 v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+__device__ __forceinline__ f32x4 stg_get(const float* __restrict__ p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+
+// s_waitcnt immediate for "at most n (0..63) vector-memory ops outstanding, no
+// LDS ops outstanding" (gfx9: vmcnt bits 3:0 and 15:14, expcnt 6:4 left at 7).
+#define NC_WAIT_VM_LGKM0_WIDE(n) __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 15) | (((n) >> 4) << 14))
+// only LDS ops: vmcnt at its maximum
+#define NC_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
 template <Epi EPI, bool AK, bool BKC>
 __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
   constexpr int BM = 256, BN = 256;
@@ -461,15 +484,19 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
   const int ntiles = tiles_m * tiles_n;
   const int per_item = ntiles * g0.splits;
   const int total = per_item * (g0.batch > 1 ? g0.batch : 1);
-  int bid = blockIdx.x;
-  const int nb = gridDim.x;
-  bid = (bid & 7) * (nb >> 3) + (bid >> 3);
-  if (bid >= total) return;
-  const int item = bid / per_item;
-  bid -= item * per_item;
-  const GemmArgs g = batch_item<bf16, EPI>(g0, item);
-  const int split = bid / ntiles;
-  const int t = bid - split * ntiles;
+  // Tile slots: total rounded up to a multiple of 8, dealt to the 8 XCDs in
+  // contiguous ranges of R (the hardware hands workgroups to the XCDs
+  // round-robin, so workgroup p runs on XCD p % 8). With one workgroup per
+  // slot (gridDim = 8R) each workgroup takes one tile; with fewer (a
+  // persistent launch, one workgroup per compute unit) workgroup p walks
+  // slots p/8, p/8 + J, p/8 + 2J, ... of its XCD's range (J = gridDim / 8),
+  // the order in which a one-tile-per-workgroup launch would run them.
+  const int R = ((total + 7) >> 3);
+  const int J = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7;
+  int slot = blockIdx.x >> 3;
+  auto tile_of = [&](int sl) { return xcd * R + sl; };
+  if (slot >= R || tile_of(slot) >= total) return;
   // row tiles per group of the XCD's walk (measured per shape, in the step):
   // 4 for the narrow (<= 5 column tiles) unsplit products; 6 for the narrow
   // split-K products (6 x 5 tiles: a whole group is resident on the XCD's 32
@@ -479,33 +506,41 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
   // 640 KB A panels stay in a 4 MB L2 while the B panels stream); 8 otherwise
   const int GROUP = (tiles_n <= 5 && g0.splits == 1) ? 4 : ((tiles_n >= 64 || tiles_n <= 5) ? 6 : 8);
   const int per_group = GROUP * tiles_n;
-  const int first_m = (t / per_group) * GROUP;
-  const int gsize = min(tiles_m - first_m, GROUP);
-  const int tm = first_m + (t % per_group) % gsize;
-  const int tn = (t % per_group) / gsize;
-  const int m0 = tm * BM, n0 = tn * BN;
-  // split `split` takes the 64-wide k slabs [split * ns / splits, (split + 1) * ns / splits)
-  const int ns = g.K / 64;
-  const int sb = (int)((long)split * ns / g.splits), se = (int)((long)(split + 1) * ns / g.splits);
-  const int kbeg = sb * 64;
-  const int nk = 2 * (se - sb);                                // 32-wide stages
+  // split-K: split `split` takes the 64-wide k slabs [split * ns / splits, (split + 1) * ns / splits)
+  const int ns = g0.K / 64;
+  struct TileAt {
+    int item, split, m0, n0, kbeg, nk;
+  };
+  auto locate = [&](int bid) {
+    TileAt a;
+    a.item = bid / per_item;
+    bid -= a.item * per_item;
+    a.split = bid / ntiles;
+    const int t = bid - a.split * ntiles;
+    const int first_m = (t / per_group) * GROUP;
+    const int gsize = min(tiles_m - first_m, GROUP);
+    a.m0 = (first_m + (t % per_group) % gsize) * BM;
+    a.n0 = ((t % per_group) / gsize) * BN;
+    const int sb = (int)((long)a.split * ns / g0.splits), se = (int)((long)(a.split + 1) * ns / g0.splits);
+    a.kbeg = sb * 64;
+    a.nk = 2 * (se - sb);                                      // 32-wide stages
+    return a;
+  };
+  TileAt cur = locate(tile_of(slot));
+  GemmArgs g = batch_item<bf16, EPI>(g0, cur.item);
 
   DmaOperand<AK> da;
   DmaOperand<BKC> db;
-  da.init(static_cast<const bf16*>(g.A), g.lda, g.M, m0, kbeg, wave, lane);
-  db.init(static_cast<const bf16*>(g.B), g.ldb, g.N, n0, kbeg, wave, lane);
+  da.init(static_cast<const bf16*>(g.A), g.lda, g.M, cur.m0, cur.kbeg, wave, lane);
+  db.init(static_cast<const bf16*>(g.B), g.ldb, g.N, cur.n0, cur.kbeg, wave, lane);
+  // ring slot of stage s of the current tile: (base + s) % kStages
+  int base = 0;
   auto issue = [&](int st) {
-    bf16* S = smem + (st % kStages) * STAGE;
+    bf16* S = smem + ((base + st) & (kStages - 1)) * STAGE;
     da.issue(S, st);
     db.issue(S + kSlab, st);
   };
   f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int ar = wm * TM, br = wn * TN;
   auto read_step = [&](const bf16* S, int ks, bf16x8 (&fa)[FM], bf16x8 (&fb)[FN]) {
@@ -535,6 +570,30 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // Epilogue shape: the lane holds C[m][n..n+3] for m = 32i + l32,
+  // n = 32j + 8q + 4*lh; each wavefront stages one 32 x 64 fp32 block at a
+  // time and reads it back as row segments (256 contiguous bytes per row).
+  // An epilogue that reads memory (the residual for AddF32, the saved
+  // activation for Relu2Bwd) keeps one register per staged chunk and refills
+  // it with the next 32-row block's chunk as soon as it has been used.
+  constexpr int CPR = TN / 4;                                  // 16-byte chunks per row
+  constexpr int CH = 32 * CPR / 64;                            // chunks per lane per block
+  constexpr bool READS = EPI == Epi::AddF32 || EPI == Epi::Relu2Bwd || EPI == Epi::AxpbyT ||
+                        EPI == Epi::AxpbyF32;
+  constexpr bool READS_C2 = EPI == Epi::Relu2Bwd || EPI == Epi::AxpbyT || EPI == Epi::AxpbyF32;
+  constexpr bool WIDE = !READS && (EPI == Epi::StoreT || EPI == Epi::Relu2);
+  constexpr int CPR8 = TN / 8, CH8 = 32 * CPR8 / 64;
+  // Vector-memory instructions one wavefront's epilogue issues for a whole
+  // tile (every row and column inside the matrix): its stores, plus the
+  // operand loads of the epilogues that read memory.
+  constexpr int EPI_VMEM = WIDE ? FM * CH8 : (READS ? 2 * FM * CH : FM * CH);
+  // wait counts with the epilogue's operations behind one or two stages
+  // (capped at the counter's 63: a smaller count only waits longer)
+  constexpr int W_E0 = EPI_VMEM < 63 ? EPI_VMEM : 63;
+  constexpr int W_E4 = EPI_VMEM + 4 < 63 ? EPI_VMEM + 4 : 63;
+  constexpr int W_E8 = EPI_VMEM + 8 < 63 ? EPI_VMEM + 8 : 63;
+  typedef typename EpiIn<EPI>::type In;
+
   // Ping-pong schedule. Each stage is one memory phase (read all fragments of
   // the stage, issue this wavefront's direct loads three stages ahead, wait)
   // and one compute phase (its 16 MFMAs), each closed by a barrier.
@@ -548,7 +607,20 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
   // stage's loads from both groups have landed before the barrier that opens
   // the leading group's memory phase for it, since each wavefront waits for
   // its own share of stage s + 1 in its memory phase for stage s.
+  //
+  // Persistent launch: after the last stage of a tile (every ring read done),
+  // the first two stages of the next tile are requested into the next two
+  // slots, then the epilogue runs, staging through the other two slots while
+  // those loads are in flight. The epilogue's own loads and stores are issued
+  // after them; gfx9 counts loads and stores in one in-order counter, so the
+  // first two waits of the next tile allow the epilogue's EPI_VMEM operations
+  // to remain outstanding (when the tile was whole, so that every one of them
+  // was issued; otherwise they wait for everything). A barrier after the
+  // epilogue frees the staging slots before the next tile's third stage is
+  // requested into them.
   const bool lag = __builtin_amdgcn_readfirstlane(wave) >= 4;
+  const bool whole = (g0.M % BM) == 0 && (g0.N % BN) == 0;
+  int nk = cur.nk;
 #pragma unroll
   for (int st = 0; st < kStages - 1; ++st)
     if (st < nk) issue(st);
@@ -556,107 +628,151 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
   // here, so their loads are not scheduled into the loop.
   asm volatile("" ::"s"(g.C), "s"(g.C2), "s"(g.ldc), "s"(g.ldc2));
   wait_after(min(kStages - 2, nk - 1));
-  barrier();
-  if (lag) barrier();
-  bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  for (int s = 0; s < nk; ++s) {
-    const bf16* S = smem + (s % kStages) * STAGE;
-    read_step(S, 0, fa0, fb0);
-    read_step(S, 1, fa1, fb1);
-    if (s + kStages - 1 < nk) issue(s + kStages - 1);
-    wait_after(min(s + kStages - 1, nk - 1) - (s + 1));
+  bool carried = false;                                        // epilogue ops queued behind stages 0, 1
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     barrier();
-    mfma_step(fa0, fb0);
-    mfma_step(fa1, fb1);
-    barrier();
-  }
-  if (!lag) barrier();
-
-  // Epilogue, staged through LDS so that global accesses cover whole rows:
-  // the lane holds C[m][n..n+3] for m = 32i + l32, n = 32j + 8q + 4*lh; each
-  // wavefront writes one 32 x 64 fp32 block at a time into its own LDS region,
-  // then reads it back as 16-lane row segments (256 contiguous bytes per row).
-  // An epilogue that reads memory (the residual for AddF32, the saved
-  // activation for Relu2Bwd) keeps one register per staged chunk and refills
-  // it with the next 32-row block's chunk as soon as it has been used.
-  constexpr int RS = TN + 4;                                   // padded row, floats
-  constexpr int CPR = TN / 4;                                  // 16-byte chunks per row
-  constexpr int CH = 32 * CPR / 64;                            // chunks per lane per block
-  constexpr bool READS = EPI == Epi::AddF32 || EPI == Epi::Relu2Bwd || EPI == Epi::AxpbyT ||
-                        EPI == Epi::AxpbyF32;
-  constexpr bool READS_C2 = EPI == Epi::Relu2Bwd || EPI == Epi::AxpbyT || EPI == Epi::AxpbyF32;
-  typedef typename EpiIn<EPI>::type In;
-  In pre[CH];
-  auto fetch1 = [&](int i, int u) -> In {
-    const int c = lane + 64 * u;
-    const int m = min(m0 + wm * TM + i * 32 + c / CPR, g.M - 1);
-    const int n = min(n0 + wn * TN + (c % CPR) * 4, g.N - 4);
-    // read once, right before the output replaces it: non-temporal, like the stores
-    if constexpr (READS_C2)
-      return __builtin_nontemporal_load(
-          reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(g.C2) + (size_t)m * g.ldc2 + n));
-    else
-      return __builtin_nontemporal_load(
-          reinterpret_cast<const f32x4*>(static_cast<const float*>(g.C) + (size_t)m * g.ldc + n));
-  };
-  if constexpr (READS) {
-#pragma unroll
-    for (int u = 0; u < CH; ++u) pre[u] = fetch1(0, u);
-  }
-  __syncthreads();                                             // slabs no longer needed
-  float* wl = reinterpret_cast<float*>(smem) + wave * 32 * RS;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        *reinterpret_cast<f32x4*>(wl + l32 * RS + j * 32 + q * 8 + lh * 4) = v;
+    if (lag) barrier();
+    bf16x8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    for (int s = 0; s < nk; ++s) {
+      const bf16* S = smem + ((base + s) & (kStages - 1)) * STAGE;
+      read_step(S, 0, fa0, fb0);
+      read_step(S, 1, fa1, fb1);
+      if (s + kStages - 1 < nk) issue(s + kStages - 1);
+      const int after = min(s + kStages - 1, nk - 1) - (s + 1);
+      if (s == 0 && carried) {
+        // stage 1 then the previous epilogue's operations, then stages 2 and 3
+        if (after >= 2) NC_WAIT_VM_LGKM0_WIDE(W_E8);
+        else NC_WAIT_VM_LGKM0_WIDE(W_E0);
+      } else {
+        wait_after(after);
       }
-    constexpr bool WIDE = !READS && (EPI == Epi::StoreT || EPI == Epi::Relu2);
-    if constexpr (WIDE) {
-      // bf16 outputs with no extra operand: 8 values (16 bytes) per lane and
-      // store, half the store instructions of the 4-value path below
-      constexpr int CPR8 = TN / 8, CH8 = 32 * CPR8 / 64;
+      barrier();
+      mfma_step(fa0, fb0);
+      mfma_step(fa1, fb1);
+      barrier();
+    }
+    if (!lag) barrier();
+
+    // next tile of this workgroup, if any: its first two stages go out now
+    slot += J;
+    const bool more = slot < R && tile_of(slot) < total;
+    const TileAt me = cur;
+    const int tbase = base;
+    if (more) {
+      cur = locate(tile_of(slot));
+      const GemmArgs gn = batch_item<bf16, EPI>(g0, cur.item);
+      da.init(static_cast<const bf16*>(gn.A), gn.lda, gn.M, cur.m0, cur.kbeg, wave, lane);
+      db.init(static_cast<const bf16*>(gn.B), gn.ldb, gn.N, cur.n0, cur.kbeg, wave, lane);
+      base = tbase + nk;
+      issue(0);
+      if (cur.nk > 1) issue(1);
+    }
+    // nothing of the epilogue below moves above these loads
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- epilogue of tile `me` ----
+    const GemmArgs ge = batch_item<bf16, EPI>(g0, me.item);
+    const int m0 = me.m0, n0 = me.n0;
+    In pre[CH];
+    auto fetch1 = [&](int i, int u) -> In {
+      const int c = lane + 64 * u;
+      const int m = min(m0 + wm * TM + i * 32 + c / CPR, ge.M - 1);
+      const int n = min(n0 + wn * TN + (c % CPR) * 4, ge.N - 4);
+      // read once, right before the output replaces it: non-temporal, like the stores
+      if constexpr (READS_C2)
+        return __builtin_nontemporal_load(
+            reinterpret_cast<const bf16x4*>(static_cast<const bf16*>(ge.C2) + (size_t)m * ge.ldc2 + n));
+      else
+        return __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(static_cast<const float*>(ge.C) + (size_t)m * ge.ldc + n));
+    };
+    if constexpr (READS) {
 #pragma unroll
-      for (int u = 0; u < CH8; ++u) {
-        const int c = lane + 64 * u;
-        const int r = c / CPR8, cc = (c % CPR8) * 8;
-        const int m = m0 + wm * TM + i * 32 + r, n = n0 + wn * TN + cc;
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(wl + r * RS + cc);
-        const f32x4 v1 = *reinterpret_cast<const f32x4*>(wl + r * RS + cc + 4);
-        if (m < g.M && n < g.N) {
-          bf16x8 w;
+      for (int u = 0; u < CH; ++u) pre[u] = fetch1(0, u);
+    }
+    // staging: waves 0-3 in the slot two past the next tile's first stage,
+    // waves 4-7 in the one after (neither receives a load before the barrier
+    // that ends this epilogue)
+    float* wl = reinterpret_cast<float*>(smem + ((tbase + nk + 2 + (wave >> 2)) & (kStages - 1)) * STAGE) +
+                (wave & 3) * 32 * 64;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float a = v0[e], b = v1[e];
-            if constexpr (EPI == Epi::Relu2) {
-              a = fmaxf(a, 0.f); a *= a;
-              b = fmaxf(b, 0.f); b *= b;
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          stg_put(wl + stg_off(l32, 8 * j + 2 * q + lh), v);
+        }
+      if constexpr (WIDE) {
+        // bf16 outputs with no extra operand: 8 values (16 bytes) per lane and
+        // store, half the store instructions of the 4-value path below
+#pragma unroll
+        for (int u = 0; u < CH8; ++u) {
+          const int c = lane + 64 * u;
+          const int r = c / CPR8, cc = c % CPR8;
+          const int m = m0 + wm * TM + i * 32 + r, n = n0 + wn * TN + cc * 8;
+          const f32x4 v0 = stg_get(wl + stg_off(r, 2 * cc));
+          const f32x4 v1 = stg_get(wl + stg_off(r, 2 * cc + 1));
+          if (m < ge.M && n < ge.N) {
+            bf16x8 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float a = v0[e], b = v1[e];
+              if constexpr (EPI == Epi::Relu2) {
+                a = fmaxf(a, 0.f); a *= a;
+                b = fmaxf(b, 0.f); b *= b;
+              }
+              w[e] = from_f32<bf16>(a);
+              w[4 + e] = from_f32<bf16>(b);
             }
-            w[e] = from_f32<bf16>(a);
-            w[4 + e] = from_f32<bf16>(b);
+            __builtin_nontemporal_store(
+                w, reinterpret_cast<bf16x8*>(static_cast<bf16*>(ge.C) + (size_t)m * ge.ldc + n));
           }
-          __builtin_nontemporal_store(
-              w, reinterpret_cast<bf16x8*>(static_cast<bf16*>(g.C) + (size_t)m * g.ldc + n));
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+          const int c = lane + 64 * u;
+          const int r = c / CPR, cc = c % CPR;
+          const int m = m0 + wm * TM + i * 32 + r, n = n0 + wn * TN + cc * 4;
+          const f32x4 v = stg_get(wl + stg_off(r, cc));
+          if constexpr (READS) {
+            const In x = pre[u];
+            // x is waited for here on every path, also where the store below
+            // is skipped: otherwise its load could still be in flight when
+            // the next tile reuses the register, and the compiler would wait
+            // for everything outstanding there, the next tile's loads included
+            asm volatile("" ::"v"(x));
+            if (i + 1 < FM) pre[u] = fetch1(i + 1, u);
+            if (m < ge.M && n < ge.N) epilogue4_in<EPI>(ge, me.split, m, n, v, x);
+          } else {
+            if (m < ge.M && n < ge.N) epilogue4<bf16, EPI>(ge, me.split, m, n, v);
+          }
         }
       }
-      continue;
     }
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int c = lane + 64 * u;
-      const int r = c / CPR, cc = (c % CPR) * 4;
-      const int m = m0 + wm * TM + i * 32 + r, n = n0 + wn * TN + cc;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(wl + r * RS + cc);
-      if constexpr (READS) {
-        const In x = pre[u];
-        if (i + 1 < FM) pre[u] = fetch1(i + 1, u);
-        if (m < g.M && n < g.N) epilogue4_in<EPI>(g, split, m, n, v, x);
-      } else {
-        if (m < g.M && n < g.N) epilogue4<bf16, EPI>(g, split, m, n, v);
-      }
+    if (!more) break;
+
+    // every wavefront's staging reads have returned: the staging slots are free
+    NC_WAIT_LGKM0();
+    barrier();
+    nk = cur.nk;
+    if (nk > 2) issue(2);
+    carried = whole;
+    if (carried) {
+      // stage 0, then stage 1, this epilogue's operations and stage 2
+      if (nk > 2) NC_WAIT_VM_LGKM0_WIDE(W_E8);
+      else NC_WAIT_VM_LGKM0_WIDE(W_E4);
+    } else {
+      NC_WAIT_VM_LGKM0(0);
     }
   }
 }
@@ -702,6 +818,8 @@ hipError_t launch_tiles(const GemmArgs& g, hipStream_t s) {
 // slab spans 256 rows of its operand's stride, so both strides must stay
 // below 2^22 elements (2^31 bytes / (256 rows * 2 bytes)). Larger strides take
 // the 128x128 kernel, which uses full-width addresses.
+std::atomic<bool> g_gemm_persist{true};
+
 bool strides_fit_256(const GemmArgs& g) { return g.lda < (1 << 22) && g.ldb < (1 << 22); }
 
 int choose_tile(bool bf16, const GemmArgs& g) {
@@ -719,7 +837,14 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
     if (choose_tile(true, g) == 256) {
       const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256) * g.splits *
                         (g.batch > 1 ? g.batch : 1);
-      const int grid = (tiles + 7) / 8 * 8;
+      int grid = (tiles + 7) / 8 * 8;
+      // Whole-tile products with more tiles than compute units run persistent:
+      // one workgroup per compute unit walking its XCD's tiles, each next
+      // tile's first loads overlapping the current tile's epilogue.
+      const int persist = device_cus() / 8 * 8;
+      if (g_gemm_persist.load(std::memory_order_relaxed) && g.splits == 1 && g.M % 256 == 0 &&
+          g.N % 256 == 0 && persist >= 8 && grid > persist)
+        grid = persist;
       hipLaunchKernelGGL((gemm_bf16_kernel<EPI, AK, BKC>), dim3(grid), dim3(512), 0, s, g);
       return hipGetLastError();
     }
@@ -768,6 +893,8 @@ hipError_t gemm(DType t, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs
   return t == DType::BF16 ? dispatch<bf16>(a_kcontig, b_kcontig, epi, g, stream)
                           : dispatch<float>(a_kcontig, b_kcontig, epi, g, stream);
 }
+
+void gemm_set_persistent(bool on) { g_gemm_persist.store(on); }
 
 int gemm_tile(DType t, bool a_kcontig, bool b_kcontig, const GemmArgs& g) {
   (void)a_kcontig;

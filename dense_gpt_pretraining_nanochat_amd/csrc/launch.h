@@ -38,6 +38,11 @@ struct GemmArgs {
 int device_cus();
 hipError_t gemm(DType t, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs& g,
                 hipStream_t stream);
+// Schedule of the 256-tile kernel for whole-tile unsplit products with more
+// tiles than compute units: persistent (default; one workgroup per compute
+// unit, the next tile's first loads overlapping each epilogue) or one
+// workgroup per tile. Results are bitwise identical either way.
+void gemm_set_persistent(bool on);
 // Tile edge the kernel will use for these arguments (128 or 256).
 int gemm_tile(DType t, bool a_kcontig, bool b_kcontig, const GemmArgs& g);
 // out[c][r] = in[r][c] for an R x C matrix of T (row strides ld_in, ld_out)

@@ -500,6 +500,12 @@ int nc_set_lm_chunk_rows(int32_t rows) {
   return NC_OK;
 }
 
+int nc_set_gemm_persistent(int32_t on) {
+  if (on != 0 && on != 1) return NC_ERR_ARG;
+  nc::gemm_set_persistent(on == 1);
+  return NC_OK;
+}
+
 int nc_lm_chunk_rows(const nc_config* cfg, int32_t* rows) {
   const int rc = validate(cfg);
   if (rc) return rc;

@@ -144,6 +144,17 @@ int nc_workspace_pieces(const nc_config* cfg, int32_t with_backward, nc_ws_piece
 int nc_set_lm_chunk_rows(int32_t rows);
 int nc_lm_chunk_rows(const nc_config* cfg, int32_t* rows);
 
+/* Schedule of the large bf16 contractions (256 x 256 output tiles) whose
+ * output is whole tiles, is not split over K, and has more tiles than the
+ * device has compute units: on = 1 (the default) runs them persistent, one
+ * workgroup per compute unit walking its XCD's tiles, with each next tile's
+ * first operand loads in flight during the current tile's epilogue; on = 0
+ * runs one workgroup per tile. The tiles, their order per XCD and every
+ * result are the same either way (bitwise). Process-wide, for measurement and
+ * tests; not for use while calls are in flight. on other than 0 or 1:
+ * NC_ERR_ARG. Host only. */
+int nc_set_gemm_persistent(int32_t on);
+
 /* Byte offset inside the workspace of the per-token losses (fp32 [B*T],
  * row-major like tokens), valid after a forward call until the next call on
  * the same workspace. Host only. */

@@ -179,6 +179,18 @@ def test_lm_chunk_rows_bound_the_workspace():
     assert abs((b64 - b32) - 2 * (b32 - b16)) <= 2 ** 26
 
 
+def test_gemm_schedule_switch_checks_its_argument():
+    """The contraction schedule switch takes 0 or 1 only (host-only call)."""
+    try:
+        for bad in (2, -1):
+            with pytest.raises(nc.NcError):
+                nc.nc_set_gemm_persistent(bad)
+        assert nc.lib().nc_set_gemm_persistent(0) == 0
+        assert nc.lib().nc_set_gemm_persistent(1) == 0
+    finally:
+        nc.nc_set_gemm_persistent(True)
+
+
 def _optim(**kw):
     base = dict(lr_adamw=0.01, beta1=0.8, beta2=0.95, eps=1e-10, wd_adamw=0.0, lr_muon=0.02,
                 momentum=0.95, wd_muon=0.0, max_grad_norm=1.0, ns_steps=5, step=1)
