@@ -459,6 +459,17 @@ __device__ __forceinline__ f32x4 stg_get(const float* __restrict__ p) {
   return *reinterpret_cast<const f32x4*>(p);
 }
 
+// bf16 staging of a 32 x 64 block (128-byte rows, 16-byte chunk c of row r at
+// chunk slot c ^ ((r >> 2) & 7)): 8-byte column writes and 16-byte row reads
+// both conflict-free.
+__device__ __forceinline__ int stg16_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 7)) << 3); }
+__device__ __forceinline__ void stg_put8(bf16* __restrict__ p, bf16x4 v) {
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ bf16x8 stg_get16(const bf16* __restrict__ p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
 // s_waitcnt immediate for "at most n (0..63) vector-memory ops outstanding, no
 // LDS ops outstanding" (gfx9: vmcnt bits 3:0 and 15:14, expcnt 6:4 left at 7).
 #define NC_WAIT_VM_LGKM0_WIDE(n) __builtin_amdgcn_s_waitcnt(0x0070 | ((n) & 15) | (((n) >> 4) << 14))
@@ -704,40 +715,45 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
                 (wave & 3) * 32 * 64;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          stg_put(wl + stg_off(l32, 8 * j + 2 * q + lh), v);
-        }
       if constexpr (WIDE) {
-        // bf16 outputs with no extra operand: 8 values (16 bytes) per lane and
-        // store, half the store instructions of the 4-value path below
+        // bf16 outputs with no extra operand: the values are rounded (after
+        // relu^2) in registers and staged as bf16, half the LDS traffic of
+        // fp32 staging; read back 8 values (16 bytes) per lane and store
+        bf16* wb = reinterpret_cast<bf16*>(wl);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            bf16x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float a = acc[i][j][4 * q + e];
+              if constexpr (EPI == Epi::Relu2) {
+                a = fmaxf(a, 0.f);
+                a *= a;
+              }
+              w[e] = from_f32<bf16>(a);
+            }
+            stg_put8(wb + stg16_off(l32, 4 * j + q) + 4 * lh, w);
+          }
 #pragma unroll
         for (int u = 0; u < CH8; ++u) {
           const int c = lane + 64 * u;
           const int r = c / CPR8, cc = c % CPR8;
           const int m = m0 + wm * TM + i * 32 + r, n = n0 + wn * TN + cc * 8;
-          const f32x4 v0 = stg_get(wl + stg_off(r, 2 * cc));
-          const f32x4 v1 = stg_get(wl + stg_off(r, 2 * cc + 1));
-          if (m < ge.M && n < ge.N) {
-            bf16x8 w;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              float a = v0[e], b = v1[e];
-              if constexpr (EPI == Epi::Relu2) {
-                a = fmaxf(a, 0.f); a *= a;
-                b = fmaxf(b, 0.f); b *= b;
-              }
-              w[e] = from_f32<bf16>(a);
-              w[4 + e] = from_f32<bf16>(b);
-            }
+          const bf16x8 w = stg_get16(wb + stg16_off(r, cc));
+          if (m < ge.M && n < ge.N)
             __builtin_nontemporal_store(
                 w, reinterpret_cast<bf16x8*>(static_cast<bf16*>(ge.C) + (size_t)m * ge.ldc + n));
-          }
         }
       } else {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            stg_put(wl + stg_off(l32, 8 * j + 2 * q + lh), v);
+          }
 #pragma unroll
         for (int u = 0; u < CH; ++u) {
           const int c = lane + 64 * u;
