@@ -1,5 +1,6 @@
-// Causal multi-query attention on the CDNA4 matrix cores: forward, the
-// delta = <dO, O> preprocess, and a two-kernel backward without atomics.
+// Causal multi-query attention on the CDNA4 matrix cores: forward and a
+// two-kernel backward without atomics (the dQ kernel, which runs first, also
+// computes delta = <dO, O> for the dK/dV kernel).
 //
 // All query heads share one key/value head (followin.io release article,
 // architecture list: multi-query attention); the objective is next-token
@@ -355,44 +356,17 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void attn_fwd_kernel(
 }
 
 // --------------------------------------------------------------------------
-// delta[b, h, t] = sum_d dO * O
-// --------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o,
-                                                         const T* __restrict__ dout, int Tn,
-                                                         int H, size_t total,
-                                                         float* __restrict__ delta) {
-  // 16 lanes per (token, head) row of 128, 16-byte loads
-  typedef AttnTypes<T> A;
-  constexpr int PER = D / 16;                  // elements per lane
-  const size_t w = blockIdx.x * 16ull + (threadIdx.x >> 4);
-  const int sl = threadIdx.x & 15;
-  if (w >= total) return;
-  const size_t m = w / H;
-  const int h = (int)(w % H);
-  const size_t off = m * (size_t)(H * D) + h * D + sl * PER;
-  float s = 0.f;
-#pragma unroll
-  for (int v = 0; v < PER / A::VEC; ++v) {
-    const typename A::V a = *reinterpret_cast<const typename A::V*>(o + off + v * A::VEC);
-    const typename A::V b = *reinterpret_cast<const typename A::V*>(dout + off + v * A::VEC);
-#pragma unroll
-    for (int e = 0; e < A::VEC; ++e) s += to_f32(a[e]) * to_f32(b[e]);
-  }
-  s = lane16_sum(s);
-  if (sl == 0) {
-    const size_t b = m / Tn, t = m % Tn;
-    delta[(b * H + h) * Tn + t] = s;
-  }
-}
-
-// --------------------------------------------------------------------------
 // backward, dQ: shaped like the forward (one wavefront per head, 32 rows)
 // --------------------------------------------------------------------------
+// It also computes delta[b, h, t] = <dO, O> of its own query rows (each row's
+// 128 values sit in the four lanes of one column of the dO fragments; O is
+// read in the same layout) and writes it for the dK/dV kernel, which runs
+// after it.
 template <typename T>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
-    const T* __restrict__ qkv, int ldq, const T* __restrict__ dout, const float* __restrict__ lse,
-    const float* __restrict__ delta, int Tn, int H, T* __restrict__ dqkv, int ldd) {
+    const T* __restrict__ qkv, int ldq, const T* __restrict__ o, const T* __restrict__ dout,
+    const float* __restrict__ lse, float* __restrict__ delta, int Tn, int H, T* __restrict__ dqkv,
+    int ldd) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
   constexpr int BK = BKVQ;                      // keys per tile
@@ -416,13 +390,18 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int t = tq0 + c * 16 + l16;
+    float pd = 0.f;
 #pragma unroll
     for (int s = 0; s < A::NS; ++s) {
       qf[c][s] = active ? *reinterpret_cast<const V*>(qkv + (row0 + t) * ldq + h * D + s * A::KB + lg * A::VEC) : V{};
       df[c][s] = active ? *reinterpret_cast<const V*>(dout + (row0 + t) * ldo + h * D + s * A::KB + lg * A::VEC) : V{};
+      const V of = active ? *reinterpret_cast<const V*>(o + (row0 + t) * ldo + h * D + s * A::KB + lg * A::VEC) : V{};
+#pragma unroll
+      for (int e = 0; e < A::VEC; ++e) pd = fmaf(to_f32(df[c][s][e]), to_f32(of[e]), pd);
     }
+    dl[c] = group4_sum(pd);
     lse2[c] = active ? lse[((size_t)qbk.b * H + h) * Tn + t] * kLog2e : 0.f;
-    dl[c] = active ? delta[((size_t)qbk.b * H + h) * Tn + t] : 0.f;
+    if (active && lg == 0) delta[((size_t)qbk.b * H + h) * Tn + t] = dl[c];
   }
   f32x4 dq[8][2];
 #pragma unroll
@@ -833,26 +812,13 @@ hipError_t attn_fwd(DType t, const void* qkv, int ldq, int B, int T, int H, void
   return hipGetLastError();
 }
 
-hipError_t attn_bwd_delta(DType t, const void* o, const void* dout, int B, int T, int H,
-                          float* delta, hipStream_t s) {
-  const size_t total = (size_t)B * T * H;
-  dim3 grid((unsigned)((total + 15) / 16)), block(256);
-  if (t == DType::BF16)
-    hipLaunchKernelGGL(attn_delta_kernel<bf16>, grid, block, 0, s, static_cast<const bf16*>(o),
-                       static_cast<const bf16*>(dout), T, H, total, delta);
-  else
-    hipLaunchKernelGGL(attn_delta_kernel<float>, grid, block, 0, s, static_cast<const float*>(o),
-                       static_cast<const float*>(dout), T, H, total, delta);
-  return hipGetLastError();
-}
-
 size_t attn_bwd_scratch_floats(int B, int T) {
   const int nch = dkv_chunks(T, 0);
   return nch > 1 ? (size_t)nch * B * T * 2 * D : 0;   // one chunk: dK/dV written directly
 }
 
-hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const float* lse,
-                    const float* delta, int B, int T, int H, void* dqkv, int ldd, float* scratch,
+hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* o, const void* dout, const float* lse,
+                    float* delta, int B, int T, int H, void* dqkv, int ldd, float* scratch,
                     hipStream_t s) {
   if (T % BKV || H < 1 || H > 16) return hipErrorInvalidValue;
   dim3 gq(B * (T / FQB) * ((H + 1) / 2)), bq(256);
@@ -866,6 +832,9 @@ hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const f
     const bf16* q = static_cast<const bf16*>(qkv);
     const bf16* d = static_cast<const bf16*>(dout);
     bf16* g = static_cast<bf16*>(dqkv);
+    // dQ first: it writes the delta rows that dK/dV reads
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<bf16>, gq, bq, 0, s, q, ldq, static_cast<const bf16*>(o), d, lse,
+                       delta, T, H, g, ldd);
     if (direct) {
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<bf16, true>), gk, bk, 0, s, q, ldq, d, lse, delta, B, T,
                          H, scratch, g, ldd);
@@ -874,11 +843,12 @@ hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const f
                          T, H, scratch, g, ldd);
       hipLaunchKernelGGL(attn_dkv_reduce_kernel<bf16>, gr, br, 0, s, scratch, B, T, H, g, ldd);
     }
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<bf16>, gq, bq, 0, s, q, ldq, d, lse, delta, T, H, g, ldd);
   } else {
     const float* q = static_cast<const float*>(qkv);
     const float* d = static_cast<const float*>(dout);
     float* g = static_cast<float*>(dqkv);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<float>, gq, bq, 0, s, q, ldq, static_cast<const float*>(o), d, lse,
+                       delta, T, H, g, ldd);
     if (direct) {
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<float, true>), gk, bk, 0, s, q, ldq, d, lse, delta, B,
                          T, H, scratch, g, ldd);
@@ -887,7 +857,6 @@ hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const f
                          B, T, H, scratch, g, ldd);
       hipLaunchKernelGGL(attn_dkv_reduce_kernel<float>, gr, br, 0, s, scratch, B, T, H, g, ldd);
     }
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<float>, gq, bq, 0, s, q, ldq, d, lse, delta, T, H, g, ldd);
   }
   return hipGetLastError();
 }

@@ -98,15 +98,13 @@ hipError_t rope_qknorm_bwd(DType t, void* dqkv, int ldd, const void* qkv, int ld
 // qkv: [B*T, ldq] with q heads, then k, then v (each 128 wide); o: [B*T, H*128]; lse: [B, H, T]
 hipError_t attn_fwd(DType t, const void* qkv, int ldq, int B, int T, int H, void* o, float* lse,
                     hipStream_t s);
-// delta[b,h,t] = <dO, O>
-hipError_t attn_bwd_delta(DType t, const void* o, const void* dout, int B, int T, int H,
-                          float* delta, hipStream_t s);
-// writes dq into dqkv[:, 0:H*128], dk and dv into the next two 128-col blocks;
+// writes dq into dqkv[:, 0:H*128], dk and dv into the next two 128-col blocks,
+// and delta[b,h,t] = <dO, O> (o: the forward's output, [B*T, H*128]);
 // scratch holds attn_bwd_scratch_floats(B, T) floats of partial dK/dV sums
 // (none, and scratch may be null, when T <= 2048: dK/dV are written directly)
 size_t attn_bwd_scratch_floats(int B, int T);
-hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* dout, const float* lse,
-                    const float* delta, int B, int T, int H, void* dqkv, int ldd, float* scratch,
+hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* o, const void* dout, const float* lse,
+                    float* delta, int B, int T, int H, void* dqkv, int ldd, float* scratch,
                     hipStream_t s);
 // Device address (current device) of the library's fixed attention-backward
 // scratch array of kAttnFixedScratchBytes, for the entry point that allocates

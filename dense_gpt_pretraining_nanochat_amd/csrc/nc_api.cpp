@@ -444,8 +444,7 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
     HIPCHECK(wgrad(dt, g, o, G(base + 1), partial, M, D.d, D.d, pO, s, accumulate));
     HIPCHECK(gemm_simple(dt, true, false, Epi::StoreT, g, W(base + 1), dout, nullptr, M, D.d, D.d,
                          D.d, D.d, D.d, 0, s));
-    HIPCHECK(nc::attn_bwd_delta(dt, o, dout, D.B, D.T, D.H, delta, s));
-    HIPCHECK(nc::attn_bwd(dt, qkv, D.Q, dout, at<float>(ws, A.lse), delta, D.B, D.T, D.H, dbig,
+    HIPCHECK(nc::attn_bwd(dt, qkv, D.Q, o, dout, at<float>(ws, A.lse), delta, D.B, D.T, D.H, dbig,
                           D.Q, at<float>(ws, P.attn_part), s));
     HIPCHECK(nc::rope_qknorm_bwd(dt, dbig, D.Q, qkv, D.Q, Mi, D.T, D.H, cs,
                                  at<float>(ws, A.rqk), s));
@@ -1390,8 +1389,7 @@ int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* do
   if (!scratch && nc::attn_bwd_scratch_floats(B, T) > 0) return NC_ERR_NULL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int ld = H * 128 + 256;
-  HIPCHECK(nc::attn_bwd_delta(dt_of(dtype), o, dout, B, T, H, delta, s));
-  HIPCHECK(nc::attn_bwd(dt_of(dtype), qkv, ld, dout, lse, delta, B, T, H, dqkv, ld, scratch, s));
+  HIPCHECK(nc::attn_bwd(dt_of(dtype), qkv, ld, o, dout, lse, delta, B, T, H, dqkv, ld, scratch, s));
   return NC_OK;
 }
 
@@ -1410,8 +1408,7 @@ int nc_op_attn_bwd_noalloc(int32_t dtype, const void* qkv, const void* o, const 
   float* part = at<float>(base, delta_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int ld = H * 128 + 256;
-  HIPCHECK(nc::attn_bwd_delta(dt_of(dtype), o, dout, B, T, H, delta, s));
-  HIPCHECK(nc::attn_bwd(dt_of(dtype), qkv, ld, dout, lse, delta, B, T, H, dqkv, ld, part, s));
+  HIPCHECK(nc::attn_bwd(dt_of(dtype), qkv, ld, o, dout, lse, delta, B, T, H, dqkv, ld, part, s));
   return NC_OK;
 }
 

@@ -402,8 +402,8 @@ int nc_op_attn_fwd(int32_t dtype, const void* qkv, int32_t B, int32_t T, int32_t
  * dK/dV are then summed and written by one workgroup) and for invalid sizes.
  * Host only. */
 uint64_t nc_op_attn_bwd_scratch_bytes(int32_t B, int32_t T);
-/* dqkv [B*T, d+256] (T) from qkv, o, dout [B*T, H*128], lse; delta scratch
- * [B, H, T] fp32; scratch of nc_op_attn_bwd_scratch_bytes(B, T) bytes (may be
+/* dqkv [B*T, d+256] (T) from qkv, o, dout [B*T, H*128], lse; delta [B, H, T]
+ * fp32 is written with <dO, O> per row and head (scratch to the caller); scratch of nc_op_attn_bwd_scratch_bytes(B, T) bytes (may be
  * NULL when that is 0). */
 int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* dout,
                    const float* lse, float* delta, int32_t B, int32_t T, int32_t H, void* dqkv,
