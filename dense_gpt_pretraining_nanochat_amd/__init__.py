@@ -124,6 +124,15 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -c 'import __graft_entry__ as g; g.build()'`")
+        # torch first: the library then binds to the HIP runtime torch ships
+        # (same sonames), so one runtime serves torch's allocations and
+        # streams and these kernels. Loaded the other way round, the system
+        # runtime is loaded first and, on the GPU machines used here, calls
+        # then fail with hipErrorNoDevice.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         for name, args in _SIGS.items():
             f = getattr(L, name)
