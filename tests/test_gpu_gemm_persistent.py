@@ -9,7 +9,9 @@ one-workgroup-per-tile launch itself meets the float64 products element by
 element in test_gpu_ops.py). Shapes: 2 tiles per workgroup at K of 2, 4 and
 10 slabs of 32 (the shortest main loop, one as deep as the ring, one that
 refills it), 1-2 tiles per workgroup over five column tiles, 4 per workgroup
-over 64 column tiles, and a batched alpha*AB^T + beta*C2 product."""
+over 64 column tiles, 257 tiles in one column (0-2 per workgroup: part of
+the last XCD's workgroups find no tile and return), and a batched
+alpha*AB^T + beta*C2 product."""
 import numpy as np
 import pytest
 
@@ -22,7 +24,7 @@ import dense_gpt_pretraining_nanochat_amd as nc  # noqa: E402
 
 EPIS = [nc.EPI_STORE_T, nc.EPI_STORE_F32, nc.EPI_ADD_F32, nc.EPI_RELU2, nc.EPI_RELU2_BWD]
 SHAPES = [(8192, 4096, 64), (8192, 4096, 128), (8192, 4096, 320), (16384, 1280, 256),
-          (4096, 16384, 192)]
+          (4096, 16384, 192), (65792, 256, 128)]
 ROWS = 24
 
 
