@@ -163,64 +163,129 @@ constexpr int kSortCap = 4096;   // buckets up to this size are sorted in LDS
 
 __device__ __forceinline__ int clamp_id(int t, int V) { return t < 0 ? 0 : (t >= V ? V - 1 : t); }
 
-__global__ void embed_count_kernel(const int32_t* __restrict__ tok, int M, int V,
-                                   int32_t* __restrict__ counts) {
+// Wavefront-aggregated updates: the lowest remaining lane's id is broadcast
+// and every lane holding it is served by one atomic, so a frequent id (the
+// token law is Zipf-like) costs one atomic per wavefront instead of one per
+// occurrence. Each round removes at least the leading lane.
+__global__ __launch_bounds__(256) void embed_count_kernel(const int32_t* __restrict__ tok, int M, int V,
+                                                          int32_t* __restrict__ counts) {
   const int m = blockIdx.x * blockDim.x + threadIdx.x;
-  if (m < M) atomicAdd(&counts[clamp_id(tok[m], V)], 1);
+  const int lane = threadIdx.x & 63;
+  const bool in = m < M;
+  const int id = in ? clamp_id(tok[m], V) : -1;
+  unsigned long long rem = __ballot(in);
+  while (rem) {
+    const int leader = __ffsll(rem) - 1;
+    const int lid = __shfl(id, leader);
+    const unsigned long long same = __ballot(in && id == lid);
+    if (lane == leader) atomicAdd(&counts[lid], __popcll(same));
+    rem &= ~same;
+  }
 }
 
-// One block: exclusive scans over ids of (rows, pieces, pieces of multi-piece
-// buckets); also writes the owning id of every piece.
-__global__ __launch_bounds__(1024) void embed_scan_kernel(const int32_t* __restrict__ counts, int V,
-                                                          EmbedBwdScratch ws) {
-  __shared__ int32_t sc[3][1024];
-  const int tid = threadIdx.x;
-  const int per = (V + 1023) / 1024;
-  const int b = tid * per, e = min(b + per, V);
-  int a0 = 0, a1 = 0, a2 = 0;
-  for (int i = b; i < e; ++i) {
-    const int n = counts[i], it = (n + kSeg - 1) / kSeg;
-    a0 += n;
-    a1 += it;
-    a2 += it > 1 ? it : 0;
+// Exclusive scans over ids of (rows, pieces, pieces of multi-piece buckets),
+// in two coalesced passes over blocks of 1024 ids: the first writes each
+// block's three sums, the second adds the earlier blocks' sums to a
+// block-wide scan and writes the offsets, cursors, piece offsets and the
+// owning id of every piece.
+constexpr int kScanBlock = 1024;
+__device__ __forceinline__ void scan_counts_of(int n, int* v) {
+  const int it = (n + kSeg - 1) / kSeg;
+  v[0] = n;
+  v[1] = it;
+  v[2] = it > 1 ? it : 0;
+}
+
+__global__ __launch_bounds__(kScanBlock) void embed_scan_blocks_kernel(const int32_t* __restrict__ counts,
+                                                                       int V, int32_t* __restrict__ blocks) {
+  __shared__ int red[3][kScanBlock / 64];
+  const int i = blockIdx.x * kScanBlock + threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int v[3];
+  scan_counts_of(i < V ? counts[i] : 0, v);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    int x = v[k];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    if (lane == 0) red[k][w] = x;
   }
-  sc[0][tid] = a0;
-  sc[1][tid] = a1;
-  sc[2][tid] = a2;
   __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {     // Hillis-Steele inclusive scans
-    int v0 = 0, v1 = 0, v2 = 0;
-    if (tid >= o) { v0 = sc[0][tid - o]; v1 = sc[1][tid - o]; v2 = sc[2][tid - o]; }
-    __syncthreads();
-    sc[0][tid] += v0;
-    sc[1][tid] += v1;
-    sc[2][tid] += v2;
-    __syncthreads();
-  }
-  int r0 = tid ? sc[0][tid - 1] : 0, r1 = tid ? sc[1][tid - 1] : 0, r2 = tid ? sc[2][tid - 1] : 0;
-  for (int i = b; i < e; ++i) {
-    const int n = counts[i], it = (n + kSeg - 1) / kSeg;
-    ws.offsets[i] = r0;
-    ws.cursor[i] = r0;
-    ws.item_off[i] = r1;
-    ws.part_off[i] = r2;
-    for (int j = 0; j < it; ++j) ws.item_bucket[r1 + j] = i;
-    r0 += n;
-    r1 += it;
-    r2 += it > 1 ? it : 0;
-  }
-  if (tid == 1023) {
-    ws.offsets[V] = sc[0][1023];
-    ws.item_off[V] = sc[1][1023];
-    ws.part_off[V] = sc[2][1023];
+  if (threadIdx.x < 3) {
+    int t = 0;
+    for (int j = 0; j < kScanBlock / 64; ++j) t += red[threadIdx.x][j];
+    blocks[blockIdx.x * 3 + threadIdx.x] = t;
   }
 }
 
-__global__ void fill_list_kernel(const int32_t* __restrict__ tok, int M, int V,
-                                 int32_t* __restrict__ cursor, int32_t* __restrict__ list) {
+__global__ __launch_bounds__(kScanBlock) void embed_scan_kernel(const int32_t* __restrict__ counts, int V,
+                                                                const int32_t* __restrict__ blocks,
+                                                                EmbedBwdScratch ws) {
+  __shared__ int wtot[3][kScanBlock / 64];
+  __shared__ int carry[3];
+  const int i = blockIdx.x * kScanBlock + threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x < 3) {
+    int c = 0;
+    for (int b = 0; b < (int)blockIdx.x; ++b) c += blocks[b * 3 + threadIdx.x];
+    carry[threadIdx.x] = c;
+  }
+  int v[3], inc[3];
+  scan_counts_of(i < V ? counts[i] : 0, v);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {                // inclusive scan inside the wavefront
+    int x = v[k];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    inc[k] = x;
+    if (lane == 63) wtot[k][w] = x;
+  }
+  __syncthreads();
+  int ex[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    int before = carry[k];
+    for (int j = 0; j < w; ++j) before += wtot[k][j];
+    ex[k] = before + inc[k] - v[k];
+  }
+  if (i < V) {
+    ws.offsets[i] = ex[0];
+    ws.cursor[i] = ex[0];
+    ws.item_off[i] = ex[1];
+    ws.part_off[i] = ex[2];
+    for (int j = 0; j < v[1]; ++j) ws.item_bucket[ex[1] + j] = i;
+    if (i == V - 1) {
+      ws.offsets[V] = ex[0] + v[0];
+      ws.item_off[V] = ex[1] + v[1];
+      ws.part_off[V] = ex[2] + v[2];
+    }
+  }
+}
+
+// Bucket fill, aggregated like the count: one atomic per id and wavefront
+// reserves the lanes' slots, each lane taking the one of its rank among them
+// (the order inside a bucket is fixed afterwards by the sort).
+__global__ __launch_bounds__(256) void fill_list_kernel(const int32_t* __restrict__ tok, int M, int V,
+                                                        int32_t* __restrict__ cursor,
+                                                        int32_t* __restrict__ list) {
   const int m = blockIdx.x * blockDim.x + threadIdx.x;
-  if (m >= M) return;
-  list[atomicAdd(&cursor[clamp_id(tok[m], V)], 1)] = m;
+  const int lane = threadIdx.x & 63;
+  const bool in = m < M;
+  const int id = in ? clamp_id(tok[m], V) : -1;
+  unsigned long long rem = __ballot(in);
+  while (rem) {
+    const int leader = __ffsll(rem) - 1;
+    const int lid = __shfl(id, leader);
+    const unsigned long long same = __ballot(in && id == lid);
+    int base = 0;
+    if (lane == leader) base = atomicAdd(&cursor[lid], __popcll(same));
+    base = __shfl(base, leader);
+    if (in && id == lid) list[base + __popcll(same & ((1ull << lane) - 1))] = m;
+    rem &= ~same;
+  }
 }
 
 // One block per id: put the bucket's positions in increasing order (the atomic
@@ -486,6 +551,7 @@ uint64_t embed_bwd_max_pieces(int64_t M, int V) {
   return (uint64_t)std::min<int64_t>(M, V) + (uint64_t)(M / kSeg) + 1;
 }
 uint64_t embed_bwd_max_parts(int64_t M) { return 2 * (uint64_t)(M / kSeg) + 1; }
+uint64_t embed_bwd_scan_blocks(int V) { return 3 * (uint64_t)((V + kScanBlock - 1) / kScanBlock); }
 
 hipError_t embed_bwd(DType t, const void* E, const int32_t* tok, const float* rinv0,
                      const float* dx, int M, int d, int V, EmbedBwdScratch ws, float* dE,
@@ -497,7 +563,11 @@ hipError_t embed_bwd(DType t, const void* E, const int32_t* tok, const float* ri
   const unsigned pieces = (unsigned)embed_bwd_max_pieces(M, V);
   hipLaunchKernelGGL(embed_count_kernel, dim3((M + 255) / 256), dim3(256), 0, s, tok, M, V,
                      ws.counts);
-  hipLaunchKernelGGL(embed_scan_kernel, dim3(1), dim3(1024), 0, s, ws.counts, V, ws);
+  const unsigned sblocks = (unsigned)((V + kScanBlock - 1) / kScanBlock);
+  hipLaunchKernelGGL(embed_scan_blocks_kernel, dim3(sblocks), dim3(kScanBlock), 0, s, ws.counts, V,
+                     ws.scan_blocks);
+  hipLaunchKernelGGL(embed_scan_kernel, dim3(sblocks), dim3(kScanBlock), 0, s, ws.counts, V,
+                     ws.scan_blocks, ws);
   hipLaunchKernelGGL(fill_list_kernel, dim3((M + 255) / 256), dim3(256), 0, s, tok, M, V,
                      ws.cursor, ws.list);
   hipLaunchKernelGGL(embed_sort_kernel, dim3(V), dim3(256), 0, s, tok, M, V, ws.offsets, ws.list);

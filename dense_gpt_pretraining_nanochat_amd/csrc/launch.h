@@ -74,8 +74,11 @@ struct EmbedBwdScratch {
   int32_t* item_off;     // [V + 1]
   int32_t* part_off;     // [V + 1]
   int32_t* item_bucket;  // [embed_bwd_max_pieces(M, V)]
+  int32_t* scan_blocks;  // [embed_bwd_scan_blocks(V)]
   float* part;           // [embed_bwd_max_parts(M), d]
 };
+// int32 entries of the id scan's per-block sums
+uint64_t embed_bwd_scan_blocks(int V);
 uint64_t embed_bwd_max_pieces(int64_t M, int V);
 uint64_t embed_bwd_max_parts(int64_t M);
 hipError_t embed_bwd(DType t, const void* E, const int32_t* tok, const float* rinv0,

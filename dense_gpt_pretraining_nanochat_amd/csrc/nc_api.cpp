@@ -175,7 +175,7 @@ struct Plan {
   std::vector<LayerActs> acts;
   // backward only
   uint64_t dx, g, dh, dbig, dout, delta, partial, attn_part, counts, offsets, cursor, list;
-  uint64_t item_off, part_off, item_bucket;
+  uint64_t item_off, part_off, item_bucket, scan_blocks;
   uint64_t total;
 };
 
@@ -244,6 +244,7 @@ Plan plan_of(const Dims& D, bool bwd, bool record = false) {
     p.item_off = take_named("item_off", (uint64_t)(D.V + 1) * 4);
     p.part_off = take_named("part_off", (uint64_t)(D.V + 1) * 4);
     p.item_bucket = take_named("item_bucket", nc::embed_bwd_max_pieces(M, D.V) * 4);
+    p.scan_blocks = take_named("scan_blocks", nc::embed_bwd_scan_blocks(D.V) * 4);
   }
   p.total = off;
   return p;
@@ -461,6 +462,7 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
   es.item_off = at<int32_t>(ws, P.item_off);
   es.part_off = at<int32_t>(ws, P.part_off);
   es.item_bucket = at<int32_t>(ws, P.item_bucket);
+  es.scan_blocks = at<int32_t>(ws, P.scan_blocks);
   es.part = static_cast<float*>(dh);     // embed_bwd_max_parts(M) * d floats <= M * d
   HIPCHECK(nc::embed_bwd(dt, W(iE), tokens, rinv0, dx, (int)M, D.d, D.V, es, G(iE), accumulate, s));
   return NC_OK;
