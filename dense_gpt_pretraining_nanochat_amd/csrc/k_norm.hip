@@ -163,24 +163,10 @@ constexpr int kSortCap = 4096;   // buckets up to this size are sorted in LDS
 
 __device__ __forceinline__ int clamp_id(int t, int V) { return t < 0 ? 0 : (t >= V ? V - 1 : t); }
 
-// Wavefront-aggregated updates: the lowest remaining lane's id is broadcast
-// and every lane holding it is served by one atomic, so a frequent id (the
-// token law is Zipf-like) costs one atomic per wavefront instead of one per
-// occurrence. Each round removes at least the leading lane.
-__global__ __launch_bounds__(256) void embed_count_kernel(const int32_t* __restrict__ tok, int M, int V,
-                                                          int32_t* __restrict__ counts) {
+__global__ void embed_count_kernel(const int32_t* __restrict__ tok, int M, int V,
+                                   int32_t* __restrict__ counts) {
   const int m = blockIdx.x * blockDim.x + threadIdx.x;
-  const int lane = threadIdx.x & 63;
-  const bool in = m < M;
-  const int id = in ? clamp_id(tok[m], V) : -1;
-  unsigned long long rem = __ballot(in);
-  while (rem) {
-    const int leader = __ffsll(rem) - 1;
-    const int lid = __shfl(id, leader);
-    const unsigned long long same = __ballot(in && id == lid);
-    if (lane == leader) atomicAdd(&counts[lid], __popcll(same));
-    rem &= ~same;
-  }
+  if (m < M) atomicAdd(&counts[clamp_id(tok[m], V)], 1);
 }
 
 // Exclusive scans over ids of (rows, pieces, pieces of multi-piece buckets),
@@ -265,27 +251,11 @@ __global__ __launch_bounds__(kScanBlock) void embed_scan_kernel(const int32_t* _
   }
 }
 
-// Bucket fill, aggregated like the count: one atomic per id and wavefront
-// reserves the lanes' slots, each lane taking the one of its rank among them
-// (the order inside a bucket is fixed afterwards by the sort).
-__global__ __launch_bounds__(256) void fill_list_kernel(const int32_t* __restrict__ tok, int M, int V,
-                                                        int32_t* __restrict__ cursor,
-                                                        int32_t* __restrict__ list) {
+__global__ void fill_list_kernel(const int32_t* __restrict__ tok, int M, int V,
+                                 int32_t* __restrict__ cursor, int32_t* __restrict__ list) {
   const int m = blockIdx.x * blockDim.x + threadIdx.x;
-  const int lane = threadIdx.x & 63;
-  const bool in = m < M;
-  const int id = in ? clamp_id(tok[m], V) : -1;
-  unsigned long long rem = __ballot(in);
-  while (rem) {
-    const int leader = __ffsll(rem) - 1;
-    const int lid = __shfl(id, leader);
-    const unsigned long long same = __ballot(in && id == lid);
-    int base = 0;
-    if (lane == leader) base = atomicAdd(&cursor[lid], __popcll(same));
-    base = __shfl(base, leader);
-    if (in && id == lid) list[base + __popcll(same & ((1ull << lane) - 1))] = m;
-    rem &= ~same;
-  }
+  if (m >= M) return;
+  list[atomicAdd(&cursor[clamp_id(tok[m], V)], 1)] = m;
 }
 
 // One block per id: put the bucket's positions in increasing order (the atomic
