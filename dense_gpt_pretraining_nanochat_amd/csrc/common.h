@@ -80,6 +80,19 @@ __device__ __forceinline__ float lane16_sum(float v) {
   return v;
 }
 
+// sum over the 16 lanes of a DPP row (lanes sharing l / 16), in registers:
+// rotations of the row by 8, 4, 2 and 1 lanes (DPP row_ror, controls
+// 0x128 / 0x124 / 0x122 / 0x121). Every lane gets the row's sum; lanes may
+// differ in the last bit (each adds in its own order), so a caller stores the
+// value of one fixed lane.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false));
+  return v;
+}
+
 // Block-wide sum for blockDim.x threads (a multiple of 64, <= 1024); every
 // thread gets the result. `red` must hold 16 floats of shared memory.
 __device__ __forceinline__ float block_sum(float v, float* red) {

@@ -543,13 +543,14 @@ __device__ inline void dkv_item(int Tn, int i, int* kblk, int* chunk) {
 }
 
 // DIRECT (one query chunk per key block, T <= QCH): dK (scaled by 1/sqrt(D))
-// and dV go straight into the key and value columns of dqkv; otherwise each
-// chunk leaves an fp32 partial for attn_dkv_reduce_kernel.
+// and dV (times rs of its row, when rs is given) go straight into the key and
+// value columns of dqkv; otherwise each chunk leaves an fp32 partial for
+// attn_dkv_reduce_kernel.
 template <typename T, bool DIRECT>
 __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
     const T* __restrict__ qkv, int ldq, const T* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, int B, int Tn, int H, float* __restrict__ part,
-    T* __restrict__ dqkv, int ldd) {
+    T* __restrict__ dqkv, int ldd, const float* __restrict__ rs) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
   constexpr int SQ = BQK;                      // query rows per step
@@ -749,13 +750,14 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
     const float scale = 1.0f / sqrtf((float)D);
     typedef T T4 __attribute__((ext_vector_type(4)));
     T* dst = dqkv + (row0 + key0 + l16) * ldd + H * D;
+    const float vs = rs ? rs[row0 + key0 + l16] : 1.0f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       T4 wk, wv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         wk[r] = from_f32<T>(dk[dt][0][r] * scale);
-        wv[r] = from_f32<T>(dv[dt][0][r]);
+        wv[r] = from_f32<T>(dv[dt][0][r] * vs);
       }
       *reinterpret_cast<T4*>(dst + dt * 16 + lg * 4) = wk;
       *reinterpret_cast<T4*>(dst + D + dt * 16 + lg * 4) = wv;
@@ -775,12 +777,14 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
   }
 }
 
-// dK (scaled by 1/sqrt(D)) and dV of each key: the sum of its chunk partials
-// in chunk order, written into the key and value columns of dqkv.
+// dK (scaled by 1/sqrt(D)) and dV (times rs of its row, when given) of each
+// key: the sum of its chunk partials in chunk order, written into the key and
+// value columns of dqkv.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(const float* __restrict__ part,
                                                               int B, int Tn, int H,
-                                                              T* __restrict__ dqkv, int ldd) {
+                                                              T* __restrict__ dqkv, int ldd,
+                                                              const float* __restrict__ rs) {
   const size_t M = (size_t)B * Tn;
   const size_t row = blockIdx.x * 4ull + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= M) return;
@@ -790,7 +794,7 @@ __global__ __launch_bounds__(256) void attn_dkv_reduce_kernel(const float* __res
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int c = 0; c < nch; ++c)
     acc += *reinterpret_cast<const f32x4*>(part + ((size_t)c * M + row) * (2 * D) + lane * 4);
-  const float scale = lane < 32 ? 1.0f / sqrtf((float)D) : 1.0f;
+  const float scale = lane < 32 ? 1.0f / sqrtf((float)D) : (rs ? rs[row] : 1.0f);
   typedef T T4 __attribute__((ext_vector_type(4)));
   T4 w = {from_f32<T>(acc[0] * scale), from_f32<T>(acc[1] * scale), from_f32<T>(acc[2] * scale),
           from_f32<T>(acc[3] * scale)};
@@ -819,7 +823,7 @@ size_t attn_bwd_scratch_floats(int B, int T) {
 
 hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* o, const void* dout, const float* lse,
                     float* delta, int B, int T, int H, void* dqkv, int ldd, float* scratch,
-                    hipStream_t s) {
+                    hipStream_t s, const float* rs) {
   if (T % BKV || H < 1 || H > 16) return hipErrorInvalidValue;
   dim3 gq(B * (T / FQB) * ((H + 1) / 2)), bq(256);
   int items = 0;
@@ -837,11 +841,11 @@ hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* o, const void
                        delta, T, H, g, ldd);
     if (direct) {
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<bf16, true>), gk, bk, 0, s, q, ldq, d, lse, delta, B, T,
-                         H, scratch, g, ldd);
+                         H, scratch, g, ldd, rs);
     } else {
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<bf16, false>), gk, bk, 0, s, q, ldq, d, lse, delta, B,
-                         T, H, scratch, g, ldd);
-      hipLaunchKernelGGL(attn_dkv_reduce_kernel<bf16>, gr, br, 0, s, scratch, B, T, H, g, ldd);
+                         T, H, scratch, g, ldd, rs);
+      hipLaunchKernelGGL(attn_dkv_reduce_kernel<bf16>, gr, br, 0, s, scratch, B, T, H, g, ldd, rs);
     }
   } else {
     const float* q = static_cast<const float*>(qkv);
@@ -851,11 +855,11 @@ hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* o, const void
                        delta, T, H, g, ldd);
     if (direct) {
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<float, true>), gk, bk, 0, s, q, ldq, d, lse, delta, B,
-                         T, H, scratch, g, ldd);
+                         T, H, scratch, g, ldd, rs);
     } else {
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<float, false>), gk, bk, 0, s, q, ldq, d, lse, delta,
-                         B, T, H, scratch, g, ldd);
-      hipLaunchKernelGGL(attn_dkv_reduce_kernel<float>, gr, br, 0, s, scratch, B, T, H, g, ldd);
+                         B, T, H, scratch, g, ldd, rs);
+      hipLaunchKernelGGL(attn_dkv_reduce_kernel<float>, gr, br, 0, s, scratch, B, T, H, g, ldd, rs);
     }
   }
   return hipGetLastError();

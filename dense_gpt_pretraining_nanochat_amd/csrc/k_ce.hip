@@ -61,8 +61,8 @@ __device__ __forceinline__ float shifted_exp(float t, const CapConsts& q) {
 // GRAD: also write the logit gradient (dl may equal logits).
 template <typename T, int CB, bool GRAD>
 __global__ __launch_bounds__(kCeThreads, sizeof(T) == 2 && CB == 16 ? 8 : 4) void softcap_ce_kernel(
-    const T* logits, const int32_t* __restrict__ tgt, int V, int nch, float cap, float w,
-    float* __restrict__ loss_rows, T* dl, uint32_t* status) {
+    const T* logits, const int32_t* __restrict__ tgt, int V, int nch, float cap, float w0,
+    float* __restrict__ loss_rows, T* dl, uint32_t* status, const float* __restrict__ rs) {
   constexpr int E = CB / (int)sizeof(T);                       // logits per chunk
   constexpr int NCH = kCeMaxV / (kCeThreads * E);              // chunks per thread, at most
   typedef T TV __attribute__((ext_vector_type(E)));
@@ -70,6 +70,8 @@ __global__ __launch_bounds__(kCeThreads, sizeof(T) == 2 && CB == 16 ? 8 : 4) voi
   __shared__ float lt_s;                          // the target's logit
   const int row = blockIdx.x;
   const int tid = threadIdx.x, nt = blockDim.x;
+  // the final RMSNorm's row scale, folded into the lm_head, carried by the gradient
+  const float w = (GRAD && rs) ? w0 * rs[row] : w0;
   const T* src = logits + (size_t)row * V;
   const CapConsts q = {-2.0f * 1.44269504088896341f / cap, cap * 1.44269504088896341f};
 
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(kCeThreads, sizeof(T) == 2 && CB == 16 ? 8 : 4) voi
 
 template <typename T, int CB>
 hipError_t launch_ce(const void* logits, const int32_t* tgt, int R, int V, float cap, float w,
-                     float* loss_rows, void* dlogits, uint32_t* status, hipStream_t s) {
+                     float* loss_rows, void* dlogits, uint32_t* status, const float* rs, hipStream_t s) {
   constexpr int E = CB / (int)sizeof(T);
   int nt = ((V / E + 63) / 64) * 64;
   if (nt > kCeThreads) nt = kCeThreads;
@@ -149,25 +151,26 @@ hipError_t launch_ce(const void* logits, const int32_t* tgt, int R, int V, float
   if (dlogits)
     hipLaunchKernelGGL((softcap_ce_kernel<T, CB, true>), dim3(R), dim3(nt), 0, s,
                        static_cast<const T*>(logits), tgt, V, nch, cap, w, loss_rows,
-                       static_cast<T*>(dlogits), status);
+                       static_cast<T*>(dlogits), status, rs);
   else
     hipLaunchKernelGGL((softcap_ce_kernel<T, CB, false>), dim3(R), dim3(nt), 0, s,
                        static_cast<const T*>(logits), tgt, V, nch, cap, w, loss_rows,
-                       static_cast<T*>(nullptr), status);
+                       static_cast<T*>(nullptr), status, rs);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t softcap_ce(DType t, const void* logits, const int32_t* tgt, int R, int V, float cap,
-                      float w, float* loss_rows, void* dlogits, uint32_t* status, hipStream_t s) {
+                      float w, float* loss_rows, void* dlogits, uint32_t* status, hipStream_t s,
+                      const float* rs) {
   if (V % 4 || V > kCeMaxV || V <= 0 || R <= 0) return hipErrorInvalidValue;
   if (t == DType::BF16) {
     if (V % 8 == 0)
-      return launch_ce<bf16, 16>(logits, tgt, R, V, cap, w, loss_rows, dlogits, status, s);
-    return launch_ce<bf16, 8>(logits, tgt, R, V, cap, w, loss_rows, dlogits, status, s);
+      return launch_ce<bf16, 16>(logits, tgt, R, V, cap, w, loss_rows, dlogits, status, rs, s);
+    return launch_ce<bf16, 8>(logits, tgt, R, V, cap, w, loss_rows, dlogits, status, rs, s);
   }
-  return launch_ce<float, 16>(logits, tgt, R, V, cap, w, loss_rows, dlogits, status, s);
+  return launch_ce<float, 16>(logits, tgt, R, V, cap, w, loss_rows, dlogits, status, rs, s);
 }
 
 }  // namespace nc

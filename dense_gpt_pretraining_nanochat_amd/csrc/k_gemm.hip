@@ -7,7 +7,14 @@
 // The linear layers are bias-free (followin.io release article, architecture
 // list), so a contraction plus an epilogue is the whole layer. Epilogues fuse
 // the residual add, the relu^2 activation of the MLP (same list) and its
-// derivative, so no separate elementwise pass touches HBM.
+// derivative, so no separate elementwise pass touches HBM. The parameter-free
+// RMSNorm in front of the attention, the MLP and the lm_head (same list) is
+// folded into the products around it: the residual-add epilogue (AddF32Xs)
+// also writes the new residual row in the activation type and its sums of
+// squares per 64 columns, and the product that consumes the normalised row
+// takes that unnormalised copy as its A operand and multiplies each output
+// row by the norm's 1/rms (rs) before its epilogue operation - the norm is a
+// per-row scale, which commutes with the contraction over the row.
 //
 // Two kernels. Large bf16 products (at least 256 output tiles) take
 // gemm_bf16_kernel: a 256x256 output tile per 512-thread workgroup (one per
@@ -275,15 +282,39 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g0) {
   }
 
   // ---- epilogue: lane holds C[m][n..n+3] of each 16x16 tile ----------------
+  constexpr bool SCALED = EPI == Epi::StoreT || EPI == Epi::Relu2 || EPI == Epi::Relu2Bwd;
+  static_assert(EPI != Epi::AddF32Xs || TN == 64, "AddF32Xs: one 64-column group per wavefront");
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = m0 + wm * TM + i * 16 + l16;
+    // lanes l16 + 16 lg hold the same row: they skip (or not) together
     if (m >= g.M) continue;
+    const float rsm = (SCALED && g.rs) ? g.rs[m] : 1.0f;
+    float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = n0 + wn * TN + j * 16 + lg * 4;
       if (n >= g.N) continue;
-      epilogue4<T, EPI>(g, split, m, n, acc[i][j]);
+      if constexpr (EPI == Epi::AddF32Xs) {
+        const size_t off = (size_t)m * g.ldc + n;
+        f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + off);
+        const f32x4 y = *p + acc[i][j];
+        *p = y;
+        typedef T T4 __attribute__((ext_vector_type(4)));
+        const T4 w = {from_f32<T>(y[0]), from_f32<T>(y[1]), from_f32<T>(y[2]), from_f32<T>(y[3])};
+        *reinterpret_cast<T4*>(static_cast<T*>(g.xc) + off) = w;
+        ss += y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
+      } else if constexpr (SCALED) {
+        epilogue4<T, EPI>(g, split, m, n, acc[i][j] * rsm);
+      } else {
+        epilogue4<T, EPI>(g, split, m, n, acc[i][j]);
+      }
+    }
+    if constexpr (EPI == Epi::AddF32Xs) {
+      // the wavefront's 64 columns of row m (N % 64 == 0: all inside or all outside)
+      ss = group4_sum(ss);
+      const int n64 = n0 + wn * TN;
+      if (lg == 0 && n64 < g.N) g.ssq[(size_t)m * (g.N / 64) + n64 / 64] = ss;
     }
   }
 }
@@ -589,15 +620,20 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
   // it with the next 32-row block's chunk as soon as it has been used.
   constexpr int CPR = TN / 4;                                  // 16-byte chunks per row
   constexpr int CH = 32 * CPR / 64;                            // chunks per lane per block
-  constexpr bool READS = EPI == Epi::AddF32 || EPI == Epi::Relu2Bwd || EPI == Epi::AxpbyT ||
-                        EPI == Epi::AxpbyF32;
+  constexpr bool READS = EPI == Epi::AddF32 || EPI == Epi::AddF32Xs || EPI == Epi::Relu2Bwd ||
+                        EPI == Epi::AxpbyT || EPI == Epi::AxpbyF32;
+  constexpr bool SCALED = EPI == Epi::StoreT || EPI == Epi::Relu2 || EPI == Epi::Relu2Bwd;
   constexpr bool READS_C2 = EPI == Epi::Relu2Bwd || EPI == Epi::AxpbyT || EPI == Epi::AxpbyF32;
   constexpr bool WIDE = !READS && (EPI == Epi::StoreT || EPI == Epi::Relu2);
   constexpr int CPR8 = TN / 8, CH8 = 32 * CPR8 / 64;
   // Vector-memory instructions one wavefront's epilogue issues for a whole
   // tile (every row and column inside the matrix): its stores, plus the
-  // operand loads of the epilogues that read memory.
-  constexpr int EPI_VMEM = WIDE ? FM * CH8 : (READS ? 2 * FM * CH : FM * CH);
+  // operand loads of the epilogues that read memory (AddF32Xs: the residual
+  // load, its store and the copy's store; its sum-of-squares stores and the
+  // row-scale loads are left out: counting fewer operations than are issued
+  // only makes a wait wait longer).
+  constexpr int EPI_VMEM =
+      WIDE ? FM * CH8 : (EPI == Epi::AddF32Xs ? 3 * FM * CH : (READS ? 2 * FM * CH : FM * CH));
   // wait counts with the epilogue's operations behind one or two stages
   // (capped at the counter's 63: a smaller count only waits longer)
   constexpr int W_E0 = EPI_VMEM < 63 ? EPI_VMEM : 63;
@@ -670,6 +706,18 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
     }
     if (!lag) barrier();
 
+    // row scales of this tile's rows (the lane's accumulator rows), requested
+    // before the next tile's loads so that waiting for them never waits for those
+    float rsv[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) rsv[i] = 1.0f;
+    if constexpr (SCALED) {
+      if (g0.rs) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) rsv[i] = g0.rs[min(cur.m0 + wm * TM + i * 32 + l32, g0.M - 1)];
+      }
+    }
+
     // next tile of this workgroup, if any: its first two stages go out now
     slot += J;
     const bool more = slot < R && tile_of(slot) < total;
@@ -727,7 +775,7 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
             bf16x4 w;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              float a = acc[i][j][4 * q + e];
+              float a = acc[i][j][4 * q + e] * rsv[i];
               if constexpr (EPI == Epi::Relu2) {
                 a = fmaxf(a, 0.f);
                 a *= a;
@@ -751,7 +799,8 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            if constexpr (SCALED) v *= rsv[i];
             stg_put(wl + stg_off(l32, 8 * j + 2 * q + lh), v);
           }
 #pragma unroll
@@ -768,7 +817,23 @@ __global__ __launch_bounds__(512) void gemm_bf16_kernel(GemmArgs g0) {
             // for everything outstanding there, the next tile's loads included
             asm volatile("" ::"v"(x));
             if (i + 1 < FM) pre[u] = fetch1(i + 1, u);
-            if (m < ge.M && n < ge.N) epilogue4_in<EPI>(ge, me.split, m, n, v, x);
+            if constexpr (EPI == Epi::AddF32Xs) {
+              // new residual row segment, its bf16 copy, and the sum of its
+              // squares over the wavefront's 64 columns: the 16 lanes of a
+              // DPP row hold one row's 16 chunks
+              const f32x4 y = x + v;
+              const float ss = row16_sum(y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3]);
+              if (m < ge.M && n < ge.N) {
+                const size_t off = (size_t)m * ge.ldc + n;
+                __builtin_nontemporal_store(y, reinterpret_cast<f32x4*>(static_cast<float*>(ge.C) + off));
+                const bf16x4 w = {from_f32<bf16>(y[0]), from_f32<bf16>(y[1]), from_f32<bf16>(y[2]),
+                                  from_f32<bf16>(y[3])};
+                __builtin_nontemporal_store(w, reinterpret_cast<bf16x4*>(static_cast<bf16*>(ge.xc) + off));
+                if (cc == 0) ge.ssq[(size_t)m * (ge.N / 64) + (n0 + wn * TN) / 64] = ss;
+              }
+            } else {
+              if (m < ge.M && n < ge.N) epilogue4_in<EPI>(ge, me.split, m, n, v, x);
+            }
           } else {
             if (m < ge.M && n < ge.N) epilogue4<bf16, EPI>(ge, me.split, m, n, v);
           }
@@ -879,6 +944,7 @@ hipError_t dispatch_epi(Epi epi, const GemmArgs& g, hipStream_t s) {
     case Epi::PartialF32: return launch<T, AK, BKC, Epi::PartialF32>(g, s);
     case Epi::AxpbyT: return launch<T, AK, BKC, Epi::AxpbyT>(g, s);
     case Epi::AxpbyF32: return launch<T, AK, BKC, Epi::AxpbyF32>(g, s);
+    case Epi::AddF32Xs: return launch<T, AK, BKC, Epi::AddF32Xs>(g, s);
   }
   return hipErrorInvalidValue;
 }
@@ -901,6 +967,9 @@ hipError_t gemm(DType t, bool a_kcontig, bool b_kcontig, Epi epi, const GemmArgs
   if (epi != Epi::PartialF32 && g.splits != 1) return hipErrorInvalidValue;
   if (g.batch < 0 || (g.batch > 1 && epi == Epi::PartialF32)) return hipErrorInvalidValue;
   if ((epi == Epi::Relu2Bwd || epi == Epi::AxpbyT || epi == Epi::AxpbyF32) && !g.C2)
+    return hipErrorInvalidValue;
+  if (epi == Epi::AddF32Xs && (!g.xc || !g.ssq || g.N % 64 || g.batch > 1)) return hipErrorInvalidValue;
+  if (g.rs && (g.batch > 1 || !(epi == Epi::StoreT || epi == Epi::Relu2 || epi == Epi::Relu2Bwd)))
     return hipErrorInvalidValue;
   if (t == DType::BF16 && g.tile == 256 && !strides_fit_256(g)) return hipErrorInvalidValue;
   if ((long)((g.M + 127) / 128) * ((g.N + 127) / 128) * g.splits * (g.batch > 1 ? g.batch : 1) >

@@ -5,6 +5,11 @@
 // normalised (followin.io release article, architecture list). The norm is
 // n(v) = v / sqrt(mean(v^2) + eps); its gradient is
 // dv = rinv * (dy - y * mean(dy * y)) with y = n(v), rinv = 1/sqrt(mean+eps).
+// In the training step the norms in front of the blocks and the lm_head are
+// folded into the products (the consumer scales its output rows by rinv, the
+// gradients arriving there carry rinv), so the backward here also takes the
+// prescaled form dv = dy' - rinv^2 * v * mean(dy' * v) with dy' = rinv * dy,
+// and rinv itself comes from per-64-column sums of squares (ssq_rinv).
 //
 // One 64-lane wavefront owns one row (d <= 2048 floats): each lane keeps up to
 // 8 float4 of the row in registers, so a row is read from HBM once and written
@@ -33,14 +38,17 @@ __device__ __forceinline__ void store4(T* p, const float* o) {
   *reinterpret_cast<T4*>(p) = v;
 }
 
-// x[m] = n(E[tok[m]]) in fp32, rinv[m]
-template <typename T>
+// x[m] = n(E[tok[m]]) in fp32, rinv[m]; with XB also xb[m] = T(x[m]) and
+// rinv_x[m] = 1/sqrt(mean(x[m]^2) + eps), the first block's norm of x folded
+// into its QKV product
+template <typename T, bool XB>
 __global__ __launch_bounds__(256) void embed_norm_fwd_kernel(const T* __restrict__ E,
                                                              const int32_t* __restrict__ tok,
                                                              int M, int d, int V, float eps,
                                                              float* __restrict__ x,
                                                              float* __restrict__ rinv,
-                                                             uint32_t* status) {
+                                                             uint32_t* status, T* __restrict__ xb,
+                                                             float* __restrict__ rinv_x) {
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (m >= M) return;
@@ -63,15 +71,44 @@ __global__ __launch_bounds__(256) void embed_norm_fwd_kernel(const T* __restrict
   ss = wave_sum(ss);
   const float r = 1.0f / sqrtf(ss / d + eps);
   float* dst = x + (size_t)m * d;
+  float ss2 = 0.f;
 #pragma unroll
   for (int i = 0; i < kMaxVec; ++i) {
     const int c = (i * 64 + lane) * 4;
     if (c < d) {
       f32x4 o = {v[i][0] * r, v[i][1] * r, v[i][2] * r, v[i][3] * r};
       *reinterpret_cast<f32x4*>(dst + c) = o;
+      if constexpr (XB) {
+        float oo[4] = {o[0], o[1], o[2], o[3]};
+        store4(xb + (size_t)m * d + c, oo);
+        ss2 += o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+      }
     }
   }
   if (lane == 0) rinv[m] = r;
+  if constexpr (XB) {
+    ss2 = wave_sum(ss2);
+    if (lane == 0) rinv_x[m] = 1.0f / sqrtf(ss2 / d + eps);
+  }
+}
+
+// rinv[m] = 1/sqrt(sum_p ssq[m][p] / d + eps), the partial sums of squares
+// (per 64 columns, written by the residual-add product) added in column order.
+// One thread per row; its P loads are independent and issued together.
+constexpr int kSsqMaxP = 32;                   // d <= 2048
+__global__ __launch_bounds__(128) void ssq_rinv_kernel(const float* __restrict__ ssq, int M, int P, int d,
+                                                       float eps, float* __restrict__ rinv) {
+  const int m = blockIdx.x * 128 + threadIdx.x;
+  if (m >= M) return;
+  const float* p = ssq + (size_t)m * P;
+  float v[kSsqMaxP];
+#pragma unroll
+  for (int i = 0; i < kSsqMaxP; ++i) v[i] = i < P ? p[i] : 0.f;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kSsqMaxP; ++i)
+    if (i < P) ss += v[i];
+  rinv[m] = 1.0f / sqrtf(ss / d + eps);
 }
 
 template <typename T>
@@ -106,7 +143,10 @@ __global__ __launch_bounds__(256) void rmsnorm_fwd_kernel(const float* __restric
   if (lane == 0) rinv[m] = r;
 }
 
-template <typename T, bool ACC, bool WRITE_G>
+// PRE: y is the unnormalised input v and dy already carries the factor rinv
+// (the norm folded into the products): dx = dy - rinv^2 v mean(dy v), the same
+// gradient as rinv (dy0 - y0 mean(dy0 y0)) for dy0 = dy / rinv, y0 = rinv v.
+template <typename T, bool ACC, bool WRITE_G, bool PRE>
 __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ dy,
                                                           const T* __restrict__ y,
                                                           const float* __restrict__ rinv, int M,
@@ -136,7 +176,10 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const T* __restrict__ 
     if (c < d) {
       f32x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = r * (gy[i][e] - yy[i][e] * dot);
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (PRE) o[e] = gy[i][e] - yy[i][e] * (r * r * dot);
+        else o[e] = r * (gy[i][e] - yy[i][e] * dot);
+      }
       f32x4* p = reinterpret_cast<f32x4*>(dx + base + c);
       if (ACC) o += *p;
       *p = o;
@@ -472,15 +515,31 @@ inline int row_grid(int M) { return (M + kRowsPerBlock - 1) / kRowsPerBlock; }
 
 }  // namespace
 
-hipError_t embed_norm_fwd(DType t, const void* E, const int32_t* tok, int M, int d, int V,
-                          float eps, float* x, float* rinv, uint32_t* status, hipStream_t s) {
-  if (d % 4 || d > 2048) return hipErrorInvalidValue;
-  if (t == DType::BF16)
-    hipLaunchKernelGGL(embed_norm_fwd_kernel<bf16>, dim3(row_grid(M)), dim3(256), 0, s,
-                       static_cast<const bf16*>(E), tok, M, d, V, eps, x, rinv, status);
+template <typename T>
+static void launch_embed_norm(const void* E, const int32_t* tok, int M, int d, int V, float eps, float* x,
+                              float* rinv, uint32_t* status, void* xb, float* rinv_x, hipStream_t s) {
+  if (xb && rinv_x)
+    hipLaunchKernelGGL((embed_norm_fwd_kernel<T, true>), dim3(row_grid(M)), dim3(256), 0, s,
+                       static_cast<const T*>(E), tok, M, d, V, eps, x, rinv, status, static_cast<T*>(xb),
+                       rinv_x);
   else
-    hipLaunchKernelGGL(embed_norm_fwd_kernel<float>, dim3(row_grid(M)), dim3(256), 0, s,
-                       static_cast<const float*>(E), tok, M, d, V, eps, x, rinv, status);
+    hipLaunchKernelGGL((embed_norm_fwd_kernel<T, false>), dim3(row_grid(M)), dim3(256), 0, s,
+                       static_cast<const T*>(E), tok, M, d, V, eps, x, rinv, status, static_cast<T*>(nullptr),
+                       static_cast<float*>(nullptr));
+}
+
+hipError_t embed_norm_fwd(DType t, const void* E, const int32_t* tok, int M, int d, int V,
+                          float eps, float* x, float* rinv, uint32_t* status, hipStream_t s, void* xb,
+                          float* rinv_x) {
+  if (d % 4 || d > 2048) return hipErrorInvalidValue;
+  if (t == DType::BF16) launch_embed_norm<bf16>(E, tok, M, d, V, eps, x, rinv, status, xb, rinv_x, s);
+  else launch_embed_norm<float>(E, tok, M, d, V, eps, x, rinv, status, xb, rinv_x, s);
+  return hipGetLastError();
+}
+
+hipError_t ssq_rinv(const float* ssq, int M, int P, int d, float eps, float* rinv, hipStream_t s) {
+  if (M <= 0 || P <= 0 || P > kSsqMaxP || d <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(ssq_rinv_kernel, dim3((M + 127) / 128), dim3(128), 0, s, ssq, M, P, d, eps, rinv);
   return hipGetLastError();
 }
 
@@ -496,24 +555,29 @@ hipError_t rmsnorm_fwd(DType t, const float* x, int M, int d, float eps, void* y
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool PRE>
 static void launch_norm_bwd(const void* dyv, const void* y, const float* rinv, int M, int d,
                             float* dx, bool acc, void* g, hipStream_t s) {
   const T* dy = static_cast<const T*>(dyv);
   const T* yt = static_cast<const T*>(y);
   T* gt = static_cast<T*>(g);
   dim3 grid(row_grid(M)), block(256);
-  if (acc && g) hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, true, true>), grid, block, 0, s, dy, yt, rinv, M, d, dx, gt);
-  else if (acc) hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, true, false>), grid, block, 0, s, dy, yt, rinv, M, d, dx, gt);
-  else if (g) hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, false, true>), grid, block, 0, s, dy, yt, rinv, M, d, dx, gt);
-  else hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, false, false>), grid, block, 0, s, dy, yt, rinv, M, d, dx, gt);
+  if (acc && g) hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, true, true, PRE>), grid, block, 0, s, dy, yt, rinv, M, d, dx, gt);
+  else if (acc) hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, true, false, PRE>), grid, block, 0, s, dy, yt, rinv, M, d, dx, gt);
+  else if (g) hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, false, true, PRE>), grid, block, 0, s, dy, yt, rinv, M, d, dx, gt);
+  else hipLaunchKernelGGL((rmsnorm_bwd_kernel<T, false, false, PRE>), grid, block, 0, s, dy, yt, rinv, M, d, dx, gt);
 }
 
 hipError_t rmsnorm_bwd(DType t, const void* dy, const void* y, const float* rinv, int M, int d,
-                       float* dx, bool accumulate, void* g, hipStream_t s) {
+                       float* dx, bool accumulate, void* g, hipStream_t s, bool prescaled) {
   if (d % 4 || d > 2048) return hipErrorInvalidValue;
-  if (t == DType::BF16) launch_norm_bwd<bf16>(dy, y, rinv, M, d, dx, accumulate, g, s);
-  else launch_norm_bwd<float>(dy, y, rinv, M, d, dx, accumulate, g, s);
+  if (t == DType::BF16) {
+    if (prescaled) launch_norm_bwd<bf16, true>(dy, y, rinv, M, d, dx, accumulate, g, s);
+    else launch_norm_bwd<bf16, false>(dy, y, rinv, M, d, dx, accumulate, g, s);
+  } else {
+    if (prescaled) launch_norm_bwd<float, true>(dy, y, rinv, M, d, dx, accumulate, g, s);
+    else launch_norm_bwd<float, false>(dy, y, rinv, M, d, dx, accumulate, g, s);
+  }
   return hipGetLastError();
 }
 

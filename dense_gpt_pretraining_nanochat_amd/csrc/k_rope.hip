@@ -97,13 +97,16 @@ __global__ __launch_bounds__(256) void rope_qknorm_fwd_kernel(T* __restrict__ qk
   }
 }
 
-// dz' = r (dy - y mean(dy y)) with y the saved normalised vector, then rotate by -theta
-template <typename T>
+// dz' = r (dy - y mean(dy y)) with y the saved normalised vector, then rotate by -theta.
+// RS: the result is then multiplied by rs[m] (the row scale of the RMSNorm folded
+// into the QKV product; the attention backward applies it to the value gradient).
+template <typename T, bool RS>
 __global__ __launch_bounds__(256) void rope_qknorm_bwd_kernel(T* __restrict__ dqkv, int ldd,
                                                               const T* __restrict__ qkv, int ldq,
                                                               int M, int Tlen, int H,
                                                               const float* __restrict__ cs,
-                                                              const float* __restrict__ rinv_qk) {
+                                                              const float* __restrict__ rinv_qk,
+                                                              const float* __restrict__ rs) {
   const int sl = threadIdx.x & 15;
   const size_t w = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int nh = H + 1;
@@ -131,6 +134,14 @@ __global__ __launch_bounds__(256) void rope_qknorm_bwd_kernel(T* __restrict__ dq
     const float da = r * (ga[e] - ya[e] * dot), db = r * (gb[e] - yb[e] * dot);
     oa[e] = da * c[e] + db * sn[e];
     ob[e] = -da * sn[e] + db * c[e];
+  }
+  if constexpr (RS) {
+    const float f = rs[m];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      oa[e] *= f;
+      ob[e] *= f;
+    }
   }
   Quad<T>::store(g, oa);
   Quad<T>::store(g + kHalf, ob);
@@ -160,16 +171,23 @@ hipError_t rope_qknorm_fwd(DType t, void* qkv, int ldq, int M, int T, int H, con
   return hipGetLastError();
 }
 
-hipError_t rope_qknorm_bwd(DType t, void* dqkv, int ldd, const void* qkv, int ldq, int M, int T,
-                           int H, const float* cs, const float* rinv_qk, hipStream_t s) {
+template <typename T>
+static void launch_rope_bwd(void* dqkv, int ldd, const void* qkv, int ldq, int M, int Tlen, int H,
+                            const float* cs, const float* rinv_qk, const float* rs, hipStream_t s) {
   const size_t vecs = (size_t)M * (H + 1);
   dim3 grid((unsigned)((vecs + 15) / 16)), block(256);
-  if (t == DType::BF16)
-    hipLaunchKernelGGL(rope_qknorm_bwd_kernel<bf16>, grid, block, 0, s, static_cast<bf16*>(dqkv), ldd,
-                       static_cast<const bf16*>(qkv), ldq, M, T, H, cs, rinv_qk);
+  if (rs)
+    hipLaunchKernelGGL((rope_qknorm_bwd_kernel<T, true>), grid, block, 0, s, static_cast<T*>(dqkv), ldd,
+                       static_cast<const T*>(qkv), ldq, M, Tlen, H, cs, rinv_qk, rs);
   else
-    hipLaunchKernelGGL(rope_qknorm_bwd_kernel<float>, grid, block, 0, s, static_cast<float*>(dqkv),
-                       ldd, static_cast<const float*>(qkv), ldq, M, T, H, cs, rinv_qk);
+    hipLaunchKernelGGL((rope_qknorm_bwd_kernel<T, false>), grid, block, 0, s, static_cast<T*>(dqkv), ldd,
+                       static_cast<const T*>(qkv), ldq, M, Tlen, H, cs, rinv_qk, rs);
+}
+
+hipError_t rope_qknorm_bwd(DType t, void* dqkv, int ldd, const void* qkv, int ldq, int M, int T,
+                           int H, const float* cs, const float* rinv_qk, hipStream_t s, const float* rs) {
+  if (t == DType::BF16) launch_rope_bwd<bf16>(dqkv, ldd, qkv, ldq, M, T, H, cs, rinv_qk, rs, s);
+  else launch_rope_bwd<float>(dqkv, ldd, qkv, ldq, M, T, H, cs, rinv_qk, rs, s);
   return hipGetLastError();
 }
 

@@ -20,6 +20,8 @@ enum class Epi {
   PartialF32,  // C (float) + split*M*ldc = acc over this split's K range
   AxpbyT,      // C (T) = alpha * acc + beta * C2[m,n] (C2 of type T)
   AxpbyF32,    // C (float) = alpha * acc + beta * C2[m,n] (C2 of type T)
+  AddF32Xs,    // C (float) += acc; xc (T) = the new C; ssq[m * (N/64) + n/64] = sum of the new
+               // C[m, :]^2 over each 64-column group (N % 64 == 0)
 };
 struct GemmArgs {
   const void* A;
@@ -33,6 +35,12 @@ struct GemmArgs {
   int batch;         // independent products of this shape (0 or 1: one)
   int64_t sa, sb, sc, sc2;  // element strides between batch items of A, B, C and C2
   float alpha, beta;        // Axpby epilogues
+  void* xc;                 // AddF32Xs: copy of the new C rows in T (ld ldc)
+  float* ssq;               // AddF32Xs: [M][N/64] sums of squares of the new C rows
+  // StoreT, Relu2, Relu2Bwd: acc of row m is multiplied by rs[m] before the
+  // epilogue's operation (an RMSNorm's row scale folded into the product whose
+  // A operand is the unnormalised row); null: no scale. Unbatched only.
+  const float* rs;
 };
 // compute units of the current device (256 when it cannot be queried)
 int device_cus();
@@ -57,14 +65,21 @@ hipError_t splitk_reduce_t(DType t, const float* part, int splits, size_t n, voi
 
 // ---- norms and embedding --------------------------------------------------
 // x[m,:] = n(E[tok[m],:]) (fp32), rinv[m]; ids outside [0,V) are clamped and flagged.
+// Optionally xb[m,:] = T(x[m,:]) and rinv_x[m] = 1/sqrt(mean(x[m,:]^2) + eps) (the next
+// norm's row scale), when both are non-null.
 hipError_t embed_norm_fwd(DType t, const void* E, const int32_t* tok, int M, int d, int V,
-                          float eps, float* x, float* rinv, uint32_t* status, hipStream_t s);
+                          float eps, float* x, float* rinv, uint32_t* status, hipStream_t s,
+                          void* xb = nullptr, float* rinv_x = nullptr);
+// rinv[m] = 1 / sqrt(sum_p ssq[m * P + p] / d + eps), p = 0..P-1 in order
+hipError_t ssq_rinv(const float* ssq, int M, int P, int d, float eps, float* rinv, hipStream_t s);
 // y[m,:] = n(x[m,:]) as T, rinv[m]
 hipError_t rmsnorm_fwd(DType t, const float* x, int M, int d, float eps, void* y, float* rinv,
                        hipStream_t s);
-// dx[m,:] (=|+=) rinv*(dy - y*mean(dy*y)); dy and y of type T; optionally g = T(dx)
+// dx[m,:] (=|+=) rinv*(dy - y*mean(dy*y)); dy and y of type T; optionally g = T(dx).
+// prescaled: y is the unnormalised input v and dy the gradient already multiplied by
+// rinv, so dx (=|+=) dy - rinv^2 * v * mean(dy * v) (the same gradient).
 hipError_t rmsnorm_bwd(DType t, const void* dy, const void* y, const float* rinv, int M, int d,
-                       float* dx, bool accumulate, void* g, hipStream_t s);
+                       float* dx, bool accumulate, void* g, hipStream_t s, bool prescaled = false);
 // embedding-norm backward + deterministic scatter into dE (fp32, every row written)
 struct EmbedBwdScratch {
   int32_t* counts;       // [V + 1]
@@ -94,8 +109,10 @@ hipError_t rope_table(int T, int half, double base, float* cs, hipStream_t s, in
 hipError_t rope_qknorm_fwd(DType t, void* qkv, int ldq, int M, int T, int H, const float* cs,
                            float eps, float* rinv_qk, hipStream_t s, void* cache = nullptr,
                            int max_seq = 0, int pos0 = 0);
+// rs (may be null): the query and key gradients of row m are multiplied by rs[m]
 hipError_t rope_qknorm_bwd(DType t, void* dqkv, int ldd, const void* qkv, int ldq, int M, int T,
-                           int H, const float* cs, const float* rinv_qk, hipStream_t s);
+                           int H, const float* cs, const float* rinv_qk, hipStream_t s,
+                           const float* rs = nullptr);
 
 // ---- attention -------------------------------------------------------------
 // qkv: [B*T, ldq] with q heads, then k, then v (each 128 wide); o: [B*T, H*128]; lse: [B, H, T]
@@ -106,9 +123,11 @@ hipError_t attn_fwd(DType t, const void* qkv, int ldq, int B, int T, int H, void
 // scratch holds attn_bwd_scratch_floats(B, T) floats of partial dK/dV sums
 // (none, and scratch may be null, when T <= 2048: dK/dV are written directly)
 size_t attn_bwd_scratch_floats(int B, int T);
+// rs (may be null): dV of key row m is multiplied by rs[m] (the row scale of the
+// RMSNorm folded into the QKV product; rope_qknorm_bwd applies it to dQ and dK)
 hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* o, const void* dout, const float* lse,
                     float* delta, int B, int T, int H, void* dqkv, int ldd, float* scratch,
-                    hipStream_t s);
+                    hipStream_t s, const float* rs = nullptr);
 // Device address (current device) of the library's fixed attention-backward
 // scratch array of kAttnFixedScratchBytes, for the entry point that allocates
 // nothing; looked up once per device.
@@ -117,9 +136,11 @@ hipError_t attn_fixed_scratch(void** ptr);
 
 // ---- cross-entropy -----------------------------------------------------------
 // rows of logits [R, V] (T): per-row loss (fp32) and dlogits (T) = (softmax(z)-onehot)*(1-(z/c)^2)*w;
-// dlogits may equal logits (the gradient then replaces them)
+// dlogits may equal logits (the gradient then replaces them); rs (may be null): the
+// gradient of row r is also multiplied by rs[r]
 hipError_t softcap_ce(DType t, const void* logits, const int32_t* tgt, int R, int V, float cap,
-                      float w, float* loss_rows, void* dlogits, uint32_t* status, hipStream_t s);
+                      float w, float* loss_rows, void* dlogits, uint32_t* status, hipStream_t s,
+                      const float* rs = nullptr);
 hipError_t loss_mean(const float* loss_rows, int M, float* out, uint32_t* status, hipStream_t s);
 // out[0] = sum of loss_rows[i] over i with token_bytes[targets[i]] > 0, out[1] = sum of those
 // lengths, out[2] = out[0] / (ln 2 * out[1]) (NaN when out[1] = 0); fp64, fixed order

@@ -171,7 +171,7 @@ struct Piece {
 
 struct Plan {
   std::vector<Piece> pieces;
-  uint64_t status, cs, x, rinv0, xf, rinvf, loss_rows, logits;
+  uint64_t status, cs, x, rinv0, xf, rinvf, ssq, loss_rows, logits;
   std::vector<LayerActs> acts;
   // backward only
   uint64_t dx, g, dh, dbig, dout, delta, partial, attn_part, counts, offsets, cursor, list;
@@ -205,6 +205,7 @@ Plan plan_of(const Dims& D, bool bwd, bool record = false) {
   p.rinv0 = take_named("rinv0", M * 4);
   p.xf = take_named("xf", M * D.d * e);
   p.rinvf = take_named("rinvf", M * 4);
+  p.ssq = take_named("ssq", M * (D.d / 64) * 4);              // per-64-column sums of squares
   p.loss_rows = take_named("loss_rows", M * 4);
   p.logits = take_named("logits", Mc * D.V * e);                // the logit gradient replaces them
   const int nsets = bwd ? D.L : 1;
@@ -291,10 +292,16 @@ hipError_t wgrad(DType dt, const void* X1, const void* X2, float* dW, float* par
   return nc::splitk_reduce(partial, p.splits, (size_t)N1 * N2, dW, accumulate, s);
 }
 
+// rs: row scale of a folded RMSNorm (StoreT / Relu2 / Relu2Bwd); xc, ssq: the
+// copy and the sums of squares an AddF32Xs product writes for the next norm
 hipError_t gemm_simple(DType dt, bool ak, bool bk, Epi epi, const void* A, const void* B, void* C,
                        void* C2, int64_t M, int N, int K, int lda, int ldb, int ldc, int ldc2,
-                       hipStream_t s) {
+                       hipStream_t s, const float* rs = nullptr, void* xc = nullptr,
+                       float* ssq = nullptr) {
   nc::GemmArgs g{};
+  g.rs = rs;
+  g.xc = xc;
+  g.ssq = ssq;
   g.A = A;
   g.B = B;
   g.C = C;
@@ -344,7 +351,15 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
 
   HIPCHECK(nc::fill_zero(status, 256, s));
   HIPCHECK(nc::rope_table(D.T, 64, (double)cfg->rope_base, cs, s));
-  HIPCHECK(nc::embed_norm_fwd(dt, W(iE), tokens, (int)M, D.d, D.V, eps, x, rinv0, status, s));
+  // The RMSNorms in front of the attention, the MLP and the lm_head are folded
+  // into the products around them: the product that feeds the residual stream
+  // also writes the new residual in the activation type (h, h2, xf hold these
+  // unnormalised copies) and its per-64-column sums of squares, one small pass
+  // turns those into 1/rms per row, and the consuming product scales its
+  // output rows by it. The embedding kernel does the first block's norm itself.
+  float* ssq = at<float>(ws, P.ssq);
+  HIPCHECK(nc::embed_norm_fwd(dt, W(iE), tokens, (int)M, D.d, D.V, eps, x, rinv0, status, s,
+                              at<char>(ws, P.acts[0].h), at<float>(ws, P.acts[0].rinv1)));
 
   // ---------------- forward through the blocks ----------------
   for (int l = 0; l < D.L; ++l) {
@@ -354,21 +369,27 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
     void* o = at<char>(ws, A.o);
     void* h2 = at<char>(ws, A.h2);
     void* a = at<char>(ws, A.a);
+    const float* rinv1 = at<float>(ws, A.rinv1);
+    float* rinv2 = at<float>(ws, A.rinv2);
+    // where this block's output residual (the next norm's input) goes
+    const bool last = l + 1 == D.L;
+    const LayerActs& An = P.acts[bwd && !last ? l + 1 : 0];
+    void* xnext = last ? xf : at<char>(ws, An.h);
+    float* rnext = last ? rinvf : at<float>(ws, An.rinv1);
     const int base = 1 + 4 * l;
-    HIPCHECK(nc::rmsnorm_fwd(dt, x, (int)M, D.d, eps, h, at<float>(ws, A.rinv1), s));
     HIPCHECK(gemm_simple(dt, true, true, Epi::StoreT, h, W(base + 0), qkv, nullptr, M, D.Q, D.d,
-                         D.d, D.d, D.Q, 0, s));
+                         D.d, D.d, D.Q, 0, s, rinv1));
     HIPCHECK(nc::rope_qknorm_fwd(dt, qkv, D.Q, (int)M, D.T, D.H, cs, eps, at<float>(ws, A.rqk), s));
     HIPCHECK(nc::attn_fwd(dt, qkv, D.Q, D.B, D.T, D.H, o, at<float>(ws, A.lse), s));
-    HIPCHECK(gemm_simple(dt, true, true, Epi::AddF32, o, W(base + 1), x, nullptr, M, D.d, D.d,
-                         D.d, D.d, D.d, 0, s));
-    HIPCHECK(nc::rmsnorm_fwd(dt, x, (int)M, D.d, eps, h2, at<float>(ws, A.rinv2), s));
+    HIPCHECK(gemm_simple(dt, true, true, Epi::AddF32Xs, o, W(base + 1), x, nullptr, M, D.d, D.d,
+                         D.d, D.d, D.d, 0, s, nullptr, h2, ssq));
+    HIPCHECK(nc::ssq_rinv(ssq, (int)M, D.d / 64, D.d, eps, rinv2, s));
     HIPCHECK(gemm_simple(dt, true, true, Epi::Relu2, h2, W(base + 2), a, nullptr, M, D.F, D.d,
-                         D.d, D.d, D.F, 0, s));
-    HIPCHECK(gemm_simple(dt, true, true, Epi::AddF32, a, W(base + 3), x, nullptr, M, D.d, D.F,
-                         D.F, D.F, D.d, 0, s));
+                         D.d, D.d, D.F, 0, s, rinv2));
+    HIPCHECK(gemm_simple(dt, true, true, Epi::AddF32Xs, a, W(base + 3), x, nullptr, M, D.d, D.F,
+                         D.F, D.F, D.d, 0, s, nullptr, xnext, ssq));
+    HIPCHECK(nc::ssq_rinv(ssq, (int)M, D.d / 64, D.d, eps, rnext, s));
   }
-  HIPCHECK(nc::rmsnorm_fwd(dt, x, (int)M, D.d, eps, xf, rinvf, s));
 
   // ---------------- lm_head + softcap cross-entropy, by row chunks ----------------
   const int64_t Mc = chunk_rows(D);
@@ -379,9 +400,11 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
     const int64_t mc = std::min<int64_t>(Mc, M - r0);
     const char* xfc = static_cast<const char*>(xf) + r0 * D.d * e;
     HIPCHECK(gemm_simple(dt, true, true, Epi::StoreT, xfc, W(iU), logits, nullptr, mc, D.V,
-                         D.d, D.d, D.d, D.V, 0, s));
+                         D.d, D.d, D.d, D.V, 0, s, rinvf + r0));
+    // the logit gradient carries the final norm's row scale, so dxf and dU
+    // below come out right from the unnormalised xf
     HIPCHECK(nc::softcap_ce(dt, logits, targets + r0, (int)mc, D.V, cfg->softcap, w,
-                            loss_rows + r0, bwd ? dlog : nullptr, status, s));
+                            loss_rows + r0, bwd ? dlog : nullptr, status, s, rinvf + r0));
     if (bwd) {
       // dxf = dlog . U (U read K-strided: contraction over its rows), split
       // over the vocabulary when the chunk alone would not fill the chip
@@ -420,7 +443,7 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
   void* dout = at<char>(ws, P.dout);
   float* delta = at<float>(ws, P.delta);
   float* partial = at<float>(ws, P.partial);
-  HIPCHECK(nc::rmsnorm_bwd(dt, dxf, xf, rinvf, (int)M, D.d, dx, false, g, s));
+  HIPCHECK(nc::rmsnorm_bwd(dt, dxf, xf, rinvf, (int)M, D.d, dx, false, g, s, true));
   const WgradPlan pQ = wgrad_plan(dt, D.Q, D.d, M), pO = wgrad_plan(dt, D.d, D.d, M);
   const WgradPlan pFC = wgrad_plan(dt, D.F, D.d, M), pPR = wgrad_plan(dt, D.d, D.F, M);
   void* dh = at<char>(ws, P.dh);
@@ -435,24 +458,27 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
     void* a = at<char>(ws, A.a);
     // MLP: x_out = x_mid + relu(h2 Wfc^T)^2 Wpr^T
     HIPCHECK(wgrad(dt, g, a, G(base + 3), partial, M, D.d, D.F, pPR, s, accumulate));
+    // d(pre-activation) times the MLP norm's row scale: with h2 unnormalised,
+    // the weight gradient and the norm input gradient below then come out right
     HIPCHECK(gemm_simple(dt, true, false, Epi::Relu2Bwd, g, W(base + 3), dbig, a, M, D.F, D.d,
-                         D.d, D.F, D.F, D.F, s));
+                         D.d, D.F, D.F, D.F, s, at<float>(ws, A.rinv2)));
     HIPCHECK(wgrad(dt, dbig, h2, G(base + 2), partial, M, D.F, D.d, pFC, s, accumulate));
     HIPCHECK(gemm_simple(dt, true, false, Epi::StoreT, dbig, W(base + 2), dh, nullptr, M, D.d,
                          D.F, D.F, D.d, D.d, 0, s));
-    HIPCHECK(nc::rmsnorm_bwd(dt, dh, h2, at<float>(ws, A.rinv2), Mi, D.d, dx, true, g, s));
+    HIPCHECK(nc::rmsnorm_bwd(dt, dh, h2, at<float>(ws, A.rinv2), Mi, D.d, dx, true, g, s, true));
     // attention: x_mid = x_in + o Wo^T
     HIPCHECK(wgrad(dt, g, o, G(base + 1), partial, M, D.d, D.d, pO, s, accumulate));
     HIPCHECK(gemm_simple(dt, true, false, Epi::StoreT, g, W(base + 1), dout, nullptr, M, D.d, D.d,
                          D.d, D.d, D.d, 0, s));
+    // every gradient of qkv carries the attention norm's row scale (h is unnormalised)
     HIPCHECK(nc::attn_bwd(dt, qkv, D.Q, o, dout, at<float>(ws, A.lse), delta, D.B, D.T, D.H, dbig,
-                          D.Q, at<float>(ws, P.attn_part), s));
+                          D.Q, at<float>(ws, P.attn_part), s, at<float>(ws, A.rinv1)));
     HIPCHECK(nc::rope_qknorm_bwd(dt, dbig, D.Q, qkv, D.Q, Mi, D.T, D.H, cs,
-                                 at<float>(ws, A.rqk), s));
+                                 at<float>(ws, A.rqk), s, at<float>(ws, A.rinv1)));
     HIPCHECK(wgrad(dt, dbig, h, G(base + 0), partial, M, D.Q, D.d, pQ, s, accumulate));
     HIPCHECK(gemm_simple(dt, true, false, Epi::StoreT, dbig, W(base + 0), dh, nullptr, M, D.d,
                          D.Q, D.Q, D.d, D.d, 0, s));
-    HIPCHECK(nc::rmsnorm_bwd(dt, dh, h, at<float>(ws, A.rinv1), Mi, D.d, dx, true, g, s));
+    HIPCHECK(nc::rmsnorm_bwd(dt, dh, h, at<float>(ws, A.rinv1), Mi, D.d, dx, true, g, s, true));
   }
   nc::EmbedBwdScratch es;
   es.counts = at<int32_t>(ws, P.counts);
