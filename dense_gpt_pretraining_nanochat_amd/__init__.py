@@ -114,6 +114,8 @@ _SIGS = {
     "nc_op_attn_bwd": [_I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P],
     "nc_op_softcap_ce": [_I32, _P, _P, _I32, _I32, _F32, _F32, _P, _P, _P, _P],
     "nc_op_attn_bwd_noalloc": [_I32, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P],
+    "nc_op_attn_bwd_ds_bytes": [_I32, _I32, _I32, _I32],
+    "nc_op_attn_bwd_stored_ds": [_I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P],
 }
 
 
@@ -138,7 +140,8 @@ def lib():
             f = getattr(L, name)
             f.argtypes = args
             f.restype = {"nc_status_string": ctypes.c_char_p,
-                         "nc_op_attn_bwd_scratch_bytes": ctypes.c_uint64}.get(name, ctypes.c_int)
+                         "nc_op_attn_bwd_scratch_bytes": ctypes.c_uint64,
+                         "nc_op_attn_bwd_ds_bytes": ctypes.c_uint64}.get(name, ctypes.c_int)
         _lib = L
     return _lib
 
@@ -412,6 +415,24 @@ def nc_op_attn_bwd(dtype, qkv, o, dout, lse, delta, B, T, H, dqkv, scratch=None,
         scratch = torch.empty(nc_op_attn_bwd_scratch_bytes(B, T), dtype=torch.uint8, device="cuda")
     _check(lib().nc_op_attn_bwd(_dt(dtype), _ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
                                 B, T, H, _ptr(dqkv), _ptr(scratch), _stream(stream)), "nc_op_attn_bwd")
+
+
+def nc_op_attn_bwd_ds_bytes(dtype, B, T, H) -> int:
+    return int(lib().nc_op_attn_bwd_ds_bytes(_dt(dtype), B, T, H))
+
+
+def nc_op_attn_bwd_stored_ds(dtype, qkv, o, dout, lse, delta, B, T, H, dqkv, scratch=None, ds=None,
+                             stream=None):
+    """scratch as for nc_op_attn_bwd; ds: a device buffer of nc_op_attn_bwd_ds_bytes
+    bytes (allocated here when omitted)."""
+    import torch
+    if scratch is None and nc_op_attn_bwd_scratch_bytes(B, T) > 0:
+        scratch = torch.empty(nc_op_attn_bwd_scratch_bytes(B, T), dtype=torch.uint8, device="cuda")
+    if ds is None:
+        ds = torch.empty(nc_op_attn_bwd_ds_bytes(dtype, B, T, H), dtype=torch.uint8, device="cuda")
+    _check(lib().nc_op_attn_bwd_stored_ds(_dt(dtype), _ptr(qkv), _ptr(o), _ptr(dout), _ptr(lse), _ptr(delta),
+                                          B, T, H, _ptr(dqkv), _ptr(scratch), _ptr(ds), _stream(stream)),
+           "nc_op_attn_bwd_stored_ds")
 
 
 def nc_op_attn_bwd_noalloc(dtype, qkv, o, dout, lse, B, T, H, dqkv, stream=None):

@@ -521,6 +521,207 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_kernel(
 }
 
 // --------------------------------------------------------------------------
+// delta[b, h, t] = <dO, O> of each query row and head: 16 lanes per row of 128,
+// 16-byte loads (the dK/dV kernel needs it before any dQ work when dQ is
+// formed from the stored dS).
+// --------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o,
+                                                         const T* __restrict__ dout, int Tn,
+                                                         int H, size_t total,
+                                                         float* __restrict__ delta) {
+  typedef AttnTypes<T> A;
+  constexpr int PER = D / 16;                  // elements per lane
+  const size_t w = blockIdx.x * 16ull + (threadIdx.x >> 4);
+  const int sl = threadIdx.x & 15;
+  if (w >= total) return;
+  const size_t m = w / H;
+  const int h = (int)(w % H);
+  const size_t off = m * (size_t)(H * D) + h * D + sl * PER;
+  float acc = 0.f;
+#pragma unroll
+  for (int v = 0; v < PER / A::VEC; ++v) {
+    const typename A::V a = *reinterpret_cast<const typename A::V*>(o + off + v * A::VEC);
+    const typename A::V c = *reinterpret_cast<const typename A::V*>(dout + off + v * A::VEC);
+#pragma unroll
+    for (int e = 0; e < A::VEC; ++e) acc = fmaf(to_f32(c[e]), to_f32(a[e]), acc);
+  }
+  acc = lane16_sum(acc);
+  if (sl == 0) {
+    const size_t bb = m / Tn, t = m % Tn;
+    delta[(bb * H + h) * Tn + t] = acc;
+  }
+}
+
+// Stored dS^T: within each 64-query block of a key row, lane group lg of the
+// writing wavefront keeps its 16 values (queries 16c + 4lg + r, c and r < 4)
+// as 16-byte chunks lg, 4 + lg, ... (bf16: 8 values per chunk, fp32: 4), so
+// query q = 16c + 4lg + r sits at position chunk * E + e with
+// idx = 4c + r, chunk = (idx / E) * 4 + lg, e = idx % E.
+template <typename T>
+__device__ __forceinline__ int ds_chunk_pos(int c, int lg, int r) {
+  constexpr int E = Vec16<T>::N;
+  const int idx = 4 * c + r;
+  return ((idx / E) * 4 + lg) * E + idx % E;
+}
+
+// B operand of dQ^T += K^T dS^T from an LDS copy of stored dS^T rows (keys
+// k0.., 64 queries per row in the order above): the same fragment that
+// CFrag<T>::read gives for plain rows, query tile c (16 queries) of the block.
+template <typename T> struct DsFrag;
+template <> struct DsFrag<bf16> {
+  __device__ __forceinline__ static bf16x8 read(const bf16* X, int stride, int k0, int c, int lane) {
+    // source lane 4j + q names row k0 + j, the four values of queries
+    // 16c + 4q .. +3, which are consecutive positions
+    const int g = lane >> 4, s = lane & 15;
+    const bf16* p0 = X + (k0 + 4 * g + (s >> 2)) * stride + ds_chunk_pos<bf16>(c, s & 3, 0);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p0);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0 + 16 * stride));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, ab);
+  }
+};
+template <> struct DsFrag<float> {
+  __device__ __forceinline__ static f32x4 read(const float* X, int stride, int k0, int c, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const float* p = X + (k0 + 4 * g) * stride + ds_chunk_pos<float>(c, i >> 2, i & 3);
+    return f32x4{p[0], p[stride], p[2 * stride], p[3 * stride]};
+  }
+};
+
+// --------------------------------------------------------------------------
+// dQ from the stored dS: dQ^T[d][t] = sum_u K^T[d][u] dS^T[u][t] / sqrt(128),
+// one product instead of the three of attn_bwd_dq_kernel (which recomputes S
+// and dP). Same workgroup shape: 64 query tokens x 2 heads, one wavefront per
+// (head, 32 tokens), 32-key tiles; each tile stages K [32 x 128] and the two
+// heads' dS^T [32 keys x 64 queries] in LDS (registers one tile ahead), and
+// both operands are read with the LDS transpose read (contraction over rows).
+// dS^T was written for every (key, query) pair this reads, zero where the
+// causal mask removes it, so no mask is applied here; tiles wholly past a
+// wavefront's queries are skipped.
+// --------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(const T* __restrict__ qkv, int ldq,
+                                                                const T* __restrict__ ds, int Tn,
+                                                                int H, T* __restrict__ dqkv,
+                                                                int ldd) {
+  typedef AttnTypes<T> A;
+  typedef typename A::V V;
+  constexpr int BK = BKVQ;                      // keys per tile
+  constexpr int KT = BK * A::VSTR;              // K tile (elements)
+  constexpr int DSTR = FQB + (sizeof(T) == 2 ? 2 * A::VEC : A::VEC);   // dS^T row: 64 queries + pad
+  constexpr int DT = BK * DSTR;                 // dS^T tile of one head
+  constexpr int KCH = BK * A::DC;               // 16-byte chunks of a K tile
+  constexpr int DCH = FQB / A::VEC;             // 16-byte chunks of a dS^T row
+  constexpr int CH = KCH + 2 * BK * DCH;        // chunks staged per tile
+  constexpr int NT = 256;
+  static_assert(CH % NT == 0, "whole chunks per thread");
+  constexpr int PF = CH / NT;
+  __shared__ __align__(16) T Ks[2 * KT];
+  __shared__ __align__(16) T Ds[2 * 2 * DT];   // [buffer][head of the pair]
+
+  const QBlock qbk = qblock_of(blockIdx.x, Tn / FQB, (H + 1) / 2);
+  const int tb0 = qbk.qb * FQB;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int hl = wave & 1;
+  const int h = 2 * qbk.hg + hl;
+  const int tq0 = tb0 + BQ * (wave >> 1);
+  const bool active = h < H;
+  const size_t row0 = (size_t)qbk.b * Tn;
+  const int Tpad = (Tn + BKW - 1) / BKW * BKW;
+  // for an odd head count the last pair's second head reads the first's rows (never stored)
+  const int h1 = min(2 * qbk.hg + 1, H - 1);
+  const T* ds0 = ds + ((size_t)qbk.b * H + 2 * qbk.hg) * Tpad * Tn + tb0;
+  const T* ds1 = ds + ((size_t)qbk.b * H + h1) * Tpad * Tn + tb0;
+  const T* kbase = qkv + row0 * ldq + H * D;
+
+  auto src_of = [&](int kv0, int c) -> const T* {
+    if (c < KCH) return kbase + (size_t)(kv0 + c / A::DC) * ldq + (c % A::DC) * A::VEC;
+    c -= KCH;
+    const int j = c / (BK * DCH), r = (c / DCH) % BK, dc = c % DCH;
+    return (j ? ds1 : ds0) + (size_t)(kv0 + r) * Tn + dc * A::VEC;
+  };
+  auto dst_of = [&](int buf, int c) -> T* {
+    if (c < KCH) return Ks + buf * KT + (c / A::DC) * A::VSTR + (c % A::DC) * A::VEC;
+    c -= KCH;
+    const int j = c / (BK * DCH), r = (c / DCH) % BK, dc = c % DCH;
+    return Ds + (buf * 2 + j) * DT + r * DSTR + dc * A::VEC;
+  };
+  typedef V Regs[PF];
+  auto load = [&](int kv0, Regs& reg) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) reg[i] = *reinterpret_cast<const V*>(src_of(kv0, tid + i * NT));
+  };
+  auto store = [&](int buf, const Regs& reg) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) *reinterpret_cast<V*>(dst_of(buf, tid + i * NT)) = reg[i];
+  };
+
+  f32x4 dq[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dq[i][0] = dq[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int NPT = CFrag<T>::NPT;
+  const int ntiles = (tb0 + FQB) / BK;          // keys 0 .. tb0 + 63 (at least 2 tiles)
+  // Tiles go HBM -> registers two tiles ahead of their use (two register
+  // sets, alternating) -> LDS one tile ahead (two buffers): one tile of
+  // loads in flight per workgroup did not cover the load latency.
+  Regs ra, rb;
+  load(0, ra);
+  store(0, ra);
+  __syncthreads();
+  load(BK, ra);                                 // tile 1
+  if (ntiles > 2) load(2 * BK, rb);             // tile 2
+  // step it computes tile it from buffer it & 1; `nxt` holds tile it + 1
+  auto step = [&](int it, Regs& nxt) {
+    const int kv0 = it * BK;
+    if (kv0 < tq0 + BQ) {                       // some key of the tile is <= a query of the wavefront
+      const T* K = Ks + (it & 1) * KT;
+      const T* Dh = Ds + ((it & 1) * 2 + hl) * DT;
+#pragma unroll
+      for (int kk = 0; kk < BK / 16 / NPT; ++kk) {
+        const V b0 = DsFrag<T>::read(Dh, DSTR, kk * 16 * NPT, (tq0 - tb0) / 16, lane);
+        const V b1 = DsFrag<T>::read(Dh, DSTR, kk * 16 * NPT, (tq0 - tb0) / 16 + 1, lane);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const V ka = CFrag<T>::read(K, A::VSTR, kk * 16 * NPT, dt * 16, lane);   // K^T
+          Mma<T>::run(dq[dt][0], ka, b0);
+          Mma<T>::run(dq[dt][1], ka, b1);
+        }
+      }
+    }
+    if (it + 1 < ntiles) {
+      // buffer (it + 1) & 1 was last read in step it - 1, before the barrier that ended it
+      store((it + 1) & 1, nxt);
+      if (it + 3 < ntiles) load((it + 3) * BK, nxt);
+      __syncthreads();
+    }
+  };
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    step(it, ra);
+    step(it + 1, rb);
+  }
+  if (it < ntiles) step(it, ra);
+  if (!active) return;
+  const float scale = 1.0f / sqrtf((float)D);
+  const int l16 = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int t = tq0 + c * 16 + l16;
+    T* dst = dqkv + (row0 + t) * ldd + h * D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      typename A::T4 w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) w[r] = from_f32<T>(dq[dt][c][r] * scale);
+      *reinterpret_cast<typename A::T4*>(dst + dt * 16 + lg * 4) = w;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
 // backward, dK and dV: one workgroup per 128-key block (and query chunk), 8
 // wavefronts x 16 keys, looping over the chunk's 64-token query blocks (from
 // the last one down) and, inside each, every head.
@@ -546,11 +747,16 @@ __device__ inline void dkv_item(int Tn, int i, int* kblk, int* chunk) {
 // and dV (times rs of its row, when rs is given) go straight into the key and
 // value columns of dqkv; otherwise each chunk leaves an fp32 partial for
 // attn_dkv_reduce_kernel.
-template <typename T, bool DIRECT>
+// STORE_DS: the workgroup also writes the dS^T values it forms (its 128 keys x
+// its query chunk, every head) in the activation type into ds, laid out
+// [b][h][key < Tpad][query < Tn] (Tpad = T rounded up to 128, so a wavefront
+// whose keys lie past T writes into pad rows instead of branching), for the
+// dQ kernel that reads them instead of recomputing S and dP.
+template <typename T, bool DIRECT, bool STORE_DS>
 __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
     const T* __restrict__ qkv, int ldq, const T* __restrict__ dout, const float* __restrict__ lse,
     const float* __restrict__ delta, int B, int Tn, int H, float* __restrict__ part,
-    T* __restrict__ dqkv, int ldd, const float* __restrict__ rs) {
+    T* __restrict__ dqkv, int ldd, const float* __restrict__ rs, T* __restrict__ ds) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
   constexpr int SQ = BQK;                      // query rows per step
@@ -695,6 +901,25 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
     };
     if (tq0 < key0 + 16) softmax(std::true_type{});
     else softmax(std::false_type{});
+    if constexpr (STORE_DS) {
+      // row key0 + l16 of dS^T: the lane holds queries tq0 + 16c + 4lg + r
+      // (c, r < 4) and writes them as 16-byte chunks in the order of
+      // ds_chunk_pos (each store instruction then covers 64 contiguous bytes
+      // of every row it touches)
+      const int Tpad = (Tn + BKW - 1) / BKW * BKW;
+      T* drow = ds + (((size_t)b * H + it % H) * Tpad + key0 + l16) * Tn + tq0;
+      constexpr int E16 = A::VEC;                // values per 16-byte chunk
+#pragma unroll
+      for (int v = 0; v < 16 / E16; ++v) {
+        V w;
+#pragma unroll
+        for (int e = 0; e < E16; ++e) {
+          const int idx = v * E16 + e;           // the lane's 16 values in (c, r) order
+          w[e] = from_f32<T>(dsa[0][idx / 4][idx % 4]);
+        }
+        *reinterpret_cast<V*>(drow + (v * 4 + lg) * E16) = w;
+      }
+    }
     // dV^T[d][key] += dO^T[d][rows] P[rows][key];  dK^T += Q^T dS
 #pragma unroll
     for (int kk = 0; kk < NC / NPT; ++kk)
@@ -821,48 +1046,62 @@ size_t attn_bwd_scratch_floats(int B, int T) {
   return nch > 1 ? (size_t)nch * B * T * 2 * D : 0;   // one chunk: dK/dV written directly
 }
 
-hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* o, const void* dout, const float* lse,
-                    float* delta, int B, int T, int H, void* dqkv, int ldd, float* scratch,
-                    hipStream_t s, const float* rs) {
-  if (T % BKV || H < 1 || H > 16) return hipErrorInvalidValue;
-  dim3 gq(B * (T / FQB) * ((H + 1) / 2)), bq(256);
+size_t attn_bwd_ds_elems(int B, int T, int H) {
+  return (size_t)B * H * ((T + BKW - 1) / BKW * BKW) * T;
+}
+
+namespace {
+template <typename T>
+hipError_t attn_bwd_t(const T* q, int ldq, const T* o, const T* d, const float* lse, float* delta, int B, int T_,
+                      int H, T* g, int ldd, float* scratch, const float* rs, T* ds, hipStream_t s) {
+  dim3 gq(B * (T_ / FQB) * ((H + 1) / 2)), bq(256);
   int items = 0;
-  for (int kb = 0; kb < (T + BKW - 1) / BKW; ++kb) items += dkv_chunks(T, kb);
+  for (int kb = 0; kb < (T_ + BKW - 1) / BKW; ++kb) items += dkv_chunks(T_, kb);
   dim3 gk(B * items), bk(DKW_THREADS);
-  const bool direct = dkv_chunks(T, 0) == 1;     // every key block in one work item
-  const size_t M = (size_t)B * T;
+  const bool direct = dkv_chunks(T_, 0) == 1;     // every key block in one work item
+  const size_t M = (size_t)B * T_;
   dim3 gr((unsigned)((M + 3) / 4)), br(256);
-  if (t == DType::BF16) {
-    const bf16* q = static_cast<const bf16*>(qkv);
-    const bf16* d = static_cast<const bf16*>(dout);
-    bf16* g = static_cast<bf16*>(dqkv);
-    // dQ first: it writes the delta rows that dK/dV reads
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<bf16>, gq, bq, 0, s, q, ldq, static_cast<const bf16*>(o), d, lse,
-                       delta, T, H, g, ldd);
+  if (ds) {
+    // delta first, then dK/dV (which also stores dS^T), then dQ from dS
+    const size_t total = M * H;
+    hipLaunchKernelGGL(attn_delta_kernel<T>, dim3((unsigned)((total + 15) / 16)), dim3(256), 0, s, o, d, T_, H,
+                       total, delta);
     if (direct) {
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<bf16, true>), gk, bk, 0, s, q, ldq, d, lse, delta, B, T,
-                         H, scratch, g, ldd, rs);
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, true, true>), gk, bk, 0, s, q, ldq, d, lse, delta, B, T_, H,
+                         scratch, g, ldd, rs, ds);
     } else {
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<bf16, false>), gk, bk, 0, s, q, ldq, d, lse, delta, B,
-                         T, H, scratch, g, ldd, rs);
-      hipLaunchKernelGGL(attn_dkv_reduce_kernel<bf16>, gr, br, 0, s, scratch, B, T, H, g, ldd, rs);
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, false, true>), gk, bk, 0, s, q, ldq, d, lse, delta, B, T_, H,
+                         scratch, g, ldd, rs, ds);
+      hipLaunchKernelGGL(attn_dkv_reduce_kernel<T>, gr, br, 0, s, scratch, B, T_, H, g, ldd, rs);
     }
+    hipLaunchKernelGGL(attn_bwd_dq_ds_kernel<T>, gq, bq, 0, s, q, ldq, static_cast<const T*>(ds), T_, H, g, ldd);
+    return hipGetLastError();
+  }
+  // dQ first: it writes the delta rows that dK/dV reads
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<T>, gq, bq, 0, s, q, ldq, o, d, lse, delta, T_, H, g, ldd);
+  if (direct) {
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, true, false>), gk, bk, 0, s, q, ldq, d, lse, delta, B, T_, H,
+                       scratch, g, ldd, rs, static_cast<T*>(nullptr));
   } else {
-    const float* q = static_cast<const float*>(qkv);
-    const float* d = static_cast<const float*>(dout);
-    float* g = static_cast<float*>(dqkv);
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<float>, gq, bq, 0, s, q, ldq, static_cast<const float*>(o), d, lse,
-                       delta, T, H, g, ldd);
-    if (direct) {
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<float, true>), gk, bk, 0, s, q, ldq, d, lse, delta, B,
-                         T, H, scratch, g, ldd, rs);
-    } else {
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<float, false>), gk, bk, 0, s, q, ldq, d, lse, delta,
-                         B, T, H, scratch, g, ldd, rs);
-      hipLaunchKernelGGL(attn_dkv_reduce_kernel<float>, gr, br, 0, s, scratch, B, T, H, g, ldd, rs);
-    }
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, false, false>), gk, bk, 0, s, q, ldq, d, lse, delta, B, T_, H,
+                       scratch, g, ldd, rs, static_cast<T*>(nullptr));
+    hipLaunchKernelGGL(attn_dkv_reduce_kernel<T>, gr, br, 0, s, scratch, B, T_, H, g, ldd, rs);
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* o, const void* dout, const float* lse,
+                    float* delta, int B, int T, int H, void* dqkv, int ldd, float* scratch,
+                    hipStream_t s, const float* rs, void* ds) {
+  if (T % BKV || H < 1 || H > 16) return hipErrorInvalidValue;
+  if (t == DType::BF16)
+    return attn_bwd_t<bf16>(static_cast<const bf16*>(qkv), ldq, static_cast<const bf16*>(o),
+                            static_cast<const bf16*>(dout), lse, delta, B, T, H, static_cast<bf16*>(dqkv), ldd,
+                            scratch, rs, static_cast<bf16*>(ds), s);
+  return attn_bwd_t<float>(static_cast<const float*>(qkv), ldq, static_cast<const float*>(o),
+                           static_cast<const float*>(dout), lse, delta, B, T, H, static_cast<float*>(dqkv), ldd,
+                           scratch, rs, static_cast<float*>(ds), s);
 }
 
 // ---------------------------------------------------------------------------

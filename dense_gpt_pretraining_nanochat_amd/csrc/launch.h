@@ -124,10 +124,14 @@ hipError_t attn_fwd(DType t, const void* qkv, int ldq, int B, int T, int H, void
 // (none, and scratch may be null, when T <= 2048: dK/dV are written directly)
 size_t attn_bwd_scratch_floats(int B, int T);
 // rs (may be null): dV of key row m is multiplied by rs[m] (the row scale of the
-// RMSNorm folded into the QKV product; rope_qknorm_bwd applies it to dQ and dK)
+// RMSNorm folded into the QKV product; rope_qknorm_bwd applies it to dQ and dK).
+// ds (may be null): attn_bwd_ds_elems(B, T, H) elements of T; when given, delta is
+// computed first, the dK/dV kernel stores the dS it forms there and dQ is one
+// product over it (instead of a dQ kernel that recomputes S and dP).
+size_t attn_bwd_ds_elems(int B, int T, int H);
 hipError_t attn_bwd(DType t, const void* qkv, int ldq, const void* o, const void* dout, const float* lse,
                     float* delta, int B, int T, int H, void* dqkv, int ldd, float* scratch,
-                    hipStream_t s, const float* rs = nullptr);
+                    hipStream_t s, const float* rs = nullptr, void* ds = nullptr);
 // Device address (current device) of the library's fixed attention-backward
 // scratch array of kAttnFixedScratchBytes, for the entry point that allocates
 // nothing; looked up once per device.

@@ -174,7 +174,7 @@ struct Plan {
   uint64_t status, cs, x, rinv0, xf, rinvf, ssq, loss_rows, logits;
   std::vector<LayerActs> acts;
   // backward only
-  uint64_t dx, g, dh, dbig, dout, delta, partial, attn_part, counts, offsets, cursor, list;
+  uint64_t dx, g, dh, dbig, dout, delta, partial, attn_part, attn_ds, counts, offsets, cursor, list;
   uint64_t item_off, part_off, item_bucket, scan_blocks;
   uint64_t total;
 };
@@ -238,6 +238,11 @@ Plan plan_of(const Dims& D, bool bwd, bool record = false) {
     if (sx > 1) part = std::max<uint64_t>(part, (uint64_t)sx * Mc * D.d);
     p.partial = take_named("partial", part * 4);
     p.attn_part = take_named("attn_part", nc::attn_bwd_scratch_floats(D.B, D.T) * 4);
+    // dS^T of one layer's attention backward: the logits chunk is free by then
+    // (the lm_head and loss finish before the blocks' backward), so it holds
+    // dS^T when large enough (every workload here), otherwise a piece of its own
+    const uint64_t ds_bytes = nc::attn_bwd_ds_elems(D.B, D.T, D.H) * e;
+    p.attn_ds = ds_bytes <= Mc * D.V * e ? p.logits : take_named("attn_ds", ds_bytes);
     p.counts = take_named("counts", (uint64_t)(D.V + 1) * 4);
     p.offsets = take_named("offsets", (uint64_t)(D.V + 1) * 4);
     p.cursor = take_named("cursor", (uint64_t)D.V * 4);
@@ -472,7 +477,8 @@ int run_step(const nc_config* cfg, const void* params, const int32_t* tokens,
                          D.d, D.d, D.d, 0, s));
     // every gradient of qkv carries the attention norm's row scale (h is unnormalised)
     HIPCHECK(nc::attn_bwd(dt, qkv, D.Q, o, dout, at<float>(ws, A.lse), delta, D.B, D.T, D.H, dbig,
-                          D.Q, at<float>(ws, P.attn_part), s, at<float>(ws, A.rinv1)));
+                          D.Q, at<float>(ws, P.attn_part), s, at<float>(ws, A.rinv1),
+                          at<char>(ws, P.attn_ds)));
     HIPCHECK(nc::rope_qknorm_bwd(dt, dbig, D.Q, qkv, D.Q, Mi, D.T, D.H, cs,
                                  at<float>(ws, A.rqk), s, at<float>(ws, A.rinv1)));
     HIPCHECK(wgrad(dt, dbig, h, G(base + 0), partial, M, D.Q, D.d, pQ, s, accumulate));
@@ -1418,6 +1424,25 @@ int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* do
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int ld = H * 128 + 256;
   HIPCHECK(nc::attn_bwd(dt_of(dtype), qkv, ld, o, dout, lse, delta, B, T, H, dqkv, ld, scratch, s));
+  return NC_OK;
+}
+
+uint64_t nc_op_attn_bwd_ds_bytes(int32_t dtype, int32_t B, int32_t T, int32_t H) {
+  if (bad_dtype(dtype) || B <= 0 || T < 64 || T % 64 || H < 1 || H > 16) return 0;
+  return (uint64_t)nc::attn_bwd_ds_elems(B, T, H) * (dtype == NC_BF16 ? 2 : 4);
+}
+
+int nc_op_attn_bwd_stored_ds(int32_t dtype, const void* qkv, const void* o, const void* dout,
+                             const float* lse, float* delta, int32_t B, int32_t T, int32_t H, void* dqkv,
+                             float* scratch, void* ds, void* stream) {
+  if (bad_dtype(dtype)) return NC_ERR_ARG;
+  if (!qkv || !o || !dout || !lse || !delta || !dqkv || !ds) return NC_ERR_NULL;
+  if (B <= 0 || T < 64 || T % 64 || H < 1 || H > 16) return NC_ERR_ARG;
+  if (!scratch && nc::attn_bwd_scratch_floats(B, T) > 0) return NC_ERR_NULL;
+  if (misaligned(ds)) return NC_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int ld = H * 128 + 256;
+  HIPCHECK(nc::attn_bwd(dt_of(dtype), qkv, ld, o, dout, lse, delta, B, T, H, dqkv, ld, scratch, s, nullptr, ds));
   return NC_OK;
 }
 

@@ -106,6 +106,11 @@ def test_argument_checks_before_any_launch():
     assert nc.nc_op_attn_bwd_scratch_bytes(32, 2048) == 0
     assert nc.nc_op_attn_bwd_scratch_bytes(1, 2112) == 2 * 2112 * 256 * 4
     assert nc.nc_op_attn_bwd_scratch_bytes(2, 4160) == 3 * 2 * 4160 * 256 * 4
+    # stored dS: keys padded to a multiple of 128, elements of the dtype
+    assert nc.nc_op_attn_bwd_ds_bytes("bf16", 32, 2048, 10) == 32 * 10 * 2048 * 2048 * 2
+    assert nc.nc_op_attn_bwd_ds_bytes("f32", 2, 192, 3) == 2 * 3 * 256 * 192 * 4
+    assert nc.nc_op_attn_bwd_ds_bytes("bf16", 1, 100, 1) == 0
+    assert L.nc_op_attn_bwd_stored_ds(1, p(a), p(a), p(a), p(a), p(a), 1, 128, 1, p(a), None, None, None) == -3
     assert L.nc_op_attn_bwd(1, p(a), p(a), p(a), p(a), p(a), 1, 2112, 2, p(a), None, None) == -3
 
 
@@ -167,8 +172,12 @@ def test_lm_chunk_rows_bound_the_workspace():
         nc.nc_set_lm_chunk_rows(0)
     assert nc.nc_workspace_bytes(c4, True) == small
     assert small < 33 * 2 ** 30
+    # the attention backward's stored dS (2.5 GiB at depth 20) lives in the
+    # 4 GiB logits chunk, free by then; a 16,384-row chunk (2 GiB) is too small
+    # for it, so dS takes a piece of its own there
     nc.nc_set_lm_chunk_rows(16384)
-    assert nc.nc_workspace_bytes(c4, True) < small
+    ds = nc.nc_op_attn_bwd_ds_bytes("bf16", 32, 2048, 10)
+    assert abs(nc.nc_workspace_bytes(c4, True) - (small - 2 ** 31 + ds)) <= 4096
     nc.nc_set_lm_chunk_rows(0)
     # rows fewer than the chunk: one chunk of the whole batch
     assert nc.nc_lm_chunk_rows(_cfg("C2")) == 4096
@@ -176,7 +185,9 @@ def test_lm_chunk_rows_bound_the_workspace():
     b16 = nc.nc_workspace_bytes(nc.nc_config_from_depth(20, 65536, 2048, 16, 1), True)
     b32 = nc.nc_workspace_bytes(nc.nc_config_from_depth(20, 65536, 2048, 32, 1), True)
     b64 = nc.nc_workspace_bytes(nc.nc_config_from_depth(20, 65536, 2048, 64, 1), True)
-    assert abs((b64 - b32) - 2 * (b32 - b16)) <= 2 ** 26
+    # (at B = 64 the stored dS, 5 GiB, outgrows the 4 GiB logits chunk and takes its own piece)
+    ds64 = nc.nc_op_attn_bwd_ds_bytes("bf16", 64, 2048, 10)
+    assert abs((b64 - ds64 - b32) - 2 * (b32 - b16)) <= 2 ** 26
 
 
 def test_gemm_schedule_switch_checks_its_argument():

@@ -267,14 +267,18 @@ def _attn_inputs(rng, B, T, H, dtype):
     return _as(z.reshape(M, Q), dtype)
 
 
+@pytest.mark.parametrize("path", ["recompute", "stored_ds"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("B,T,H", [(2, 64, 1), (1, 256, 3), (2, 192, 10), (1, 128, 13),
                                    (1, 1024, 2), (1, 2048, 10), (1, 2560, 2), (1, 4160, 1)])
-def test_attention_fwd_bwd(dtype, B, T, H):
+def test_attention_fwd_bwd(dtype, B, T, H, path):
     """Up to T = 2048 at the depth-20 head count (one dK/dV work item per key
     block), and beyond: T = 2560 and 4160 give key blocks with two and three
     2048-token query chunks, whose partials meet in the fixed-order reduction
-    (the last chunk and, at 4160, the last key block ragged)."""
+    (the last chunk and, at 4160, the last key block ragged). Both backward
+    forms: dQ recomputing S and dP, and dQ from the dS the dK/dV pass stores
+    (T = 192 and 4160 leave a key block half past T: its idle wavefronts write
+    into the buffer's pad rows)."""
     rng = np.random.default_rng(B + T + H)
     d = 128 * H
     Q = d + 256
@@ -304,8 +308,14 @@ def test_attention_fwd_bwd(dtype, B, T, H):
     do, do64 = _as(rng.standard_normal((M, d)), dtype)
     dqkv = _empty((M, Q), dtype)
     delta = torch.zeros((B, H, T), dtype=torch.float32, device="cuda")
-    nc.nc_op_attn_bwd(dtype, qkv, o, do, lse, delta, B, T, H, dqkv)
+    if path == "recompute":
+        nc.nc_op_attn_bwd(dtype, qkv, o, do, lse, delta, B, T, H, dqkv)
+    else:
+        nc.nc_op_attn_bwd_stored_ds(dtype, qkv, o, do, lse, delta, B, T, H, dqkv)
     torch.cuda.synchronize()
+    # delta = <dO, O> per row and head, as both forms write it
+    dref = np.einsum("bthd,bthd->bht", do64.reshape(B, T, H, 128), og)
+    assert np.abs(host64(delta) - dref).max() <= 1e-3 * max(1.0, np.abs(dref).max())
     g = host64(dqkv).reshape(B, T, Q)
     for b in range(B):
         dq, dk, dv = oracle.causal_mqa_bwd(z[b, :, :d].reshape(T, H, 128), z[b, :, d:d + 128],
