@@ -557,12 +557,13 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T* __restrict__ o
 // writing wavefront keeps its 16 values (queries 16c + 4lg + r, c and r < 4)
 // as 16-byte chunks lg, 4 + lg, ... (bf16: 8 values per chunk, fp32: 4), so
 // query q = 16c + 4lg + r sits at position chunk * E + e with
-// idx = 4c + r, chunk = (idx / E) * 4 + lg, e = idx % E.
+// idx = 4c + r, chunk = (idx / E) * 4 + lg, e = idx % E. Here c counts 16-query
+// tiles from the start of a run of 64-query blocks (block c / 4).
 template <typename T>
 __device__ __forceinline__ int ds_chunk_pos(int c, int lg, int r) {
   constexpr int E = Vec16<T>::N;
-  const int idx = 4 * c + r;
-  return ((idx / E) * 4 + lg) * E + idx % E;
+  const int idx = 4 * (c & 3) + r;
+  return 64 * (c >> 2) + ((idx / E) * 4 + lg) * E + idx % E;
 }
 
 // B operand of dQ^T += K^T dS^T from an LDS copy of stored dS^T rows (keys
@@ -593,55 +594,59 @@ template <> struct DsFrag<float> {
 // --------------------------------------------------------------------------
 // dQ from the stored dS: dQ^T[d][t] = sum_u K^T[d][u] dS^T[u][t] / sqrt(128),
 // one product instead of the three of attn_bwd_dq_kernel (which recomputes S
-// and dP). Same workgroup shape: 64 query tokens x 2 heads, one wavefront per
-// (head, 32 tokens), 32-key tiles; each tile stages K [32 x 128] and the two
-// heads' dS^T [32 keys x 64 queries] in LDS (registers one tile ahead), and
-// both operands are read with the LDS transpose read (contraction over rows).
-// dS^T was written for every (key, query) pair this reads, zero where the
-// causal mask removes it, so no mask is applied here; tiles wholly past a
-// wavefront's queries are skipped.
+// and dP). A workgroup owns 128 query tokens of two heads, one wavefront per
+// (head, 32 tokens); each 32-key tile stages K [32 x 128] once for the eight
+// wavefronts and the two heads' dS^T [32 keys x 128 queries] in LDS
+// (registers two tiles ahead), and both operands are read with the LDS
+// transpose read (contraction over rows). dS^T was written for every
+// (key, query) pair this reads, zero where the causal mask removes it, so no
+// mask is applied here; tiles wholly past a wavefront's queries are skipped.
+// When T is not a multiple of 128 the last block's upper half lies past T:
+// its wavefronts only help stage and store nothing.
 // --------------------------------------------------------------------------
+constexpr int DQB = 128;      // query tokens per dQ-from-dS workgroup
 template <typename T>
-__global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(const T* __restrict__ qkv, int ldq,
-                                                                const T* __restrict__ ds, int Tn,
-                                                                int H, T* __restrict__ dqkv,
-                                                                int ldd) {
+__global__ __launch_bounds__(512, 4) void attn_bwd_dq_ds_kernel(const T* __restrict__ qkv, int ldq,
+                                                             const T* __restrict__ ds, int Tn,
+                                                             int H, T* __restrict__ dqkv,
+                                                             int ldd) {
   typedef AttnTypes<T> A;
   typedef typename A::V V;
   constexpr int BK = BKVQ;                      // keys per tile
   constexpr int KT = BK * A::VSTR;              // K tile (elements)
-  constexpr int DSTR = FQB + (sizeof(T) == 2 ? 2 * A::VEC : A::VEC);   // dS^T row: 64 queries + pad
+  constexpr int DSTR = DQB + (sizeof(T) == 2 ? 2 * A::VEC : A::VEC);   // dS^T row: 128 queries + pad
   constexpr int DT = BK * DSTR;                 // dS^T tile of one head
   constexpr int KCH = BK * A::DC;               // 16-byte chunks of a K tile
-  constexpr int DCH = FQB / A::VEC;             // 16-byte chunks of a dS^T row
+  constexpr int DCH = DQB / A::VEC;             // 16-byte chunks of a dS^T row
   constexpr int CH = KCH + 2 * BK * DCH;        // chunks staged per tile
-  constexpr int NT = 256;
+  constexpr int NT = 512;
   static_assert(CH % NT == 0, "whole chunks per thread");
   constexpr int PF = CH / NT;
   __shared__ __align__(16) T Ks[2 * KT];
   __shared__ __align__(16) T Ds[2 * 2 * DT];   // [buffer][head of the pair]
 
-  const QBlock qbk = qblock_of(blockIdx.x, Tn / FQB, (H + 1) / 2);
-  const int tb0 = qbk.qb * FQB;
+  const QBlock qbk = qblock_of(blockIdx.x, (Tn + DQB - 1) / DQB, (H + 1) / 2);
+  const int tb0 = qbk.qb * DQB;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int hl = wave & 1;
   const int h = 2 * qbk.hg + hl;
   const int tq0 = tb0 + BQ * (wave >> 1);
-  const bool active = h < H;
+  const bool active = h < H && tq0 < Tn;
   const size_t row0 = (size_t)qbk.b * Tn;
-  const int Tpad = (Tn + BKW - 1) / BKW * BKW;
+  const int Tpad = (Tn + BKW - 1) / BKW * BKW, nqb = (Tn + DQB - 1) / DQB;
   // for an odd head count the last pair's second head reads the first's rows (never stored)
   const int h1 = min(2 * qbk.hg + 1, H - 1);
-  const T* ds0 = ds + ((size_t)qbk.b * H + 2 * qbk.hg) * Tpad * Tn + tb0;
-  const T* ds1 = ds + ((size_t)qbk.b * H + h1) * Tpad * Tn + tb0;
+  const T* ds0 = ds + (((size_t)qbk.b * H + 2 * qbk.hg) * nqb + qbk.qb) * Tpad * DQB;
+  const T* ds1 = ds + (((size_t)qbk.b * H + h1) * nqb + qbk.qb) * Tpad * DQB;
   const T* kbase = qkv + row0 * ldq + H * D;
 
   auto src_of = [&](int kv0, int c) -> const T* {
     if (c < KCH) return kbase + (size_t)(kv0 + c / A::DC) * ldq + (c % A::DC) * A::VEC;
     c -= KCH;
     const int j = c / (BK * DCH), r = (c / DCH) % BK, dc = c % DCH;
-    return (j ? ds1 : ds0) + (size_t)(kv0 + r) * Tn + dc * A::VEC;
+    // (queries past T, in the last block when T % 128 == 64: never written, never used)
+    return (j ? ds1 : ds0) + (size_t)(kv0 + r) * DQB + dc * A::VEC;
   };
   auto dst_of = [&](int buf, int c) -> T* {
     if (c < KCH) return Ks + buf * KT + (c / A::DC) * A::VSTR + (c % A::DC) * A::VEC;
@@ -663,7 +668,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(const T* __restr
 #pragma unroll
   for (int i = 0; i < 8; ++i) dq[i][0] = dq[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int NPT = CFrag<T>::NPT;
-  const int ntiles = (tb0 + FQB) / BK;          // keys 0 .. tb0 + 63 (at least 2 tiles)
+  const int ntiles = min(tb0 + DQB, Tn) / BK;   // keys 0 .. last query of the block (at least 2 tiles)
   // Tiles go HBM -> registers two tiles ahead of their use (two register
   // sets, alternating) -> LDS one tile ahead (two buffers): one tile of
   // loads in flight per workgroup did not cover the load latency.
@@ -673,16 +678,17 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_ds_kernel(const T* __restr
   __syncthreads();
   load(BK, ra);                                 // tile 1
   if (ntiles > 2) load(2 * BK, rb);             // tile 2
+  const int c0 = (tq0 - tb0) / 16;              // the wavefront's first 16-query tile in the block
   // step it computes tile it from buffer it & 1; `nxt` holds tile it + 1
   auto step = [&](int it, Regs& nxt) {
     const int kv0 = it * BK;
-    if (kv0 < tq0 + BQ) {                       // some key of the tile is <= a query of the wavefront
+    if (active && kv0 < tq0 + BQ) {             // some key of the tile is <= a query of the wavefront
       const T* K = Ks + (it & 1) * KT;
       const T* Dh = Ds + ((it & 1) * 2 + hl) * DT;
 #pragma unroll
       for (int kk = 0; kk < BK / 16 / NPT; ++kk) {
-        const V b0 = DsFrag<T>::read(Dh, DSTR, kk * 16 * NPT, (tq0 - tb0) / 16, lane);
-        const V b1 = DsFrag<T>::read(Dh, DSTR, kk * 16 * NPT, (tq0 - tb0) / 16 + 1, lane);
+        const V b0 = DsFrag<T>::read(Dh, DSTR, kk * 16 * NPT, c0, lane);
+        const V b1 = DsFrag<T>::read(Dh, DSTR, kk * 16 * NPT, c0 + 1, lane);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
           const V ka = CFrag<T>::read(K, A::VSTR, kk * 16 * NPT, dt * 16, lane);   // K^T
@@ -749,9 +755,10 @@ __device__ inline void dkv_item(int Tn, int i, int* kblk, int* chunk) {
 // attn_dkv_reduce_kernel.
 // STORE_DS: the workgroup also writes the dS^T values it forms (its 128 keys x
 // its query chunk, every head) in the activation type into ds, laid out
-// [b][h][key < Tpad][query < Tn] (Tpad = T rounded up to 128, so a wavefront
-// whose keys lie past T writes into pad rows instead of branching), for the
-// dQ kernel that reads them instead of recomputing S and dP.
+// [b][h][query block of 128][key < Tpad][128 queries] (Tpad = T rounded up to
+// 128, so a wavefront whose keys lie past T writes into pad rows instead of
+// branching), for the dQ kernel that reads them instead of recomputing S and
+// dP: each of its workgroups then reads one contiguous stretch.
 template <typename T, bool DIRECT, bool STORE_DS>
 __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
     const T* __restrict__ qkv, int ldq, const T* __restrict__ dout, const float* __restrict__ lse,
@@ -906,8 +913,8 @@ __global__ __launch_bounds__(DKW_THREADS) void attn_bwd_dkv_kernel(
       // (c, r < 4) and writes them as 16-byte chunks in the order of
       // ds_chunk_pos (each store instruction then covers 64 contiguous bytes
       // of every row it touches)
-      const int Tpad = (Tn + BKW - 1) / BKW * BKW;
-      T* drow = ds + (((size_t)b * H + it % H) * Tpad + key0 + l16) * Tn + tq0;
+      const int Tpad = (Tn + BKW - 1) / BKW * BKW, nqb = (Tn + DQB - 1) / DQB;
+      T* drow = ds + ((((size_t)b * H + it % H) * nqb + tq0 / DQB) * Tpad + key0 + l16) * DQB + tq0 % DQB;
       constexpr int E16 = A::VEC;                // values per 16-byte chunk
 #pragma unroll
       for (int v = 0; v < 16 / E16; ++v) {
@@ -1047,7 +1054,7 @@ size_t attn_bwd_scratch_floats(int B, int T) {
 }
 
 size_t attn_bwd_ds_elems(int B, int T, int H) {
-  return (size_t)B * H * ((T + BKW - 1) / BKW * BKW) * T;
+  return (size_t)B * H * ((T + DQB - 1) / DQB) * ((T + BKW - 1) / BKW * BKW) * DQB;
 }
 
 namespace {
@@ -1074,7 +1081,8 @@ hipError_t attn_bwd_t(const T* q, int ldq, const T* o, const T* d, const float* 
                          scratch, g, ldd, rs, ds);
       hipLaunchKernelGGL(attn_dkv_reduce_kernel<T>, gr, br, 0, s, scratch, B, T_, H, g, ldd, rs);
     }
-    hipLaunchKernelGGL(attn_bwd_dq_ds_kernel<T>, gq, bq, 0, s, q, ldq, static_cast<const T*>(ds), T_, H, g, ldd);
+    dim3 gd(B * ((T_ + DQB - 1) / DQB) * ((H + 1) / 2)), bd(512);
+    hipLaunchKernelGGL(attn_bwd_dq_ds_kernel<T>, gd, bd, 0, s, q, ldq, static_cast<const T*>(ds), T_, H, g, ldd);
     return hipGetLastError();
   }
   // dQ first: it writes the delta rows that dK/dV reads

@@ -408,7 +408,7 @@ uint64_t nc_op_attn_bwd_scratch_bytes(int32_t B, int32_t T);
 int nc_op_attn_bwd(int32_t dtype, const void* qkv, const void* o, const void* dout,
                    const float* lse, float* delta, int32_t B, int32_t T, int32_t H, void* dqkv,
                    float* scratch, void* stream);
-/* Bytes of the dS buffer nc_op_attn_bwd_stored_ds needs: B*H*ceil(T/128)*128*T
+/* Bytes of the dS buffer nc_op_attn_bwd_stored_ds needs: B*H*ceil(T/128)^2*128*128
  * elements of the dtype; 0 for invalid arguments. Host only. */
 uint64_t nc_op_attn_bwd_ds_bytes(int32_t dtype, int32_t B, int32_t T, int32_t H);
 /* The same attention backward as nc_op_attn_bwd (same arguments, results equal
@@ -416,8 +416,9 @@ uint64_t nc_op_attn_bwd_ds_bytes(int32_t dtype, int32_t B, int32_t T, int32_t H)
  * multi-query attention; wmrh.cn tutorial 2.3: causal next-token objective),
  * computed the way the training step does it: delta first, then one dK/dV pass
  * that also writes dS^T = (P * (dP - delta))^T in the dtype into ds
- * ([b][h][key][query], keys padded to a multiple of 128; the caller's buffer of
- * nc_op_attn_bwd_ds_bytes bytes, 256-byte aligned, overwritten), then dQ as one
+ * ([b][h][query block of 128][key][128 queries], keys padded to a multiple of
+ * 128; the caller's buffer of nc_op_attn_bwd_ds_bytes bytes, 256-byte aligned,
+ * overwritten), then dQ as one
  * product dS.K over it - instead of a dQ pass that recomputes S and dP.
  * NC_ERR_NULL when ds is NULL. */
 int nc_op_attn_bwd_stored_ds(int32_t dtype, const void* qkv, const void* o, const void* dout,

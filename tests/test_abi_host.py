@@ -108,7 +108,7 @@ def test_argument_checks_before_any_launch():
     assert nc.nc_op_attn_bwd_scratch_bytes(2, 4160) == 3 * 2 * 4160 * 256 * 4
     # stored dS: keys padded to a multiple of 128, elements of the dtype
     assert nc.nc_op_attn_bwd_ds_bytes("bf16", 32, 2048, 10) == 32 * 10 * 2048 * 2048 * 2
-    assert nc.nc_op_attn_bwd_ds_bytes("f32", 2, 192, 3) == 2 * 3 * 256 * 192 * 4
+    assert nc.nc_op_attn_bwd_ds_bytes("f32", 2, 192, 3) == 2 * 3 * 2 * 256 * 128 * 4
     assert nc.nc_op_attn_bwd_ds_bytes("bf16", 1, 100, 1) == 0
     assert L.nc_op_attn_bwd_stored_ds(1, p(a), p(a), p(a), p(a), p(a), 1, 128, 1, p(a), None, None, None) == -3
     assert L.nc_op_attn_bwd(1, p(a), p(a), p(a), p(a), p(a), 1, 2112, 2, p(a), None, None) == -3
