@@ -1,6 +1,8 @@
-// Causal multi-query attention on the CDNA4 matrix cores: forward and a
-// two-kernel backward without atomics (the dQ kernel, which runs first, also
-// computes delta = <dO, O> for the dK/dV kernel).
+// Causal multi-query attention on the CDNA4 matrix cores: forward, and a
+// backward without atomics in one of two forms. With a dS buffer (the
+// training step): delta = <dO, O>, then dK/dV (which also stores the dS it
+// forms), then dQ as one product over the stored dS. Without one: a dQ
+// kernel that recomputes S and dP (and computes delta) runs first, then dK/dV.
 //
 // All query heads share one key/value head (followin.io release article,
 // architecture list: multi-query attention); the objective is next-token
@@ -32,8 +34,10 @@
 // in L2); the work items are issued longest first (early
 // key blocks), which balances them under the causal mask; with one chunk per
 // key block (T <= 2048) the workgroup writes dK and dV itself, otherwise a
-// second pass adds the chunk partials in a fixed order. dQ
-// comes from a kernel shaped like the forward (32-key tiles). No atomics
+// second pass adds the chunk partials in a fixed order. dQ comes either from
+// the stored dS (a bandwidth-bound product: 128 queries x 2 heads per
+// workgroup, K staged once for its eight wavefronts) or from a kernel shaped
+// like the forward that recomputes S and dP (32-key tiles). No atomics
 // anywhere, so the results are bitwise reproducible.
 #include <math.h>
 
