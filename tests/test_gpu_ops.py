@@ -311,7 +311,11 @@ def test_attention_fwd_bwd(dtype, B, T, H, path):
     if path == "recompute":
         nc.nc_op_attn_bwd(dtype, qkv, o, do, lse, delta, B, T, H, dqkv)
     else:
-        nc.nc_op_attn_bwd_stored_ds(dtype, qkv, o, do, lse, delta, B, T, H, dqkv)
+        # the dS buffer starts as all-ones bytes (NaN in both dtypes): every
+        # value the dQ product reads must have been written by this call
+        ds = torch.full((nc.nc_op_attn_bwd_ds_bytes(dtype, B, T, H),), 255, dtype=torch.uint8,
+                        device="cuda")
+        nc.nc_op_attn_bwd_stored_ds(dtype, qkv, o, do, lse, delta, B, T, H, dqkv, ds=ds)
     torch.cuda.synchronize()
     # delta = <dO, O> per row and head, as both forms write it
     dref = np.einsum("bthd,bthd->bht", do64.reshape(B, T, H, 128), og)

@@ -242,3 +242,26 @@ def test_workspace_guards_untouched(name, rows, bwd, lm_chunk):
     assert int(outside.sum().item()) >= 256 * len(pieces)
     changed = (ws[outside] != 0xA5).nonzero()
     assert changed.numel() == 0, [p for p in pieces if p[1] <= int(changed[0]) < p[1] + p[2] + 512]
+
+
+@pytest.mark.parametrize("name,rows", [("C1", 64), ("C2", 1024)])
+def test_no_read_of_unwritten_workspace(name, rows, lm_chunk):
+    """Every workspace value a step reads was written earlier in the same
+    step: with the whole workspace set to all-ones bytes (NaN in fp32 and
+    bf16) before the call, the loss and every gradient are bitwise those of a
+    step on a zeroed workspace (the lm_head chunk then also holds the stored
+    attention dS, whose unwritten pad rows are never read)."""
+    pseed, dseed = SEEDS[name]
+    c = PRESETS[name]
+    lm_chunk(rows)
+    cfg, ocfg, step, p64, tok, tgt = _setup(c.depth, c.vocab_size, c.seq_len, c.batch, c.dtype,
+                                            pseed, dseed, TOKEN_LAW[name])
+    results = []
+    for fill in (0x00, 0xFF):
+        step.ws.fill_(fill)
+        step.forward_backward(dev(tok), dev(tgt))
+        torch.cuda.synchronize()
+        results.append((float(step.loss.item()), step.grads.clone()))
+    assert results[0][0] == results[1][0]
+    assert torch.isfinite(results[1][1]).all()
+    assert torch.equal(results[0][1], results[1][1])
