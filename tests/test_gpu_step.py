@@ -85,6 +85,17 @@ def test_ragged_shapes(dtype):
     _compare(ocfg, step, p64, tok, tgt, dtype)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sequence_past_one_query_chunk(dtype):
+    """T = 2,624 (past the 2,048-token dK/dV query chunk, and 64 past a
+    multiple of 128): the step's attention backward takes the chunked dK/dV
+    with its fixed-order reduction, which also applies the folded norm's row
+    scale to dV, and stores dS with a half-empty last key block and query
+    block; depth 4 (two query heads), one sequence."""
+    _, ocfg, step, p64, tok, tgt = _setup(4, 512, 2624, 1, dtype, 31, 32, "uniform")
+    _compare(ocfg, step, p64, tok, tgt, dtype)
+
+
 def test_max_vocab_ids():
     """V = 65,536: ids at the top of the 16-bit range, tiny width."""
     _, ocfg, step, p64, tok, tgt = _setup(2, 65536, 64, 2, "bf16", 21, 22, "zipf")
